@@ -1,0 +1,177 @@
+/*
+ * ssd.h: C ABI of the Mamba-2 SSD (state-space duality) chunked-scan
+ * forward on one AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  The Mamba-2 layer keeps a fixed-size state per
+ * head that every token updates (clova.ai, "Unlocking the potential of the
+ * latest GPUs: optimizing Mamba-2 kernels for the B200", section "Why
+ * optimize Mamba-2? Long context and hybrid architectures").  For each
+ * sequence s, head h (B/C group g = h / (nheads / ngroups)) and token t:
+ *
+ *   delta_t  = clamp(softplus(dt[t,h] + dt_bias[h]), dt_min, dt_max)
+ *   h_t      = exp(delta_t * A[h]) * h_{t-1} + delta_t * x[t,h,:] (outer) B[t,g,:]
+ *   y[t,h,:] = h_t . C[t,g,:]  +  D[h] * x[t,h,:]        (h_t is P x N)
+ *   h_{-1}   = initial_states[s,h] (or 0);  final_states[s,h] = h after the
+ *              sequence's last token.
+ *
+ * It does so with the chunked scan whose forward stages the pages name
+ * (aiproviderindex.com, "Mamba-2 offers a different scaling path":
+ * chunk_cumsum, state propagation and output construction; clova.ai, table
+ * "Share of compute time by kernel": _chunk_state_fwd, _state_passing_fwd,
+ * _chunk_scan_fwd), as hand-written HIP kernels:
+ *
+ *   stage 0  plan            logical chunk table (chunks never straddle a
+ *                            sequence)
+ *   stage 1  chunk_cumsum    delta and its chunk-local running sum of delta*A
+ *   stage 2  bmm_chunk       C B^T inside each chunk (lower triangle)
+ *   stage 3  chunk_state     per-chunk state from a zero start
+ *   stage 4  state_passing   sequential chain over chunks; states entering
+ *                            each chunk and the final states
+ *   stage 5  chunk_scan      decay-masked (C B^T) x  +  exp(cumsum) C . state
+ *                            +  D x, accumulated in fp32
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library allocates nothing and keeps no state between calls.  Inputs are
+ *     only read; `out`, `final_states` and `workspace` are written.  No
+ *     pointer may alias another.
+ *   - Layouts are contiguous row-major:
+ *       x, out  [batch, seqlen, nheads, headdim]        dtype
+ *       dt      [batch, seqlen, nheads]                 fp32 (before softplus)
+ *       dt_bias [nheads] fp32 (nullable: 0);  A [nheads] fp32
+ *       B, C    [batch, seqlen, ngroups, dstate]        dtype
+ *       D       [nheads] fp32 (nullable: no skip term)
+ *       initial_states, final_states [nstates, nheads, headdim, dstate] fp32,
+ *               nstates = nseq for a packed batch, else batch (nullable)
+ *       cu_seqlens [nseq + 1] int32, seq_idx [seqlen] int32 (packed batch)
+ *   - `stream` is a hipStream_t (NULL: the null stream).  Work is enqueued
+ *     asynchronously; nothing synchronises with the host and nothing is
+ *     allocated, so a call can be captured in a HIP graph.  Kernel faults
+ *     surface at the caller's next synchronisation.
+ *   - Errors: argument checks run on the host before anything is enqueued; a
+ *     non-OK status means no work was enqueued, except SSD_ERR_HIP (a launch
+ *     failed; earlier stages of that call may have been enqueued).
+ *   - Results are deterministic: no atomics, fixed reduction orders.
+ */
+#ifndef SSD_H_
+#define SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = 1,  /* a size, pointer or combination is invalid   */
+  SSD_ERR_UNSUPPORTED = 2,  /* valid, but (dtype, headdim, dstate, chunk)  */
+                            /* has no compiled kernel                      */
+  SSD_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than required     */
+  SSD_ERR_HIP = 4           /* a HIP launch or device query failed         */
+} ssd_status_t;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
+
+/* Stage bits for ssd_fwd_stages. */
+enum {
+  SSD_STAGE_PLAN = 1u << 0,
+  SSD_STAGE_CUMSUM = 1u << 1,
+  SSD_STAGE_BMM = 1u << 2,
+  SSD_STAGE_CHUNK_STATE = 1u << 3,
+  SSD_STAGE_STATE_PASSING = 1u << 4,
+  SSD_STAGE_CHUNK_SCAN = 1u << 5,
+  SSD_STAGE_ALL = 0x3Fu
+};
+
+typedef struct {
+  int64_t batch;       /* rows; must be 1 for a packed batch               */
+  int64_t seqlen;      /* tokens per row (packed batch: total tokens); >= 0 */
+  int64_t nheads;      /* H >= 1                                            */
+  int64_t headdim;     /* P                                                 */
+  int64_t dstate;      /* N                                                 */
+  int64_t ngroups;     /* G >= 1, H % G == 0                                */
+  int64_t chunk_size;  /* L                                                 */
+  int64_t nseq;        /* 0: rows are the sequences; > 0: packed batch of   */
+                       /* nseq sequences given by cu_seqlens or seq_idx     */
+  int32_t dtype;       /* ssd_dtype_t of x, B, C and out                    */
+  float dt_min;        /* clamp of delta after softplus; use 0 and +inf for */
+  float dt_max;        /* no clamp                                          */
+} ssd_problem_t;
+
+/* Byte offsets into the workspace of the stage intermediates (all 256-byte
+ * aligned) and the bound on the number of logical chunks they are sized for.
+ *   chunk_table  int32 [max_chunks][4]: first token on the flattened token
+ *                axis, valid length (<= L), sequence, index within sequence
+ *   seq_chunks   int32 [nstates + 1]: first logical chunk of each sequence;
+ *                the last entry is the number of chunks in use
+ *   delta, dA_cumsum  fp32 [max_chunks][nheads][L]
+ *   cb           fp32 [max_chunks][ngroups][L][L] (entries with s <= l of
+ *                the valid rows are defined)
+ *   chunk_states fp32 [max_chunks][nheads][headdim][dstate]
+ *   states_in    dtype [max_chunks][nheads][headdim][dstate]: state entering
+ *                each chunk                                                */
+typedef struct {
+  int64_t max_chunks;
+  size_t chunk_table, seq_chunks, delta, dA_cumsum, cb, chunk_states, states_in;
+  size_t total_bytes;
+} ssd_workspace_layout_t;
+
+/* Workspace bytes ssd_fwd needs for this problem (0 if the problem is
+ * invalid or unsupported). */
+size_t ssd_fwd_workspace_size(const ssd_problem_t* p);
+
+/* Fills *layout for this problem.  SSD_ERR_INVALID_ARG / SSD_ERR_UNSUPPORTED
+ * as for ssd_fwd. */
+ssd_status_t ssd_workspace_layout(const ssd_problem_t* p, ssd_workspace_layout_t* layout);
+
+/* 1 if (dtype, headdim, dstate, chunk_size) has compiled kernels, else 0. */
+int ssd_config_supported(int32_t dtype, int64_t headdim, int64_t dstate, int64_t chunk_size);
+
+/*
+ * The whole SSD forward: stages 0..5 above, enqueued on `stream`.
+ *
+ * x, dt, A, B, C, out are required (they may be NULL only when
+ * batch * seqlen == 0).  dt_bias, D, initial_states, final_states are
+ * optional.  A packed batch (p->nseq > 0, p->batch == 1) takes exactly one
+ * of cu_seqlens (non-decreasing, from 0 to seqlen) or seq_idx (the sequence
+ * id of each token, non-decreasing, in [0, nseq)); an unpacked problem takes
+ * neither.  Malformed packing arrays give unspecified outputs but never an
+ * access outside the given buffers.  Tokens that belong to no sequence keep
+ * whatever `out` held.
+ *
+ * The workspace (ssd_fwd_workspace_size bytes, 256-byte aligned) holds the
+ * intermediates laid out as ssd_workspace_layout reports; its prior contents
+ * do not matter.
+ */
+ssd_status_t ssd_fwd(const ssd_problem_t* p,
+                     const void* x, const float* dt, const float* dt_bias,
+                     const float* A, const void* B, const void* C, const float* D,
+                     const float* initial_states,
+                     const int32_t* cu_seqlens, const int32_t* seq_idx,
+                     void* out, float* final_states,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * As ssd_fwd, but enqueues only the stages whose SSD_STAGE_* bit is set in
+ * `stages`, in stage order, reading the intermediates earlier stages left in
+ * the workspace.  Used to time and test stages one by one.
+ */
+ssd_status_t ssd_fwd_stages(const ssd_problem_t* p,
+                            const void* x, const float* dt, const float* dt_bias,
+                            const float* A, const void* B, const void* C, const float* D,
+                            const float* initial_states,
+                            const int32_t* cu_seqlens, const int32_t* seq_idx,
+                            void* out, float* final_states,
+                            void* workspace, size_t workspace_bytes,
+                            uint32_t stages, void* stream);
+
+/* Static description of a status code. */
+const char* ssd_status_string(ssd_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H_ */

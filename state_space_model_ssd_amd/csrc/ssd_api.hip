@@ -1,0 +1,207 @@
+// C ABI of the SSD forward (declared in include/ssd.h): host-side argument
+// checks, workspace layout, and the stage launches on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/ssd.h"
+#include "ssd_kernels.h"
+
+namespace ssd {
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+typedef hipError_t (*launch_fn)(const FwdArgs&, hipStream_t);
+
+struct Kernels {
+  int32_t dtype;
+  int64_t P, N, L;
+  launch_fn bmm, chunk_state, state_passing, chunk_scan;
+};
+
+template <typename T> constexpr int32_t dtype_of();
+template <> constexpr int32_t dtype_of<float>() { return SSD_F32; }
+template <> constexpr int32_t dtype_of<bf16>() { return SSD_BF16; }
+
+#define SSD_ROW(T, P, N, L)                                                              \
+  {dtype_of<T>(), P, N, L, &launch_bmm_chunk<T, N, L>, &launch_chunk_state<T, P, N, L>, \
+   &launch_state_passing<T>, &launch_chunk_scan<T, P, N, L>},
+const Kernels kKernels[] = {SSD_FOR_EACH_CONFIG(SSD_ROW)};
+#undef SSD_ROW
+
+const Kernels* find_kernels(int32_t dtype, int64_t P, int64_t N, int64_t L) {
+  for (const Kernels& k : kKernels)
+    if (k.dtype == dtype && k.P == P && k.N == N && k.L == L) return &k;
+  return nullptr;
+}
+
+size_t elem_size(int32_t dtype) { return dtype == SSD_BF16 ? 2 : 4; }
+
+// Shape checks that do not look at pointers.
+ssd_status_t check_problem(const ssd_problem_t* p) {
+  if (!p) return SSD_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->seqlen < 0 || p->nheads < 1 || p->headdim < 1 || p->dstate < 1 ||
+      p->ngroups < 1 || p->chunk_size < 1 || p->nseq < 0)
+    return SSD_ERR_INVALID_ARG;
+  if (p->nheads % p->ngroups != 0) return SSD_ERR_INVALID_ARG;
+  if (p->dtype != SSD_F32 && p->dtype != SSD_BF16) return SSD_ERR_INVALID_ARG;
+  if (p->nseq > 0 && p->batch != 1) return SSD_ERR_INVALID_ARG;
+  if (isnan(p->dt_min) || isnan(p->dt_max) || p->dt_min > p->dt_max) return SSD_ERR_INVALID_ARG;
+  // int32 token and chunk indices on the device; grid limits
+  if (p->batch * p->seqlen > (int64_t)INT32_MAX / 2) return SSD_ERR_UNSUPPORTED;
+  if (p->nheads > 65535) return SSD_ERR_UNSUPPORTED;
+  const int64_t nstates = p->nseq > 0 ? p->nseq : p->batch;
+  if (nstates > 65535) return SSD_ERR_UNSUPPORTED;
+  if (!find_kernels(p->dtype, p->headdim, p->dstate, p->chunk_size)) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+int64_t max_chunks_of(const ssd_problem_t* p) {
+  const int64_t L = p->chunk_size;
+  if (p->nseq > 0) {
+    // sum_s ceil(len_s / L) <= (T + nseq (L - 1)) / L, and never more than
+    // one chunk per token
+    const int64_t bound = (p->seqlen + p->nseq * (L - 1)) / L;
+    return bound < p->seqlen ? bound : p->seqlen;
+  }
+  return p->batch * ((p->seqlen + L - 1) / L);
+}
+
+void layout_of(const ssd_problem_t* p, ssd_workspace_layout_t* w) {
+  const int64_t mc = max_chunks_of(p);
+  const int64_t nstates = p->nseq > 0 ? p->nseq : p->batch;
+  const size_t H = p->nheads, L = p->chunk_size, PN = p->headdim * p->dstate;
+  size_t off = 0;
+  w->max_chunks = mc;
+  w->chunk_table = off;  off = align_up(off + sizeof(int32_t) * 4 * (size_t)mc);
+  w->seq_chunks = off;   off = align_up(off + sizeof(int32_t) * (size_t)(nstates + 1));
+  w->delta = off;        off = align_up(off + sizeof(float) * (size_t)mc * H * L);
+  w->dA_cumsum = off;    off = align_up(off + sizeof(float) * (size_t)mc * H * L);
+  w->cb = off;           off = align_up(off + sizeof(float) * (size_t)mc * p->ngroups * L * L);
+  w->chunk_states = off; off = align_up(off + sizeof(float) * (size_t)mc * H * PN);
+  w->states_in = off;    off = align_up(off + elem_size(p->dtype) * (size_t)mc * H * PN);
+  w->total_bytes = off;
+}
+
+ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias,
+                 const float* A, const void* B, const void* C, const float* D,
+                 const float* initial_states, const int32_t* cu_seqlens, const int32_t* seq_idx,
+                 void* out, float* final_states, void* workspace, size_t workspace_bytes,
+                 uint32_t stages, void* stream) {
+  ssd_status_t st = check_problem(p);
+  if (st != SSD_OK) return st;
+  if (stages & ~(uint32_t)SSD_STAGE_ALL) return SSD_ERR_INVALID_ARG;
+  const bool packed = p->nseq > 0;
+  if (packed && ((cu_seqlens != nullptr) + (seq_idx != nullptr)) != 1) return SSD_ERR_INVALID_ARG;
+  if (!packed && (cu_seqlens || seq_idx)) return SSD_ERR_INVALID_ARG;
+  const int64_t tokens = p->batch * p->seqlen;
+  if (tokens > 0 && (!x || !dt || !A || !B || !C || !out)) return SSD_ERR_INVALID_ARG;
+
+  ssd_workspace_layout_t w;
+  layout_of(p, &w);
+  if (!workspace || workspace_bytes < w.total_bytes) return SSD_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
+  const Kernels* k = find_kernels(p->dtype, p->headdim, p->dstate, p->chunk_size);
+
+  FwdArgs a;
+  a.batch = (int)p->batch;
+  a.seqlen = (int)p->seqlen;
+  a.H = (int)p->nheads;
+  a.P = (int)p->headdim;
+  a.N = (int)p->dstate;
+  a.G = (int)p->ngroups;
+  a.L = (int)p->chunk_size;
+  a.nstates = (int)(packed ? p->nseq : p->batch);
+  a.max_chunks = (int)w.max_chunks;
+  a.nc_row = (int)((p->seqlen + p->chunk_size - 1) / p->chunk_size);
+  a.packed = packed;
+  a.dt_min = p->dt_min;
+  a.dt_max = p->dt_max;
+  a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.D = D;
+  a.init = initial_states;
+  a.cu_seqlens = cu_seqlens;
+  a.seq_idx = seq_idx;
+  a.out = out;
+  a.final_states = final_states;
+  char* base = static_cast<char*>(workspace);
+  a.table = reinterpret_cast<int4*>(base + w.chunk_table);
+  a.seq_chunks = reinterpret_cast<int*>(base + w.seq_chunks);
+  a.delta = reinterpret_cast<float*>(base + w.delta);
+  a.dAcs = reinterpret_cast<float*>(base + w.dA_cumsum);
+  a.cb = reinterpret_cast<float*>(base + w.cb);
+  a.chunk_states = reinterpret_cast<float*>(base + w.chunk_states);
+  a.states_in = base + w.states_in;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  struct Step { uint32_t bit; launch_fn fn; };
+  const Step steps[] = {
+      {SSD_STAGE_PLAN, &launch_plan},
+      {SSD_STAGE_CUMSUM, &launch_chunk_cumsum},
+      {SSD_STAGE_BMM, k->bmm},
+      {SSD_STAGE_CHUNK_STATE, k->chunk_state},
+      {SSD_STAGE_STATE_PASSING, k->state_passing},
+      {SSD_STAGE_CHUNK_SCAN, k->chunk_scan},
+  };
+  for (const Step& stp : steps) {
+    if (!(stages & stp.bit)) continue;
+    if (stp.fn(a, s) != hipSuccess) return SSD_ERR_HIP;
+  }
+  return SSD_OK;
+}
+
+}  // namespace
+}  // namespace ssd
+
+extern "C" {
+
+size_t ssd_fwd_workspace_size(const ssd_problem_t* p) {
+  if (ssd::check_problem(p) != SSD_OK) return 0;
+  ssd_workspace_layout_t w;
+  ssd::layout_of(p, &w);
+  return w.total_bytes;
+}
+
+ssd_status_t ssd_workspace_layout(const ssd_problem_t* p, ssd_workspace_layout_t* layout) {
+  if (!layout) return SSD_ERR_INVALID_ARG;
+  ssd_status_t st = ssd::check_problem(p);
+  if (st != SSD_OK) return st;
+  ssd::layout_of(p, layout);
+  return SSD_OK;
+}
+
+int ssd_config_supported(int32_t dtype, int64_t headdim, int64_t dstate, int64_t chunk_size) {
+  return ssd::find_kernels(dtype, headdim, dstate, chunk_size) != nullptr;
+}
+
+ssd_status_t ssd_fwd(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias,
+                     const float* A, const void* B, const void* C, const float* D,
+                     const float* initial_states, const int32_t* cu_seqlens,
+                     const int32_t* seq_idx, void* out, float* final_states, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return ssd::run(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, out,
+                  final_states, workspace, workspace_bytes, SSD_STAGE_ALL, stream);
+}
+
+ssd_status_t ssd_fwd_stages(const ssd_problem_t* p, const void* x, const float* dt,
+                            const float* dt_bias, const float* A, const void* B, const void* C,
+                            const float* D, const float* initial_states,
+                            const int32_t* cu_seqlens, const int32_t* seq_idx, void* out,
+                            float* final_states, void* workspace, size_t workspace_bytes,
+                            uint32_t stages, void* stream) {
+  return ssd::run(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, out,
+                  final_states, workspace, workspace_bytes, stages, stream);
+}
+
+const char* ssd_status_string(ssd_status_t s) {
+  switch (s) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_INVALID_ARG: return "invalid argument";
+    case SSD_ERR_UNSUPPORTED: return "unsupported (dtype, headdim, dstate, chunk_size) or size";
+    case SSD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case SSD_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// Internal device-side definitions shared by the SSD forward kernels
+// (gfx950 / CDNA4 only: 64-wide wavefronts, MFMA 16x16 tiles, LDS).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+using bf16 = __bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Logical chunks.  A chunk never straddles a sequence: sequence s owns
+// ceil(len_s / L) chunks that start at its first token, so only its last
+// chunk can be short.  For unpacked rows the map is arithmetic (row r owns
+// chunks [r*nc_row, (r+1)*nc_row)); for a packed batch it is the table the
+// plan kernels write into the workspace.
+// ---------------------------------------------------------------------------
+struct ChunkDesc {
+  int start;  // first token on the flattened (batch * seqlen) token axis
+  int len;    // valid tokens, 0 for an unused table slot
+  int seq;    // sequence (row, or packed sequence)
+  int idx;    // index of the chunk within its sequence
+};
+
+struct ChunkMap {
+  const int4* table;       // packed batch: [max_chunks]; nullptr for rows
+  const int* seq_chunks;   // packed batch: [nstates + 1]
+  int seqlen;              // tokens per row (rows mode)
+  int nc_row;              // chunks per row (rows mode)
+  int L;
+
+  __device__ __forceinline__ ChunkDesc desc(int j) const {
+    ChunkDesc d;
+    if (table) {
+      int4 v = table[j];
+      d.start = v.x; d.len = v.y; d.seq = v.z; d.idx = v.w;
+    } else {
+      int r = j / nc_row, c = j - r * nc_row;
+      d.start = r * seqlen + c * L;
+      d.len = min(L, seqlen - c * L);
+      d.seq = r;
+      d.idx = c;
+    }
+    return d;
+  }
+  // [first, last) logical chunks of sequence s
+  __device__ __forceinline__ int2 seq_range(int s) const {
+    if (table) return make_int2(seq_chunks[s], seq_chunks[s + 1]);
+    return make_int2(s * nc_row, (s + 1) * nc_row);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Element types.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
+
+// exp on the fp32 path keeps the accurate library routine; the bf16 path uses
+// the hardware exp2 (its relative error is far below bf16's 2^-9).
+template <typename T> __device__ __forceinline__ float fexp(float v);
+template <> __device__ __forceinline__ float fexp<float>(float v) { return expf(v); }
+template <> __device__ __forceinline__ float fexp<bf16>(float v) { return __expf(v); }
+
+// ---------------------------------------------------------------------------
+// MFMA 16x16 tiles, fp32 accumulation.
+//   A operand: lane i holds A[i % 16][kb + KPL*(i/16) + e], e < KPL
+//   B operand: lane i holds B[kb + KPL*(i/16) + e][i % 16]
+//   C/D:       lane i holds D[4*(i/16) + r][i % 16], r < 4
+// fp32 inputs use v_mfma_f32_16x16x4_f32 (K = 4, one value per lane),
+// bf16 inputs the gfx950 v_mfma_f32_16x16x32_bf16 (K = 32, eight per lane).
+// ---------------------------------------------------------------------------
+template <typename T> struct Mfma;
+
+template <> struct Mfma<float> {
+  static constexpr int K = 4;
+  static constexpr int KPL = 1;
+  using frag = float;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const float* p) { return *p; }
+  __device__ __forceinline__ static frag pack(const float* v) { return v[0]; }
+};
+
+template <> struct Mfma<bf16> {
+  static constexpr int K = 32;
+  static constexpr int KPL = 8;
+  using frag = bf16x8;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+  __device__ __forceinline__ static frag pack(const float* v) {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = static_cast<bf16>(v[e]);
+    return f;
+  }
+};
+
+// 16-byte global vector of T
+template <typename T> struct Vec16 {
+  static constexpr int n = 16 / sizeof(T);
+};
+
+__device__ __forceinline__ void load_f32(const float* p, float* v, int n) {
+  for (int i = 0; i < n; ++i) v[i] = p[i];
+}
+
+// Load 16 bytes (4 fp32 or 8 bf16) as fp32 values; zeros when !valid.
+__device__ __forceinline__ void load16_as_f32(const float* p, bool valid, float* v) {
+  if (valid) {
+    float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  } else {
+    v[0] = v[1] = v[2] = v[3] = 0.f;
+  }
+}
+__device__ __forceinline__ void load16_as_f32(const bf16* p, bool valid, float* v) {
+  if (valid) {
+    bf16x8 q = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(q[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  }
+}
+
+// Raw 16-byte copy helpers.
+__device__ __forceinline__ uint4 load16(const void* p, bool valid) {
+  if (valid) return *reinterpret_cast<const uint4*>(p);
+  return make_uint4(0, 0, 0, 0);
+}
+
+}  // namespace ssd

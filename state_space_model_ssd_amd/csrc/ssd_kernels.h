@@ -1,0 +1,79 @@
+// Host-side launch interface of the SSD forward stages (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssd_common.h"
+
+namespace ssd {
+
+// Everything one forward call needs: shapes, caller buffers, workspace.
+struct FwdArgs {
+  int batch, seqlen, H, P, N, G, L;
+  int nstates;      // sequences: rows, or packed sequences
+  int max_chunks;   // logical chunks the workspace is sized for
+  int nc_row;       // chunks per row (rows mode)
+  bool packed;
+  float dt_min, dt_max;
+
+  const void* x;
+  const float* dt;
+  const float* dt_bias;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const float* init;
+  const int32_t* cu_seqlens;
+  const int32_t* seq_idx;
+  void* out;
+  float* final_states;
+
+  int4* table;
+  int* seq_chunks;
+  float* delta;
+  float* dAcs;
+  float* cb;
+  float* chunk_states;
+  void* states_in;
+
+  ChunkMap cmap() const {
+    ChunkMap m;
+    m.table = packed ? table : nullptr;
+    m.seq_chunks = packed ? seq_chunks : nullptr;
+    m.seqlen = seqlen;
+    m.nc_row = nc_row;
+    m.L = L;
+    return m;
+  }
+};
+
+// Stage 0: logical chunk table of a packed batch.
+hipError_t launch_plan(const FwdArgs& a, hipStream_t s);
+// Stage 1: delta and its chunk-local cumulative sum times A.
+hipError_t launch_chunk_cumsum(const FwdArgs& a, hipStream_t s);
+// Stage 2: C B^T per chunk and group.
+template <typename T, int N, int L>
+hipError_t launch_bmm_chunk(const FwdArgs& a, hipStream_t s);
+// Stage 3: per-chunk states.
+template <typename T, int P, int N, int L>
+hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t s);
+// Stage 4: inter-chunk chain.
+template <typename T>
+hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s);
+// Stage 5: outputs.
+template <typename T, int P, int N, int L>
+hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s);
+
+}  // namespace ssd
+
+// (dtype, headdim, dstate, chunk_size) combinations with compiled kernels.
+#define SSD_FOR_EACH_CONFIG(X) \
+  X(float, 32, 16, 64)         \
+  X(float, 64, 128, 64)        \
+  X(float, 64, 128, 256)       \
+  X(bf16, 32, 32, 64)          \
+  X(bf16, 64, 128, 64)         \
+  X(bf16, 64, 128, 128)        \
+  X(bf16, 64, 128, 256)
