@@ -48,12 +48,12 @@ def algorithmic_work(prob, nchunks):
     work = {
         "plan": (0, 0),
         "chunk_cumsum": (4 * tok * H + 8 * nchunks * H * L, 0),
-        "bmm_chunk": (2 * e * tok * G * N + 4 * nchunks * G * tri, 2 * N * tri * nchunks * G),
+        "bmm_chunk": (2 * e * tok * G * N + e * nchunks * G * tri, 2 * N * tri * nchunks * G),
         "chunk_state": (e * tok * H * P + e * tok * G * N + 8 * nchunks * H * L
                         + 4 * nchunks * H * P * N, 2 * L * P * N * nchunks * H),
         "state_passing": ((4 + e) * nchunks * H * P * N + 4 * (1 + has_init) * nst * H * P * N,
                           2 * P * N * nchunks * H),
-        "chunk_scan": (2 * e * tok * H * P + e * tok * G * N + 4 * nchunks * G * tri
+        "chunk_scan": (2 * e * tok * H * P + e * tok * G * N + e * nchunks * G * tri
                        + 8 * nchunks * H * L + e * nchunks * H * P * N,
                        (2 * P * tri + 2 * L * N * P) * nchunks * H),
     }
@@ -85,6 +85,9 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, copy a buffer of MIB MiB three times (a plain copy "
+                         "kernel of known size, for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
@@ -192,6 +195,15 @@ def main():
                 "unit": "GB/s", "frac": round(ds["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
                 "launch_us": ds["us"], "alg_bytes_per_launch": ds["alg_bytes"]}
     total_bytes = sum(v[0] for v in work.values())
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # --- CPU baseline: the fp64 oracle on this host's cores, same workload
     cpu = None

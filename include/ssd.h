@@ -107,8 +107,9 @@ typedef struct {
  *   seq_chunks   int32 [nstates + 1]: first logical chunk of each sequence;
  *                the last entry is the number of chunks in use
  *   delta, dA_cumsum  fp32 [max_chunks][nheads][L]
- *   cb           fp32 [max_chunks][ngroups][L][L] (entries with s <= l of
- *                the valid rows are defined)
+ *   cb           dtype [max_chunks][ngroups][L][L] (entries with s <= l of
+ *                the valid rows are defined; fp32 accumulation, stored in
+ *                the dtype of x)
  *   chunk_states fp32 [max_chunks][nheads][headdim][dstate]
  *   states_in    dtype [max_chunks][nheads][headdim][dstate]: state entering
  *                each chunk                                                */

@@ -214,8 +214,8 @@ def _run(x, dt, A, B, C, chunk_size, D, dt_bias, init, cu, sidx, nseq, dt_min, d
 def intermediates(workspace: torch.Tensor, prob: ProblemC) -> dict:
     """Views of the stage intermediates inside a workspace (layout of
     ssd_workspace_layout): chunk_table (mc,4), seq_chunks (nstates+1),
-    delta/dA_cumsum (mc,H,L), cb (mc,G,L,L), chunk_states (mc,H,P,N) fp32,
-    states_in (mc,H,P,N) in the problem dtype."""
+    delta/dA_cumsum (mc,H,L), chunk_states (mc,H,P,N) fp32, cb (mc,G,L,L)
+    and states_in (mc,H,P,N) in the problem dtype."""
     lay = workspace_layout(prob)
     mc, H, L, G = lay.max_chunks, prob.nheads, prob.chunk_size, prob.ngroups
     P, N = prob.headdim, prob.dstate
@@ -235,7 +235,7 @@ def intermediates(workspace: torch.Tensor, prob: ProblemC) -> dict:
         seq_chunks=view(lay.seq_chunks, torch.int32, (nstates + 1,)),
         delta=view(lay.delta, torch.float32, (mc, H, L)),
         dA_cumsum=view(lay.dA_cumsum, torch.float32, (mc, H, L)),
-        cb=view(lay.cb, torch.float32, (mc, G, L, L)),
+        cb=view(lay.cb, sdt, (mc, G, L, L)),
         chunk_states=view(lay.chunk_states, torch.float32, (mc, H, P, N)),
         states_in=view(lay.states_in, sdt, (mc, H, P, N)),
     )

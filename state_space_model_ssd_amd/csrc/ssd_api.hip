@@ -3,7 +3,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "../../include/ssd.h"
+#include "ssd.h"
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -78,7 +78,7 @@ void layout_of(const ssd_problem_t* p, ssd_workspace_layout_t* w) {
   w->seq_chunks = off;   off = align_up(off + sizeof(int32_t) * (size_t)(nstates + 1));
   w->delta = off;        off = align_up(off + sizeof(float) * (size_t)mc * H * L);
   w->dA_cumsum = off;    off = align_up(off + sizeof(float) * (size_t)mc * H * L);
-  w->cb = off;           off = align_up(off + sizeof(float) * (size_t)mc * p->ngroups * L * L);
+  w->cb = off;           off = align_up(off + elem_size(p->dtype) * (size_t)mc * p->ngroups * L * L);
   w->chunk_states = off; off = align_up(off + sizeof(float) * (size_t)mc * H * PN);
   w->states_in = off;    off = align_up(off + elem_size(p->dtype) * (size_t)mc * H * PN);
   w->total_bytes = off;
@@ -129,7 +129,7 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
   a.seq_chunks = reinterpret_cast<int*>(base + w.seq_chunks);
   a.delta = reinterpret_cast<float*>(base + w.delta);
   a.dAcs = reinterpret_cast<float*>(base + w.dA_cumsum);
-  a.cb = reinterpret_cast<float*>(base + w.cb);
+  a.cb = base + w.cb;
   a.chunk_states = reinterpret_cast<float*>(base + w.chunk_states);
   a.states_in = base + w.states_in;
 

@@ -1,5 +1,5 @@
 // Stage 2, bmm_chunk: CB[j,g,l,s] = sum_n C[t0+l,g,n] * B[t0+s,g,n] inside
-// each logical chunk j (the intra-chunk C B^T that the output construction
+// each logical chunk j, accumulated in fp32 and stored in the input dtype (the intra-chunk C B^T that the output construction
 // of the chunked scan consumes; aiproviderindex.com, "Mamba-2 offers a
 // different scaling path").  Only 64x64 tiles on or below the diagonal are
 // computed: the output stage never reads s > l.
@@ -17,7 +17,7 @@ namespace {
 template <typename T, int N, int L>
 __global__ __launch_bounds__(256) void bmm_chunk_kernel(ChunkMap cm, const T* __restrict__ C,
                                                         const T* __restrict__ B, int G,
-                                                        float* __restrict__ cb) {
+                                                        T* __restrict__ cb) {
   using M = Mfma<T>;
   constexpr int V = 16 / sizeof(T);   // elements per 16-byte vector
   constexpr int LD = N + V;           // padded LDS row
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void bmm_chunk_kernel(ChunkMap cm, const T* __
       for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = M::mma(a[mi], b[ni], acc[mi][ni]);
   }
 
-  float* out = cb + ((int64_t)j * G + g) * L * L;
+  T* out = cb + ((int64_t)j * G + g) * L * L;
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void bmm_chunk_kernel(ChunkMap cm, const T* __
       for (int r = 0; r < 4; ++r) {
         const int row = ti * 64 + wr + mi * 16 + (lane >> 4) * 4 + r;
         const int col = tj * 64 + wc + ni * 16 + lr;
-        out[(int64_t)row * L + col] = acc[mi][ni][r];
+        out[(int64_t)row * L + col] = from_f32<T>(acc[mi][ni][r]);
       }
 }
 
@@ -88,7 +88,7 @@ hipError_t launch_bmm_chunk(const FwdArgs& a, hipStream_t s) {
   constexpr int nt = L / 64;
   dim3 grid(a.max_chunks * a.G, nt * (nt + 1) / 2);
   hipLaunchKernelGGL((bmm_chunk_kernel<T, N, L>), grid, dim3(256), 0, s, a.cmap(),
-                     (const T*)a.C, (const T*)a.B, a.G, a.cb);
+                     (const T*)a.C, (const T*)a.B, a.G, (T*)a.cb);
   return hipGetLastError();
 }
 

@@ -5,11 +5,17 @@
 //   w[l]       = exp(dAcs[len-1] - dAcs[l]) * delta[l].
 // A P x N result with a K = chunk-length contraction over tokens: MFMA.
 //
-// One workgroup (4 waves) per (chunk, head).  Tokens are the contraction
-// index, and both operands arrive token-major from HBM, so each 64-token
-// slice is transposed on its way into LDS (k contiguous per row, 16-byte
-// padded rows): x scaled by w[l] and rounded once to the operand type, B
-// as is.  The waves split the P x N output into rectangles of 16x16 tiles.
+// One workgroup (4 waves) per (chunk, head); the waves split the P x N
+// output into rectangles of 16x16 tiles.  Tokens are the contraction index
+// and both operands arrive token-major from HBM.
+//  - bf16 kernel (production): each 64-token slice of x (scaled by w[l] and
+//    rounded once to bf16) and of B is staged in LDS in its natural
+//    token-major layout with coalesced 16-byte accesses, and the MFMA A and B
+//    operands come out of it through the gfx950 LDS transpose read.  The next
+//    slice is loaded into registers while the current one is multiplied.
+//    Workgroups of one chunk share an XCD, so B stays in its L2.
+//  - fp32 kernel (exactness path): each slice is transposed on its way into
+//    LDS (k contiguous per row, 16-byte padded rows).
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -122,14 +128,138 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(
       }
 }
 
+
+// ------------------------------------------------------------- bf16 kernel
+template <int P, int N, int L>
+__global__ __launch_bounds__(256) void chunk_state_bf16_kernel(
+    ChunkMap cm, int nslots, const bf16* __restrict__ x, const bf16* __restrict__ B,
+    const float* __restrict__ delta, const float* __restrict__ dAcs, int H, int G,
+    float* __restrict__ S) {
+  static_assert(L % 64 == 0 && P % 16 == 0 && N % 16 == 0, "tile shape");
+  constexpr int KS = 64;                  // tokens per slice
+  constexpr int XP = P + 8, BP = N + 8;   // LDS row pitches (elements)
+  constexpr int XC = P / 8, BC = N / 8;   // 16-byte pieces per row
+  constexpr int XU = (KS * XC + 255) / 256, BU = (KS * BC + 255) / 256;
+  constexpr int PT = P / 16, NT = N / 16;
+  constexpr int WN = NT < 4 ? NT : 4;
+  constexpr int WP = (4 / WN) < PT ? (4 / WN) : PT;
+  constexpr int TP = PT / WP, TN = NT / WN;
+  static_assert(PT % WP == 0 && NT % WN == 0, "tile split");
+  __shared__ __align__(16) bf16 xs[KS * XP];
+  __shared__ __align__(16) bf16 bs[KS * BP];
+  __shared__ float wl[L];
+
+  const int2 jh = xcd_chunk_head(blockIdx.x, H);
+  const int j = jh.x, h = jh.y;
+  if (j >= nslots) return;
+  const ChunkDesc d = cm.desc(j);
+  if (d.len <= 0) return;
+  const int g = h / (H / G);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  {
+    const float* dA = dAcs + ((int64_t)j * H + h) * L;
+    const float* dl = delta + ((int64_t)j * H + h) * L;
+    const float last = dA[d.len - 1] * kLog2e;
+    for (int l = tid; l < L; l += 256)
+      wl[l] = (l < d.len) ? exp2_fast(last - dA[l] * kLog2e) * dl[l] : 0.f;
+  }
+
+  uint4 xr[XU], br[BU];
+  auto fetch = [&](int l0) {
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int i = tid + 256 * u, r = i / XC, c = i - (i / XC) * XC;
+      xr[u] = make_uint4(0, 0, 0, 0);
+      if (i < KS * XC && l0 + r < d.len)
+        xr[u] = *reinterpret_cast<const uint4*>(x + ((int64_t)(d.start + l0 + r) * H + h) * P + c * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      const int i = tid + 256 * u, r = i / BC, c = i - (i / BC) * BC;
+      br[u] = make_uint4(0, 0, 0, 0);
+      if (i < KS * BC && l0 + r < d.len)
+        br[u] = *reinterpret_cast<const uint4*>(B + ((int64_t)(d.start + l0 + r) * G + g) * N + c * 8);
+    }
+  };
+
+  const int wp = w / WN, wn = w - (w / WN) * WN;
+  const bool active = w < WP * WN;
+  f32x4 acc[TP][TN];
+#pragma unroll
+  for (int a = 0; a < TP; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsl = (d.len + KS - 1) / KS;
+  fetch(0);
+  __syncthreads();                        // wl ready
+  for (int sl = 0; sl < nsl; ++sl) {
+    const int l0 = sl * KS;
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int i = tid + 256 * u, r = i / XC, c = i - (i / XC) * XC;
+      if (i < KS * XC) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, xr[u]);
+        const float wv = wl[l0 + r];
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = static_cast<bf16>(static_cast<float>(v[e]) * wv);
+        *reinterpret_cast<bf16x8*>(&xs[r * XP + c * 8]) = o;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      const int i = tid + 256 * u, r = i / BC, c = i - (i / BC) * BC;
+      if (i < KS * BC) *reinterpret_cast<uint4*>(&bs[r * BP + c * 8]) = br[u];
+    }
+    __syncthreads();
+    if (sl + 1 < nsl) fetch(l0 + KS);     // in flight while this slice multiplies
+    if (active) {
+#pragma unroll
+      for (int k0 = 0; k0 < KS; k0 += 32) {
+        bf16x8 fa[TP], fb[TN];
+#pragma unroll
+        for (int a = 0; a < TP; ++a) fa[a] = lds_operand_kmajor(xs, XP, k0, 16 * (wp * TP + a), lane);
+#pragma unroll
+        for (int b = 0; b < TN; ++b) fb[b] = lds_operand_kmajor(bs, BP, k0, 16 * (wn * TN + b), lane);
+#pragma unroll
+        for (int a = 0; a < TP; ++a)
+#pragma unroll
+          for (int b = 0; b < TN; ++b) acc[a][b] = Mfma<bf16>::mma(fa[a], fb[b], acc[a][b]);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!active) return;
+  float* out = S + ((int64_t)j * H + h) * P * N;
+  const int lr = lane & 15;
+#pragma unroll
+  for (int a = 0; a < TP; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = 16 * (wp * TP + a) + (lane >> 4) * 4 + r;
+        const int n = 16 * (wn * TN + b) + lr;
+        out[(int64_t)p * N + n] = acc[a][b][r];
+      }
+}
+
 }  // namespace
 
 template <typename T, int P, int N, int L>
 hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t s) {
   if (a.max_chunks <= 0) return hipSuccess;
-  dim3 grid(a.max_chunks, a.H);
-  hipLaunchKernelGGL((chunk_state_kernel<T, P, N, L>), grid, dim3(256), 0, s, a.cmap(),
-                     (const T*)a.x, (const T*)a.B, a.delta, a.dAcs, a.H, a.G, a.chunk_states);
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, L>), dim3(xcd_grid(a.max_chunks, a.H)),
+                       dim3(256), 0, s, a.cmap(), a.max_chunks, (const bf16*)a.x,
+                       (const bf16*)a.B, a.delta, a.dAcs, a.H, a.G, a.chunk_states);
+  } else {
+    dim3 grid(a.max_chunks, a.H);
+    hipLaunchKernelGGL((chunk_state_kernel<T, P, N, L>), grid, dim3(256), 0, s, a.cmap(),
+                       (const T*)a.x, (const T*)a.B, a.delta, a.dAcs, a.H, a.G, a.chunk_states);
+  }
   return hipGetLastError();
 }
 

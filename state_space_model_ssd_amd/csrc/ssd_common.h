@@ -147,4 +147,48 @@ __device__ __forceinline__ uint4 load16(const void* p, bool valid) {
   return make_uint4(0, 0, 0, 0);
 }
 
+
+// ---------------------------------------------------------------------------
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j receives elements j, 16+j, 32+j, 48+j of the group's
+// concatenated 8-byte reads.  So if lane m of the group reads 4 bf16 at
+// row (k0 + m/4), columns (c0 + 4*(m%4)) of a row-major [k][c] LDS tile, lane
+// j gets column c0 + j of rows k0..k0+3: four consecutive k for one column,
+// which is how the MFMA operands hold their k values.  Two such reads (rows
+// k0.. and k0+4..) fill one 8-value bf16 operand.
+// ---------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ i16x4 lds_tr16_b64(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)((__attribute__((address_space(3))) char*)(p)));
+}
+
+// MFMA operand (8 consecutive k of column c0 + lane%16, k starting at
+// k0 + 8*(lane/16)) from a row-major [k][c] bf16 LDS tile with row pitch
+// `pitch` elements.
+__device__ __forceinline__ bf16x8 lds_operand_kmajor(const bf16* tile, int pitch, int k0, int c0,
+                                                     int lane) {
+  const int m = lane & 15, kg = lane >> 4;
+  const bf16* p = tile + (k0 + 8 * kg + (m >> 2)) * pitch + c0 + 4 * (m & 3);
+  const i16x4 lo = lds_tr16_b64(p);
+  const i16x4 hi = lds_tr16_b64(p + 4 * pitch);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Workgroup id -> (chunk slot, head) so that every head of one chunk runs on
+// the same XCD (the hardware deals workgroups to the 8 XCDs round-robin), where
+// the chunk's shared B, C and CB tiles stay in that XCD's L2.
+__device__ __forceinline__ int2 xcd_chunk_head(int b, int H) {
+  const int x8 = b & 7, rest = b >> 3;
+  return make_int2(8 * (rest / H) + x8, rest % H);
+}
+inline int xcd_grid(int max_chunks, int H) { return ((max_chunks + 7) / 8) * 8 * H; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_fast(float v) { return __builtin_amdgcn_exp2f(v); }
+
 }  // namespace ssd

@@ -34,7 +34,7 @@ struct FwdArgs {
   int* seq_chunks;
   float* delta;
   float* dAcs;
-  float* cb;
+  void* cb;             // dtype of x
   float* chunk_states;
   void* states_in;
 

@@ -52,7 +52,7 @@ def _expected_layout(b, T, H, P, N, G, L, nseq, esize):
     al = lambda v: (v + 255) // 256 * 256
     mc = (min((T + nseq * (L - 1)) // L, T) if nseq else b * ((T + L - 1) // L))
     nst = nseq if nseq else b
-    sizes = [16 * mc, 4 * (nst + 1), 4 * mc * H * L, 4 * mc * H * L, 4 * mc * G * L * L,
+    sizes = [16 * mc, 4 * (nst + 1), 4 * mc * H * L, 4 * mc * H * L, esize * mc * G * L * L,
              4 * mc * H * P * N, esize * mc * H * P * N]
     offs, off = [], 0
     for s in sizes:

@@ -82,9 +82,11 @@ def test_bmm_stage(run):
         for g in range(prob.ngroups):
             got = cb[c, g, :n, :n][tri]
             want = ref["CB"][c, g, :n, :n][tri]
-            # fp32 accumulation of exact products: |err| <= ~N eps sum|c||b|
+            # fp32 accumulation of exact products: |err| <= ~N eps sum|c||b|,
+            # plus one rounding to the stored dtype (bf16: 2^-8 relative)
             scale = (Cf[t0:t0 + n, g] @ Bf[t0:t0 + n, g].T)[tri]
-            assert np.max(np.abs(got - want) / scale) < 2e-6
+            store = 0.0 if prob.dtype == "f32" else 2.0 ** -8
+            assert np.max(np.abs(got - want) / (2e-6 * scale + store * np.abs(want) + 1e-30)) <= 1.0
 
 
 def test_chunk_state_stage(run):
