@@ -60,6 +60,32 @@ def algorithmic_work(prob, nchunks):
     return work
 
 
+STAGE_SOURCE = {"plan": "ssd_prep.hip", "chunk_cumsum": "ssd_prep.hip",
+                "bmm_chunk": "ssd_bmm.hip", "chunk_state": "ssd_chunk_state.hip",
+                "state_passing": "ssd_state_passing.hip", "chunk_scan": "ssd_chunk_scan.hip"}
+
+
+def measured_traffic(kernel: str, workload_tag: str):
+    """HBM bytes per launch from the committed counter summary
+    profiles/<kernel>_<workload>_traffic.md (FETCH_SIZE and WRITE_SIZE passes,
+    scaled by a plain copy of known size), or None when there is none or the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", " ")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "state_space_model_ssd_amd", "csrc", STAGE_SOURCE[kernel])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if fields.get("kernel_source_sha256_16") != sha:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def env_info():
     info = {"host": platform.node(), "nproc": os.cpu_count()}
     try:
@@ -191,9 +217,12 @@ def main():
         raise RuntimeError("stage-by-stage run differs from the eager forward")
     dom = max(stages, key=lambda k: stages[k]["us"])
     ds = stages[dom]
+    wtag = WORKLOAD_NAMES[args.workload].split()[0]
+    traffic = measured_traffic(dom, wtag)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": ds["gbs"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ds["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
-                "launch_us": ds["us"], "alg_bytes_per_launch": ds["alg_bytes"]}
+                "unit": "GB/s", "frac": round(ds["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "traffic_unit": "bytes per launch", "launch_us": ds["us"],
+                "alg_bytes_per_launch": ds["alg_bytes"]}
     total_bytes = sum(v[0] for v in work.values())
 
     if args.copy_calibration:
@@ -212,7 +241,7 @@ def main():
         from oracle.recurrence import ssd_recurrence, max_threads
         heads = list(range(prob.nheads))
         reps, t_cpu = 0, 0.0
-        while reps < 1 or (t_cpu < args.cpu_seconds and reps < 3):
+        while reps < 1 or (t_cpu < args.cpu_seconds and reps < 10000):
             c0 = time.perf_counter()
             ssd_recurrence(inp["x"], inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"],
                            inp["D"], init=inp["init"], cu_seqlens=inp["cu_seqlens"], heads=heads)
@@ -220,8 +249,8 @@ def main():
             reps += 1
         cpu = {"value": round(tokens * reps / t_cpu, 1), "unit": "tokens/s",
                "cores": max_threads(), "kind": "oracle",
-               "sample": f"whole workload ({tokens} tokens x {prob.nheads} heads), {reps} rep(s), "
-                         f"{t_cpu:.1f} s incl. fp64 upcast"}
+               "sample": f"whole workload ({tokens} tokens x {prob.nheads} heads) repeated "
+                         f"{reps} time(s), {t_cpu:.1f} s, each including the fp64 upcast"}
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
