@@ -17,7 +17,7 @@ typedef hipError_t (*launch_fn)(const FwdArgs&, hipStream_t);
 struct Kernels {
   int32_t dtype;
   int64_t P, N, L;
-  launch_fn bmm, chunk_state, state_passing, chunk_scan;
+  launch_fn bmm, chunk_state, state_passing, chunk_scan, front;
 };
 
 template <typename T> constexpr int32_t dtype_of();
@@ -26,7 +26,8 @@ template <> constexpr int32_t dtype_of<bf16>() { return SSD_BF16; }
 
 #define SSD_ROW(T, P, N, L)                                                              \
   {dtype_of<T>(), P, N, L, &launch_bmm_chunk<T, N, L>, &launch_chunk_state<T, P, N, L>, \
-   &launch_state_passing<T>, &launch_chunk_scan<T, P, N, L>},
+   &launch_state_passing<T>, &launch_chunk_scan<T, P, N, L>,                          \
+   sizeof(T) == 2 ? &launch_front<T, P, N, L> : nullptr},
 const Kernels kKernels[] = {SSD_FOR_EACH_CONFIG(SSD_ROW)};
 #undef SSD_ROW
 
@@ -143,8 +144,15 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
       {SSD_STAGE_STATE_PASSING, k->state_passing},
       {SSD_STAGE_CHUNK_SCAN, k->chunk_scan},
   };
+  // The bf16 path runs stages 1-3 as one launch when all three are asked for.
+  constexpr uint32_t kFront = SSD_STAGE_CUMSUM | SSD_STAGE_BMM | SSD_STAGE_CHUNK_STATE;
+  const bool fuse_front = k->front && (stages & kFront) == kFront;
   for (const Step& stp : steps) {
     if (!(stages & stp.bit)) continue;
+    if (fuse_front && (stp.bit & kFront)) {
+      if (stp.bit == SSD_STAGE_CUMSUM && k->front(a, s) != hipSuccess) return SSD_ERR_HIP;
+      continue;
+    }
     if (stp.fn(a, s) != hipSuccess) return SSD_ERR_HIP;
   }
   return SSD_OK;

@@ -7,7 +7,11 @@
 // One workgroup (4 waves) per (chunk, group, lower-triangular 64x64 tile).
 // C and B rows are staged in LDS as the MFMA operand type (rows padded by 16
 // bytes); each wave computes a 32x32 quarter with 2x2 MFMA 16x16 tiles and
-// K = dstate.  Rows past the chunk's valid length load as zeros.
+// K = dstate.  Rows past the chunk's valid length load as zeros.  The bf16
+// forward runs the same tiles as extra workgroups of the chunk_state launch
+// (ssd_chunk_state.hip); this standalone launch serves the stage-by-stage
+// entry point and the fp32 path.
+#include "ssd_device.h"
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -18,64 +22,14 @@ template <typename T, int N, int L>
 __global__ __launch_bounds__(256) void bmm_chunk_kernel(ChunkMap cm, const T* __restrict__ C,
                                                         const T* __restrict__ B, int G,
                                                         T* __restrict__ cb) {
-  using M = Mfma<T>;
-  constexpr int V = 16 / sizeof(T);   // elements per 16-byte vector
-  constexpr int LD = N + V;           // padded LDS row
-  constexpr int VPR = N / V;
+  constexpr int LD = N + 16 / sizeof(T);
   __shared__ __align__(16) T Cs[64 * LD];
   __shared__ __align__(16) T Bs[64 * LD];
-
   const int j = blockIdx.x / G, g = blockIdx.x - (blockIdx.x / G) * G;
-  int t = blockIdx.y, ti = 0;
-  while (t > ti) { t -= ti + 1; ++ti; }
-  const int tj = t;
+  const int2 t = tri_tile(blockIdx.y);
   const ChunkDesc d = cm.desc(j);
-  if (d.len <= 0 || ti * 64 >= d.len) return;   // rows the output stage never reads
-
-  const int tid = threadIdx.x;
-  for (int i = tid; i < 64 * VPR; i += 256) {
-    const int r = i / VPR, cv = i - (i / VPR) * VPR;
-    const int lc = ti * 64 + r, lb = tj * 64 + r;
-    const uint4 vc = load16(C + ((int64_t)(d.start + lc) * G + g) * N + cv * V, lc < d.len);
-    const uint4 vb = load16(B + ((int64_t)(d.start + lb) * G + g) * N + cv * V, lb < d.len);
-    *reinterpret_cast<uint4*>(&Cs[r * LD + cv * V]) = vc;
-    *reinterpret_cast<uint4*>(&Bs[r * LD + cv * V]) = vb;
-  }
-  __syncthreads();
-
-  const int w = tid / kWave, lane = tid & (kWave - 1);
-  const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
-  const int lr = lane & 15, kq = (lane >> 4) * M::KPL;
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll 4
-  for (int k0 = 0; k0 < N; k0 += M::K) {
-    typename M::frag a[2], b[2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) a[mi] = M::load(&Cs[(wr + mi * 16 + lr) * LD + k0 + kq]);
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) b[ni] = M::load(&Bs[(wc + ni * 16 + lr) * LD + k0 + kq]);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = M::mma(a[mi], b[ni], acc[mi][ni]);
-  }
-
-  T* out = cb + ((int64_t)j * G + g) * L * L;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = ti * 64 + wr + mi * 16 + (lane >> 4) * 4 + r;
-        const int col = tj * 64 + wc + ni * 16 + lr;
-        out[(int64_t)row * L + col] = from_f32<T>(acc[mi][ni][r]);
-      }
+  if (d.len <= 0 || t.x * 64 >= d.len) return;   // rows the output stage never reads
+  bmm_tile<T, N, L>(d, j, g, t.x, t.y, C, B, G, cb, Cs, Bs);
 }
 
 }  // namespace

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
       dls[l] = dl[l];
     }
   }
-  const int w = tid / kWave, lane = tid & (kWave - 1);
+  const int w = wave_id(), lane = tid & (kWave - 1);
   const int lr = lane & 15, kq = (lane >> 4) * KPL;
   const int row0 = rt * RT + w * 16;     // first output row of this wave
   const int my_row = row0 + lr;          // A-operand row of this lane
@@ -225,7 +225,7 @@ chunk_scan_bf16_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
   const ChunkDesc d = cm.desc(j);
   if (d.len <= 0) return;
   const int g = h / (H / G);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
   const int lr = lane & 15, kq = (lane >> 4) * 8;
   // Row groups of this wave; with two per wave they pair from both ends of
   // the chunk, so every wave carries the same causal work.

@@ -16,6 +16,7 @@
 //    Workgroups of one chunk share an XCD, so B stays in its L2.
 //  - fp32 kernel (exactness path): each slice is transposed on its way into
 //    LDS (k contiguous per row, 16-byte padded rows).
+#include "ssd_device.h"
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(
   const float last = dA[d.len - 1];
   for (int l = tid; l < L; l += 256) wl[l] = (l < d.len) ? fexp<T>(last - dA[l]) * dl[l] : 0.f;
 
-  const int w = tid / kWave, lane = tid & (kWave - 1);
+  const int w = wave_id(), lane = tid & (kWave - 1);
   const bool active = w < WP * WN;
   const int wp = w / WN, wn = w - (w / WN) * WN;
   const int lr = lane & 15, kq = (lane >> 4) * M::KPL;
@@ -129,15 +130,31 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(
 }
 
 
-// ------------------------------------------------------------- bf16 kernel
+// ------------------------------------------------------------- bf16 kernels
 template <int P, int N, int L>
-__global__ __launch_bounds__(256) void chunk_state_bf16_kernel(
-    ChunkMap cm, int nslots, const bf16* __restrict__ x, const bf16* __restrict__ B,
-    const float* __restrict__ delta, const float* __restrict__ dAcs, int H, int G,
-    float* __restrict__ S) {
-  static_assert(L % 64 == 0 && P % 16 == 0 && N % 16 == 0, "tile shape");
-  constexpr int KS = 64;                  // tokens per slice
-  constexpr int XP = P + 8, BP = N + 8;   // LDS row pitches (elements)
+struct StateSmem {
+  static constexpr int KS = 64;                  // tokens per slice
+  static constexpr int XP = P + 8, BP = N + 8;   // LDS row pitches (elements)
+  bf16 xs[KS * XP];
+  bf16 bs[KS * BP];
+  float wl[L];
+  float cum[L];
+  float wave_tot[4];
+};
+
+// chunk_state for chunk j, head h (256 threads).  With CUMSUM the workgroup
+// also runs chunk_cumsum for its (chunk, head) -- the step and its running
+// sum come from dt here and are written to delta/dAcs for the later stages --
+// otherwise it reads them from delta/dAcs.
+template <int P, int N, int L, bool CUMSUM>
+__device__ __forceinline__ void chunk_state_bf16_body(
+    const ChunkDesc& d, int j, int h, const bf16* __restrict__ x, const bf16* __restrict__ B,
+    float* __restrict__ delta, float* __restrict__ dAcs, const float* __restrict__ dt,
+    const float* __restrict__ dt_bias, const float* __restrict__ A, float dt_min, float dt_max,
+    int H, int G, float* __restrict__ S, StateSmem<P, N, L>& sm) {
+  static_assert(L % 64 == 0 && L <= 256 && P % 16 == 0 && N % 16 == 0, "tile shape");
+  using SM = StateSmem<P, N, L>;
+  constexpr int KS = SM::KS, XP = SM::XP, BP = SM::BP;
   constexpr int XC = P / 8, BC = N / 8;   // 16-byte pieces per row
   constexpr int XU = (KS * XC + 255) / 256, BU = (KS * BC + 255) / 256;
   constexpr int PT = P / 16, NT = N / 16;
@@ -145,42 +162,45 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(
   constexpr int WP = (4 / WN) < PT ? (4 / WN) : PT;
   constexpr int TP = PT / WP, TN = NT / WN;
   static_assert(PT % WP == 0 && NT % WN == 0, "tile split");
-  __shared__ __align__(16) bf16 xs[KS * XP];
-  __shared__ __align__(16) bf16 bs[KS * BP];
-  __shared__ float wl[L];
-
-  const int2 jh = xcd_chunk_head(blockIdx.x, H);
-  const int j = jh.x, h = jh.y;
-  if (j >= nslots) return;
-  const ChunkDesc d = cm.desc(j);
-  if (d.len <= 0) return;
   const int g = h / (H / G);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  {
-    const float* dA = dAcs + ((int64_t)j * H + h) * L;
-    const float* dl = delta + ((int64_t)j * H + h) * L;
-    const float last = dA[d.len - 1] * kLog2e;
-    for (int l = tid; l < L; l += 256)
-      wl[l] = (l < d.len) ? exp2_fast(last - dA[l] * kLog2e) * dl[l] : 0.f;
-  }
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
+  const int last = d.len - 1;
 
   uint4 xr[XU], br[BU];
   auto fetch = [&](int l0) {
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
-      const int i = tid + 256 * u, r = i / XC, c = i - (i / XC) * XC;
-      xr[u] = make_uint4(0, 0, 0, 0);
-      if (i < KS * XC && l0 + r < d.len)
-        xr[u] = *reinterpret_cast<const uint4*>(x + ((int64_t)(d.start + l0 + r) * H + h) * P + c * 8);
+      const int i = min(tid + 256 * u, KS * XC - 1), r = i / XC, c = i - (i / XC) * XC;
+      xr[u] = *reinterpret_cast<const uint4*>(x + ((int64_t)(d.start + min(l0 + r, last)) * H + h) * P + c * 8);
     }
 #pragma unroll
     for (int u = 0; u < BU; ++u) {
-      const int i = tid + 256 * u, r = i / BC, c = i - (i / BC) * BC;
-      br[u] = make_uint4(0, 0, 0, 0);
-      if (i < KS * BC && l0 + r < d.len)
-        br[u] = *reinterpret_cast<const uint4*>(B + ((int64_t)(d.start + l0 + r) * G + g) * N + c * 8);
+      const int i = min(tid + 256 * u, KS * BC - 1), r = i / BC, c = i - (i / BC) * BC;
+      br[u] = *reinterpret_cast<const uint4*>(B + ((int64_t)(d.start + min(l0 + r, last)) * G + g) * N + c * 8);
     }
   };
+  fetch(0);                               // in flight while the weights are formed
+
+  // w[l] = exp(a_last - a_l) * delta_l
+  if constexpr (CUMSUM) {
+    float step, cum;
+    chunk_cumsum_block<L>(d, tid, dt, dt_bias, A, H, h, dt_min, dt_max, sm.wave_tot, step, cum);
+    if (tid < L) {
+      const int64_t o = ((int64_t)j * H + h) * L + tid;
+      delta[o] = step;
+      dAcs[o] = cum;
+      sm.cum[tid] = cum;
+      sm.wl[tid] = step;
+    }
+    __syncthreads();
+    if (tid < L) sm.wl[tid] = exp2_fast((sm.cum[last] - sm.cum[tid]) * kLog2e) * sm.wl[tid];
+  } else {
+    const float* dA = dAcs + ((int64_t)j * H + h) * L;
+    const float* dl = delta + ((int64_t)j * H + h) * L;
+    const float lastv = dA[last];
+    for (int l = tid; l < L; l += 256)
+      sm.wl[l] = (l < d.len) ? exp2_fast((lastv - dA[l]) * kLog2e) * dl[l] : 0.f;
+  }
 
   const int wp = w / WN, wn = w - (w / WN) * WN;
   const bool active = w < WP * WN;
@@ -191,7 +211,6 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(
     for (int b = 0; b < TN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsl = (d.len + KS - 1) / KS;
-  fetch(0);
   __syncthreads();                        // wl ready
   for (int sl = 0; sl < nsl; ++sl) {
     const int l0 = sl * KS;
@@ -200,17 +219,19 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(
       const int i = tid + 256 * u, r = i / XC, c = i - (i / XC) * XC;
       if (i < KS * XC) {
         const bf16x8 v = __builtin_bit_cast(bf16x8, xr[u]);
-        const float wv = wl[l0 + r];
+        const float wv = sm.wl[l0 + r];   // 0 past the chunk's end
         bf16x8 o;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = static_cast<bf16>(static_cast<float>(v[e]) * wv);
-        *reinterpret_cast<bf16x8*>(&xs[r * XP + c * 8]) = o;
+        *reinterpret_cast<bf16x8*>(&sm.xs[r * XP + c * 8]) = o;
       }
     }
 #pragma unroll
     for (int u = 0; u < BU; ++u) {
       const int i = tid + 256 * u, r = i / BC, c = i - (i / BC) * BC;
-      if (i < KS * BC) *reinterpret_cast<uint4*>(&bs[r * BP + c * 8]) = br[u];
+      if (i < KS * BC)
+        *reinterpret_cast<uint4*>(&sm.bs[r * BP + c * 8]) =
+            (l0 + r < d.len) ? br[u] : make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
     if (sl + 1 < nsl) fetch(l0 + KS);     // in flight while this slice multiplies
@@ -219,9 +240,9 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(
       for (int k0 = 0; k0 < KS; k0 += 32) {
         bf16x8 fa[TP], fb[TN];
 #pragma unroll
-        for (int a = 0; a < TP; ++a) fa[a] = lds_operand_kmajor(xs, XP, k0, 16 * (wp * TP + a), lane);
+        for (int a = 0; a < TP; ++a) fa[a] = lds_operand_kmajor(sm.xs, XP, k0, 16 * (wp * TP + a), lane);
 #pragma unroll
-        for (int b = 0; b < TN; ++b) fb[b] = lds_operand_kmajor(bs, BP, k0, 16 * (wn * TN + b), lane);
+        for (int b = 0; b < TN; ++b) fb[b] = lds_operand_kmajor(sm.bs, BP, k0, 16 * (wn * TN + b), lane);
 #pragma unroll
         for (int a = 0; a < TP; ++a)
 #pragma unroll
@@ -246,6 +267,55 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(
       }
 }
 
+template <int P, int N, int L>
+__global__ __launch_bounds__(256) void chunk_state_bf16_kernel(
+    ChunkMap cm, int nslots, const bf16* __restrict__ x, const bf16* __restrict__ B,
+    float* __restrict__ delta, float* __restrict__ dAcs, int H, int G, float* __restrict__ S) {
+  __shared__ __align__(16) StateSmem<P, N, L> sm;
+  const int2 jh = xcd_chunk_head(blockIdx.x, H);
+  if (jh.x >= nslots) return;
+  const ChunkDesc d = cm.desc(jh.x);
+  if (d.len <= 0) return;
+  chunk_state_bf16_body<P, N, L, false>(d, jh.x, jh.y, x, B, delta, dAcs, nullptr, nullptr,
+                                        nullptr, 0.f, 0.f, H, G, S, sm);
+}
+
+// The front of the bf16 forward in one launch: the first `nbmm` workgroups
+// compute bmm_chunk tiles, the rest run chunk_cumsum + chunk_state for one
+// (chunk, head) each.  The three stages are independent of each other's
+// outputs here, so they share the machine instead of running back to back.
+template <int P, int N, int L>
+__global__ __launch_bounds__(256) void front_bf16_kernel(
+    ChunkMap cm, int nslots, int nbmm, int G, const bf16* __restrict__ x,
+    const bf16* __restrict__ B, const bf16* __restrict__ C, const float* __restrict__ dt,
+    const float* __restrict__ dt_bias, const float* __restrict__ A, float dt_min, float dt_max,
+    int H, float* __restrict__ delta, float* __restrict__ dAcs, bf16* __restrict__ cb,
+    float* __restrict__ S) {
+  constexpr int LDB = N + 8;
+  constexpr int NTRI = (L / 64) * (L / 64 + 1) / 2;
+  constexpr size_t kBmm = 2 * 64 * LDB * sizeof(bf16);
+  constexpr size_t kState = sizeof(StateSmem<P, N, L>);
+  __shared__ __align__(16) unsigned char smem[kBmm > kState ? kBmm : kState];
+  const int b = blockIdx.x;
+  if (b < nbmm) {                         // nbmm is a multiple of 8: XCD order kept below
+    const int tile = b % NTRI, jg = b / NTRI;
+    const int j = jg / G, g = jg - (jg / G) * G;
+    if (j >= nslots) return;
+    const int2 t = tri_tile(tile);
+    const ChunkDesc d = cm.desc(j);
+    if (d.len <= 0 || t.x * 64 >= d.len) return;
+    bf16* Cs = reinterpret_cast<bf16*>(smem);
+    bmm_tile<bf16, N, L>(d, j, g, t.x, t.y, C, B, G, cb, Cs, Cs + 64 * LDB);
+    return;
+  }
+  const int2 jh = xcd_chunk_head(b - nbmm, H);
+  if (jh.x >= nslots) return;
+  const ChunkDesc d = cm.desc(jh.x);
+  if (d.len <= 0) return;
+  chunk_state_bf16_body<P, N, L, true>(d, jh.x, jh.y, x, B, delta, dAcs, dt, dt_bias, A, dt_min,
+                                       dt_max, H, G, S,
+                                       *reinterpret_cast<StateSmem<P, N, L>*>(smem));
+}
 }  // namespace
 
 template <typename T, int P, int N, int L>
@@ -263,7 +333,25 @@ hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-#define SSD_INST(T, P, N, L) template hipError_t launch_chunk_state<T, P, N, L>(const FwdArgs&, hipStream_t);
+template <typename T, int P, int N, int L>
+hipError_t launch_front(const FwdArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) != 2) {
+    return hipErrorInvalidValue;           // the fp32 path runs the stages one by one
+  } else {
+    if (a.max_chunks <= 0) return hipSuccess;
+    constexpr int ntri = (L / 64) * (L / 64 + 1) / 2;
+    const int nbmm = (a.max_chunks * a.G * ntri + 7) / 8 * 8;
+    hipLaunchKernelGGL((front_bf16_kernel<P, N, L>), dim3(nbmm + xcd_grid(a.max_chunks, a.H)),
+                       dim3(256), 0, s, a.cmap(), a.max_chunks, nbmm, a.G, (const bf16*)a.x,
+                       (const bf16*)a.B, (const bf16*)a.C, a.dt, a.dt_bias, a.A, a.dt_min,
+                       a.dt_max, a.H, a.delta, a.dAcs, (bf16*)a.cb, a.chunk_states);
+    return hipGetLastError();
+  }
+}
+
+#define SSD_INST(T, P, N, L)                                                           \
+  template hipError_t launch_chunk_state<T, P, N, L>(const FwdArgs&, hipStream_t); \
+  template hipError_t launch_front<T, P, N, L>(const FwdArgs&, hipStream_t);
 SSD_FOR_EACH_CONFIG(SSD_INST)
 #undef SSD_INST
 

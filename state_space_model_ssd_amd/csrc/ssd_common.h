@@ -15,6 +15,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Index of the calling wave within its workgroup, as a wave-uniform (scalar)
+// value: branches and addresses derived from it stay on the scalar unit.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+}
+
 // ---------------------------------------------------------------------------
 // Logical chunks.  A chunk never straddles a sequence: sequence s owns
 // ceil(len_s / L) chunks that start at its first token, so only its last

@@ -59,6 +59,10 @@ hipError_t launch_bmm_chunk(const FwdArgs& a, hipStream_t s);
 // Stage 3: per-chunk states.
 template <typename T, int P, int N, int L>
 hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t s);
+// Stages 1-3 of the bf16 path in one launch (bmm tiles as extra workgroups,
+// chunk_cumsum inside the chunk_state workgroups).
+template <typename T, int P, int N, int L>
+hipError_t launch_front(const FwdArgs& a, hipStream_t s);
 // Stage 4: inter-chunk chain.
 template <typename T>
 hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s);

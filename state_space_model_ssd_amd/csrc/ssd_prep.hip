@@ -8,6 +8,7 @@
 //   delta[j,h,l] = clamp(softplus(dt[t,h] + dt_bias[h]), dt_min, dt_max)
 //   dAcs[j,h,l]  = sum_{k <= l} delta[j,h,k] * A[h]
 // with delta = 0 for l >= len (the running sum stays flat there).
+#include "ssd_device.h"
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -104,36 +105,15 @@ __global__ __launch_bounds__(L) void chunk_cumsum_kernel(
     ChunkMap cm, const float* __restrict__ dt, const float* __restrict__ dt_bias,
     const float* __restrict__ A, int H, float dt_min, float dt_max,
     float* __restrict__ delta, float* __restrict__ dAcs) {
+  __shared__ float wave_tot[L / kWave];
   const int j = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
   const ChunkDesc d = cm.desc(j);
   if (d.len <= 0) return;  // unused slot: uniform over the workgroup
-  float dl = 0.f;
-  if (l < d.len) {
-    const float u = dt[(int64_t)(d.start + l) * H + h] + (dt_bias ? dt_bias[h] : 0.f);
-    // softplus(u) = log(1 + e^u), written without overflow
-    const float sp = fmaxf(u, 0.f) + log1pf(expf(-fabsf(u)));
-    dl = fminf(fmaxf(sp, dt_min), dt_max);
-  }
-  float v = dl * A[h];
-  const int lane = l & (kWave - 1);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    float t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
-  constexpr int NW = L / kWave;
-  if constexpr (NW > 1) {
-    __shared__ float wave_tot[NW];
-    if (lane == kWave - 1) wave_tot[l / kWave] = v;
-    __syncthreads();
-    float add = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW - 1; ++w) add += (w < l / kWave) ? wave_tot[w] : 0.f;
-    v += add;
-  }
+  float step, cum;
+  chunk_cumsum_block<L>(d, l, dt, dt_bias, A, H, h, dt_min, dt_max, wave_tot, step, cum);
   const int64_t o = ((int64_t)j * H + h) * L + l;
-  delta[o] = dl;
-  dAcs[o] = v;
+  delta[o] = step;
+  dAcs[o] = cum;
 }
 
 }  // namespace
