@@ -7,24 +7,22 @@
 //          + D[h] * x[l,p]
 // accumulated in fp32 and rounded once to the output type.
 //
-// bf16 kernel (the production path): one workgroup (4 waves) per (chunk,
-// head), the whole chunk at once.
-//  - x of the chunk is staged once in LDS in its natural token-major layout
-//    (coalesced 16-byte loads and stores) and read as the MFMA B operand with
-//    the gfx950 LDS transpose read.
-//  - intra-chunk term: 16-row groups are dealt to the waves round-robin (the
-//    causal work evens out).  Per 32-token k-step the lane builds its 8
-//    A-operand values from the CB row.  Below the diagonal the decay splits
-//    around the step's last token r:  exp(a_l - a_s) = exp(a_l - a_r) *
-//    exp(a_r - a_s), both factors <= 1, the second (times delta_s) kept per
-//    token in LDS, so a step costs one exp per lane instead of eight.  Steps
-//    that touch the diagonal evaluate the masked exponential directly (mask
-//    selected before the exp).
-//  - inter-chunk term: the C row scaled by exp(a_l) is the A operand, the
-//    entering state (n contiguous) the B operand, accumulated into the same
-//    tile.
-//  - epilogue: y = acc + D x is written over x in LDS by the lane that read
-//    it, then the tile leaves in coalesced 16-byte rows.
+// bf16 kernel (the production path): persistent, one workgroup of 4 L
+// threads per resident slot (one per CU at L = 256), walking the (chunk,
+// head) tiles with the next tile's inputs in flight while it computes one.
+//  - x of the tile is staged in LDS token-major (16-byte pieces XOR-swizzled
+//    per row) and read as the MFMA A operand with the gfx950 LDS transpose
+//    read; the entering state is staged row-major with a padded pitch.
+//  - intra-chunk term: per 32-token k-step the lane builds its 8 B-operand
+//    values from the CB row.  Below the diagonal the decay splits around the
+//    step's last token r:  exp(a_l - a_s) = exp(a_l - a_r) * exp(a_r - a_s),
+//    both factors <= 1, the second (times delta_s) kept per token in LDS, so a
+//    step costs one exp per lane instead of eight.  Steps on the diagonal
+//    evaluate the masked exponential directly (exp2(-inf) = 0 above it).
+//  - inter-chunk term: the entering state times the C rows on MFMA, then
+//    scaled by exp(a_l) per token.
+//  - epilogue: y = acc + D x, stored straight from the accumulators.
+// All global traffic goes through buffer resources bounded by the tile.
 //
 // fp32 kernel (exactness path): one workgroup per (chunk, 64-row tile, head);
 // each wave owns 16 output rows and all P columns (P/16 MFMA tiles).
@@ -186,231 +184,438 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
 
 
 // ------------------------------------------------------------- bf16 kernel
-// Waves per workgroup: two 16-row groups per wave for L >= 128 (8 waves for a
-// 256-token chunk), one per wave for L = 64.
-template <int L> constexpr int kScanWaves = (L / 16) / 2 < 4 ? 4 : (L / 16) / 2;
+// Buffer resources: 32-bit offsets from a per-tile base, range-checked by the
+// hardware.  A load past num_records returns zeros and a store past it is
+// dropped, so rows past a chunk's end need neither clamps nor branches, and
+// no access can leave the tile.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
 
 template <int P, int N, int L>
-__global__ __launch_bounds__(64 * kScanWaves<L>) __attribute__((amdgpu_waves_per_eu(4))) void
-chunk_scan_bf16_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
-                       const bf16* __restrict__ C, const bf16* __restrict__ cb,
-                       const float* __restrict__ delta, const float* __restrict__ dAcs,
-                       const bf16* __restrict__ states_in, const float* __restrict__ D, int H,
-                       int G, bf16* __restrict__ out) {
-  static_assert(L % 64 == 0 && P % 16 == 0 && N % 32 == 0, "tile shape");
-  constexpr int NW = kScanWaves<L>;
-  constexpr int NT = 64 * NW;            // threads
-  constexpr int XP = P + 8;              // x tile pitch (elements): conflict-free transpose reads
-  constexpr int HP = N + 8;              // state tile pitch: conflict-free 16-byte row reads
-  constexpr int RG = L / 16;             // 16-row groups of the chunk
-  constexpr int RGW = RG / NW;           // row groups per wave: 1 or 2
-  static_assert(RGW * NW == RG && (RGW == 1 || RGW == 2), "row-group split");
-  constexpr int PT = P / 16;
-  constexpr int NK = N / 32;             // k-steps of the inter-chunk term
-  constexpr int NQ = L / 32;             // k-steps of the intra-chunk term
-  constexpr int CPR = P / 8;             // 16-byte pieces per x row
-  constexpr int XU = L * CPR / NT;       // x pieces per thread
-  constexpr int HPR = N / 8;             // 16-byte pieces per state row
-  constexpr int HU = (P * HPR + NT - 1) / NT;
-  static_assert((L * CPR) % NT == 0 && L <= NT, "x staging");
-  __shared__ __align__(16) bf16 xs[L * XP];
-  __shared__ __align__(16) bf16 hsm[P * HP];
-  __shared__ __align__(16) float dal2[L];   // running sum of delta*A, times log2(e)
-  __shared__ __align__(16) float dls[L];    // delta
-  __shared__ __align__(16) float cfs[L];    // delta_s * exp(a_r - a_s), r = last token of s's 32-block
+struct ScanShape {
+  static constexpr int RG = L / 16;        // 16-row groups of a chunk
+  static constexpr int NPAIR = RG / 2;     // mirror pairs (16m.., 16(RG-1-m)..)
+  static constexpr int NW = 2 * NPAIR;     // two waves per pair
+  static constexpr int NT = 64 * NW;       // threads (= 4 L)
+  static constexpr int PT = P / 16;        // 16-column MFMA tiles over p
+  static constexpr int NK = N / 32;        // n-steps of the inter-chunk term
+  static constexpr int CPR = P / 8;        // 16-byte pieces per x row
+  static constexpr int XU = L * CPR / NT;  // x pieces per thread
+  static constexpr int HPR = N / 8;        // 16-byte pieces per state row
+  static constexpr int HN = P * HPR;
+  static constexpr int HU = (HN + NT - 1) / NT;
+  static constexpr int HP = N + 8;         // state LDS pitch: conflict-free row reads
+  // The two row groups of a pair need RG/2 + 1 intra-chunk k-steps in all;
+  // the first wave of the pair takes NS0 of them, the second NS1.
+  static constexpr int NS0 = RG / 4 + 1;
+  static constexpr int NS1 = RG / 2 + 1 - NS0;
+  static_assert(L % 64 == 0 && P % 32 == 0 && N % 32 == 0, "tile shape");
+  static_assert((L * CPR) % NT == 0 && XU >= 1, "x staging");
+};
 
-  const int2 jh = xcd_chunk_head(blockIdx.x, H);
-  const int j = jh.x, h = jh.y;
-  if (j >= nslots) return;
-  const ChunkDesc d = cm.desc(j);
-  if (d.len <= 0) return;
-  const int g = h / (H / G);
-  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
+// The x tile sits in LDS unpadded, token-major, with the 16-byte pieces of
+// row r permuted by XOR with xsw(r).  The transpose reads of one instruction
+// touch rows r0 + {0..3} and r0 + {8..11} (r0 a multiple of 8) at two
+// adjacent pieces; the XOR spreads those 8 rows x 2 pieces over distinct bank
+// groups, whether the LDS serves 16 or 32 lanes of 8-byte reads per clock.
+template <int CPR>
+__device__ __forceinline__ int xsw(int r) {
+  return (2 * ((r & 3) ^ ((r >> 3) & 1))) & (CPR - 1);
+}
+
+// One (chunk slot, head) tile as the persistent loop sees it (wave-uniform).
+struct ScanTile {
+  int j, h, start, len;
+};
+
+__device__ __forceinline__ ScanTile scan_tile(const ChunkMap& cm, int nslots, int ntiles, int t,
+                                              int H) {
+  ScanTile T{0, 0, 0, 0};
+  if (t >= ntiles) return T;
+  const int2 jh = xcd_chunk_head(t, H);
+  T.j = jh.x;
+  T.h = jh.y;
+  if (T.j < nslots) {
+    if (cm.table) {
+      // read through the constant address space: scalar loads
+      typedef const __attribute__((address_space(4))) int cint;
+      const cint* e = (const cint*)cm.table + 4 * T.j;
+      T.start = e[0];
+      T.len = max(e[1], 0);
+    } else {
+      const ChunkDesc d = cm.desc(T.j);
+      T.start = d.start;
+      T.len = max(d.len, 0);
+    }
+  }
+  return T;
+}
+
+// Registers that carry one tile's staged inputs from its prefetch to its
+// staging in LDS.
+template <int P, int N, int L>
+struct ScanStage {
+  uint4 xv[ScanShape<P, N, L>::XU];
+  uint4 hv[ScanShape<P, N, L>::HU];
+  float dA, dl;
+};
+
+// Buffer resource over a tile's x (or y) rows: token r of the chunk, head h.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* base, const ScanTile& T,
+                                                            int H, int P, uint32_t HPx) {
+  const uint32_t bytes = T.len > 0 ? ((uint32_t)(T.len - 1) * HPx + P) * 2u : 0u;
+  return buf_rsrc(base + ((int64_t)T.start * H + T.h) * P, bytes);
+}
+
+// Issue the loads of a tile's x rows, entering state, running sums and steps.
+template <int P, int N, int L>
+__device__ __forceinline__ void scan_prefetch(const ScanTile& T, int tid, ScanStage<P, N, L>& st,
+                                              const bf16* x, const bf16* states_in,
+                                              const float* dAcs, const float* delta, int H,
+                                              uint32_t HPx) {
+  using S = ScanShape<P, N, L>;
+  const auto rx = rows_rsrc(x, T, H, P, HPx);
+#pragma unroll
+  for (int u = 0; u < S::XU; ++u) {
+    const int i = tid + S::NT * u, r = i / S::CPR, c = i % S::CPR;
+    st.xv[u] = buf_load16(rx, ((uint32_t)r * HPx + c * 8) * 2u);
+  }
+  const int64_t jh = (int64_t)T.j * H + T.h;
+  const auto rh = buf_rsrc(states_in + jh * P * N, T.len > 0 ? P * N * 2 : 0);
+#pragma unroll
+  for (int u = 0; u < S::HU; ++u) st.hv[u] = buf_load16(rh, (uint32_t)(tid + S::NT * u) * 16);
+  const uint32_t lb = T.len > 0 ? L * 4 : 0;
+  st.dA = buf_load4(buf_rsrc(dAcs + jh * L, lb), tid * 4);
+  st.dl = buf_load4(buf_rsrc(delta + jh * L, lb), tid * 4);
+}
+
+// A wave's share of one mirror pair (all wave-uniform).
+struct ScanSplit {
+  int mg0, mg1;   // row groups of the pair
+  int nq0;        // 32-token k-steps reaching mg0
+  int xs1;        // k-steps of mg1 taken by the first wave
+  int kap;        // 0: first wave (owns mg0), 1: second wave (owns mg1)
+  int mown;       // row group this wave finishes
+  int nslot;      // k-steps this wave takes
+  // slots of the first wave: mg1's k-steps 0..xs1-1, then mg0's 0..nq0-1;
+  // slots of the second wave: mg1's k-steps xs1..
+  __device__ __forceinline__ int rg(int s) const { return kap ? 1 : (s < xs1 ? 1 : 0); }
+  __device__ __forceinline__ int q(int s) const { return kap ? xs1 + s : (s < xs1 ? s : s - xs1); }
+};
+
+// Issue the loads of the own row group's C rows (all n-steps).
+template <int N>
+__device__ __forceinline__ void scan_load_c(const ScanTile& T, int lane, const ScanSplit& sp,
+                                            bf16x8 (&fc)[N / 32], const bf16* C, int H, int G,
+                                            uint32_t GN) {
+  const int g = T.h / (H / G);
   const int lr = lane & 15, kq = (lane >> 4) * 8;
-  // Row groups of this wave; with two per wave they pair from both ends of
-  // the chunk, so every wave carries the same causal work.
-  int mg[RGW];
-  mg[0] = w;
-  if constexpr (RGW == 2) mg[1] = RG - 1 - w;
-  int lrow[RGW], nq[RGW];
+  const uint32_t cbytes = T.len > 0 ? ((uint32_t)(T.len - 1) * GN + N) * 2u : 0u;
+  const auto rc = buf_rsrc(C + ((int64_t)T.start * G + g) * N, cbytes);
+  const uint32_t co = ((uint32_t)(16 * sp.mown + lr) * GN + kq) * 2u;
 #pragma unroll
-  for (int i = 0; i < RGW; ++i) {
-    lrow[i] = 16 * mg[i] + lr;
-    nq[i] = (16 * mg[i] + 15) / 32 + 1;    // k-steps that reach this row group
-  }
-  const int last = d.len - 1;
+  for (int k = 0; k < N / 32; ++k) fc[k] = __builtin_bit_cast(bf16x8, buf_load16(rc, co + 64 * k));
+}
 
-  // ---- global loads issued together.  Addresses are clamped into the chunk
-  // and out-of-chunk values replaced after arrival, so nothing branches.
-  uint4 xv[XU];
+// Issue the loads of the CB rows of every k-step this wave takes.
+template <int P, int N, int L>
+__device__ __forceinline__ void scan_load_cb(const ScanTile& T, int lane, const ScanSplit& sp,
+                                             bf16x8 (&cbs)[ScanShape<P, N, L>::NS0],
+                                             const bf16* cb, int H, int G) {
+  using S = ScanShape<P, N, L>;
+  const int g = T.h / (H / G);
+  const int lr = lane & 15, kq = (lane >> 4) * 8;
+  const auto rcb = buf_rsrc(cb + ((int64_t)T.j * G + g) * L * L, T.len > 0 ? L * L * 2 : 0);
 #pragma unroll
-  for (int u = 0; u < XU; ++u) {
-    const int i = tid + NT * u, r = i / CPR, c = i - (i / CPR) * CPR;
-    xv[u] = *reinterpret_cast<const uint4*>(x + ((int64_t)(d.start + min(r, last)) * H + h) * P + c * 8);
+  for (int sl = 0; sl < S::NS0; ++sl) {
+    if (sl < sp.nslot) {                   // wave-uniform
+      const int m = sp.rg(sl) ? sp.mg1 : sp.mg0;
+      const uint32_t o = ((uint32_t)(16 * m + lr) * L + kq + 32 * sp.q(sl)) * 2u;
+      cbs[sl] = __builtin_bit_cast(bf16x8, buf_load16(rcb, o));
+    }
   }
-  const bf16* hs = states_in + ((int64_t)j * H + h) * P * N;
-  uint4 hv[HU];
-#pragma unroll
-  for (int u = 0; u < HU; ++u) {
-    const int i = min(tid + NT * u, P * HPR - 1);
-    hv[u] = *reinterpret_cast<const uint4*>(hs + i * 8);
-  }
-  const int tl = tid < L ? tid : L - 1;
-  const float dA_t = dAcs[((int64_t)j * H + h) * L + tl];
-  const float dl_t = delta[((int64_t)j * H + h) * L + tl];
-  bf16x8 fc[RGW][NK];                      // C rows of this lane, all n-steps
-  const bf16* cbrow[RGW];
-#pragma unroll
-  for (int i = 0; i < RGW; ++i) {
-    const bf16* crow = C + ((int64_t)(d.start + min(lrow[i], last)) * G + g) * N + kq;
-#pragma unroll
-    for (int k = 0; k < NK; ++k) fc[i][k] = *reinterpret_cast<const bf16x8*>(crow + 32 * k);
-    cbrow[i] = cb + (((int64_t)j * G + g) * L + lrow[i]) * L + kq;
-  }
-  bf16x8 cur[RGW];                         // CB rows of the current k-step
-#pragma unroll
-  for (int i = 0; i < RGW; ++i) cur[i] = *reinterpret_cast<const bf16x8*>(cbrow[i]);
+}
 
-  // ---- stage x, the state, the running sums and the per-token factors
-#pragma unroll
-  for (int u = 0; u < XU; ++u) {
-    const int i = tid + NT * u, r = i / CPR, c = i - (i / CPR) * CPR;
-    *reinterpret_cast<uint4*>(&xs[r * XP + c * 8]) = r < d.len ? xv[u] : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int u = 0; u < HU; ++u) {
-    const int i = tid + NT * u, r = i / HPR, c = i - (i / HPR) * HPR;
-    if (i < P * HPR) *reinterpret_cast<uint4*>(&hsm[r * HP + c * 8]) = hv[u];
-  }
-  if (tid < L) {
-    dal2[tid] = dA_t * kLog2e;
-    dls[tid] = dl_t;
-  }
-  __syncthreads();
-  if (tid < L) cfs[tid] = dls[tid] * exp2_fast(dal2[tid | 31] - dal2[tid]);
-
-  // The MFMAs compute the transposed tile y^T[p][l]: A = x^T or the state
-  // (rows p), B = the decay-masked CB row or the C row (columns l).  A lane
-  // then holds four consecutive p of one token.
-  f32x4 acc[RGW][PT];
-#pragma unroll
-  for (int i = 0; i < RGW; ++i)
-#pragma unroll
-    for (int a = 0; a < PT; ++a) acc[i][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // ---- inter-chunk term: y^T[p][l] = exp(a_l) * sum_n state[p][n] C[l][n].
-  // C enters the MFMA as loaded; exp(a_l) scales the accumulator afterwards
-  // (a lane's column is one token).  Columns of tokens past the chunk end
-  // hold junk that no store reads: an output column depends on its own
-  // B-operand column only.
-#pragma unroll
-  for (int k = 0; k < NK; ++k) {
-    bf16x8 fh[PT];
-#pragma unroll
-    for (int a = 0; a < PT; ++a)
-      fh[a] = *reinterpret_cast<const bf16x8*>(&hsm[(16 * a + lr) * HP + 32 * k + kq]);
-#pragma unroll
-    for (int i = 0; i < RGW; ++i)
-#pragma unroll
-      for (int a = 0; a < PT; ++a) acc[i][a] = Mfma<bf16>::mma(fh[a], fc[i][k], acc[i][a]);
-  }
-#pragma unroll
-  for (int i = 0; i < RGW; ++i) {
-    const float rsc = exp2_fast(dal2[lrow[i]]);
-#pragma unroll
-    for (int a = 0; a < PT; ++a) acc[i][a] *= rsc;
-  }
-  __syncthreads();                         // cfs ready
-
-  // ---- intra-chunk term, k-steps outer: the x^T operands of a step serve
-  // both row groups of the wave; the next step's CB rows are in flight.
-  const int nq_wave = nq[RGW - 1];
-  for (int q = 0; q < nq_wave; ++q) {
-    const int s0 = 32 * q;
-    const int sn = min(s0 + 32, L - 32);   // next step (clamped: always in the row)
-    bf16x8 nxt[RGW];
-#pragma unroll
-    for (int i = 0; i < RGW; ++i) nxt[i] = *reinterpret_cast<const bf16x8*>(cbrow[i] + sn);
-    bf16x8 fx[PT];
-#pragma unroll
-    for (int a = 0; a < PT; ++a) fx[a] = lds_operand_kmajor(xs, XP, s0, 16 * a, lane);
-    const float dal_r = dal2[s0 + 31];
+// One intra-chunk k-step of row group m (tokens s0 = 32q .. s0+31):
+// acc += x^T (decay-masked CB rows)^T, the B operand built in registers from
+// the lane's CB row piece.
+template <int P>
+__device__ __forceinline__ void scan_kstep(f32x4 (&acc)[P / 16], int m, int q, const bf16x8& cbr,
+                                           int lr, int kq, int xrow, int xsl, int xcol,
+                                           const float* dal2, const float* dls, const float* cfs,
+                                           const bf16* xs) {
+  using M = Mfma<bf16>;
+  const int s0 = 32 * q;
+  const int lrow = 16 * m + lr;
+  const float dal = dal2[lrow];
+  float mv[8];
+  if (s0 + 32 <= 16 * m) {               // below the diagonal: factored decay
+    const float rf = exp2_fast(dal - dal2[s0 + 31]);
     const float4 f0 = *reinterpret_cast<const float4*>(&cfs[s0 + kq]);
     const float4 f1 = *reinterpret_cast<const float4*>(&cfs[s0 + kq + 4]);
     const float cf[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
-    for (int i = 0; i < RGW; ++i) {
-      const int m = mg[i];
-      if (q >= nq[i]) continue;            // wave-uniform: above this row group
-      float cbv[8];
+    for (int e = 0; e < 8; ++e) mv[e] = static_cast<float>(cbr[e]) * (rf * cf[e]);
+  } else {                               // on the diagonal: masked exponential
+    const float4 a0 = *reinterpret_cast<const float4*>(&dal2[s0 + kq]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&dal2[s0 + kq + 4]);
+    const float4 d0 = *reinterpret_cast<const float4*>(&dls[s0 + kq]);
+    const float4 d1 = *reinterpret_cast<const float4*>(&dls[s0 + kq + 4]);
+    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) cbv[e] = static_cast<float>(cur[i][e]);
-      const float dal = dal2[lrow[i]];
-      float mv[8];
-      if (s0 + 32 <= 16 * m) {             // below the diagonal: factored decay
-        const float rf = exp2_fast(dal - dal_r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mv[e] = cbv[e] * (rf * cf[e]);
-      } else {                             // on the diagonal: masked exponential
-        const float4 a0 = *reinterpret_cast<const float4*>(&dal2[s0 + kq]);
-        const float4 a1 = *reinterpret_cast<const float4*>(&dal2[s0 + kq + 4]);
-        const float4 d0 = *reinterpret_cast<const float4*>(&dls[s0 + kq]);
-        const float4 d1 = *reinterpret_cast<const float4*>(&dls[s0 + kq + 4]);
-        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool ok = s0 + kq + e <= lrow[i];
-          const float arg = ok ? dal - av[e] : 0.f;
-          mv[e] = ok ? cbv[e] * exp2_fast(arg) * dv[e] : 0.f;
-        }
-      }
-      const bf16x8 fm = Mfma<bf16>::pack(mv);
-#pragma unroll
-      for (int a = 0; a < PT; ++a) acc[i][a] = Mfma<bf16>::mma(fx[a], fm, acc[i][a]);
+    for (int e = 0; e < 8; ++e) {
+      // above the diagonal the exponent is -inf, and exp2 gives exactly 0
+      const float arg = s0 + kq + e <= lrow ? dal - av[e] : -__builtin_inff();
+      mv[e] = static_cast<float>(cbr[e]) * dv[e] * exp2_fast(arg);
     }
+  }
+  const bf16x8 fm = M::pack(mv);
+  const int rb = (s0 + xrow) * P * 2;
 #pragma unroll
-    for (int i = 0; i < RGW; ++i) cur[i] = nxt[i];
+  for (int a = 0; a < P / 16; ++a) {
+    const int off = rb + ((2 * (a ^ xsl)) * 8 + xcol) * 2;
+    const bf16* p = reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(xs) + off);
+    const i16x4 lo = lds_tr16_b64(p);
+    const i16x4 hi = lds_tr16_b64(p + 4 * P);
+    const bf16x8 fx = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    acc[a] = M::mma(fx, fm, acc[a]);
+  }
+}
+
+// Persistent chunk_scan for bf16: workgroup b walks the tiles b, b + grid,
+// b + 2 grid, ... (grid a multiple of 8, so each tile stays on the XCD of its
+// chunk) and has the next tile's inputs in flight while it computes one.
+//
+// Waves w and w + NPAIR share the mirror pair of row groups m0 = pi and
+// m1 = RG-1-pi, which together need RG/2 + 1 intra-chunk k-steps whatever pi
+// is.  The first wave owns m0: its inter-chunk term, all of its k-steps, and
+// the first k-steps of m1 (NS0 k-steps in all).  The second wave owns m1: its
+// inter-chunk term and its remaining NS1 k-steps, which include the diagonal.
+// The first wave hands its partial sums for m1 to the second through LDS.
+//
+// MFMAs compute the transposed tile y^T[p][l]: A = x^T (LDS transpose read)
+// or the state (rows p), B = the decay-masked CB row or the C row (columns
+// l); a lane holds four consecutive p of one token.
+template <int P, int N, int L>
+__global__ __launch_bounds__(4 * L) __attribute__((amdgpu_waves_per_eu(4))) void chunk_scan_bf16_kernel(
+    ChunkMap cm, int nslots, int ntiles, const bf16* __restrict__ x, const bf16* __restrict__ C,
+    const bf16* __restrict__ cb, const float* __restrict__ delta, const float* __restrict__ dAcs,
+    const bf16* __restrict__ states_in, const float* __restrict__ D, int H, int G,
+    bf16* __restrict__ out) {
+  using S = ScanShape<P, N, L>;
+  using M = Mfma<bf16>;
+  __shared__ __align__(16) bf16 xs[L * P];
+  __shared__ __align__(16) bf16 hsm[P * S::HP];
+  __shared__ __align__(16) f32x4 red[S::NPAIR * S::PT * kWave];
+  __shared__ __align__(16) float dal2[L];   // running sum of delta*A, times log2(e)
+  __shared__ __align__(16) float dls[L];    // delta
+  __shared__ __align__(16) float cfs[L];    // delta_s * exp(a_r - a_s), r = last token of s's 32-block
+
+  const int w = wave_id();
+  const int pi = w % S::NPAIR, kap = w / S::NPAIR;
+  const int mg0 = pi, mg1 = S::RG - 1 - pi;          // this pair's row groups
+  const int nq0 = mg0 / 2 + 1;                       // 32-token k-steps reaching m0
+  const int xs1 = S::NS0 - nq0;                      // k-steps of m1 the first wave takes
+  const int mown = kap ? mg1 : mg0;                  // row group this wave finishes
+  const int nslot = kap ? S::NS1 : S::NS0;
+  const uint32_t HPx = (uint32_t)H * P, GN = (uint32_t)G * N;
+  const int grid = gridDim.x;
+
+  ScanSplit sp;
+  sp.mg0 = mg0;
+  sp.mg1 = mg1;
+  sp.nq0 = nq0;
+  sp.xs1 = xs1;
+  sp.kap = kap;
+  sp.mown = mown;
+  sp.nslot = nslot;
+
+  int t = blockIdx.x;
+  if (t >= ntiles) return;                 // uniform over the workgroup
+  ScanTile T = scan_tile(cm, nslots, ntiles, t, H);
+  ScanStage<P, N, L> st;
+  bf16x8 fc[S::NK];
+  bf16x8 cbs[S::NS0];
+  {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    scan_prefetch<P, N, L>(T, tid, st, x, states_in, dAcs, delta, H, HPx);
+    scan_load_c<N>(T, lane, sp, fc, C, H, G, GN);
+    scan_load_cb<P, N, L>(T, lane, sp, cbs, cb, H, G);
   }
 
-  // ---- epilogue: y = acc + D x, written over x in LDS (each element read
-  // and written by one lane), then the rows leave coalesced
-  __syncthreads();
-  const float Dh = D ? D[h] : 0.f;
-  const int p4 = (lane >> 4) * 4;
+  for (; t < ntiles; t += grid) {
+    // Lane indices come from an opaque copy of threadIdx.x each tile, so the
+    // compiler rebuilds the lane's offsets here instead of holding them in
+    // registers across the whole loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
+    const int lr = lane & 15, kg = lane >> 4, kq = kg * 8;
+
+    // ---- stage this tile: x (swizzled), state, running sums, factors
 #pragma unroll
-  for (int i = 0; i < RGW; ++i)
-#pragma unroll
-    for (int a = 0; a < PT; ++a) {
-      bf16x4* e = reinterpret_cast<bf16x4*>(&xs[lrow[i] * XP + 16 * a + p4]);
-      const bf16x4 xo = *e;
-      bf16x4 yo;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) yo[r] = static_cast<bf16>(acc[i][a][r] + Dh * static_cast<float>(xo[r]));
-      *e = yo;
+    for (int u = 0; u < S::XU; ++u) {
+      const int i = tid + S::NT * u, r = i / S::CPR, c = i % S::CPR;
+      *reinterpret_cast<uint4*>(&xs[r * P + ((c ^ xsw<S::CPR>(r)) << 3)]) = st.xv[u];
     }
-  __syncthreads();
 #pragma unroll
-  for (int u = 0; u < XU; ++u) {
-    const int i = tid + NT * u, r = i / CPR, c = i - (i / CPR) * CPR;
-    if (r < d.len)
-      *reinterpret_cast<uint4*>(out + ((int64_t)(d.start + r) * H + h) * P + c * 8) =
-          *reinterpret_cast<const uint4*>(&xs[r * XP + c * 8]);
+    for (int u = 0; u < S::HU; ++u) {
+      const int i = tid + S::NT * u;
+      if (i < S::HN) {
+        const int r = i / S::HPR, c = i % S::HPR;
+        *reinterpret_cast<uint4*>(&hsm[r * S::HP + c * 8]) = st.hv[u];
+      }
+    }
+    {
+      const float a2 = st.dA * kLog2e;
+      const float a2r = __shfl(a2, lane | 31);   // token tid|31 is in this wave
+      if (tid < L) {                             // whole waves
+        dal2[tid] = a2;
+        dls[tid] = st.dl;
+        cfs[tid] = st.dl * exp2_fast(a2r - a2);
+      }
+    }
+    const ScanTile TC = T;
+    const float Dh = D ? D[TC.h] : 0.f;
+    __syncthreads();
+
+    // ---- the next tile's inputs go in flight (after this tile's operands:
+    // the count of outstanding loads drains in issue order)
+    T = scan_tile(cm, nslots, ntiles, t + grid, H);
+    scan_prefetch<P, N, L>(T, tid, st, x, states_in, dAcs, delta, H, HPx);
+
+    // ---- one intra-chunk k-step: acc += x^T (decay-masked CB row)^T for row
+    // group m, tokens s0..s0+31
+    f32x4 acc[S::PT];
+#pragma unroll
+    for (int a = 0; a < S::PT; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int xrow = 8 * kg + (lr >> 2);
+    const int xsl = xsw<S::CPR>(xrow) >> 1;          // rows xrow + 32q (and +4) share it
+    const int xcol = ((lr & 3) >> 1) * 8 + (lr & 1) * 4;
+    // ---- phase A (first wave only): its k-steps of the partner's row group
+#pragma unroll
+    for (int sl = 0; sl < S::NS0; ++sl)
+      if (kap == 0 && sl < xs1)             // wave-uniform
+        scan_kstep<P>(acc, mg1, sl, cbs[sl], lr, kq, xrow, xsl, xcol, dal2, dls, cfs, xs);
+    if (kap == 0) {
+#pragma unroll
+      for (int a = 0; a < S::PT; ++a) {
+        red[(pi * S::PT + a) * kWave + lane] = acc[a];
+        acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+
+    // ---- phase B: inter-chunk term of the own row group,
+    //      y^T[p][l] = exp(a_l) * sum_n state[p][n] C[l][n]
+#pragma unroll
+    for (int k = 0; k < S::NK; ++k)
+#pragma unroll
+      for (int a = 0; a < S::PT; ++a) {
+        const bf16x8 fh = *reinterpret_cast<const bf16x8*>(&hsm[(16 * a + lr) * S::HP + 32 * k + kq]);
+        acc[a] = M::mma(fh, fc[k], acc[a]);
+      }
+    {
+      const float rsc = exp2_fast(dal2[16 * mown + lr]);
+#pragma unroll
+      for (int a = 0; a < S::PT; ++a) acc[a] *= rsc;
+    }
+    // Loads for the next tile go out in the order they will be used: its C
+    // rows now, its CB rows after this tile's last CB use, and only then this
+    // tile's stores (the count of outstanding memory operations drains in
+    // issue order, so a load queued behind a store waits for that store).
+    scan_load_c<N>(T, lane, sp, fc, C, H, G, GN);
+
+    // ---- phase C: the own row group's k-steps
+    {
+      const int lo = kap ? 0 : xs1;
+#pragma unroll
+      for (int sl = 0; sl < S::NS0; ++sl)
+        if (sl >= lo && sl < nslot)           // wave-uniform
+          scan_kstep<P>(acc, mown, kap ? xs1 + sl : sl - xs1, cbs[sl], lr, kq, xrow, xsl, xcol, dal2, dls, cfs, xs);
+    }
+    scan_load_cb<P, N, L>(T, lane, sp, cbs, cb, H, G);
+
+    // ---- the second wave adds the first wave's part, then each wave
+    // finishes its own row group: y = acc + D x, written over x in LDS (each
+    // element read and written by the same lane)
+    __syncthreads();
+    {
+      if (kap == 1) {
+#pragma unroll
+        for (int a = 0; a < S::PT; ++a) acc[a] += red[(pi * S::PT + a) * kWave + lane];
+      }
+      const int l = 16 * mown + lr;
+      const int p4 = kg * 4;
+#pragma unroll
+      for (int a = 0; a < S::PT; ++a) {
+        const int pc = 16 * a + p4;
+        bf16x4* e = reinterpret_cast<bf16x4*>(&xs[l * P + (((pc >> 3) ^ xsw<S::CPR>(l)) << 3) + (pc & 7)]);
+        const bf16x4 xo = *e;
+        bf16x4 yo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yo[r] = static_cast<bf16>(acc[a][r] + Dh * static_cast<float>(xo[r]));
+        *e = yo;
+      }
+    }
+    __syncthreads();
+    {
+      // the tile's rows leave as coalesced 16-byte pieces
+      const auto ry = rows_rsrc(out, TC, H, P, HPx);
+#pragma unroll
+      for (int u = 0; u < S::XU; ++u) {
+        const int i = tid + S::NT * u, r = i / S::CPR, c = i % S::CPR;
+        buf_store16(ry, ((uint32_t)r * HPx + c * 8) * 2u,
+                    *reinterpret_cast<const uint4*>(&xs[r * P + ((c ^ xsw<S::CPR>(r)) << 3)]));
+      }
+    }
+    __syncthreads();                       // LDS free for the next tile
   }
 }
 
 }  // namespace
+
+// Workgroups that stay resident per CU times the CU count, cached per device.
+template <typename K>
+static int persistent_grid(K kernel, int block, int lds_dynamic) {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] > 0) return cached[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds_dynamic) != hipSuccess)
+    return 0;
+  const int g = (cus * per_cu) / 8 * 8;
+  cached[dev] = g;
+  return g;
+}
 
 template <typename T, int P, int N, int L>
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s) {
   static_assert(L % 64 == 0, "chunk size must be a multiple of 64");
   if (a.max_chunks <= 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((chunk_scan_bf16_kernel<P, N, L>), dim3(xcd_grid(a.max_chunks, a.H)),
-                       dim3(64 * kScanWaves<L>), 0, s, a.cmap(), a.max_chunks, (const bf16*)a.x,
-                       (const bf16*)a.C, (const bf16*)a.cb, a.delta, a.dAcs,
-                       (const bf16*)a.states_in, a.D,
-                       a.H, a.G, (bf16*)a.out);
+    auto kern = chunk_scan_bf16_kernel<P, N, L>;
+    const int ntiles = xcd_grid(a.max_chunks, a.H);
+    const int g = persistent_grid(kern, 4 * L, 0);
+    if (g <= 0) return hipErrorInvalidDevice;
+    const int grid = min(ntiles, g);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(4 * L), 0, s, a.cmap(), a.max_chunks, ntiles,
+                       (const bf16*)a.x, (const bf16*)a.C, (const bf16*)a.cb, a.delta, a.dAcs,
+                       (const bf16*)a.states_in, a.D, a.H, a.G, (bf16*)a.out);
   } else {
     dim3 grid(a.max_chunks * (L / 64), a.H);
     hipLaunchKernelGGL((chunk_scan_kernel<T, P, N, L>), grid, dim3(256), 0, s, a.cmap(),
