@@ -348,15 +348,11 @@ __device__ __forceinline__ void scan_load_cb(const ScanTile& T, int lane, const 
   }
 }
 
-// One intra-chunk k-step of row group m (tokens s0 = 32q .. s0+31):
-// acc += x^T (decay-masked CB rows)^T, the B operand built in registers from
-// the lane's CB row piece.
-template <int P>
-__device__ __forceinline__ void scan_kstep(f32x4 (&acc)[P / 16], int m, int q, const bf16x8& cbr,
-                                           int lr, int kq, int xrow, int xsl, int xcol,
-                                           const float* dal2, const float* dls, const float* cfs,
-                                           const bf16* xs) {
-  using M = Mfma<bf16>;
+// Decay-masked CB piece of row group m at k-step q (the MFMA B operand):
+// M[l][s] = CB[l][s] exp(a_l - a_s) delta_s for s <= l, else 0.
+__device__ __forceinline__ bf16x8 scan_masked_cb(int m, int q, const bf16x8& cbr, int lr, int kq,
+                                                 const float* dal2, const float* dls,
+                                                 const float* cfs) {
   const int s0 = 32 * q;
   const int lrow = 16 * m + lr;
   const float dal = dal2[lrow];
@@ -382,17 +378,32 @@ __device__ __forceinline__ void scan_kstep(f32x4 (&acc)[P / 16], int m, int q, c
       mv[e] = static_cast<float>(cbr[e]) * dv[e] * exp2_fast(arg);
     }
   }
-  const bf16x8 fm = M::pack(mv);
-  const int rb = (s0 + xrow) * P * 2;
+  return Mfma<bf16>::pack(mv);
+}
+
+// x^T operand (rows p of p-tile a, 8 consecutive tokens of k-step q per lane)
+// by transpose read from the swizzled x tile.
+template <int P>
+__device__ __forceinline__ bf16x8 scan_x_operand(const bf16* xs, int q, int a, int xrow, int xsl,
+                                                 int xcol) {
+  const int off = ((32 * q + xrow) * P + (2 * (a ^ xsl)) * 8 + xcol) * 2;
+  const bf16* p = reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(xs) + off);
+  const i16x4 lo = lds_tr16_b64(p);
+  const i16x4 hi = lds_tr16_b64(p + 4 * P);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// One intra-chunk k-step of row group m (tokens 32q .. 32q+31):
+// acc += x^T (decay-masked CB rows)^T.
+template <int P>
+__device__ __forceinline__ void scan_kstep(f32x4 (&acc)[P / 16], int m, int q, const bf16x8& cbr,
+                                           int lr, int kq, int xrow, int xsl, int xcol,
+                                           const float* dal2, const float* dls, const float* cfs,
+                                           const bf16* xs) {
+  const bf16x8 fm = scan_masked_cb(m, q, cbr, lr, kq, dal2, dls, cfs);
 #pragma unroll
-  for (int a = 0; a < P / 16; ++a) {
-    const int off = rb + ((2 * (a ^ xsl)) * 8 + xcol) * 2;
-    const bf16* p = reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(xs) + off);
-    const i16x4 lo = lds_tr16_b64(p);
-    const i16x4 hi = lds_tr16_b64(p + 4 * P);
-    const bf16x8 fx = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    acc[a] = M::mma(fx, fm, acc[a]);
-  }
+  for (int a = 0; a < P / 16; ++a)
+    acc[a] = Mfma<bf16>::mma(scan_x_operand<P>(xs, q, a, xrow, xsl, xcol), fm, acc[a]);
 }
 
 // Persistent chunk_scan for bf16: workgroup b walks the tiles b, b + grid,
@@ -585,7 +596,205 @@ __global__ __launch_bounds__(4 * L) __attribute__((amdgpu_waves_per_eu(4))) void
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, one workgroup per (chunk, head) tile: for small grids (a few tiles per
+// CU), where two tiles resident per CU overlap each other's loads better than
+// one persistent workgroup overlaps its own.  Waves own mirror pairs of row
+// groups (two per wave for L >= 128); every load is issued up front in the
+// order of use; x is staged XOR-swizzled and read with the transpose read;
+// the next k-step's CB rows are in flight while one is multiplied.
+template <int L> constexpr int kTileWaves = (L / 16) / 2 < 4 ? 4 : (L / 16) / 2;
+
+template <int P, int N, int L>
+__global__ __launch_bounds__(64 * kTileWaves<L>) __attribute__((amdgpu_waves_per_eu(4))) void
+chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
+                            const bf16* __restrict__ C, const bf16* __restrict__ cb,
+                            const float* __restrict__ delta, const float* __restrict__ dAcs,
+                            const bf16* __restrict__ states_in, const float* __restrict__ D, int H,
+                            int G, bf16* __restrict__ out) {
+  static_assert(L % 64 == 0 && P % 32 == 0 && N % 32 == 0, "tile shape");
+  using M = Mfma<bf16>;
+  constexpr int NW = kTileWaves<L>;
+  constexpr int NT = 64 * NW;            // threads
+  constexpr int HP = N + 8;              // state tile pitch: conflict-free 16-byte row reads
+  constexpr int RG = L / 16;             // 16-row groups of the chunk
+  constexpr int RGW = RG / NW;           // row groups per wave: 1 or 2
+  static_assert(RGW * NW == RG && (RGW == 1 || RGW == 2), "row-group split");
+  constexpr int PT = P / 16;
+  constexpr int NK = N / 32;             // k-steps of the inter-chunk term
+  constexpr int CPR = P / 8;             // 16-byte pieces per x row
+  constexpr int XU = L * CPR / NT;       // x pieces per thread
+  constexpr int HPR = N / 8;             // 16-byte pieces per state row
+  constexpr int HU = (P * HPR + NT - 1) / NT;
+  static_assert((L * CPR) % NT == 0 && L <= NT, "x staging");
+  __shared__ __align__(16) bf16 xs[L * P];
+  __shared__ __align__(16) bf16 hsm[P * HP];
+  __shared__ __align__(16) float dal2[L];   // running sum of delta*A, times log2(e)
+  __shared__ __align__(16) float dls[L];    // delta
+  __shared__ __align__(16) float cfs[L];    // delta_s * exp(a_r - a_s), r = last token of s's 32-block
+
+  const int2 jh = xcd_chunk_head(blockIdx.x, H);
+  if (jh.x >= nslots) return;
+  ScanTile T{jh.x, jh.y, 0, 0};
+  {
+    const ChunkDesc d = cm.desc(T.j);
+    T.start = d.start;
+    T.len = d.len;
+  }
+  if (T.len <= 0) return;
+  const int h = T.h, g = h / (H / G);
+  const uint32_t HPx = (uint32_t)H * P, GN = (uint32_t)G * N;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
+  const int lr = lane & 15, kg = lane >> 4, kq = kg * 8;
+  // Row groups of this wave; with two per wave they pair from both ends of
+  // the chunk, so every wave carries the same causal work.
+  int mg[RGW];
+  mg[0] = w;
+  if constexpr (RGW == 2) mg[1] = RG - 1 - w;
+  int lrow[RGW], nq[RGW];
+#pragma unroll
+  for (int i = 0; i < RGW; ++i) {
+    lrow[i] = 16 * mg[i] + lr;
+    nq[i] = mg[i] / 2 + 1;               // k-steps that reach this row group
+  }
+
+  // ---- global loads issued together, in the order they are used
+  const auto rx = rows_rsrc(x, T, H, P, HPx);
+  uint4 xv[XU];
+#pragma unroll
+  for (int u = 0; u < XU; ++u) {
+    const int i = tid + NT * u, r = i / CPR, c = i % CPR;
+    xv[u] = buf_load16(rx, ((uint32_t)r * HPx + c * 8) * 2u);
+  }
+  const int64_t jhl = (int64_t)T.j * H + h;
+  const auto rh = buf_rsrc(states_in + jhl * P * N, P * N * 2);
+  uint4 hv[HU];
+#pragma unroll
+  for (int u = 0; u < HU; ++u) hv[u] = buf_load16(rh, (uint32_t)(tid + NT * u) * 16);
+  const float dA_t = buf_load4(buf_rsrc(dAcs + jhl * L, L * 4), tid * 4);
+  const float dl_t = buf_load4(buf_rsrc(delta + jhl * L, L * 4), tid * 4);
+  const auto rc = buf_rsrc(C + ((int64_t)T.start * G + g) * N, ((uint32_t)(T.len - 1) * GN + N) * 2u);
+  bf16x8 fc[RGW][NK];                      // C rows of this lane, all n-steps
+#pragma unroll
+  for (int i = 0; i < RGW; ++i)
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+      fc[i][k] = __builtin_bit_cast(bf16x8, buf_load16(rc, ((uint32_t)lrow[i] * GN + 32 * k + kq) * 2u));
+  const auto rcb = buf_rsrc(cb + ((int64_t)T.j * G + g) * L * L, L * L * 2);
+  uint32_t cbo[RGW];
+  bf16x8 cur[RGW];                         // CB rows of the current k-step
+#pragma unroll
+  for (int i = 0; i < RGW; ++i) {
+    cbo[i] = ((uint32_t)lrow[i] * L + kq) * 2u;
+    cur[i] = __builtin_bit_cast(bf16x8, buf_load16(rcb, cbo[i]));
+  }
+
+  // ---- stage x (swizzled; rows past the end arrived as zeros), the state,
+  // the running sums and the per-token factors
+#pragma unroll
+  for (int u = 0; u < XU; ++u) {
+    const int i = tid + NT * u, r = i / CPR, c = i % CPR;
+    *reinterpret_cast<uint4*>(&xs[r * P + ((c ^ xsw<CPR>(r)) << 3)]) = xv[u];
+  }
+#pragma unroll
+  for (int u = 0; u < HU; ++u) {
+    const int i = tid + NT * u, r = i / HPR, c = i % HPR;
+    if (i < P * HPR) *reinterpret_cast<uint4*>(&hsm[r * HP + c * 8]) = hv[u];
+  }
+  {
+    const float a2 = dA_t * kLog2e;
+    const float a2r = __shfl(a2, lane | 31);   // token tid|31 is in this wave
+    if (tid < L) {                             // whole waves
+      dal2[tid] = a2;
+      dls[tid] = dl_t;
+      cfs[tid] = dl_t * exp2_fast(a2r - a2);
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc[RGW][PT];
+#pragma unroll
+  for (int i = 0; i < RGW; ++i)
+#pragma unroll
+    for (int a = 0; a < PT; ++a) acc[i][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- inter-chunk term: y^T[p][l] = exp(a_l) * sum_n state[p][n] C[l][n]
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    bf16x8 fh[PT];
+#pragma unroll
+    for (int a = 0; a < PT; ++a)
+      fh[a] = *reinterpret_cast<const bf16x8*>(&hsm[(16 * a + lr) * HP + 32 * k + kq]);
+#pragma unroll
+    for (int i = 0; i < RGW; ++i)
+#pragma unroll
+      for (int a = 0; a < PT; ++a) acc[i][a] = M::mma(fh[a], fc[i][k], acc[i][a]);
+  }
+#pragma unroll
+  for (int i = 0; i < RGW; ++i) {
+    const float rsc = exp2_fast(dal2[lrow[i]]);
+#pragma unroll
+    for (int a = 0; a < PT; ++a) acc[i][a] *= rsc;
+  }
+
+  // ---- intra-chunk term, k-steps outer: the x^T operands of a step serve
+  // both row groups of the wave; the next step's CB rows are in flight.
+  const int xrow = 8 * kg + (lr >> 2);
+  const int xsl = xsw<CPR>(xrow) >> 1;
+  const int xcol = ((lr & 3) >> 1) * 8 + (lr & 1) * 4;
+  const int nq_wave = nq[RGW - 1];
+  for (int q = 0; q < nq_wave; ++q) {
+    const int sn = min(32 * q + 32, L - 32);   // next step (clamped: always in the row)
+    bf16x8 nxt[RGW];
+#pragma unroll
+    for (int i = 0; i < RGW; ++i) nxt[i] = __builtin_bit_cast(bf16x8, buf_load16(rcb, cbo[i] + sn * 2));
+    bf16x8 fm[RGW];
+#pragma unroll
+    for (int i = 0; i < RGW; ++i)
+      if (q < nq[i]) fm[i] = scan_masked_cb(mg[i], q, cur[i], lr, kq, dal2, dls, cfs);
+#pragma unroll
+    for (int a = 0; a < PT; ++a) {
+      const bf16x8 fx = scan_x_operand<P>(xs, q, a, xrow, xsl, xcol);
+#pragma unroll
+      for (int i = 0; i < RGW; ++i)
+        if (q < nq[i]) acc[i][a] = M::mma(fx, fm[i], acc[i][a]);   // wave-uniform
+    }
+#pragma unroll
+    for (int i = 0; i < RGW; ++i) cur[i] = nxt[i];
+  }
+
+  // ---- epilogue: y = acc + D x, written over x in LDS (each element read
+  // and written by one lane), then the rows leave coalesced
+  __syncthreads();
+  const float Dh = D ? D[h] : 0.f;
+  const int p4 = kg * 4;
+#pragma unroll
+  for (int i = 0; i < RGW; ++i)
+#pragma unroll
+    for (int a = 0; a < PT; ++a) {
+      const int l = lrow[i], pc = 16 * a + p4;
+      bf16x4* e = reinterpret_cast<bf16x4*>(&xs[l * P + (((pc >> 3) ^ xsw<CPR>(l)) << 3) + (pc & 7)]);
+      const bf16x4 xo = *e;
+      bf16x4 yo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yo[r] = static_cast<bf16>(acc[i][a][r] + Dh * static_cast<float>(xo[r]));
+      *e = yo;
+    }
+  __syncthreads();
+  const auto ry = rows_rsrc(out, T, H, P, HPx);
+#pragma unroll
+  for (int u = 0; u < XU; ++u) {
+    const int i = tid + NT * u, r = i / CPR, c = i % CPR;
+    buf_store16(ry, ((uint32_t)r * HPx + c * 8) * 2u,
+                *reinterpret_cast<const uint4*>(&xs[r * P + ((c ^ xsw<CPR>(r)) << 3)]));
+  }
+}
+
 }  // namespace
+
+// The persistent kernel pays off once each resident workgroup has this many
+// tiles to walk; below that, one workgroup per tile.
+constexpr int kPersistentMinTiles = 6;
 
 // Workgroups that stay resident per CU times the CU count, cached per device.
 template <typename K>
@@ -612,10 +821,16 @@ hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s) {
     const int ntiles = xcd_grid(a.max_chunks, a.H);
     const int g = persistent_grid(kern, 4 * L, 0);
     if (g <= 0) return hipErrorInvalidDevice;
-    const int grid = min(ntiles, g);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(4 * L), 0, s, a.cmap(), a.max_chunks, ntiles,
-                       (const bf16*)a.x, (const bf16*)a.C, (const bf16*)a.cb, a.delta, a.dAcs,
-                       (const bf16*)a.states_in, a.D, a.H, a.G, (bf16*)a.out);
+    if (ntiles >= kPersistentMinTiles * g) {
+      hipLaunchKernelGGL(kern, dim3(g), dim3(4 * L), 0, s, a.cmap(), a.max_chunks, ntiles,
+                         (const bf16*)a.x, (const bf16*)a.C, (const bf16*)a.cb, a.delta, a.dAcs,
+                         (const bf16*)a.states_in, a.D, a.H, a.G, (bf16*)a.out);
+    } else {
+      hipLaunchKernelGGL((chunk_scan_bf16_tile_kernel<P, N, L>), dim3(ntiles),
+                         dim3(64 * kTileWaves<L>), 0, s, a.cmap(), a.max_chunks, (const bf16*)a.x,
+                         (const bf16*)a.C, (const bf16*)a.cb, a.delta, a.dAcs,
+                         (const bf16*)a.states_in, a.D, a.H, a.G, (bf16*)a.out);
+    }
   } else {
     dim3 grid(a.max_chunks * (L / 64), a.H);
     hipLaunchKernelGGL((chunk_scan_kernel<T, P, N, L>), grid, dim3(256), 0, s, a.cmap(),

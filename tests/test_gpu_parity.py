@@ -85,6 +85,28 @@ def test_ragged_shapes(shape, init_std):
     check(prob, inp)
 
 
+# Shapes with enough (chunk, head) tiles that the bf16 chunk_scan runs its
+# persistent kernel (at least 6 tiles per resident workgroup; the sizes below
+# leave a margin of 2-5x for every supported chunk size and tile shape), with
+# ragged tails and initial states; the small shapes above run the one
+# workgroup per tile kernel.
+PERSISTENT = [
+    # (b, T, H, P, N, G, L)
+    (1, 16384 + 40, 128, 64, 128, 4, 64),
+    (1, 16384 + 100, 96, 64, 128, 8, 128),
+    (3, 5000, 64, 64, 128, 4, 256),
+    (2, 20000, 32, 32, 32, 2, 64),
+]
+
+
+@pytest.mark.parametrize("shape", PERSISTENT, ids=lambda s: "b{}T{}H{}P{}N{}G{}L{}".format(*s))
+def test_persistent_path_configs(shape):
+    b, T, H, P, N, G, L = shape
+    prob = Problem(b, T, H, P, N, G, L, "bf16")
+    inp = make_inputs(prob, Recipe(init_std=0.2), seed=L + H)
+    check(prob, inp, heads=[0, H // 2 + 1, H - 1])
+
+
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 255, 256, 257])
 def test_edge_lengths(T):
     prob = Problem(1, T, 4, 64, 128, 2, 64 if T < 200 else 256, "bf16")
