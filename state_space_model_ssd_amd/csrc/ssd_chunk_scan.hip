@@ -184,25 +184,6 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
 
 
 // ------------------------------------------------------------- bf16 kernel
-// Buffer resources: 32-bit offsets from a per-tile base, range-checked by the
-// hardware.  A load past num_records returns zeros and a store past it is
-// dropped, so rows past a chunk's end need neither clamps nor branches, and
-// no access can leave the tile.
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
-}
-
 template <int P, int N, int L>
 struct ScanShape {
   static constexpr int RG = L / 16;        // 16-row groups of a chunk
@@ -224,16 +205,6 @@ struct ScanShape {
   static_assert(L % 64 == 0 && P % 32 == 0 && N % 32 == 0, "tile shape");
   static_assert((L * CPR) % NT == 0 && XU >= 1, "x staging");
 };
-
-// The x tile sits in LDS unpadded, token-major, with the 16-byte pieces of
-// row r permuted by XOR with xsw(r).  The transpose reads of one instruction
-// touch rows r0 + {0..3} and r0 + {8..11} (r0 a multiple of 8) at two
-// adjacent pieces; the XOR spreads those 8 rows x 2 pieces over distinct bank
-// groups, whether the LDS serves 16 or 32 lanes of 8-byte reads per clock.
-template <int CPR>
-__device__ __forceinline__ int xsw(int r) {
-  return (2 * ((r & 3) ^ ((r >> 3) & 1))) & (CPR - 1);
-}
 
 // One (chunk slot, head) tile as the persistent loop sees it (wave-uniform).
 struct ScanTile {
@@ -480,7 +451,7 @@ __global__ __launch_bounds__(4 * L) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
     for (int u = 0; u < S::XU; ++u) {
       const int i = tid + S::NT * u, r = i / S::CPR, c = i % S::CPR;
-      *reinterpret_cast<uint4*>(&xs[r * P + ((c ^ xsw<S::CPR>(r)) << 3)]) = st.xv[u];
+      *reinterpret_cast<uint4*>(&xs[r * P + ((c ^ tile_sw<S::CPR>(r)) << 3)]) = st.xv[u];
     }
 #pragma unroll
     for (int u = 0; u < S::HU; ++u) {
@@ -514,7 +485,7 @@ __global__ __launch_bounds__(4 * L) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
     for (int a = 0; a < S::PT; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int xrow = 8 * kg + (lr >> 2);
-    const int xsl = xsw<S::CPR>(xrow) >> 1;          // rows xrow + 32q (and +4) share it
+    const int xsl = tile_sw<S::CPR>(xrow) >> 1;          // rows xrow + 32q (and +4) share it
     const int xcol = ((lr & 3) >> 1) * 8 + (lr & 1) * 4;
     // ---- phase A (first wave only): its k-steps of the partner's row group
 #pragma unroll
@@ -573,7 +544,7 @@ __global__ __launch_bounds__(4 * L) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
       for (int a = 0; a < S::PT; ++a) {
         const int pc = 16 * a + p4;
-        bf16x4* e = reinterpret_cast<bf16x4*>(&xs[l * P + (((pc >> 3) ^ xsw<S::CPR>(l)) << 3) + (pc & 7)]);
+        bf16x4* e = reinterpret_cast<bf16x4*>(&xs[l * P + (((pc >> 3) ^ tile_sw<S::CPR>(l)) << 3) + (pc & 7)]);
         const bf16x4 xo = *e;
         bf16x4 yo;
 #pragma unroll
@@ -589,7 +560,7 @@ __global__ __launch_bounds__(4 * L) __attribute__((amdgpu_waves_per_eu(4))) void
       for (int u = 0; u < S::XU; ++u) {
         const int i = tid + S::NT * u, r = i / S::CPR, c = i % S::CPR;
         buf_store16(ry, ((uint32_t)r * HPx + c * 8) * 2u,
-                    *reinterpret_cast<const uint4*>(&xs[r * P + ((c ^ xsw<S::CPR>(r)) << 3)]));
+                    *reinterpret_cast<const uint4*>(&xs[r * P + ((c ^ tile_sw<S::CPR>(r)) << 3)]));
       }
     }
     __syncthreads();                       // LDS free for the next tile
@@ -694,7 +665,7 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
 #pragma unroll
   for (int u = 0; u < XU; ++u) {
     const int i = tid + NT * u, r = i / CPR, c = i % CPR;
-    *reinterpret_cast<uint4*>(&xs[r * P + ((c ^ xsw<CPR>(r)) << 3)]) = xv[u];
+    *reinterpret_cast<uint4*>(&xs[r * P + ((c ^ tile_sw<CPR>(r)) << 3)]) = xv[u];
   }
 #pragma unroll
   for (int u = 0; u < HU; ++u) {
@@ -740,7 +711,7 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
   // ---- intra-chunk term, k-steps outer: the x^T operands of a step serve
   // both row groups of the wave; the next step's CB rows are in flight.
   const int xrow = 8 * kg + (lr >> 2);
-  const int xsl = xsw<CPR>(xrow) >> 1;
+  const int xsl = tile_sw<CPR>(xrow) >> 1;
   const int xcol = ((lr & 3) >> 1) * 8 + (lr & 1) * 4;
   const int nq_wave = nq[RGW - 1];
   for (int q = 0; q < nq_wave; ++q) {
@@ -773,7 +744,7 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
 #pragma unroll
     for (int a = 0; a < PT; ++a) {
       const int l = lrow[i], pc = 16 * a + p4;
-      bf16x4* e = reinterpret_cast<bf16x4*>(&xs[l * P + (((pc >> 3) ^ xsw<CPR>(l)) << 3) + (pc & 7)]);
+      bf16x4* e = reinterpret_cast<bf16x4*>(&xs[l * P + (((pc >> 3) ^ tile_sw<CPR>(l)) << 3) + (pc & 7)]);
       const bf16x4 xo = *e;
       bf16x4 yo;
 #pragma unroll
@@ -786,7 +757,7 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
   for (int u = 0; u < XU; ++u) {
     const int i = tid + NT * u, r = i / CPR, c = i % CPR;
     buf_store16(ry, ((uint32_t)r * HPx + c * 8) * 2u,
-                *reinterpret_cast<const uint4*>(&xs[r * P + ((c ^ xsw<CPR>(r)) << 3)]));
+                *reinterpret_cast<const uint4*>(&xs[r * P + ((c ^ tile_sw<CPR>(r)) << 3)]));
   }
 }
 

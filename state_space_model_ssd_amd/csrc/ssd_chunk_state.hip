@@ -131,21 +131,30 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(
 
 
 // ------------------------------------------------------------- bf16 kernels
+// Threads of the bf16 chunk_state and front workgroups (8 waves).
+constexpr int kStateThreads = 512;
+
 template <int P, int N, int L>
 struct StateSmem {
-  static constexpr int KS = 64;                  // tokens per slice
-  static constexpr int XP = P + 8, BP = N + 8;   // LDS row pitches (elements)
-  bf16 xs[KS * XP];
-  bf16 bs[KS * BP];
+  static constexpr int KS = 64;    // tokens per slice
+  bf16 xs[KS * P];                 // weighted x slice, token-major, swizzled
+  bf16 bs[KS * N];                 // B slice, token-major, swizzled
   float wl[L];
   float cum[L];
-  float wave_tot[4];
+  float wave_tot[kStateThreads / 64];
 };
 
-// chunk_state for chunk j, head h (256 threads).  With CUMSUM the workgroup
+// chunk_state for chunk j, head h (kStateThreads threads).  With CUMSUM the workgroup
 // also runs chunk_cumsum for its (chunk, head) -- the step and its running
 // sum come from dt here and are written to delta/dAcs for the later stages --
 // otherwise it reads them from delta/dAcs.
+//
+// Each 64-token slice of x (scaled by w[l] in fp32 and rounded once to bf16)
+// and of B is staged token-major in LDS; the MFMA operands come out through
+// the transpose read.  The MFMAs produce the transposed tile S^T[n][p], so a
+// lane holds four consecutive n of one p and S leaves in 16-byte stores.
+// Loads and stores go through buffer resources bounded by the chunk: tokens
+// past its end read as zeros.
 template <int P, int N, int L, bool CUMSUM>
 __device__ __forceinline__ void chunk_state_bf16_body(
     const ChunkDesc& d, int j, int h, const bf16* __restrict__ x, const bf16* __restrict__ B,
@@ -154,32 +163,38 @@ __device__ __forceinline__ void chunk_state_bf16_body(
     int H, int G, float* __restrict__ S, StateSmem<P, N, L>& sm) {
   static_assert(L % 64 == 0 && L <= 256 && P % 16 == 0 && N % 16 == 0, "tile shape");
   using SM = StateSmem<P, N, L>;
-  constexpr int KS = SM::KS, XP = SM::XP, BP = SM::BP;
+  constexpr int KS = SM::KS;
   constexpr int XC = P / 8, BC = N / 8;   // 16-byte pieces per row
-  constexpr int XU = (KS * XC + 255) / 256, BU = (KS * BC + 255) / 256;
+  constexpr int TH = kStateThreads, NWV = TH / 64;
+  constexpr int XU = (KS * XC + TH - 1) / TH, BU = (KS * BC + TH - 1) / TH;
   constexpr int PT = P / 16, NT = N / 16;
-  constexpr int WN = NT < 4 ? NT : 4;
-  constexpr int WP = (4 / WN) < PT ? (4 / WN) : PT;
+  constexpr int WN = NT < 4 ? NT : 4;                       // waves along n
+  constexpr int WP = (NWV / WN) < PT ? (NWV / WN) : PT;     // waves along p
   constexpr int TP = PT / WP, TN = NT / WN;
   static_assert(PT % WP == 0 && NT % WN == 0, "tile split");
   const int g = h / (H / G);
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
   const int last = d.len - 1;
+  const uint32_t HP = (uint32_t)H * P, GN = (uint32_t)G * N;
+  const auto rx = buf_rsrc(x + ((int64_t)d.start * H + h) * P, ((uint32_t)last * HP + P) * 2u);
+  const auto rb = buf_rsrc(B + ((int64_t)d.start * G + g) * N, ((uint32_t)last * GN + N) * 2u);
 
   uint4 xr[XU], br[BU];
-  auto fetch = [&](int l0) {
-#pragma unroll
-    for (int u = 0; u < XU; ++u) {
-      const int i = min(tid + 256 * u, KS * XC - 1), r = i / XC, c = i - (i / XC) * XC;
-      xr[u] = *reinterpret_cast<const uint4*>(x + ((int64_t)(d.start + min(l0 + r, last)) * H + h) * P + c * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < BU; ++u) {
-      const int i = min(tid + 256 * u, KS * BC - 1), r = i / BC, c = i - (i / BC) * BC;
-      br[u] = *reinterpret_cast<const uint4*>(B + ((int64_t)(d.start + min(l0 + r, last)) * G + g) * N + c * 8);
-    }
-  };
-  fetch(0);                               // in flight while the weights are formed
+  const int nsl = (d.len + KS - 1) / KS;
+  // slice `sl` into registers (pieces past a thread's share, if any, read
+  // out of range as zeros and are never staged)
+#define SSD_STATE_FETCH(sl)                                                               \
+  {                                                                                       \
+    _Pragma("unroll") for (int u = 0; u < XU; ++u) {                                      \
+      const int i = tid + TH * u, r = (sl) * KS + i / XC, c = i % XC;                     \
+      xr[u] = buf_load16(rx, i < KS * XC ? ((uint32_t)r * HP + c * 8) * 2u : 0xFFFFFFF0u);  \
+    }                                                                                     \
+    _Pragma("unroll") for (int u = 0; u < BU; ++u) {                                      \
+      const int i = tid + TH * u, r = (sl) * KS + i / BC, c = i % BC;                     \
+      br[u] = buf_load16(rb, i < KS * BC ? ((uint32_t)r * GN + c * 8) * 2u : 0xFFFFFFF0u);  \
+    }                                                                                     \
+  }
+  SSD_STATE_FETCH(0)                      // in flight while the weights are formed
 
   // w[l] = exp(a_last - a_l) * delta_l
   if constexpr (CUMSUM) {
@@ -198,77 +213,72 @@ __device__ __forceinline__ void chunk_state_bf16_body(
     const float* dA = dAcs + ((int64_t)j * H + h) * L;
     const float* dl = delta + ((int64_t)j * H + h) * L;
     const float lastv = dA[last];
-    for (int l = tid; l < L; l += 256)
+    for (int l = tid; l < L; l += TH)
       sm.wl[l] = (l < d.len) ? exp2_fast((lastv - dA[l]) * kLog2e) * dl[l] : 0.f;
   }
 
   const int wp = w / WN, wn = w - (w / WN) * WN;
   const bool active = w < WP * WN;
-  f32x4 acc[TP][TN];
+  f32x4 acc[TN][TP];                      // S^T tiles: rows n, columns p
 #pragma unroll
-  for (int a = 0; a < TP; ++a)
+  for (int b = 0; b < TN; ++b)
 #pragma unroll
-    for (int b = 0; b < TN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < TP; ++a) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nsl = (d.len + KS - 1) / KS;
   __syncthreads();                        // wl ready
   for (int sl = 0; sl < nsl; ++sl) {
-    const int l0 = sl * KS;
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
-      const int i = tid + 256 * u, r = i / XC, c = i - (i / XC) * XC;
+      const int i = tid + TH * u, r = i / XC, c = i % XC;
       if (i < KS * XC) {
         const bf16x8 v = __builtin_bit_cast(bf16x8, xr[u]);
-        const float wv = sm.wl[l0 + r];   // 0 past the chunk's end
+        const float wv = sm.wl[sl * KS + r];   // 0 past the chunk's end
         bf16x8 o;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = static_cast<bf16>(static_cast<float>(v[e]) * wv);
-        *reinterpret_cast<bf16x8*>(&sm.xs[r * XP + c * 8]) = o;
+        *reinterpret_cast<bf16x8*>(&sm.xs[tile_at<P>(r, c * 8)]) = o;
       }
     }
 #pragma unroll
     for (int u = 0; u < BU; ++u) {
-      const int i = tid + 256 * u, r = i / BC, c = i - (i / BC) * BC;
-      if (i < KS * BC)
-        *reinterpret_cast<uint4*>(&sm.bs[r * BP + c * 8]) =
-            (l0 + r < d.len) ? br[u] : make_uint4(0, 0, 0, 0);
+      const int i = tid + TH * u, r = i / BC, c = i % BC;
+      if (i < KS * BC) *reinterpret_cast<uint4*>(&sm.bs[tile_at<N>(r, c * 8)]) = br[u];
     }
     __syncthreads();
-    if (sl + 1 < nsl) fetch(l0 + KS);     // in flight while this slice multiplies
+    if (sl + 1 < nsl) SSD_STATE_FETCH(sl + 1)   // in flight while this slice multiplies
     if (active) {
 #pragma unroll
       for (int k0 = 0; k0 < KS; k0 += 32) {
         bf16x8 fa[TP], fb[TN];
 #pragma unroll
-        for (int a = 0; a < TP; ++a) fa[a] = lds_operand_kmajor(sm.xs, XP, k0, 16 * (wp * TP + a), lane);
+        for (int a = 0; a < TP; ++a) fa[a] = lds_operand_sw<P>(sm.xs, k0, 16 * (wp * TP + a), lane);
 #pragma unroll
-        for (int b = 0; b < TN; ++b) fb[b] = lds_operand_kmajor(sm.bs, BP, k0, 16 * (wn * TN + b), lane);
+        for (int b = 0; b < TN; ++b) fb[b] = lds_operand_sw<N>(sm.bs, k0, 16 * (wn * TN + b), lane);
 #pragma unroll
-        for (int a = 0; a < TP; ++a)
+        for (int b = 0; b < TN; ++b)
 #pragma unroll
-          for (int b = 0; b < TN; ++b) acc[a][b] = Mfma<bf16>::mma(fa[a], fb[b], acc[a][b]);
+          for (int a = 0; a < TP; ++a) acc[b][a] = Mfma<bf16>::mma(fb[b], fa[a], acc[b][a]);
       }
     }
     __syncthreads();
   }
+#undef SSD_STATE_FETCH
 
   if (!active) return;
-  float* out = S + ((int64_t)j * H + h) * P * N;
+  const auto rs = buf_rsrc(S + ((int64_t)j * H + h) * P * N, P * N * 4);
   const int lr = lane & 15;
 #pragma unroll
-  for (int a = 0; a < TP; ++a)
+  for (int b = 0; b < TN; ++b)
 #pragma unroll
-    for (int b = 0; b < TN; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = 16 * (wp * TP + a) + (lane >> 4) * 4 + r;
-        const int n = 16 * (wn * TN + b) + lr;
-        out[(int64_t)p * N + n] = acc[a][b][r];
-      }
+    for (int a = 0; a < TP; ++a) {
+      const int p = 16 * (wp * TP + a) + lr;
+      const int n = 16 * (wn * TN + b) + (lane >> 4) * 4;
+      buf_store16(rs, ((uint32_t)p * N + n) * 4u, __builtin_bit_cast(uint4, acc[b][a]));
+    }
 }
 
 template <int P, int N, int L>
-__global__ __launch_bounds__(256) void chunk_state_bf16_kernel(
+__global__ __launch_bounds__(kStateThreads) void chunk_state_bf16_kernel(
     ChunkMap cm, int nslots, const bf16* __restrict__ x, const bf16* __restrict__ B,
     float* __restrict__ delta, float* __restrict__ dAcs, int H, int G, float* __restrict__ S) {
   __shared__ __align__(16) StateSmem<P, N, L> sm;
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(
 // (chunk, head) each.  The three stages are independent of each other's
 // outputs here, so they share the machine instead of running back to back.
 template <int P, int N, int L>
-__global__ __launch_bounds__(256) void front_bf16_kernel(
+__global__ __launch_bounds__(kStateThreads) void front_bf16_kernel(
     ChunkMap cm, int nslots, int nbmm, int G, const bf16* __restrict__ x,
     const bf16* __restrict__ B, const bf16* __restrict__ C, const float* __restrict__ dt,
     const float* __restrict__ dt_bias, const float* __restrict__ A, float dt_min, float dt_max,
@@ -305,7 +315,7 @@ __global__ __launch_bounds__(256) void front_bf16_kernel(
     const ChunkDesc d = cm.desc(j);
     if (d.len <= 0 || t.x * 64 >= d.len) return;
     bf16* Cs = reinterpret_cast<bf16*>(smem);
-    bmm_tile<bf16, N, L>(d, j, g, t.x, t.y, C, B, G, cb, Cs, Cs + 64 * LDB);
+    bmm_tile<bf16, N, L, kStateThreads>(d, j, g, t.x, t.y, C, B, G, cb, Cs, Cs + 64 * LDB);
     return;
   }
   const int2 jh = xcd_chunk_head(b - nbmm, H);
@@ -323,7 +333,7 @@ hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t s) {
   if (a.max_chunks <= 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
     hipLaunchKernelGGL((chunk_state_bf16_kernel<P, N, L>), dim3(xcd_grid(a.max_chunks, a.H)),
-                       dim3(256), 0, s, a.cmap(), a.max_chunks, (const bf16*)a.x,
+                       dim3(kStateThreads), 0, s, a.cmap(), a.max_chunks, (const bf16*)a.x,
                        (const bf16*)a.B, a.delta, a.dAcs, a.H, a.G, a.chunk_states);
   } else {
     dim3 grid(a.max_chunks, a.H);
@@ -342,7 +352,7 @@ hipError_t launch_front(const FwdArgs& a, hipStream_t s) {
     constexpr int ntri = (L / 64) * (L / 64 + 1) / 2;
     const int nbmm = (a.max_chunks * a.G * ntri + 7) / 8 * 8;
     hipLaunchKernelGGL((front_bf16_kernel<P, N, L>), dim3(nbmm + xcd_grid(a.max_chunks, a.H)),
-                       dim3(256), 0, s, a.cmap(), a.max_chunks, nbmm, a.G, (const bf16*)a.x,
+                       dim3(kStateThreads), 0, s, a.cmap(), a.max_chunks, nbmm, a.G, (const bf16*)a.x,
                        (const bf16*)a.B, (const bf16*)a.C, a.dt, a.dt_bias, a.A, a.dt_min,
                        a.dt_max, a.H, a.delta, a.dAcs, (bf16*)a.cb, a.chunk_states);
     return hipGetLastError();

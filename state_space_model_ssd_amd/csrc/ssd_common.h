@@ -194,6 +194,63 @@ __device__ __forceinline__ int2 xcd_chunk_head(int b, int H) {
 }
 inline int xcd_grid(int max_chunks, int H) { return ((max_chunks + 7) / 8) * 8 * H; }
 
+// ---------------------------------------------------------------------------
+// Buffer resources: 32-bit offsets from a per-tile base, range-checked by the
+// hardware.  A load past num_records returns zeros (also into LDS) and a
+// store past it is dropped, so rows past a chunk's end need neither clamps
+// nor branches, and no access can leave the tile.
+// ---------------------------------------------------------------------------
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Token-major bf16 tiles in LDS, unpadded, with the 16-byte pieces of row r
+// permuted by XOR with tile_sw(r).  One transpose read instruction touches
+// rows r0 + {0..3} and r0 + {8..11} (r0 a multiple of 8) at two adjacent
+// pieces; the XOR spreads those 8 rows x 2 pieces over distinct bank groups
+// whether the LDS serves 16 or 32 lanes of 8-byte reads per clock.  Rows of
+// 16 or more pieces (256 bytes: every row starts on the same bank) need all
+// 16 pieces distinct; narrower rows alternate bank halves by themselves.
+// tile_sw(r + 4) == tile_sw(r) whenever r % 8 < 4.
+// ---------------------------------------------------------------------------
+template <int CPR>
+__device__ __forceinline__ int tile_sw(int r) {
+  if constexpr (CPR >= 16) return (2 * ((r & 3) | ((r >> 1) & 4))) & (CPR - 1);
+  else return (2 * ((r & 3) ^ ((r >> 3) & 1))) & (CPR - 1);
+}
+
+// Element offset of (row r, column c) in a swizzled tile of COLS columns.
+template <int COLS>
+__device__ __forceinline__ int tile_at(int r, int c) {
+  return r * COLS + ((((c >> 3) ^ tile_sw<COLS / 8>(r))) << 3) + (c & 7);
+}
+
+// MFMA operand (8 consecutive k of column c0 + lane%16, k starting at
+// k0 + 8*(lane/16); k0 a multiple of 8) from a swizzled token-major tile,
+// by two transpose reads.
+template <int COLS>
+__device__ __forceinline__ bf16x8 lds_operand_sw(const bf16* tile, int k0, int c0, int lane) {
+  const int m = lane & 15, kg = lane >> 4;
+  const int r = k0 + 8 * kg + (m >> 2);
+  const bf16* p = tile + tile_at<COLS>(r, c0 + 4 * (m & 3));
+  const i16x4 lo = lds_tr16_b64(p);
+  const i16x4 hi = lds_tr16_b64(p + 4 * COLS);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_fast(float v) { return __builtin_amdgcn_exp2f(v); }
 

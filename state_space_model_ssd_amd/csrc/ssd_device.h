@@ -47,19 +47,22 @@ __device__ __forceinline__ void chunk_cumsum_block(const ChunkDesc& d, int l,
 }
 
 // One lower-triangular 64x64 tile (ti >= tj) of CB = C B^T for chunk d and
-// group g, accumulated in fp32 on MFMA and stored in T.  256 threads; Cs and
-// Bs are LDS tiles of 64 x (N + 16 bytes).  Rows past the chunk's end load as
-// zeros, so their CB entries are exactly 0.
-template <typename T, int N, int L>
+// group g, accumulated in fp32 on MFMA and stored in T.  TH threads (4 or 8
+// waves: each wave owns 4 or 2 of the 16 output 16x16 tiles); Cs and Bs are
+// LDS tiles of 64 x (N + 16 bytes).  Rows past the chunk's end load as zeros,
+// so their CB entries are exactly 0.
+template <typename T, int N, int L, int TH = 256>
 __device__ __forceinline__ void bmm_tile(const ChunkDesc& d, int j, int g, int ti, int tj,
                                          const T* __restrict__ C, const T* __restrict__ B, int G,
                                          T* __restrict__ cb, T* Cs, T* Bs) {
   using M = Mfma<T>;
+  static_assert(TH == 256 || TH == 512, "4 or 8 waves");
   constexpr int V = 16 / sizeof(T);   // elements per 16-byte vector
   constexpr int LD = N + V;           // padded LDS row
   constexpr int VPR = N / V;
+  constexpr int MI = TH == 256 ? 2 : 1;   // 16-row tiles per wave
   const int tid = threadIdx.x;
-  for (int i = tid; i < 64 * VPR; i += 256) {
+  for (int i = tid; i < 64 * VPR; i += TH) {
     const int r = i / VPR, cv = i - (i / VPR) * VPR;
     const int lc = ti * 64 + r, lb = tj * 64 + r;
     const uint4 vc = load16(C + ((int64_t)(d.start + lc) * G + g) * N + cv * V, lc < d.len);
@@ -69,28 +72,28 @@ __device__ __forceinline__ void bmm_tile(const ChunkDesc& d, int j, int g, int t
   }
   __syncthreads();
   const int w = wave_id(), lane = tid & (kWave - 1);
-  const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+  const int wr = TH == 256 ? (w >> 1) * 32 : (w >> 1) * 16, wc = (w & 1) * 32;
   const int lr = lane & 15, kq = (lane >> 4) * M::KPL;
-  f32x4 acc[2][2];
+  f32x4 acc[MI][2];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int k0 = 0; k0 < N; k0 += M::K) {
-    typename M::frag a[2], b[2];
+    typename M::frag a[MI], b[2];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) a[mi] = M::load(&Cs[(wr + mi * 16 + lr) * LD + k0 + kq]);
+    for (int mi = 0; mi < MI; ++mi) a[mi] = M::load(&Cs[(wr + mi * 16 + lr) * LD + k0 + kq]);
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) b[ni] = M::load(&Bs[(wc + ni * 16 + lr) * LD + k0 + kq]);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = M::mma(a[mi], b[ni], acc[mi][ni]);
   }
   T* out = cb + ((int64_t)j * G + g) * L * L;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
