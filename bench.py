@@ -51,9 +51,10 @@ def algorithmic_work(prob, nchunks):
         "plan": (0, 0),
         # chunk_cumsum + bmm_chunk + chunk_state in one launch: the step and its
         # running sum are formed in-kernel (dt in, delta and sums out once)
+        # (B is read once: the bmm tiles and the state workgroups share it)
         "front": (4 * tok * H + 8 * nchunks * H * L
                   + 2 * e * tok * G * N + e * nchunks * G * tri
-                  + e * tok * H * P + e * tok * G * N + 4 * nchunks * H * P * N,
+                  + e * tok * H * P + 4 * nchunks * H * P * N,
                   2 * N * tri * nchunks * G + 2 * L * P * N * nchunks * H),
         "chunk_cumsum": (4 * tok * H + 8 * nchunks * H * L, 0),
         "bmm_chunk": (2 * e * tok * G * N + e * nchunks * G * tri, 2 * N * tri * nchunks * G),
@@ -199,6 +200,33 @@ def main():
     tokens = prob.batch * prob.seqlen
     value = tokens / (ms_per_step * 1e-3)
 
+    # --- context: the same step with cold caches (a 1 GiB write evicts the
+    # 256 MB last-level cache before each replay; only the replay is timed),
+    # and what a plain device copy sustains on this GPU
+    log("[bench] cold-cache steps and copy bandwidth")
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(10):
+        flush.fill_(1.0)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        graph.replay()
+        c1.record()
+        torch.cuda.synchronize()
+        cold.append(c0.elapsed_time(c1))
+    ms_cold = sorted(cold)[len(cold) // 2]
+    src = flush
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del flush, src, dst
+
     # --- per stage: R back-to-back launches between two events on the
     # launch stream, queued behind a GPU sleep so the CPU is never the limit
     log("[bench] per-stage timing")
@@ -247,7 +275,8 @@ def main():
                 "unit": "GB/s", "frac": round(ds["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "traffic_unit": "bytes per launch", "launch_us": ds["us"],
                 "alg_bytes_per_launch": ds["alg_bytes"]}
-    total_bytes = sum(v[0] for v in work.values())
+    total_bytes = sum(work[n][0] for n in step_launches if n in work and
+                      (n != "plan" or prob.seq_lens))
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
@@ -295,6 +324,12 @@ def main():
                   f"{R} back-to-back launches between HIP events; 'stages' are the launches "
                   "of one step, 'stages_unfused' the stages a fused launch covers, run alone",
         "wall_s_timed_region": round(wall, 4),
+        "context": {"ms_per_step_cold_cache": round(ms_cold, 5),
+                    "tokens_per_s_cold_cache": round(tokens / (ms_cold * 1e-3), 1),
+                    "device_copy_gbs": round(copy_gbs, 1),
+                    "note": "cold: median of 10 replays, each after a 1 GiB write that evicts "
+                            "the last-level cache; copy: torch device-to-device copy of 1 GiB, "
+                            "read + write bytes (measured, not the roofline peak)"},
         "env": env_info(),
     }
     print(json.dumps(res), flush=True)
