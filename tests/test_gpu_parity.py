@@ -107,6 +107,15 @@ def test_persistent_path_configs(shape):
     check(prob, inp, heads=[0, H // 2 + 1, H - 1])
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_chain_longer_than_one_decay_batch(dt):
+    # 1094 chunks in one sequence: the state chain crosses the 1024-chunk
+    # batches in which state_passing stages the chunk decays
+    prob = Problem(1, 70000, 4, 64, 128, 1, 64, dt)
+    inp = make_inputs(prob, Recipe(init_std=0.2), seed=11)
+    check(prob, inp)
+
+
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 255, 256, 257])
 def test_edge_lengths(T):
     prob = Problem(1, T, 4, 64, 128, 2, 64 if T < 200 else 256, "bf16")
