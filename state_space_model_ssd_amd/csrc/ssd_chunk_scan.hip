@@ -574,6 +574,82 @@ __global__ __launch_bounds__(4 * L) __attribute__((amdgpu_waves_per_eu(4))) void
 // groups (two per wave for L >= 128); every load is issued up front in the
 // order of use; x is staged XOR-swizzled and read with the transpose read;
 // the next k-step's CB rows are in flight while one is multiplied.
+// B operands of the MFMAs that add D x to y: column l of the k-step holds
+// D at the row of token l itself and zeros elsewhere.  D is split into two
+// bf16 parts (hi + lo) so that the products keep about 16 significant bits;
+// the MFMA multiplies bf16 exactly and sums in fp32.  t = l - (first token of
+// the lane's 8 k values); only 0 <= t < 8 puts a nonzero in this lane.
+__device__ __forceinline__ void skip_operands(uint32_t hi, uint32_t lo, int t, bf16x8& fh,
+                                              bf16x8& fl) {
+  const int sh = (t & 1) * 16;
+  const uint32_t vh = hi << sh, vl = lo << sh;
+  u32x4 a, b;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const bool on = (t >> 1) == d;       // t < 0 shifts to a negative index
+    a[d] = on ? vh : 0u;
+    b[d] = on ? vl : 0u;
+  }
+  fh = __builtin_bit_cast(bf16x8, a);
+  fl = __builtin_bit_cast(bf16x8, b);
+}
+
+// 8-byte piece of row l of the output tile (P bf16 per row, pieces of 4):
+// piece k is stored at k ^ out_sw<P>(l).  Sixteen consecutive rows with one
+// logical piece, and two half-rows of 16-byte reads, land on distinct banks.
+template <int P>
+__device__ __forceinline__ int out_sw(int l) {
+  static_assert(P == 32 || P == 64, "output tile swizzle");
+  if constexpr (P == 64) return l & 15;
+  else return (l >> 1) & 7;
+}
+
+// Largest whole-chunk decay, in powers of two, for which chunk_scan stages x
+// scaled by delta_s 2^(-a_s) and rescales rows by 2^(a_l): both factors stay
+// inside [2^-64, 2^64], far from fp32 and bf16 overflow and underflow.
+constexpr float kScanFastMaxLog2 = 64.f;
+
+// Eight bf16 values times w, rounded once to bf16.
+__device__ __forceinline__ bf16x8 scale_bf16x8(uint4 v, float w) {
+  const bf16x8 b = __builtin_bit_cast(bf16x8, v);
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = static_cast<float>(b[e]) * w;
+  return Mfma<bf16>::pack(f);
+}
+
+// A CB piece of the diagonal k-step with the tokens after the lane's own
+// zeroed: element e (token first + e) stays when e <= t = l - first.
+__device__ __forceinline__ bf16x8 causal_mask(const bf16x8& v, int t) {
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int n = t - 2 * d;               // >= 1: both halves stay; 0: the low one
+    u[d] = n >= 1 ? u[d] : (n == 0 ? (u[d] & 0xffffu) : 0u);
+  }
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Inter-chunk MFMAs of a wave: y^T[p][l] += sum_n state[p][n] C[l][n] for its
+// row groups (the row factor 2^(a_l) is applied by the caller).
+template <int P, int N, int RGW, int HP>
+__device__ __forceinline__ void scan_tile_inter(f32x4 (&acc)[RGW][P / 16],
+                                                const bf16x8 (&fc)[RGW][N / 32], const bf16* hsm,
+                                                int lr, int kq) {
+  using M = Mfma<bf16>;
+#pragma unroll
+  for (int k = 0; k < N / 32; ++k) {
+    bf16x8 fh[P / 16];
+#pragma unroll
+    for (int a = 0; a < P / 16; ++a)
+      fh[a] = *reinterpret_cast<const bf16x8*>(&hsm[(16 * a + lr) * HP + 32 * k + kq]);
+#pragma unroll
+    for (int i = 0; i < RGW; ++i)
+#pragma unroll
+      for (int a = 0; a < P / 16; ++a) acc[i][a] = M::mma(fh[a], fc[i][k], acc[i][a]);
+  }
+}
+
 template <int L> constexpr int kTileWaves = (L / 16) / 2 < 4 ? 4 : (L / 16) / 2;
 
 template <int P, int N, int L>
@@ -593,6 +669,7 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
   static_assert(RGW * NW == RG && (RGW == 1 || RGW == 2), "row-group split");
   constexpr int PT = P / 16;
   constexpr int NK = N / 32;             // k-steps of the inter-chunk term
+  constexpr int NQ = RG / 2;             // most intra-chunk k-steps of one row group
   constexpr int CPR = P / 8;             // 16-byte pieces per x row
   constexpr int XU = L * CPR / NT;       // x pieces per thread
   constexpr int HPR = N / 8;             // 16-byte pieces per state row
@@ -617,6 +694,8 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
   const uint32_t HPx = (uint32_t)H * P, GN = (uint32_t)G * N;
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
   const int lr = lane & 15, kg = lane >> 4, kq = kg * 8;
+  const bool has_d = D != nullptr;
+  const float Dh = has_d ? D[h] : 0.f;
   // Row groups of this wave; with two per wave they pair from both ends of
   // the chunk, so every wave carries the same causal work.
   int mg[RGW];
@@ -652,16 +731,14 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
     for (int k = 0; k < NK; ++k)
       fc[i][k] = __builtin_bit_cast(bf16x8, buf_load16(rc, ((uint32_t)lrow[i] * GN + 32 * k + kq) * 2u));
   const auto rcb = buf_rsrc(cb + ((int64_t)T.j * G + g) * L * L, L * L * 2);
-  uint32_t cbo[RGW];
-  bf16x8 cur[RGW];                         // CB rows of the current k-step
-#pragma unroll
-  for (int i = 0; i < RGW; ++i) {
-    cbo[i] = ((uint32_t)lrow[i] * L + kq) * 2u;
-    cur[i] = __builtin_bit_cast(bf16x8, buf_load16(rcb, cbo[i]));
-  }
 
-  // ---- stage x (swizzled; rows past the end arrived as zeros), the state,
-  // the running sums and the per-token factors
+  // Whole-chunk decay.  The running sum is monotone inside a chunk (delta is
+  // never negative and A is one number per head), so its last value bounds
+  // every |a_s|; small enough, the fast path below is exact up to rounding.
+  const bool fast = fabsf(dAcs[jhl * L + T.len - 1]) * kLog2e <= kScanFastMaxLog2;
+
+  // ---- stage x as loaded (swizzled; rows past the end arrived as zeros),
+  // the state, the running sums and the per-token factors
 #pragma unroll
   for (int u = 0; u < XU; ++u) {
     const int i = tid + NT * u, r = i / CPR, c = i % CPR;
@@ -681,83 +758,174 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
       cfs[tid] = dl_t * exp2_fast(a2r - a2);
     }
   }
-  __syncthreads();
-
+  const int xrow = 8 * kg + (lr >> 2);
+  const int xsl = tile_sw<CPR>(xrow) >> 1;
+  const int xcol = ((lr & 3) >> 1) * 8 + (lr & 1) * 4;
+  const int nq_wave = nq[RGW - 1];
   f32x4 acc[RGW][PT];
 #pragma unroll
   for (int i = 0; i < RGW; ++i)
 #pragma unroll
     for (int a = 0; a < PT; ++a) acc[i][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  scan_tile_inter<P, N, RGW, HP>(acc, fc, hsm, lr, kq);
 
-  // ---- inter-chunk term: y^T[p][l] = exp(a_l) * sum_n state[p][n] C[l][n]
+  if (fast) {                              // wave-uniform (one value per tile)
+    // Every term of the chunk is accumulated without its row factor 2^(a_l),
+    // applied once at the end: D x enters divided by it (while x is still
+    // staged as loaded), and x is then rescaled in place to x_s delta_s
+    // 2^(-a_s), so that the intra-chunk terms carry their decay
+    // 2^(a_l - a_s) and the CB rows enter the MFMAs as loaded.
+    // |a| <= kScanFastMaxLog2 keeps every factor far from over- and underflow.
+    if (has_d) {
 #pragma unroll
-  for (int k = 0; k < NK; ++k) {
-    bf16x8 fh[PT];
+      for (int i = 0; i < RGW; ++i) {
+        const int q = nq[i] - 1;           // the row group's diagonal step
+        const float dd = Dh * exp2_fast(-dal2[lrow[i]]);
+        const bf16 d1 = static_cast<bf16>(dd);
+        const bf16 d2 = static_cast<bf16>(dd - static_cast<float>(d1));
+        bf16x8 fdh, fdl;
+        skip_operands(__builtin_bit_cast(unsigned short, d1), __builtin_bit_cast(unsigned short, d2),
+                      lrow[i] - 32 * q - kq, fdh, fdl);
 #pragma unroll
-    for (int a = 0; a < PT; ++a)
-      fh[a] = *reinterpret_cast<const bf16x8*>(&hsm[(16 * a + lr) * HP + 32 * k + kq]);
+        for (int a = 0; a < PT; ++a) {
+          const bf16x8 fx = scan_x_operand<P>(xs, q, a, xrow, xsl, xcol);
+          acc[i][a] = M::mma(fx, fdh, acc[i][a]);
+          acc[i][a] = M::mma(fx, fdl, acc[i][a]);
+        }
+      }
+    }
+    // CB pieces stream through a ring of three per row group: the first two
+    // steps' pieces are in flight while x is rescaled, and each step issues
+    // the pieces two steps ahead (the loop is unrolled, so the slots are
+    // fixed registers).  Steps past a row group's last load nothing.
+    bf16x8 ring[RGW][3];
 #pragma unroll
     for (int i = 0; i < RGW; ++i)
 #pragma unroll
-      for (int a = 0; a < PT; ++a) acc[i][a] = M::mma(fh[a], fc[i][k], acc[i][a]);
-  }
+      for (int q = 0; q < 2; ++q)
+        if (q < nq[i])                     // wave-uniform
+          ring[i][q] = __builtin_bit_cast(bf16x8, buf_load16(rcb, ((uint32_t)lrow[i] * L + kq + 32 * q) * 2u));
+    __syncthreads();                       // x as loaded is no longer read
 #pragma unroll
-  for (int i = 0; i < RGW; ++i) {
-    const float rsc = exp2_fast(dal2[lrow[i]]);
+    for (int u = 0; u < XU; ++u) {
+      const int i = tid + NT * u, r = i / CPR, c = i % CPR;
+      uint4* e = reinterpret_cast<uint4*>(&xs[r * P + ((c ^ tile_sw<CPR>(r)) << 3)]);
+      *e = __builtin_bit_cast(uint4, scale_bf16x8(*e, dls[r] * exp2_fast(-dal2[r])));
+    }
+    __syncthreads();
 #pragma unroll
-    for (int a = 0; a < PT; ++a) acc[i][a] *= rsc;
-  }
-
-  // ---- intra-chunk term, k-steps outer: the x^T operands of a step serve
-  // both row groups of the wave; the next step's CB rows are in flight.
-  const int xrow = 8 * kg + (lr >> 2);
-  const int xsl = tile_sw<CPR>(xrow) >> 1;
-  const int xcol = ((lr & 3) >> 1) * 8 + (lr & 1) * 4;
-  const int nq_wave = nq[RGW - 1];
-  for (int q = 0; q < nq_wave; ++q) {
-    const int sn = min(32 * q + 32, L - 32);   // next step (clamped: always in the row)
-    bf16x8 nxt[RGW];
-#pragma unroll
-    for (int i = 0; i < RGW; ++i) nxt[i] = __builtin_bit_cast(bf16x8, buf_load16(rcb, cbo[i] + sn * 2));
-    bf16x8 fm[RGW];
-#pragma unroll
-    for (int i = 0; i < RGW; ++i)
-      if (q < nq[i]) fm[i] = scan_masked_cb(mg[i], q, cur[i], lr, kq, dal2, dls, cfs);
-#pragma unroll
-    for (int a = 0; a < PT; ++a) {
-      const bf16x8 fx = scan_x_operand<P>(xs, q, a, xrow, xsl, xcol);
+    for (int q = 0; q < NQ; ++q) {
+      if (q >= nq_wave) break;             // wave-uniform
 #pragma unroll
       for (int i = 0; i < RGW; ++i)
-        if (q < nq[i]) acc[i][a] = M::mma(fx, fm[i], acc[i][a]);   // wave-uniform
+        if (q + 2 < nq[i])                 // wave-uniform
+          ring[i][(q + 2) % 3] = __builtin_bit_cast(
+              bf16x8, buf_load16(rcb, ((uint32_t)lrow[i] * L + kq + 32 * (q + 2)) * 2u));
+      bf16x8 fb[RGW];
+#pragma unroll
+      for (int i = 0; i < RGW; ++i)        // the last step of a row group holds its diagonal
+        if (q < nq[i])
+          fb[i] = q == nq[i] - 1 ? causal_mask(ring[i][q % 3], lrow[i] - 32 * q - kq) : ring[i][q % 3];
+#pragma unroll
+      for (int a = 0; a < PT; ++a) {
+        const bf16x8 fx = scan_x_operand<P>(xs, q, a, xrow, xsl, xcol);
+#pragma unroll
+        for (int i = 0; i < RGW; ++i)
+          if (q < nq[i]) acc[i][a] = M::mma(fx, fb[i], acc[i][a]);   // wave-uniform
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep each step's reads in its own step
     }
 #pragma unroll
-    for (int i = 0; i < RGW; ++i) cur[i] = nxt[i];
+    for (int i = 0; i < RGW; ++i) {
+      const float rsc = exp2_fast(dal2[lrow[i]]);
+#pragma unroll
+      for (int a = 0; a < PT; ++a) acc[i][a] *= rsc;
+    }
+  } else {
+    // ---- exact path: each CB piece is masked with its decay
+    // exp(a_l - a_s) delta_s; the next step's CB rows are in flight while
+    // one is multiplied.
+    uint32_t cbo[RGW];
+    bf16x8 cur[RGW];                       // CB rows of the current k-step
+#pragma unroll
+    for (int i = 0; i < RGW; ++i) {
+      cbo[i] = ((uint32_t)lrow[i] * L + kq) * 2u;
+      cur[i] = __builtin_bit_cast(bf16x8, buf_load16(rcb, cbo[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < RGW; ++i) {
+      const float rsc = exp2_fast(dal2[lrow[i]]);
+#pragma unroll
+      for (int a = 0; a < PT; ++a) acc[i][a] *= rsc;
+    }
+    for (int q = 0; q < nq_wave; ++q) {
+      const int sn = min(32 * q + 32, L - 32);   // next step (clamped: always in the row)
+      bf16x8 nxt[RGW];
+#pragma unroll
+      for (int i = 0; i < RGW; ++i) nxt[i] = __builtin_bit_cast(bf16x8, buf_load16(rcb, cbo[i] + sn * 2));
+      bf16x8 fm[RGW];
+#pragma unroll
+      for (int i = 0; i < RGW; ++i)
+        if (q < nq[i]) fm[i] = scan_masked_cb(mg[i], q, cur[i], lr, kq, dal2, dls, cfs);
+#pragma unroll
+      for (int a = 0; a < PT; ++a) {
+        const bf16x8 fx = scan_x_operand<P>(xs, q, a, xrow, xsl, xcol);
+#pragma unroll
+        for (int i = 0; i < RGW; ++i)
+          if (q < nq[i]) acc[i][a] = M::mma(fx, fm[i], acc[i][a]);   // wave-uniform
+      }
+#pragma unroll
+      for (int i = 0; i < RGW; ++i) cur[i] = nxt[i];
+    }
+    // y = acc + D x, written over x (each element read and written by one lane)
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < RGW; ++i)
+#pragma unroll
+      for (int a = 0; a < PT; ++a) {
+        const int l = lrow[i], pc = 16 * a + 4 * kg;
+        bf16x4* e = reinterpret_cast<bf16x4*>(&xs[l * P + (((pc >> 3) ^ tile_sw<CPR>(l)) << 3) + (pc & 7)]);
+        const bf16x4 xo = *e;
+        bf16x4 yo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yo[r] = static_cast<bf16>(acc[i][a][r] + Dh * static_cast<float>(xo[r]));
+        *e = yo;
+      }
+    __syncthreads();
+    const auto ry = rows_rsrc(out, T, H, P, HPx);
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int i = tid + NT * u, r = i / CPR, c = i % CPR;
+      buf_store16(ry, ((uint32_t)r * HPx + c * 8) * 2u,
+                  *reinterpret_cast<const uint4*>(&xs[r * P + ((c ^ tile_sw<CPR>(r)) << 3)]));
+    }
+    return;
   }
 
-  // ---- epilogue: y = acc + D x, written over x in LDS (each element read
-  // and written by one lane), then the rows leave coalesced
+  // ---- fast path epilogue: y goes to LDS over x (every wave is done with
+  // x) in the out_sw layout, a lane's four p of one token as one 8-byte
+  // piece; then the rows leave coalesced
   __syncthreads();
-  const float Dh = D ? D[h] : 0.f;
-  const int p4 = kg * 4;
 #pragma unroll
   for (int i = 0; i < RGW; ++i)
 #pragma unroll
     for (int a = 0; a < PT; ++a) {
-      const int l = lrow[i], pc = 16 * a + p4;
-      bf16x4* e = reinterpret_cast<bf16x4*>(&xs[l * P + (((pc >> 3) ^ tile_sw<CPR>(l)) << 3) + (pc & 7)]);
-      const bf16x4 xo = *e;
+      const int l = lrow[i];
       bf16x4 yo;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) yo[r] = static_cast<bf16>(acc[i][a][r] + Dh * static_cast<float>(xo[r]));
-      *e = yo;
+      for (int r = 0; r < 4; ++r) yo[r] = static_cast<bf16>(acc[i][a][r]);
+      *reinterpret_cast<bf16x4*>(&xs[l * P + ((4 * a + kg) ^ out_sw<P>(l)) * 4]) = yo;
     }
   __syncthreads();
   const auto ry = rows_rsrc(out, T, H, P, HPx);
 #pragma unroll
   for (int u = 0; u < XU; ++u) {
     const int i = tid + NT * u, r = i / CPR, c = i % CPR;
-    buf_store16(ry, ((uint32_t)r * HPx + c * 8) * 2u,
-                *reinterpret_cast<const uint4*>(&xs[r * P + ((c ^ tile_sw<CPR>(r)) << 3)]));
+    const int sw = out_sw<P>(r);
+    const uint2 v0 = *reinterpret_cast<const uint2*>(&xs[r * P + ((2 * c) ^ sw) * 4]);
+    const uint2 v1 = *reinterpret_cast<const uint2*>(&xs[r * P + ((2 * c + 1) ^ sw) * 4]);
+    buf_store16(ry, ((uint32_t)r * HPx + c * 8) * 2u, make_uint4(v0.x, v0.y, v1.x, v1.y));
   }
 }
 

@@ -8,6 +8,8 @@ batch row or sequence of those heads), in the launch configuration the bench
 times.
 """
 import numpy as np
+import math
+
 import pytest
 import torch
 
@@ -113,6 +115,30 @@ def test_chain_longer_than_one_decay_batch(dt):
     # batches in which state_passing stages the chunk decays
     prob = Problem(1, 70000, 4, 64, 128, 1, 64, dt)
     inp = make_inputs(prob, Recipe(init_std=0.2), seed=11)
+    check(prob, inp)
+
+
+@pytest.mark.parametrize("P,N,L", [(32, 32, 64), (64, 128, 64), (64, 128, 128), (64, 128, 256)])
+def test_decay_regimes_per_head(P, N, L):
+    # Heads cycle through a negligible decay, a whole-chunk decay near 2^-60
+    # and one far below 2^-64, so one launch runs both chunk_scan paths (the
+    # rescaled one for a chunk decay within 2^64, the masked one beyond).
+    H = 6
+    prob = Problem(2, 3 * L + 37, H, P, N, 2, L, "bf16")
+    inp = make_inputs(prob, Recipe(init_std=0.3), seed=P + L)
+    delta = torch.nn.functional.softplus(inp["dt"].double() + inp["dt_bias"].double())
+    mean_delta = float(delta.mean())
+    log2e = 1.0 / math.log(2.0)
+    A = inp["A"].clone()
+    for h in range(H):
+        if h % 3 == 0:
+            A[h] = -1e-4
+        elif h % 3 == 1:
+            A[h] = -60.0 / (log2e * L * mean_delta)
+        else:
+            A[h] = -16.0
+    assert 16.0 * L * mean_delta * log2e > 4 * 64    # the third kind is far past the switch
+    inp["A"] = A
     check(prob, inp)
 
 
