@@ -652,14 +652,18 @@ __device__ __forceinline__ void scan_tile_inter(f32x4 (&acc)[RGW][P / 16],
 
 template <int L> constexpr int kTileWaves = (L / 16) / 2 < 4 ? 4 : (L / 16) / 2;
 
-template <int P, int N, int L>
-__global__ __launch_bounds__(64 * kTileWaves<L>) __attribute__((amdgpu_waves_per_eu(4))) void
-chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
-                            const bf16* __restrict__ C, const bf16* __restrict__ cb,
-                            const float* __restrict__ delta, const float* __restrict__ dAcs,
-                            const bf16* __restrict__ states_in, const float* __restrict__ D, int H,
-                            int G, bf16* __restrict__ out) {
-  static_assert(L % 64 == 0 && P % 32 == 0 && N % 32 == 0, "tile shape");
+// One tile of the bf16 chunk_scan.  FAST: the chunk's whole decay is within
+// 2^kScanFastMaxLog2, and the rescaled path runs; otherwise the masked one.
+// The two paths share their loads and the inter-chunk term but are compiled
+// as separate bodies, so that neither carries the other's registers.
+template <int P, int N, int L, bool FAST>
+__device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __restrict__ x,
+                                               const bf16* __restrict__ C, const bf16* __restrict__ cb,
+                                               const float* __restrict__ delta,
+                                               const float* __restrict__ dAcs,
+                                               const bf16* __restrict__ states_in,
+                                               const float* __restrict__ D, int H, int G, bf16* __restrict__ out,
+                                               bf16* xs, bf16* hsm, float* dal2, float* dls, float* cfs) {
   using M = Mfma<bf16>;
   constexpr int NW = kTileWaves<L>;
   constexpr int NT = 64 * NW;            // threads
@@ -675,21 +679,6 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
   constexpr int HPR = N / 8;             // 16-byte pieces per state row
   constexpr int HU = (P * HPR + NT - 1) / NT;
   static_assert((L * CPR) % NT == 0 && L <= NT, "x staging");
-  __shared__ __align__(16) bf16 xs[L * P];
-  __shared__ __align__(16) bf16 hsm[P * HP];
-  __shared__ __align__(16) float dal2[L];   // running sum of delta*A, times log2(e)
-  __shared__ __align__(16) float dls[L];    // delta
-  __shared__ __align__(16) float cfs[L];    // delta_s * exp(a_r - a_s), r = last token of s's 32-block
-
-  const int2 jh = xcd_chunk_head(blockIdx.x, H);
-  if (jh.x >= nslots) return;
-  ScanTile T{jh.x, jh.y, 0, 0};
-  {
-    const ChunkDesc d = cm.desc(T.j);
-    T.start = d.start;
-    T.len = d.len;
-  }
-  if (T.len <= 0) return;
   const int h = T.h, g = h / (H / G);
   const uint32_t HPx = (uint32_t)H * P, GN = (uint32_t)G * N;
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
@@ -732,11 +721,6 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
       fc[i][k] = __builtin_bit_cast(bf16x8, buf_load16(rc, ((uint32_t)lrow[i] * GN + 32 * k + kq) * 2u));
   const auto rcb = buf_rsrc(cb + ((int64_t)T.j * G + g) * L * L, L * L * 2);
 
-  // Whole-chunk decay.  The running sum is monotone inside a chunk (delta is
-  // never negative and A is one number per head), so its last value bounds
-  // every |a_s|; small enough, the fast path below is exact up to rounding.
-  const bool fast = fabsf(dAcs[jhl * L + T.len - 1]) * kLog2e <= kScanFastMaxLog2;
-
   // ---- stage x as loaded (swizzled; rows past the end arrived as zeros),
   // the state, the running sums and the per-token factors
 #pragma unroll
@@ -770,7 +754,7 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
   __syncthreads();
   scan_tile_inter<P, N, RGW, HP>(acc, fc, hsm, lr, kq);
 
-  if (fast) {                              // wave-uniform (one value per tile)
+  if constexpr (FAST) {
     // Every term of the chunk is accumulated without its row factor 2^(a_l),
     // applied once at the end: D x enters divided by it (while x is still
     // staged as loaded), and x is then rescaled in place to x_s delta_s
@@ -814,27 +798,35 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
       *e = __builtin_bit_cast(uint4, scale_bf16x8(*e, dls[r] * exp2_fast(-dal2[r])));
     }
     __syncthreads();
+    // The x^T operands run through a ring of XR registers over the sequence
+    // (step, p-tile): each is read XR operands before its MFMAs, so the LDS
+    // latency overlaps the MFMAs of the ones before it.  Reads past the last
+    // step stay inside the tile and go unused.
+    constexpr int XR = 3;
+    constexpr int NOP = NQ * PT;
+    bf16x8 fxr[XR];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      if (q >= nq_wave) break;             // wave-uniform
+    for (int n = 0; n < XR; ++n) fxr[n] = scan_x_operand<P>(xs, n / PT, n % PT, xrow, xsl, xcol);
+    bf16x8 fb[RGW];
 #pragma unroll
-      for (int i = 0; i < RGW; ++i)
-        if (q + 2 < nq[i])                 // wave-uniform
-          ring[i][(q + 2) % 3] = __builtin_bit_cast(
-              bf16x8, buf_load16(rcb, ((uint32_t)lrow[i] * L + kq + 32 * (q + 2)) * 2u));
-      bf16x8 fb[RGW];
-#pragma unroll
-      for (int i = 0; i < RGW; ++i)        // the last step of a row group holds its diagonal
-        if (q < nq[i])
-          fb[i] = q == nq[i] - 1 ? causal_mask(ring[i][q % 3], lrow[i] - 32 * q - kq) : ring[i][q % 3];
-#pragma unroll
-      for (int a = 0; a < PT; ++a) {
-        const bf16x8 fx = scan_x_operand<P>(xs, q, a, xrow, xsl, xcol);
+    for (int n = 0; n < NOP; ++n) {
+      const int q = n / PT, a = n % PT;
+      if (a == 0) {
+        if (q >= nq_wave) break;           // wave-uniform
 #pragma unroll
         for (int i = 0; i < RGW; ++i)
-          if (q < nq[i]) acc[i][a] = M::mma(fx, fb[i], acc[i][a]);   // wave-uniform
+          if (q + 2 < nq[i])               // wave-uniform
+            ring[i][(q + 2) % 3] = __builtin_bit_cast(
+                bf16x8, buf_load16(rcb, ((uint32_t)lrow[i] * L + kq + 32 * (q + 2)) * 2u));
+#pragma unroll
+        for (int i = 0; i < RGW; ++i)      // the last step of a row group holds its diagonal
+          if (q < nq[i])
+            fb[i] = q == nq[i] - 1 ? causal_mask(ring[i][q % 3], lrow[i] - 32 * q - kq) : ring[i][q % 3];
       }
-      __builtin_amdgcn_sched_barrier(0);   // keep each step's reads in its own step
+#pragma unroll
+      for (int i = 0; i < RGW; ++i)
+        if (q < nq[i]) acc[i][a] = M::mma(fxr[n % XR], fb[i], acc[i][a]);   // wave-uniform
+      if (n + XR < NOP) fxr[n % XR] = scan_x_operand<P>(xs, (n + XR) / PT, (n + XR) % PT, xrow, xsl, xcol);
     }
 #pragma unroll
     for (int i = 0; i < RGW; ++i) {
@@ -927,6 +919,42 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
     const uint2 v1 = *reinterpret_cast<const uint2*>(&xs[r * P + ((2 * c + 1) ^ sw) * 4]);
     buf_store16(ry, ((uint32_t)r * HPx + c * 8) * 2u, make_uint4(v0.x, v0.y, v1.x, v1.y));
   }
+}
+
+template <int P, int N, int L>
+__global__ __launch_bounds__(64 * kTileWaves<L>) __attribute__((amdgpu_waves_per_eu(4))) void
+chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
+                            const bf16* __restrict__ C, const bf16* __restrict__ cb,
+                            const float* __restrict__ delta, const float* __restrict__ dAcs,
+                            const bf16* __restrict__ states_in, const float* __restrict__ D, int H,
+                            int G, bf16* __restrict__ out) {
+  static_assert(L % 64 == 0 && P % 32 == 0 && N % 32 == 0, "tile shape");
+  constexpr int HP = N + 8;
+  __shared__ __align__(16) bf16 xs[L * P];
+  __shared__ __align__(16) bf16 hsm[P * HP];
+  __shared__ __align__(16) float dal2[L];   // running sum of delta*A, times log2(e)
+  __shared__ __align__(16) float dls[L];    // delta
+  __shared__ __align__(16) float cfs[L];    // delta_s * exp(a_r - a_s), r = last token of s's 32-block
+
+
+  const int2 jh = xcd_chunk_head(blockIdx.x, H);
+  if (jh.x >= nslots) return;
+  // Whole-chunk decay.  The running sum is monotone inside a chunk (delta is
+  // never negative and A is one number per head) and flat past its end, so
+  // its value at the last position bounds every |a_s|; read together with
+  // the chunk descriptor.
+  const float last = dAcs[((int64_t)jh.x * H + jh.y) * L + L - 1];
+  ScanTile T{jh.x, jh.y, 0, 0};
+  {
+    const ChunkDesc d = cm.desc(T.j);
+    T.start = d.start;
+    T.len = d.len;
+  }
+  if (T.len <= 0) return;
+  if (fabsf(last) * kLog2e <= kScanFastMaxLog2)   // uniform over the workgroup
+    scan_tile_body<P, N, L, true>(T, x, C, cb, delta, dAcs, states_in, D, H, G, out, xs, hsm, dal2, dls, cfs);
+  else
+    scan_tile_body<P, N, L, false>(T, x, C, cb, delta, dAcs, states_in, D, H, G, out, xs, hsm, dal2, dls, cfs);
 }
 
 }  // namespace
