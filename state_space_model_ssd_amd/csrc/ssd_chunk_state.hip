@@ -290,13 +290,14 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_bf16_kernel(
                                         nullptr, 0.f, 0.f, H, G, S, sm);
 }
 
-// The front of the bf16 forward in one launch: the first `nbmm` workgroups
-// compute bmm_chunk tiles, the rest run chunk_cumsum + chunk_state for one
-// (chunk, head) each.  The three stages are independent of each other's
-// outputs here, so they share the machine instead of running back to back.
+// The front of the bf16 forward in one launch: the first `nstate` workgroups
+// run chunk_cumsum + chunk_state for one (chunk, head) each, the rest compute
+// bmm_chunk tiles.  The three stages are independent of each other's outputs
+// here, so they share the machine instead of running back to back; the short
+// bmm workgroups come last and fill the CUs the chunk_state tail leaves idle.
 template <int P, int N, int L>
 __global__ __launch_bounds__(kStateThreads) void front_bf16_kernel(
-    ChunkMap cm, int nslots, int nbmm, int G, const bf16* __restrict__ x,
+    ChunkMap cm, int nslots, int nstate, int G, const bf16* __restrict__ x,
     const bf16* __restrict__ B, const bf16* __restrict__ C, const float* __restrict__ dt,
     const float* __restrict__ dt_bias, const float* __restrict__ A, float dt_min, float dt_max,
     int H, float* __restrict__ delta, float* __restrict__ dAcs, bf16* __restrict__ cb,
@@ -307,8 +308,8 @@ __global__ __launch_bounds__(kStateThreads) void front_bf16_kernel(
   constexpr size_t kState = sizeof(StateSmem<P, N, L>);
   __shared__ __align__(16) unsigned char smem[kBmm > kState ? kBmm : kState];
   const int b = blockIdx.x;
-  if (b < nbmm) {                         // nbmm is a multiple of 8: XCD order kept below
-    const int tile = b % NTRI, jg = b / NTRI;
+  if (b >= nstate) {                      // nstate is a multiple of 8: XCD order kept above
+    const int tile = (b - nstate) % NTRI, jg = (b - nstate) / NTRI;
     const int j = jg / G, g = jg - (jg / G) * G;
     if (j >= nslots) return;
     const int2 t = tri_tile(tile);
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(kStateThreads) void front_bf16_kernel(
     bmm_tile<bf16, N, L, kStateThreads>(d, j, g, t.x, t.y, C, B, G, cb, Cs, Cs + 64 * LDB);
     return;
   }
-  const int2 jh = xcd_chunk_head(b - nbmm, H);
+  const int2 jh = xcd_chunk_head(b, H);
   if (jh.x >= nslots) return;
   const ChunkDesc d = cm.desc(jh.x);
   if (d.len <= 0) return;
@@ -350,9 +351,10 @@ hipError_t launch_front(const FwdArgs& a, hipStream_t s) {
   } else {
     if (a.max_chunks <= 0) return hipSuccess;
     constexpr int ntri = (L / 64) * (L / 64 + 1) / 2;
-    const int nbmm = (a.max_chunks * a.G * ntri + 7) / 8 * 8;
-    hipLaunchKernelGGL((front_bf16_kernel<P, N, L>), dim3(nbmm + xcd_grid(a.max_chunks, a.H)),
-                       dim3(kStateThreads), 0, s, a.cmap(), a.max_chunks, nbmm, a.G, (const bf16*)a.x,
+    const int nbmm = a.max_chunks * a.G * ntri;
+    const int nstate = xcd_grid(a.max_chunks, a.H);
+    hipLaunchKernelGGL((front_bf16_kernel<P, N, L>), dim3(nstate + nbmm),
+                       dim3(kStateThreads), 0, s, a.cmap(), a.max_chunks, nstate, a.G, (const bf16*)a.x,
                        (const bf16*)a.B, (const bf16*)a.C, a.dt, a.dt_bias, a.A, a.dt_min,
                        a.dt_max, a.H, a.delta, a.dAcs, (bf16*)a.cb, a.chunk_states);
     return hipGetLastError();
