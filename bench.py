@@ -152,6 +152,8 @@ def main():
                                  prob.ngroups, prob.chunk_size, 1 if prob.dtype == "bf16" else 0,
                                  nseq=len(prob.seq_lens) if prob.seq_lens else 0)
     lay = binding.workspace_layout(cprob)
+    from state_space_model_ssd_amd import tuning
+    tuned = tuning.lookup(cprob)            # the binding applies the same lookup
     ws = torch.empty(lay.total_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(d["x"])
     fin = torch.empty((prob.nseq, prob.nheads, prob.headdim, prob.dstate), dtype=torch.float32,
@@ -316,6 +318,8 @@ def main():
                    "chunk_size": prob.chunk_size, "tokens": tokens, "chunks": nchunks},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "tuning": {"source": "tuned config" if tuned else "library's own choice",
+                   "key": tuning.shape_key(cprob), "choice": tuned or {}},
         "stages": stages,
         "stages_unfused": singles,
         "step_alg_bytes": int(total_bytes),

@@ -168,6 +168,45 @@ ssd_status_t ssd_fwd_stages(const ssd_problem_t* p,
                             void* workspace, size_t workspace_bytes,
                             uint32_t stages, void* stream);
 
+/*
+ * Kernel choices a caller may pin for one call.  0 in a field keeps the
+ * library's own choice for the shape.  An offline tuner times the choices
+ * per problem shape and records the fastest in a config file; the Python
+ * binding reads that file and falls back to 0 (the built-in choice) for
+ * shapes it does not list.  None of the choices changes what is computed;
+ * they move rounding only where noted.
+ *   scan_kernel  chunk_scan for bf16: 1 = one workgroup per (chunk, head)
+ *                tile (its rescaled path rounds differently from the
+ *                masked one), 2 = the persistent walk over tiles.  Must be 0
+ *                for fp32.
+ *   sp_vec       consecutive state elements per state_passing thread: 1, 2
+ *                or 4 (identical results).
+ *   front        bf16 stages 1-3: 1 = one fused launch, 2 = one launch per
+ *                stage (identical results).  Must be 0 for fp32.
+ *   reserved     must be 0.
+ * A field outside its range, or a choice the dtype does not have, is
+ * rejected with SSD_ERR_INVALID_ARG before anything is enqueued.
+ */
+typedef struct {
+  int32_t scan_kernel;
+  int32_t sp_vec;
+  int32_t front;
+  int32_t reserved;
+} ssd_tuning_t;
+
+/*
+ * As ssd_fwd_stages, with kernel choices pinned by `tuning` (NULL: all 0).
+ * Meant for tuners and for callers replaying a tuned configuration.
+ */
+ssd_status_t ssd_fwd_tuned(const ssd_problem_t* p,
+                           const void* x, const float* dt, const float* dt_bias,
+                           const float* A, const void* B, const void* C, const float* D,
+                           const float* initial_states,
+                           const int32_t* cu_seqlens, const int32_t* seq_idx,
+                           void* out, float* final_states,
+                           void* workspace, size_t workspace_bytes,
+                           uint32_t stages, const ssd_tuning_t* tuning, void* stream);
+
 /* Static description of a status code. */
 const char* ssd_status_string(ssd_status_t s);
 

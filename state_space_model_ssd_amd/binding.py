@@ -28,7 +28,7 @@ STAGES = {"plan": STAGE_PLAN, "chunk_cumsum": STAGE_CUMSUM, "bmm_chunk": STAGE_B
           "chunk_scan": STAGE_CHUNK_SCAN}
 
 EXPORTED = ("ssd_fwd_workspace_size", "ssd_workspace_layout", "ssd_config_supported",
-            "ssd_fwd", "ssd_fwd_stages", "ssd_status_string")
+            "ssd_fwd", "ssd_fwd_stages", "ssd_fwd_tuned", "ssd_status_string")
 
 
 class SsdError(RuntimeError):
@@ -52,6 +52,12 @@ class LayoutC(ctypes.Structure):
                 ("dA_cumsum", ctypes.c_size_t), ("cb", ctypes.c_size_t),
                 ("chunk_states", ctypes.c_size_t), ("states_in", ctypes.c_size_t),
                 ("total_bytes", ctypes.c_size_t)]
+
+
+class TuningC(ctypes.Structure):
+    """ssd_tuning_t: pinned kernel choices, 0 = the library's own."""
+    _fields_ = [("scan_kernel", ctypes.c_int32), ("sp_vec", ctypes.c_int32),
+                ("front", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -80,6 +86,9 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_fwd.restype = ctypes.c_int
     lib.ssd_fwd_stages.argtypes = [PP] + [vp] * 12 + [vp, sz, ctypes.c_uint32, vp]
     lib.ssd_fwd_stages.restype = ctypes.c_int
+    lib.ssd_fwd_tuned.argtypes = [PP] + [vp] * 12 + [vp, sz, ctypes.c_uint32,
+                                                     ctypes.POINTER(TuningC), vp]
+    lib.ssd_fwd_tuned.restype = ctypes.c_int
     lib.ssd_status_string.argtypes = [ctypes.c_int]
     lib.ssd_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -141,13 +150,18 @@ def _need(t, name, dtype, shape, device):
 def ssd_fwd(x, dt, A, B, C, chunk_size, D=None, dt_bias=None, initial_states=None,
             cu_seqlens=None, seq_idx=None, dt_min=0.0, dt_max=math.inf, out=None,
             final_states=None, return_final_states=True, workspace=None,
-            stages: int = STAGE_ALL):
+            stages: int = STAGE_ALL, tuning="config"):
     """SSD forward on the GPU through the C ABI.
 
     x (b, T, H, P) fp32|bf16; dt (b, T, H) fp32; A (H) fp32; B, C (b, T, G, N)
     in x's dtype; D, dt_bias (H) fp32 or None; initial_states (nstates, H, P, N)
     fp32 or None; cu_seqlens (nseq + 1) / seq_idx (T) int32 for a packed batch
     (b == 1).  Returns (out, final_states, workspace).
+
+    tuning: "config" looks the shape up in the tuned config file (see
+    tuning.py) and keeps the library's own choices for shapes it does not
+    list; None keeps the library's choices; a dict with any of scan_kernel,
+    sp_vec, front pins them (ssd_tuning_t in include/ssd.h).
     """
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -160,7 +174,8 @@ def ssd_fwd(x, dt, A, B, C, chunk_size, D=None, dt_bias=None, initial_states=Non
     elif seq_idx is not None:
         raise ValueError("pass nseq through cu_seqlens, or use ssd_fwd_seq_idx")
     return _run(x, dt, A, B, C, chunk_size, D, dt_bias, initial_states, cu_seqlens, None, nseq,
-                dt_min, dt_max, out, final_states, return_final_states, workspace, stages)
+                dt_min, dt_max, out, final_states, return_final_states, workspace, stages,
+                tuning)
 
 
 def ssd_fwd_seq_idx(x, dt, A, B, C, chunk_size, seq_idx, nseq, **kw):
@@ -169,11 +184,23 @@ def ssd_fwd_seq_idx(x, dt, A, B, C, chunk_size, seq_idx, nseq, **kw):
                 kw.get("initial_states"), None, seq_idx, int(nseq), kw.get("dt_min", 0.0),
                 kw.get("dt_max", math.inf), kw.get("out"), kw.get("final_states"),
                 kw.get("return_final_states", True), kw.get("workspace"),
-                kw.get("stages", STAGE_ALL))
+                kw.get("stages", STAGE_ALL), kw.get("tuning", "config"))
+
+
+def make_tuning(choice) -> TuningC:
+    """TuningC from None or a dict of scan_kernel / sp_vec / front."""
+    t = TuningC(0, 0, 0, 0)
+    if choice:
+        unknown = set(choice) - {"scan_kernel", "sp_vec", "front"}
+        if unknown:
+            raise ValueError(f"unknown tuning fields {sorted(unknown)}")
+        for k, v in choice.items():
+            setattr(t, k, int(v))
+    return t
 
 
 def _run(x, dt, A, B, C, chunk_size, D, dt_bias, init, cu, sidx, nseq, dt_min, dt_max, out,
-         final_states, return_final, workspace, stages):
+         final_states, return_final, workspace, stages, tuning="config"):
     lib = load_library()
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -191,6 +218,12 @@ def _run(x, dt, A, B, C, chunk_size, D, dt_bias, init, cu, sidx, nseq, dt_min, d
     _need(cu, "cu_seqlens", torch.int32, (nseq + 1,), dev)
     _need(sidx, "seq_idx", torch.int32, (T,), dev)
     prob = make_problem(b, T, H, P, N, G, chunk_size, x.dtype, nseq, dt_min, dt_max)
+    if isinstance(tuning, str):
+        if tuning != "config":
+            raise ValueError("tuning is 'config', None or a dict")
+        from state_space_model_ssd_amd import tuning as _tuning
+        tuning = _tuning.lookup(prob)
+    tune = make_tuning(tuning)
     if out is None:
         out = torch.empty_like(x)
     _need(out, "out", x.dtype, (b, T, H, P), dev)
@@ -202,11 +235,11 @@ def _run(x, dt, A, B, C, chunk_size, D, dt_bias, init, cu, sidx, nseq, dt_min, d
         workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-        code = lib.ssd_fwd_stages(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A),
-                                  _ptr(B), _ptr(C), _ptr(D), _ptr(init), _ptr(cu), _ptr(sidx),
-                                  _ptr(out), _ptr(final_states), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), int(stages),
-                                  stream)
+        code = lib.ssd_fwd_tuned(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A),
+                                 _ptr(B), _ptr(C), _ptr(D), _ptr(init), _ptr(cu), _ptr(sidx),
+                                 _ptr(out), _ptr(final_states), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), int(stages),
+                                 ctypes.byref(tune), stream)
     _check(code)
     return out, final_states, workspace
 

@@ -85,14 +85,27 @@ void layout_of(const ssd_problem_t* p, ssd_workspace_layout_t* w) {
   w->total_bytes = off;
 }
 
+// Ranges of the pinned kernel choices (0 keeps the library's choice).
+ssd_status_t check_tuning(const ssd_problem_t* p, const ssd_tuning_t& t) {
+  const bool bf16 = p->dtype == SSD_BF16;
+  if (t.reserved != 0) return SSD_ERR_INVALID_ARG;
+  if (t.scan_kernel < 0 || t.scan_kernel > 2 || (!bf16 && t.scan_kernel != 0)) return SSD_ERR_INVALID_ARG;
+  if (t.sp_vec != 0 && t.sp_vec != 1 && t.sp_vec != 2 && t.sp_vec != 4) return SSD_ERR_INVALID_ARG;
+  if (t.front < 0 || t.front > 2 || (!bf16 && t.front != 0)) return SSD_ERR_INVALID_ARG;
+  return SSD_OK;
+}
+
 ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias,
                  const float* A, const void* B, const void* C, const float* D,
                  const float* initial_states, const int32_t* cu_seqlens, const int32_t* seq_idx,
                  void* out, float* final_states, void* workspace, size_t workspace_bytes,
-                 uint32_t stages, void* stream) {
+                 uint32_t stages, const ssd_tuning_t* tuning, void* stream) {
   ssd_status_t st = check_problem(p);
   if (st != SSD_OK) return st;
   if (stages & ~(uint32_t)SSD_STAGE_ALL) return SSD_ERR_INVALID_ARG;
+  const ssd_tuning_t tune = tuning ? *tuning : ssd_tuning_t{0, 0, 0, 0};
+  st = check_tuning(p, tune);
+  if (st != SSD_OK) return st;
   const bool packed = p->nseq > 0;
   if (packed && ((cu_seqlens != nullptr) + (seq_idx != nullptr)) != 1) return SSD_ERR_INVALID_ARG;
   if (!packed && (cu_seqlens || seq_idx)) return SSD_ERR_INVALID_ARG;
@@ -119,6 +132,8 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
   a.packed = packed;
   a.dt_min = p->dt_min;
   a.dt_max = p->dt_max;
+  a.scan_kernel = tune.scan_kernel;
+  a.sp_vec = tune.sp_vec;
   a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.D = D;
   a.init = initial_states;
   a.cu_seqlens = cu_seqlens;
@@ -146,7 +161,7 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
   };
   // The bf16 path runs stages 1-3 as one launch when all three are asked for.
   constexpr uint32_t kFront = SSD_STAGE_CUMSUM | SSD_STAGE_BMM | SSD_STAGE_CHUNK_STATE;
-  const bool fuse_front = k->front && (stages & kFront) == kFront;
+  const bool fuse_front = k->front && (stages & kFront) == kFront && tune.front != 2;
   for (const Step& stp : steps) {
     if (!(stages & stp.bit)) continue;
     if (fuse_front && (stp.bit & kFront)) {
@@ -188,7 +203,7 @@ ssd_status_t ssd_fwd(const ssd_problem_t* p, const void* x, const float* dt, con
                      const int32_t* seq_idx, void* out, float* final_states, void* workspace,
                      size_t workspace_bytes, void* stream) {
   return ssd::run(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, out,
-                  final_states, workspace, workspace_bytes, SSD_STAGE_ALL, stream);
+                  final_states, workspace, workspace_bytes, SSD_STAGE_ALL, nullptr, stream);
 }
 
 ssd_status_t ssd_fwd_stages(const ssd_problem_t* p, const void* x, const float* dt,
@@ -198,7 +213,17 @@ ssd_status_t ssd_fwd_stages(const ssd_problem_t* p, const void* x, const float* 
                             float* final_states, void* workspace, size_t workspace_bytes,
                             uint32_t stages, void* stream) {
   return ssd::run(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, out,
-                  final_states, workspace, workspace_bytes, stages, stream);
+                  final_states, workspace, workspace_bytes, stages, nullptr, stream);
+}
+
+ssd_status_t ssd_fwd_tuned(const ssd_problem_t* p, const void* x, const float* dt,
+                           const float* dt_bias, const float* A, const void* B, const void* C,
+                           const float* D, const float* initial_states,
+                           const int32_t* cu_seqlens, const int32_t* seq_idx, void* out,
+                           float* final_states, void* workspace, size_t workspace_bytes,
+                           uint32_t stages, const ssd_tuning_t* tuning, void* stream) {
+  return ssd::run(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, out,
+                  final_states, workspace, workspace_bytes, stages, tuning, stream);
 }
 
 const char* ssd_status_string(ssd_status_t s) {

@@ -988,7 +988,8 @@ hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s) {
     const int ntiles = xcd_grid(a.max_chunks, a.H);
     const int g = persistent_grid(kern, 4 * L, 0);
     if (g <= 0) return hipErrorInvalidDevice;
-    if (ntiles >= kPersistentMinTiles * g) {
+    const bool persistent = a.scan_kernel == 2 || (a.scan_kernel == 0 && ntiles >= kPersistentMinTiles * g);
+    if (persistent) {
       hipLaunchKernelGGL(kern, dim3(g), dim3(4 * L), 0, s, a.cmap(), a.max_chunks, ntiles,
                          (const bf16*)a.x, (const bf16*)a.C, (const bf16*)a.cb, a.delta, a.dAcs,
                          (const bf16*)a.states_in, a.D, a.H, a.G, (bf16*)a.out);

@@ -16,6 +16,8 @@ struct FwdArgs {
   int nc_row;       // chunks per row (rows mode)
   bool packed;
   float dt_min, dt_max;
+  int scan_kernel;  // 0: by shape, 1: one workgroup per tile, 2: persistent (bf16)
+  int sp_vec;       // 0: by shape, else state elements per state_passing thread
 
   const void* x;
   const float* dt;

@@ -129,7 +129,9 @@ hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s) {
   // of 64 lanes); each wave keeps kSpDepth chunk loads in flight, so the bytes
   // in flight do not depend on the width, only the instruction count does.
   const int64_t lanes = (int64_t)a.nstates * a.H * PN;
-  const int vec = (lanes / 4 >= (int64_t)1024 * 64) ? 4 : (lanes / 2 >= (int64_t)1024 * 64) ? 2 : 1;
+  int vec = (lanes / 4 >= (int64_t)1024 * 64) ? 4 : (lanes / 2 >= (int64_t)1024 * 64) ? 2 : 1;
+  if (a.sp_vec == 1 || a.sp_vec == 2 || a.sp_vec == 4) vec = a.sp_vec;   // pinned by the caller
+  if (PN % vec != 0) return hipErrorInvalidValue;
   auto go = [&](auto kern, int v) {
     dim3 grid((PN / v + kSpThreads - 1) / kSpThreads, a.H, a.nstates);
     hipLaunchKernelGGL(kern, grid, dim3(kSpThreads), 0, s, a.cmap(), a.chunk_states, a.dAcs,
