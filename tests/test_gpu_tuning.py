@@ -24,13 +24,16 @@ CASES = {
                               Recipe(dt_bias="inv_softplus_uniform", init_std=0.3), 31),
     "bf16-L64-large-decay": (Problem(1, 333, 4, 64, 128, 1, 64, "bf16"), Recipe(init_std=0.3), 32),
     "f32-L64": (Problem(1, 300, 4, 32, 16, 1, 64, "f32"), Recipe(init_std=0.3), 33),
+    "bf16-L128-packed": (Problem(1, 650, 4, 64, 128, 2, 128, "bf16", seq_lens=(200, 1, 449)),
+                         Recipe(init_std=0.3), 34),
 }
 
 
 def _problem_c(prob):
     return binding.make_problem(prob.batch, prob.seqlen, prob.nheads, prob.headdim, prob.dstate,
                                 prob.ngroups, prob.chunk_size,
-                                torch.bfloat16 if prob.dtype == "bf16" else torch.float32)
+                                torch.bfloat16 if prob.dtype == "bf16" else torch.float32,
+                                prob.nseq if prob.seq_lens is not None else 0)
 
 
 @pytest.fixture(scope="module", params=sorted(CASES))
