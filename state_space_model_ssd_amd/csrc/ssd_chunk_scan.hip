@@ -319,6 +319,11 @@ __device__ __forceinline__ void scan_load_cb(const ScanTile& T, int lane, const 
   }
 }
 
+// Largest decay, in powers of two, of a 32-token block for which its
+// diagonal k-step uses the factored decay (factors up to 2^64 and down to
+// delta 2^-64, far from fp32 over- and underflow).
+constexpr float kDiagFactorMaxLog2 = 64.f;
+
 // Decay-masked CB piece of row group m at k-step q (the MFMA B operand):
 // M[l][s] = CB[l][s] exp(a_l - a_s) delta_s for s <= l, else 0.
 __device__ __forceinline__ bf16x8 scan_masked_cb(int m, int q, const bf16x8& cbr, int lr, int kq,
@@ -335,6 +340,17 @@ __device__ __forceinline__ bf16x8 scan_masked_cb(int m, int q, const bf16x8& cbr
     const float cf[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) mv[e] = static_cast<float>(cbr[e]) * (rf * cf[e]);
+  } else if (dal2[s0] - dal2[s0 + 31] <= kDiagFactorMaxLog2) {
+    // on the diagonal, a block whose own decay is within 2^kDiagFactorMaxLog2:
+    // the same two factors, exp(a_l - a_r) now >= 1 but bounded by that
+    // decay, and tokens after the lane's own masked to zero
+    const float rf = exp2_fast(dal - dal2[s0 + 31]);
+    const float4 f0 = *reinterpret_cast<const float4*>(&cfs[s0 + kq]);
+    const float4 f1 = *reinterpret_cast<const float4*>(&cfs[s0 + kq + 4]);
+    const float cf[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+    const int t = lrow - s0 - kq;          // element e is token s0 + kq + e
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mv[e] = e <= t ? static_cast<float>(cbr[e]) * (rf * cf[e]) : 0.f;
   } else {                               // on the diagonal: masked exponential
     const float4 a0 = *reinterpret_cast<const float4*>(&dal2[s0 + kq]);
     const float4 a1 = *reinterpret_cast<const float4*>(&dal2[s0 + kq + 4]);
