@@ -75,12 +75,17 @@ STAGE_SOURCE = {"plan": "ssd_prep.hip", "chunk_cumsum": "ssd_prep.hip", "front":
 
 
 def kernel_source_hash(kernel: str) -> str:
-    """Hash of a kernel's source file and the headers every kernel includes."""
+    """Hash of the code (comments and blank space removed) of a kernel's
+    source file and of the headers every kernel includes."""
     import hashlib
+    import re
     csrc = os.path.join(ROOT, "state_space_model_ssd_amd", "csrc")
     h = hashlib.sha256()
     for f in (STAGE_SOURCE[kernel], "ssd_common.h", "ssd_device.h", "ssd_kernels.h"):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        text = open(os.path.join(csrc, f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

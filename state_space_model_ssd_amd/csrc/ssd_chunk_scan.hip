@@ -7,22 +7,30 @@
 //          + D[h] * x[l,p]
 // accumulated in fp32 and rounded once to the output type.
 //
-// bf16 kernel (the production path): persistent, one workgroup of 4 L
-// threads per resident slot (one per CU at L = 256), walking the (chunk,
-// head) tiles with the next tile's inputs in flight while it computes one.
-//  - x of the tile is staged in LDS token-major (16-byte pieces XOR-swizzled
-//    per row) and read as the MFMA A operand with the gfx950 LDS transpose
-//    read; the entering state is staged row-major with a padded pitch.
-//  - intra-chunk term: per 32-token k-step the lane builds its 8 B-operand
-//    values from the CB row.  Below the diagonal the decay splits around the
-//    step's last token r:  exp(a_l - a_s) = exp(a_l - a_r) * exp(a_r - a_s),
-//    both factors <= 1, the second (times delta_s) kept per token in LDS, so a
-//    step costs one exp per lane instead of eight.  Steps on the diagonal
-//    evaluate the masked exponential directly (exp2(-inf) = 0 above it).
-//  - inter-chunk term: the entering state times the C rows on MFMA, then
-//    scaled by exp(a_l) per token.
-//  - epilogue: y = acc + D x, stored straight from the accumulators.
-// All global traffic goes through buffer resources bounded by the tile.
+// bf16 kernels (the production path).  Common to both:
+//  - the MFMAs compute the transposed tile y^T[p][l] (A = x^T by the gfx950
+//    LDS transpose read from a token-major, XOR-swizzled x tile, or the
+//    entering state; B = a CB row or a C row), so a lane holds four
+//    consecutive p of one token;
+//  - the masked intra-chunk term builds each lane's 8 B-operand values from
+//    the CB row.  Below the diagonal the decay splits around the k-step's
+//    last token r: exp(a_l - a_s) = exp(a_l - a_r) * exp(a_r - a_s), both
+//    factors <= 1, the second (times delta_s) kept per token in LDS, so a
+//    step costs one exp per lane instead of eight.  Diagonal steps use the
+//    same factors while the block's own decay is within 2^64, else the
+//    masked exponential (exp2(-inf) = 0 above the diagonal);
+//  - the inter-chunk term is the entering state times the C rows on MFMA,
+//    scaled by exp(a_l) per token;
+//  - all global traffic goes through buffer resources bounded by the tile.
+// Two kernels; the launcher picks by tiles per resident workgroup (or as a
+// caller pins it):
+//  - one workgroup of 8 waves per (chunk, head) tile.  Each tile takes the
+//    rescaled path when its whole decay is within 2^64 (x staged as
+//    x delta 2^(-a), CB rows used as loaded, one row factor 2^(a_l) at the
+//    end), else the masked path; the two are compiled as separate bodies;
+//  - a persistent workgroup of 4 L threads per resident slot, walking the
+//    tiles with the next tile's inputs in flight (masked path).
+// The y = acc + D x epilogue stages y in LDS and stores coalesced rows.
 //
 // fp32 kernel (exactness path): one workgroup per (chunk, 64-row tile, head);
 // each wave owns 16 output rows and all P columns (P/16 MFMA tiles).
