@@ -108,8 +108,9 @@ typedef struct {
  *                the last entry is the number of chunks in use
  *   delta, dA_cumsum  fp32 [max_chunks][nheads][L]
  *   cb           dtype [max_chunks][ngroups][L][L] (entries with s <= l of
- *                the valid rows are defined; fp32 accumulation, stored in
- *                the dtype of x)
+ *                the valid rows hold C B^T, fp32 accumulation stored in the
+ *                dtype of x; entries with s > l in the same 64-token block
+ *                as l are 0; the rest are not written)
  *   chunk_states fp32 [max_chunks][nheads][headdim][dstate]
  *   states_in    dtype [max_chunks][nheads][headdim][dstate]: state entering
  *                each chunk                                                */

@@ -2,7 +2,8 @@
 // each logical chunk j, accumulated in fp32 and stored in the input dtype (the intra-chunk C B^T that the output construction
 // of the chunked scan consumes; aiproviderindex.com, "Mamba-2 offers a
 // different scaling path").  Only 64x64 tiles on or below the diagonal are
-// computed: the output stage never reads s > l.
+// computed, and diagonal tiles hold 0 above the diagonal: the output stage
+// reads no tile with s > l and multiplies diagonal blocks unmasked.
 //
 // One workgroup (4 waves) per (chunk, group, lower-triangular 64x64 tile).
 // C and B rows are staged in LDS as the MFMA operand type (rows padded by 16

@@ -642,17 +642,6 @@ __device__ __forceinline__ bf16x8 scale_bf16x8(uint4 v, float w) {
   return Mfma<bf16>::pack(f);
 }
 
-// A CB piece of the diagonal k-step with the tokens after the lane's own
-// zeroed: element e (token first + e) stays when e <= t = l - first.
-__device__ __forceinline__ bf16x8 causal_mask(const bf16x8& v, int t) {
-  u32x4 u = __builtin_bit_cast(u32x4, v);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const int n = t - 2 * d;               // >= 1: both halves stay; 0: the low one
-    u[d] = n >= 1 ? u[d] : (n == 0 ? (u[d] & 0xffffu) : 0u);
-  }
-  return __builtin_bit_cast(bf16x8, u);
-}
 
 // Inter-chunk MFMAs of a wave: y^T[p][l] += sum_n state[p][n] C[l][n] for its
 // row groups (the row factor 2^(a_l) is applied by the caller).
@@ -803,10 +792,12 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
         }
       }
     }
-    // CB pieces stream through a ring of three per row group: the first two
-    // steps' pieces are in flight while x is rescaled, and each step issues
-    // the pieces two steps ahead (the loop is unrolled, so the slots are
-    // fixed registers).  Steps past a row group's last load nothing.
+    // CB pieces stream through a ring of three per row group, and enter the
+    // MFMAs as loaded (the stored CB is 0 above the diagonal, so the diagonal
+    // step needs no mask): the first two steps' pieces are in flight while x
+    // is rescaled, and each step issues the pieces two steps ahead (the loop
+    // is unrolled, so the slots are fixed registers).  Steps past a row
+    // group's last load nothing.
     bf16x8 ring[RGW][3];
 #pragma unroll
     for (int i = 0; i < RGW; ++i)
@@ -843,9 +834,8 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
             ring[i][(q + 2) % 3] = __builtin_bit_cast(
                 bf16x8, buf_load16(rcb, ((uint32_t)lrow[i] * L + kq + 32 * (q + 2)) * 2u));
 #pragma unroll
-        for (int i = 0; i < RGW; ++i)      // the last step of a row group holds its diagonal
-          if (q < nq[i])
-            fb[i] = q == nq[i] - 1 ? causal_mask(ring[i][q % 3], lrow[i] - 32 * q - kq) : ring[i][q % 3];
+        for (int i = 0; i < RGW; ++i)
+          if (q < nq[i]) fb[i] = ring[i][q % 3];
       }
 #pragma unroll
       for (int i = 0; i < RGW; ++i)

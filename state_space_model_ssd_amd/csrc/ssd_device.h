@@ -50,7 +50,9 @@ __device__ __forceinline__ void chunk_cumsum_block(const ChunkDesc& d, int l,
 // group g, accumulated in fp32 on MFMA and stored in T.  TH threads (4 or 8
 // waves: each wave owns 4 or 2 of the 16 output 16x16 tiles); Cs and Bs are
 // LDS tiles of 64 x (N + 16 bytes).  Rows past the chunk's end load as zeros,
-// so their CB entries are exactly 0.
+// so their CB entries are exactly 0.  A diagonal tile (ti == tj) stores 0
+// above the diagonal (s > l): the stored CB is causal, and a consumer may
+// multiply whole 32- or 64-token blocks of a row without masking them.
 template <typename T, int N, int L, int TH = 256>
 __device__ __forceinline__ void bmm_tile(const ChunkDesc& d, int j, int g, int ti, int tj,
                                          const T* __restrict__ C, const T* __restrict__ B, int G,
@@ -100,7 +102,7 @@ __device__ __forceinline__ void bmm_tile(const ChunkDesc& d, int j, int g, int t
       for (int r = 0; r < 4; ++r) {
         const int row = ti * 64 + wr + mi * 16 + (lane >> 4) * 4 + r;
         const int col = tj * 64 + wc + ni * 16 + lr;
-        out[(int64_t)row * L + col] = from_f32<T>(acc[mi][ni][r]);
+        out[(int64_t)row * L + col] = from_f32<T>(col <= row ? acc[mi][ni][r] : 0.f);
       }
 }
 

@@ -87,6 +87,12 @@ def test_bmm_stage(run):
             scale = (Cf[t0:t0 + n, g] @ Bf[t0:t0 + n, g].T)[tri]
             store = 0.0 if prob.dtype == "f32" else 2.0 ** -8
             assert np.max(np.abs(got - want) / (2e-6 * scale + store * np.abs(want) + 1e-30)) <= 1.0
+            # the stored CB is causal: 0 above the diagonal of every diagonal
+            # 64x64 block the chunk's rows reach (chunk_scan multiplies them
+            # unmasked)
+            for b0 in range(0, n, 64):
+                blk = cb[c, g, b0:b0 + 64, b0:b0 + 64]
+                assert not np.triu(blk, 1).any()
 
 
 def test_chunk_state_stage(run):
