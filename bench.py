@@ -130,7 +130,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, help="1..5")
+    ap.add_argument("--workload", type=int, default=2, help="1..6")
+    ap.add_argument("--tuning", default=None, metavar="JSON",
+                    help='pin kernel choices, e.g. \'{"sp_blocks": 1}\' (default: the tuned '
+                         'config, else the library\'s own choice)')
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -158,7 +161,9 @@ def main():
                                  nseq=len(prob.seq_lens) if prob.seq_lens else 0)
     lay = binding.workspace_layout(cprob)
     from state_space_model_ssd_amd import tuning
-    tuned = tuning.lookup(cprob)            # the binding applies the same lookup
+    pinned = json.loads(args.tuning) if args.tuning else None
+    tuned = pinned if pinned is not None else tuning.lookup(cprob)
+    tune_arg = pinned if pinned is not None else "config"   # the binding's own lookup
     ws = torch.empty(lay.total_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(d["x"])
     fin = torch.empty((prob.nseq, prob.nheads, prob.headdim, prob.dstate), dtype=torch.float32,
@@ -168,7 +173,7 @@ def main():
         binding.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, D=d["D"],
                         dt_bias=d["dt_bias"], initial_states=d["init"],
                         cu_seqlens=d["cu_seqlens"], out=out, final_states=fin, workspace=ws,
-                        stages=stages)
+                        stages=stages, tuning=tune_arg)
 
     log("[bench] warmup")
     for _ in range(max(args.warmup, 1)):
@@ -323,7 +328,8 @@ def main():
                    "chunk_size": prob.chunk_size, "tokens": tokens, "chunks": nchunks},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "tuning": {"source": "tuned config" if tuned else "library's own choice",
+        "tuning": {"source": "pinned" if pinned is not None else
+                   "tuned config" if tuned else "library's own choice",
                    "key": tuning.shape_key(cprob), "choice": tuned or {}},
         "stages": stages,
         "stages_unfused": singles,

@@ -25,8 +25,12 @@
  *   stage 1  chunk_cumsum    delta and its chunk-local running sum of delta*A
  *   stage 2  bmm_chunk       C B^T inside each chunk (lower triangle)
  *   stage 3  chunk_state     per-chunk state from a zero start
- *   stage 4  state_passing   sequential chain over chunks; states entering
- *                            each chunk and the final states
+ *   stage 4  state_passing   chain over chunks: states entering each chunk
+ *                            and the final states; one sequential chain per
+ *                            sequence, or, for problems with few state
+ *                            elements, blocks of chunks composed as an
+ *                            associative scan (clova.ai, "Stage 3. Logic and
+ *                            heuristic refinement")
  *   stage 5  chunk_scan      decay-masked (C B^T) x  +  exp(cumsum) C . state
  *                            +  D x, accumulated in fp32
  *
@@ -113,10 +117,18 @@ typedef struct {
  *                as l are 0; the rest are not written)
  *   chunk_states fp32 [max_chunks][nheads][headdim][dstate]
  *   states_in    dtype [max_chunks][nheads][headdim][dstate]: state entering
- *                each chunk                                                */
+ *                each chunk
+ *   block_states, block_logdecay  fp32 [nstates][sp_blocks][nheads][headdim *
+ *                dstate] and [nstates][sp_blocks][nheads]: the blocked
+ *                state_passing's per-block end states and log decays
+ *                (present, with sp_blocks = 16, only when nstates * nheads *
+ *                headdim * dstate < 2^18; else sp_blocks = 1 and both are
+ *                empty)                                                    */
 typedef struct {
   int64_t max_chunks;
   size_t chunk_table, seq_chunks, delta, dA_cumsum, cb, chunk_states, states_in;
+  size_t block_states, block_logdecay;
+  int64_t sp_blocks;
   size_t total_bytes;
 } ssd_workspace_layout_t;
 
@@ -184,7 +196,11 @@ ssd_status_t ssd_fwd_stages(const ssd_problem_t* p,
  *                or 4 (identical results).
  *   front        bf16 stages 1-3: 1 = one fused launch, 2 = one launch per
  *                stage (identical results).  Must be 0 for fp32.
- *   reserved     must be 0.
+ *   sp_blocks    state_passing: 1 = one sequential chain per sequence; 2, 4,
+ *                8 or 16 = that many blocks per sequence, scanned in two
+ *                launches (rounds differently: the blocks' maps are
+ *                composed in another order).  Above 1 only when the
+ *                workspace layout's sp_blocks is 16.
  * A field outside its range, or a choice the dtype does not have, is
  * rejected with SSD_ERR_INVALID_ARG before anything is enqueued.
  */
@@ -192,7 +208,7 @@ typedef struct {
   int32_t scan_kernel;
   int32_t sp_vec;
   int32_t front;
-  int32_t reserved;
+  int32_t sp_blocks;
 } ssd_tuning_t;
 
 /*

@@ -51,13 +51,14 @@ class LayoutC(ctypes.Structure):
                 ("seq_chunks", ctypes.c_size_t), ("delta", ctypes.c_size_t),
                 ("dA_cumsum", ctypes.c_size_t), ("cb", ctypes.c_size_t),
                 ("chunk_states", ctypes.c_size_t), ("states_in", ctypes.c_size_t),
-                ("total_bytes", ctypes.c_size_t)]
+                ("block_states", ctypes.c_size_t), ("block_logdecay", ctypes.c_size_t),
+                ("sp_blocks", ctypes.c_int64), ("total_bytes", ctypes.c_size_t)]
 
 
 class TuningC(ctypes.Structure):
     """ssd_tuning_t: pinned kernel choices, 0 = the library's own."""
     _fields_ = [("scan_kernel", ctypes.c_int32), ("sp_vec", ctypes.c_int32),
-                ("front", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("front", ctypes.c_int32), ("sp_blocks", ctypes.c_int32)]
 
 
 _lib = None
@@ -188,10 +189,10 @@ def ssd_fwd_seq_idx(x, dt, A, B, C, chunk_size, seq_idx, nseq, **kw):
 
 
 def make_tuning(choice) -> TuningC:
-    """TuningC from None or a dict of scan_kernel / sp_vec / front."""
+    """TuningC from None or a dict of scan_kernel / sp_vec / front / sp_blocks."""
     t = TuningC(0, 0, 0, 0)
     if choice:
-        unknown = set(choice) - {"scan_kernel", "sp_vec", "front"}
+        unknown = set(choice) - {"scan_kernel", "sp_vec", "front", "sp_blocks"}
         if unknown:
             raise ValueError(f"unknown tuning fields {sorted(unknown)}")
         for k, v in choice.items():

@@ -69,6 +69,32 @@ int64_t max_chunks_of(const ssd_problem_t* p) {
   return p->batch * ((p->seqlen + L - 1) / L);
 }
 
+// The blocked state_passing (associative scan over blocks of chunks) is
+// for problems whose state elements, one chain each, cannot keep the HBM
+// busy: fewer than kSpBlockElems (1024 waves of 64 lanes, 4 elements each).
+constexpr int64_t kSpBlockElems = int64_t(1) << 18;
+constexpr int kSpMaxBlocks = 16;
+
+int64_t state_elems(const ssd_problem_t* p) {
+  const int64_t nstates = p->nseq > 0 ? p->nseq : p->batch;
+  return nstates * p->nheads * p->headdim * p->dstate;
+}
+
+// The library's own block count.  Blocking costs a second launch and a
+// second read of the chunk states, which measured slower for sequences of
+// 32 and 64 chunks and up to 37% faster from 256 chunks on; so: sequences of
+// at least 128 chunks on average, enough blocks to reach kSpBlockElems
+// chains, and blocks of at least 16 chunks.
+int auto_sp_blocks(const ssd_problem_t* p, int64_t max_chunks) {
+  const int64_t elems = state_elems(p);
+  const int64_t nstates = p->nseq > 0 ? p->nseq : p->batch;
+  const int64_t per_seq = max_chunks / (nstates > 0 ? nstates : 1);
+  if (elems <= 0 || elems >= kSpBlockElems || per_seq < 128) return 1;
+  int kb = 1;
+  while (kb < kSpMaxBlocks && elems * kb < kSpBlockElems && per_seq >= 16 * (2 * kb)) kb *= 2;
+  return kb;
+}
+
 void layout_of(const ssd_problem_t* p, ssd_workspace_layout_t* w) {
   const int64_t mc = max_chunks_of(p);
   const int64_t nstates = p->nseq > 0 ? p->nseq : p->batch;
@@ -82,13 +108,20 @@ void layout_of(const ssd_problem_t* p, ssd_workspace_layout_t* w) {
   w->cb = off;           off = align_up(off + elem_size(p->dtype) * (size_t)mc * p->ngroups * L * L);
   w->chunk_states = off; off = align_up(off + sizeof(float) * (size_t)mc * H * PN);
   w->states_in = off;    off = align_up(off + elem_size(p->dtype) * (size_t)mc * H * PN);
+  w->sp_blocks = state_elems(p) < kSpBlockElems ? kSpMaxBlocks : 1;
+  const size_t kbw = w->sp_blocks > 1 ? (size_t)w->sp_blocks : 0;
+  w->block_states = off;   off = align_up(off + sizeof(float) * (size_t)nstates * kbw * H * PN);
+  w->block_logdecay = off; off = align_up(off + sizeof(float) * (size_t)nstates * kbw * H);
   w->total_bytes = off;
 }
 
 // Ranges of the pinned kernel choices (0 keeps the library's choice).
-ssd_status_t check_tuning(const ssd_problem_t* p, const ssd_tuning_t& t) {
+ssd_status_t check_tuning(const ssd_problem_t* p, const ssd_tuning_t& t, int64_t ws_blocks) {
   const bool bf16 = p->dtype == SSD_BF16;
-  if (t.reserved != 0) return SSD_ERR_INVALID_ARG;
+  if (t.sp_blocks != 0 && t.sp_blocks != 1 && t.sp_blocks != 2 && t.sp_blocks != 4 &&
+      t.sp_blocks != 8 && t.sp_blocks != 16)
+    return SSD_ERR_INVALID_ARG;
+  if (t.sp_blocks > ws_blocks) return SSD_ERR_INVALID_ARG;
   if (t.scan_kernel < 0 || t.scan_kernel > 2 || (!bf16 && t.scan_kernel != 0)) return SSD_ERR_INVALID_ARG;
   if (t.sp_vec != 0 && t.sp_vec != 1 && t.sp_vec != 2 && t.sp_vec != 4) return SSD_ERR_INVALID_ARG;
   if (t.front < 0 || t.front > 2 || (!bf16 && t.front != 0)) return SSD_ERR_INVALID_ARG;
@@ -104,7 +137,9 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
   if (st != SSD_OK) return st;
   if (stages & ~(uint32_t)SSD_STAGE_ALL) return SSD_ERR_INVALID_ARG;
   const ssd_tuning_t tune = tuning ? *tuning : ssd_tuning_t{0, 0, 0, 0};
-  st = check_tuning(p, tune);
+  ssd_workspace_layout_t w;
+  layout_of(p, &w);
+  st = check_tuning(p, tune, w.sp_blocks);
   if (st != SSD_OK) return st;
   const bool packed = p->nseq > 0;
   if (packed && ((cu_seqlens != nullptr) + (seq_idx != nullptr)) != 1) return SSD_ERR_INVALID_ARG;
@@ -112,8 +147,6 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
   const int64_t tokens = p->batch * p->seqlen;
   if (tokens > 0 && (!x || !dt || !A || !B || !C || !out)) return SSD_ERR_INVALID_ARG;
 
-  ssd_workspace_layout_t w;
-  layout_of(p, &w);
   if (!workspace || workspace_bytes < w.total_bytes) return SSD_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
   const Kernels* k = find_kernels(p->dtype, p->headdim, p->dstate, p->chunk_size);
@@ -134,6 +167,7 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
   a.dt_max = p->dt_max;
   a.scan_kernel = tune.scan_kernel;
   a.sp_vec = tune.sp_vec;
+  a.sp_blocks = tune.sp_blocks > 0 ? tune.sp_blocks : auto_sp_blocks(p, w.max_chunks);
   a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.D = D;
   a.init = initial_states;
   a.cu_seqlens = cu_seqlens;
@@ -148,6 +182,8 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
   a.cb = base + w.cb;
   a.chunk_states = reinterpret_cast<float*>(base + w.chunk_states);
   a.states_in = base + w.states_in;
+  a.block_states = w.sp_blocks > 1 ? reinterpret_cast<float*>(base + w.block_states) : nullptr;
+  a.block_logdecay = w.sp_blocks > 1 ? reinterpret_cast<float*>(base + w.block_logdecay) : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   struct Step { uint32_t bit; launch_fn fn; };

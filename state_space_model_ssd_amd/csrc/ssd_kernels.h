@@ -18,6 +18,7 @@ struct FwdArgs {
   float dt_min, dt_max;
   int scan_kernel;  // 0: by shape, 1: one workgroup per tile, 2: persistent (bf16)
   int sp_vec;       // 0: by shape, else state elements per state_passing thread
+  int sp_blocks;    // state_passing: 1 = one chain per sequence, KB > 1 = KB blocks
 
   const void* x;
   const float* dt;
@@ -39,6 +40,8 @@ struct FwdArgs {
   void* cb;             // dtype of x
   float* chunk_states;
   void* states_in;
+  float* block_states;     // [nstates][KB][H][P*N] when sp_blocks > 1
+  float* block_logdecay;   // [nstates][KB][H]
 
   ChunkMap cmap() const {
     ChunkMap m;

@@ -116,7 +116,10 @@ def make_inputs(prob: Problem, recipe: Recipe = Recipe(), seed: int = 0,
 
 
 # --------------------------------------------------------------------------
-# The five named workloads.  Config k is drawn from seed k - 1.
+# The named workloads.  Workload k is drawn from seed k - 1.  Workloads 1-5
+# are the five configurations of the forward; workload 6 is a shape where one
+# state chain per element leaves the HBM idle (two heads at long context),
+# for the blocked state_passing.
 # --------------------------------------------------------------------------
 
 def _cfg5_lens(seed: int) -> tuple:
@@ -124,7 +127,7 @@ def _cfg5_lens(seed: int) -> tuple:
 
 
 def workload(k: int):
-    """Return (Problem, Recipe, seed) of workload k in 1..5."""
+    """Return (Problem, Recipe, seed) of workload k in 1..6."""
     if k == 1:   # tiny, fp32 everywhere
         return (Problem(1, 512, 4, 32, 16, 1, 64, "f32"), Recipe(), 0)
     if k == 2:   # Mamba-2 layer shape, short context
@@ -138,7 +141,9 @@ def workload(k: int):
         lens = _cfg5_lens(4)
         return (Problem(1, sum(lens), 32, 64, 128, 4, 256, "bf16", seq_lens=lens),
                 Recipe(init_std=0.1), 4)
-    raise ValueError(f"workload {k} does not exist (1..5)")
+    if k == 6:   # two heads, 256-chunk chain: 16384 state elements
+        return (Problem(1, 65536, 2, 64, 128, 1, 256, "bf16"), Recipe(init_std=0.1), 5)
+    raise ValueError(f"workload {k} does not exist (1..6)")
 
 
 def workload_inputs(k: int) -> tuple:
@@ -159,6 +164,7 @@ WORKLOAD_NAMES = {
     3: "train-batch b4 T8192 H64 P64 N128 G8 L256 bf16",
     4: "long-context b1 T131072 H32 P64 N128 G1 L256 bf16 init",
     5: "packed-16seq H32 P64 N128 G4 L256 bf16 init",
+    6: "few-heads-long b1 T65536 H2 P64 N128 G1 L256 bf16 init",
 }
 
 

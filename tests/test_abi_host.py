@@ -52,13 +52,14 @@ def _expected_layout(b, T, H, P, N, G, L, nseq, esize):
     al = lambda v: (v + 255) // 256 * 256
     mc = (min((T + nseq * (L - 1)) // L, T) if nseq else b * ((T + L - 1) // L))
     nst = nseq if nseq else b
+    kb = 16 if nst * H * P * N < 2 ** 18 else 0      # blocked state_passing reserve
     sizes = [16 * mc, 4 * (nst + 1), 4 * mc * H * L, 4 * mc * H * L, esize * mc * G * L * L,
-             4 * mc * H * P * N, esize * mc * H * P * N]
+             4 * mc * H * P * N, esize * mc * H * P * N, 4 * nst * kb * H * P * N, 4 * nst * kb * H]
     offs, off = [], 0
     for s in sizes:
         offs.append(off)
         off = al(off + s)
-    return mc, offs, off
+    return mc, offs, off, max(kb, 1)
 
 
 @pytest.mark.parametrize("shape", [
@@ -72,11 +73,11 @@ def test_workspace_layout_matches_documentation(shape):
     p = _prob(**shape)
     lay = binding.workspace_layout(p)
     es = 2 if p.dtype == binding.SSD_BF16 else 4
-    mc, offs, total = _expected_layout(p.batch, p.seqlen, p.nheads, p.headdim, p.dstate,
-                                       p.ngroups, p.chunk_size, p.nseq, es)
-    assert lay.max_chunks == mc
+    mc, offs, total, kb = _expected_layout(p.batch, p.seqlen, p.nheads, p.headdim, p.dstate,
+                                           p.ngroups, p.chunk_size, p.nseq, es)
+    assert lay.max_chunks == mc and lay.sp_blocks == kb
     got = [lay.chunk_table, lay.seq_chunks, lay.delta, lay.dA_cumsum, lay.cb, lay.chunk_states,
-           lay.states_in]
+           lay.states_in, lay.block_states, lay.block_logdecay]
     assert got == offs and lay.total_bytes == total == binding.workspace_size(p)
 
 

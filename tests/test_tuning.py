@@ -35,7 +35,23 @@ def test_candidates_cover_every_choice():
     assert {c["sp_vec"] for c in bf} == {1, 2, 4}
     assert {c["front"] for c in bf} == {1, 2}
     f32 = tuning.candidates(_prob(dtype=binding.SSD_F32, headdim=32, dstate=16, chunk_size=64))
-    assert f32 == [{"sp_vec": 1}, {"sp_vec": 2}, {"sp_vec": 4}]
+    assert f32[:3] == [{"sp_vec": 1}, {"sp_vec": 2}, {"sp_vec": 4}]
+    # few state elements: the workspace reserves 16 blocks, so every block
+    # count is a candidate, with every vector width
+    assert len(f32) == 3 + 15
+    assert {c["sp_blocks"] for c in f32[3:]} == {1, 2, 4, 8, 16}
+
+
+def test_workspace_reserves_blocks_only_for_few_state_elements():
+    small = binding.workspace_layout(_prob(dtype=binding.SSD_F32, headdim=32, dstate=16,
+                                           chunk_size=64))
+    assert small.sp_blocks == 16
+    nst, H, PN = 2, 24, 32 * 16
+    assert small.block_logdecay - small.block_states >= 4 * nst * 16 * H * PN
+    assert small.total_bytes - small.block_logdecay >= 4 * nst * 16 * H
+    big = binding.workspace_layout(_prob())          # 2 * 24 * 64 * 128 >= 2^18 elements
+    assert big.sp_blocks == 1
+    assert big.block_logdecay == big.block_states == big.total_bytes
 
 
 def test_config_round_trip_and_fallback(tmp_path, monkeypatch):
@@ -68,7 +84,7 @@ def test_committed_config_is_well_formed():
 
 def test_make_tuning_rejects_unknown_fields():
     t = binding.make_tuning({"sp_vec": 2})
-    assert (t.scan_kernel, t.sp_vec, t.front, t.reserved) == (0, 2, 0, 0)
+    assert (t.scan_kernel, t.sp_vec, t.front, t.sp_blocks) == (0, 2, 0, 0)
     with pytest.raises(ValueError):
         binding.make_tuning({"tile": 1})
 
@@ -82,7 +98,9 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails on the h
     (binding.SSD_BF16, dict(sp_vec=3)),
     (binding.SSD_BF16, dict(sp_vec=8)),
     (binding.SSD_BF16, dict(front=3)),
-    (binding.SSD_BF16, dict(reserved=1)),
+    (binding.SSD_BF16, dict(sp_blocks=3)),
+    (binding.SSD_BF16, dict(sp_blocks=32)),
+    (binding.SSD_BF16, dict(sp_blocks=2)),      # a layer-size problem reserves no blocks
     (binding.SSD_F32, dict(scan_kernel=1)),     # fp32 has one chunk_scan kernel
     (binding.SSD_F32, dict(front=1)),           # and no fused front
 ])
