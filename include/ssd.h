@@ -224,6 +224,40 @@ ssd_status_t ssd_fwd_tuned(const ssd_problem_t* p,
                            void* workspace, size_t workspace_bytes,
                            uint32_t stages, const ssd_tuning_t* tuning, void* stream);
 
+/*
+ * The backward: gradients of loss = sum(out * dout) + sum(final_states *
+ * dfinal_states) with respect to every input of ssd_fwd (the layer's backward
+ * kernels are listed next to the forward ones on the clova.ai page, table
+ * "Share of compute time by kernel").  Same problem, inputs and conventions
+ * as ssd_fwd; the forward's stages 0-4 are recomputed inside, so no forward
+ * call needs to precede it.
+ *
+ *   dout           [batch, seqlen, nheads, headdim] dtype (required)
+ *   dfinal_states  [nstates, nheads, headdim, dstate] fp32 (nullable: 0)
+ *   dx             like x, dtype          ddt  like dt, fp32
+ *   dB, dC         like B and C, dtype    dA   [nheads] fp32
+ *   dD, ddt_bias   [nheads] fp32 (nullable: not computed)
+ *   dinitial_states [nstates, nheads, headdim, dstate] fp32 (nullable)
+ * dD and ddt_bias are the gradients at the given D and dt_bias (also when
+ * those are NULL, i.e. 0); dinitial_states likewise for a NULL initial
+ * state.  Gradients accumulate in fp32; dx, dB, dC are rounded once to the
+ * dtype.  Entries of tokens that belong to no sequence are not written.
+ * The workspace is ssd_bwd_workspace_size bytes (256-byte aligned); it
+ * begins with the forward's layout (ssd_workspace_layout) followed by the
+ * backward's own fp32 buffers.  Errors as for ssd_fwd.
+ */
+size_t ssd_bwd_workspace_size(const ssd_problem_t* p);
+
+ssd_status_t ssd_bwd(const ssd_problem_t* p,
+                     const void* x, const float* dt, const float* dt_bias,
+                     const float* A, const void* B, const void* C, const float* D,
+                     const float* initial_states,
+                     const int32_t* cu_seqlens, const int32_t* seq_idx,
+                     const void* dout, const float* dfinal_states,
+                     void* dx, float* ddt, float* dA, void* dB, void* dC,
+                     float* dD, float* ddt_bias, float* dinitial_states,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* ssd_status_string(ssd_status_t s);
 

@@ -28,7 +28,8 @@ STAGES = {"plan": STAGE_PLAN, "chunk_cumsum": STAGE_CUMSUM, "bmm_chunk": STAGE_B
           "chunk_scan": STAGE_CHUNK_SCAN}
 
 EXPORTED = ("ssd_fwd_workspace_size", "ssd_workspace_layout", "ssd_config_supported",
-            "ssd_fwd", "ssd_fwd_stages", "ssd_fwd_tuned", "ssd_status_string")
+            "ssd_fwd", "ssd_fwd_stages", "ssd_fwd_tuned", "ssd_bwd_workspace_size", "ssd_bwd",
+            "ssd_status_string")
 
 
 class SsdError(RuntimeError):
@@ -90,6 +91,10 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_fwd_tuned.argtypes = [PP] + [vp] * 12 + [vp, sz, ctypes.c_uint32,
                                                      ctypes.POINTER(TuningC), vp]
     lib.ssd_fwd_tuned.restype = ctypes.c_int
+    lib.ssd_bwd_workspace_size.argtypes = [PP]
+    lib.ssd_bwd_workspace_size.restype = sz
+    lib.ssd_bwd.argtypes = [PP] + [vp] * 20 + [vp, sz, vp]
+    lib.ssd_bwd.restype = ctypes.c_int
     lib.ssd_status_string.argtypes = [ctypes.c_int]
     lib.ssd_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -177,6 +182,58 @@ def ssd_fwd(x, dt, A, B, C, chunk_size, D=None, dt_bias=None, initial_states=Non
     return _run(x, dt, A, B, C, chunk_size, D, dt_bias, initial_states, cu_seqlens, None, nseq,
                 dt_min, dt_max, out, final_states, return_final_states, workspace, stages,
                 tuning)
+
+
+def bwd_workspace_size(prob: ProblemC) -> int:
+    return int(load_library().ssd_bwd_workspace_size(ctypes.byref(prob)))
+
+
+def ssd_bwd(x, dt, A, B, C, chunk_size, dout, dfinal_states=None, D=None, dt_bias=None,
+            initial_states=None, cu_seqlens=None, dt_min=0.0, dt_max=math.inf, workspace=None):
+    """SSD backward on the GPU through the C ABI: gradients of
+    sum(out * dout) + sum(final_states * dfinal_states) for the inputs of
+    ssd_fwd (same arguments).  Returns a dict with x, dt, A, B, C, D,
+    dt_bias, initial_states (gradients; D, dt_bias and initial_states always
+    computed) and the workspace."""
+    lib = load_library()
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_bwd runs on the GPU only; x is on " + str(dev))
+    f32 = torch.float32
+    nseq = cu_seqlens.numel() - 1 if cu_seqlens is not None else 0
+    nstates = nseq if nseq > 0 else b
+    _need(x, "x", x.dtype, (b, T, H, P), dev)
+    _need(dt, "dt", f32, (b, T, H), dev)
+    _need(A, "A", f32, (H,), dev)
+    _need(B, "B", x.dtype, (b, T, G, N), dev)
+    _need(C, "C", x.dtype, (b, T, G, N), dev)
+    _need(D, "D", f32, (H,), dev)
+    _need(dt_bias, "dt_bias", f32, (H,), dev)
+    _need(initial_states, "initial_states", f32, (nstates, H, P, N), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,), dev)
+    _need(dout, "dout", x.dtype, (b, T, H, P), dev)
+    _need(dfinal_states, "dfinal_states", f32, (nstates, H, P, N), dev)
+    prob = make_problem(b, T, H, P, N, G, chunk_size, x.dtype, nseq, dt_min, dt_max)
+    g = {"x": torch.zeros_like(x), "dt": torch.zeros_like(dt), "A": torch.empty(H, dtype=f32, device=dev),
+         "B": torch.zeros_like(B), "C": torch.zeros_like(C), "D": torch.empty(H, dtype=f32, device=dev),
+         "dt_bias": torch.empty(H, dtype=f32, device=dev),
+         "initial_states": torch.empty((nstates, H, P, N), dtype=f32, device=dev)}
+    need = lib.ssd_bwd_workspace_size(ctypes.byref(prob))
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        code = lib.ssd_bwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B),
+                           _ptr(C), _ptr(D), _ptr(initial_states), _ptr(cu_seqlens), None,
+                           _ptr(dout), _ptr(dfinal_states), _ptr(g["x"]), _ptr(g["dt"]),
+                           _ptr(g["A"]), _ptr(g["B"]), _ptr(g["C"]), _ptr(g["D"]),
+                           _ptr(g["dt_bias"]), _ptr(g["initial_states"]), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), stream)
+    _check(code)
+    g["workspace"] = workspace
+    return g
 
 
 def ssd_fwd_seq_idx(x, dt, A, B, C, chunk_size, seq_idx, nseq, **kw):

@@ -14,10 +14,13 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 typedef hipError_t (*launch_fn)(const FwdArgs&, hipStream_t);
 
+typedef hipError_t (*launch_bwd_fn)(const FwdArgs&, const BwdArgs&, hipStream_t);
+
 struct Kernels {
   int32_t dtype;
   int64_t P, N, L;
   launch_fn bmm, chunk_state, state_passing, chunk_scan, front;
+  launch_bwd_fn backward;
 };
 
 template <typename T> constexpr int32_t dtype_of();
@@ -27,7 +30,7 @@ template <> constexpr int32_t dtype_of<bf16>() { return SSD_BF16; }
 #define SSD_ROW(T, P, N, L)                                                              \
   {dtype_of<T>(), P, N, L, &launch_bmm_chunk<T, N, L>, &launch_chunk_state<T, P, N, L>, \
    &launch_state_passing<T>, &launch_chunk_scan<T, P, N, L>,                          \
-   sizeof(T) == 2 ? &launch_front<T, P, N, L> : nullptr},
+   sizeof(T) == 2 ? &launch_front<T, P, N, L> : nullptr, &launch_backward<T, P, N, L>},
 const Kernels kKernels[] = {SSD_FOR_EACH_CONFIG(SSD_ROW)};
 #undef SSD_ROW
 
@@ -128,30 +131,22 @@ ssd_status_t check_tuning(const ssd_problem_t* p, const ssd_tuning_t& t, int64_t
   return SSD_OK;
 }
 
-ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias,
-                 const float* A, const void* B, const void* C, const float* D,
-                 const float* initial_states, const int32_t* cu_seqlens, const int32_t* seq_idx,
-                 void* out, float* final_states, void* workspace, size_t workspace_bytes,
-                 uint32_t stages, const ssd_tuning_t* tuning, void* stream) {
-  ssd_status_t st = check_problem(p);
-  if (st != SSD_OK) return st;
-  if (stages & ~(uint32_t)SSD_STAGE_ALL) return SSD_ERR_INVALID_ARG;
-  const ssd_tuning_t tune = tuning ? *tuning : ssd_tuning_t{0, 0, 0, 0};
-  ssd_workspace_layout_t w;
-  layout_of(p, &w);
-  st = check_tuning(p, tune, w.sp_blocks);
-  if (st != SSD_OK) return st;
+// The arguments common to the forward and the backward: pointer checks and
+// the forward's part of the workspace.
+ssd_status_t fill_args(const ssd_problem_t* p, const ssd_workspace_layout_t& w,
+                       const ssd_tuning_t& tune, const void* x, const float* dt,
+                       const float* dt_bias, const float* A, const void* B, const void* C,
+                       const float* D, const float* initial_states, const int32_t* cu_seqlens,
+                       const int32_t* seq_idx, void* out, float* final_states, void* workspace,
+                       FwdArgs* out_args) {
   const bool packed = p->nseq > 0;
   if (packed && ((cu_seqlens != nullptr) + (seq_idx != nullptr)) != 1) return SSD_ERR_INVALID_ARG;
   if (!packed && (cu_seqlens || seq_idx)) return SSD_ERR_INVALID_ARG;
   const int64_t tokens = p->batch * p->seqlen;
-  if (tokens > 0 && (!x || !dt || !A || !B || !C || !out)) return SSD_ERR_INVALID_ARG;
+  if (tokens > 0 && (!x || !dt || !A || !B || !C)) return SSD_ERR_INVALID_ARG;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
 
-  if (!workspace || workspace_bytes < w.total_bytes) return SSD_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
-  const Kernels* k = find_kernels(p->dtype, p->headdim, p->dstate, p->chunk_size);
-
-  FwdArgs a;
+  FwdArgs& a = *out_args;
   a.batch = (int)p->batch;
   a.seqlen = (int)p->seqlen;
   a.H = (int)p->nheads;
@@ -184,7 +179,12 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
   a.states_in = base + w.states_in;
   a.block_states = w.sp_blocks > 1 ? reinterpret_cast<float*>(base + w.block_states) : nullptr;
   a.block_logdecay = w.sp_blocks > 1 ? reinterpret_cast<float*>(base + w.block_logdecay) : nullptr;
+  return SSD_OK;
+}
 
+ssd_status_t launch_stages(const ssd_problem_t* p, const FwdArgs& a, uint32_t stages,
+                           const ssd_tuning_t& tune, void* stream) {
+  const Kernels* k = find_kernels(p->dtype, p->headdim, p->dstate, p->chunk_size);
   hipStream_t s = static_cast<hipStream_t>(stream);
   struct Step { uint32_t bit; launch_fn fn; };
   const Step steps[] = {
@@ -206,6 +206,91 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
     }
     if (stp.fn(a, s) != hipSuccess) return SSD_ERR_HIP;
   }
+  return SSD_OK;
+}
+
+ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias,
+                 const float* A, const void* B, const void* C, const float* D,
+                 const float* initial_states, const int32_t* cu_seqlens, const int32_t* seq_idx,
+                 void* out, float* final_states, void* workspace, size_t workspace_bytes,
+                 uint32_t stages, const ssd_tuning_t* tuning, void* stream) {
+  ssd_status_t st = check_problem(p);
+  if (st != SSD_OK) return st;
+  if (stages & ~(uint32_t)SSD_STAGE_ALL) return SSD_ERR_INVALID_ARG;
+  const ssd_tuning_t tune = tuning ? *tuning : ssd_tuning_t{0, 0, 0, 0};
+  ssd_workspace_layout_t w;
+  layout_of(p, &w);
+  st = check_tuning(p, tune, w.sp_blocks);
+  if (st != SSD_OK) return st;
+  const int64_t tokens = p->batch * p->seqlen;
+  if (tokens > 0 && !out) return SSD_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < w.total_bytes) return SSD_ERR_WORKSPACE;
+  FwdArgs a;
+  st = fill_args(p, w, tune, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, out,
+                 final_states, workspace, &a);
+  if (st != SSD_OK) return st;
+  return launch_stages(p, a, stages, tune, stream);
+}
+
+
+// The backward's regions follow the forward's in its workspace.
+struct BwdLayout {
+  size_t Q, dS, dcb, dBh, dCh, dA_part, dD_part, dbias_part, total;
+};
+
+void bwd_layout_of(const ssd_problem_t* p, const ssd_workspace_layout_t& w, BwdLayout* b) {
+  const size_t mc = (size_t)w.max_chunks, H = p->nheads, L = p->chunk_size, N = p->dstate;
+  const size_t PN = (size_t)p->headdim * p->dstate;
+  size_t off = w.total_bytes;
+  b->Q = off;          off = align_up(off + sizeof(float) * mc * H * PN);
+  b->dS = off;         off = align_up(off + sizeof(float) * mc * H * PN);
+  b->dcb = off;        off = align_up(off + sizeof(float) * mc * H * L * L);
+  b->dBh = off;        off = align_up(off + sizeof(float) * mc * H * L * N);
+  b->dCh = off;        off = align_up(off + sizeof(float) * mc * H * L * N);
+  b->dA_part = off;    off = align_up(off + sizeof(float) * mc * H);
+  b->dD_part = off;    off = align_up(off + sizeof(float) * mc * H);
+  b->dbias_part = off; off = align_up(off + sizeof(float) * mc * H);
+  b->total = off;
+}
+
+ssd_status_t run_bwd(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias,
+                     const float* A, const void* B, const void* C, const float* D,
+                     const float* initial_states, const int32_t* cu_seqlens,
+                     const int32_t* seq_idx, const void* dout, const float* dfinal, void* dx,
+                     float* ddt, float* dA, void* dB, void* dC, float* dD, float* ddt_bias,
+                     float* dinit, void* workspace, size_t workspace_bytes, void* stream) {
+  ssd_status_t st = check_problem(p);
+  if (st != SSD_OK) return st;
+  const int64_t tokens = p->batch * p->seqlen;
+  if (!dA) return SSD_ERR_INVALID_ARG;
+  if (tokens > 0 && (!dout || !dx || !ddt || !dB || !dC)) return SSD_ERR_INVALID_ARG;
+  ssd_workspace_layout_t w;
+  layout_of(p, &w);
+  BwdLayout bl;
+  bwd_layout_of(p, w, &bl);
+  if (!workspace || workspace_bytes < bl.total) return SSD_ERR_WORKSPACE;
+  const ssd_tuning_t tune{0, 0, 0, 0};
+  FwdArgs a;
+  st = fill_args(p, w, tune, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx,
+                 nullptr, nullptr, workspace, &a);
+  if (st != SSD_OK) return st;
+  // the forward's stages 0-4: delta, running sums, CB, the entering states
+  st = launch_stages(p, a, SSD_STAGE_ALL & ~(uint32_t)SSD_STAGE_CHUNK_SCAN, tune, stream);
+  if (st != SSD_OK) return st;
+  char* base = static_cast<char*>(workspace);
+  BwdArgs b;
+  b.dy = dout; b.dfinal = dfinal; b.dx = dx; b.ddt = ddt; b.dA = dA; b.dB = dB; b.dC = dC;
+  b.dD = dD; b.ddt_bias = ddt_bias; b.dinit = dinit;
+  b.Q = reinterpret_cast<float*>(base + bl.Q);
+  b.dS = reinterpret_cast<float*>(base + bl.dS);
+  b.dcb = reinterpret_cast<float*>(base + bl.dcb);
+  b.dBh = reinterpret_cast<float*>(base + bl.dBh);
+  b.dCh = reinterpret_cast<float*>(base + bl.dCh);
+  b.dA_part = reinterpret_cast<float*>(base + bl.dA_part);
+  b.dD_part = reinterpret_cast<float*>(base + bl.dD_part);
+  b.dbias_part = reinterpret_cast<float*>(base + bl.dbias_part);
+  const Kernels* k = find_kernels(p->dtype, p->headdim, p->dstate, p->chunk_size);
+  if (k->backward(a, b, static_cast<hipStream_t>(stream)) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;
 }
 
@@ -260,6 +345,27 @@ ssd_status_t ssd_fwd_tuned(const ssd_problem_t* p, const void* x, const float* d
                            uint32_t stages, const ssd_tuning_t* tuning, void* stream) {
   return ssd::run(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, out,
                   final_states, workspace, workspace_bytes, stages, tuning, stream);
+}
+
+size_t ssd_bwd_workspace_size(const ssd_problem_t* p) {
+  if (ssd::check_problem(p) != SSD_OK) return 0;
+  ssd_workspace_layout_t w;
+  ssd::layout_of(p, &w);
+  ssd::BwdLayout b;
+  ssd::bwd_layout_of(p, w, &b);
+  return b.total;
+}
+
+ssd_status_t ssd_bwd(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias,
+                     const float* A, const void* B, const void* C, const float* D,
+                     const float* initial_states, const int32_t* cu_seqlens,
+                     const int32_t* seq_idx, const void* dout, const float* dfinal_states,
+                     void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
+                     float* ddt_bias, float* dinitial_states, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return ssd::run_bwd(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, dout,
+                      dfinal_states, dx, ddt, dA, dB, dC, dD, ddt_bias, dinitial_states,
+                      workspace, workspace_bytes, stream);
 }
 
 const char* ssd_status_string(ssd_status_t s) {

@@ -54,6 +54,28 @@ struct FwdArgs {
   }
 };
 
+// The backward's own buffers (gradients and its workspace regions).
+struct BwdArgs {
+  const void* dy;           // dtype of x, like the output
+  const float* dfinal;      // nullable
+  void* dx;                 // dtype of x
+  float* ddt;
+  float* dA;
+  void* dB;                 // dtype of x
+  void* dC;                 // dtype of x
+  float* dD;                // nullable
+  float* ddt_bias;          // nullable
+  float* dinit;             // nullable
+  float* Q;                 // [max_chunks][H][P*N]
+  float* dS;                // [max_chunks][H][P*N]
+  float* dcb;               // [max_chunks][H][L][L]
+  float* dBh;               // [max_chunks][H][L][N]
+  float* dCh;               // [max_chunks][H][L][N]
+  float* dA_part;           // [max_chunks][H]
+  float* dD_part;           // [max_chunks][H]
+  float* dbias_part;        // [max_chunks][H]
+};
+
 // Stage 0: logical chunk table of a packed batch.
 hipError_t launch_plan(const FwdArgs& a, hipStream_t s);
 // Stage 1: delta and its chunk-local cumulative sum times A.
@@ -74,6 +96,9 @@ hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s);
 // Stage 5: outputs.
 template <typename T, int P, int N, int L>
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s);
+// The backward, after stages 0-4 of the forward have filled `a`'s workspace.
+template <typename T, int P, int N, int L>
+hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s);
 
 }  // namespace ssd
 
