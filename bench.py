@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward (ssd_bwd) on the same workload")
+    ap.add_argument("--backward-reps", type=int, default=5)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, copy a buffer of MIB MiB three times (a plain copy "
                          "kernel of known size, for scaling HBM byte counters)")
@@ -299,6 +302,47 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # --- the backward on the same inputs: seeded output gradients, R calls
+    # between HIP events (the forward's stages 0-4 are recomputed inside)
+    backward = None
+    if not args.no_backward:
+        log("[bench] backward")
+        gb = torch.Generator().manual_seed(12345)
+        dy = torch.randn(inp["x"].shape, generator=gb).to(inp["x"].dtype).to(dev)
+        dfin = torch.randn((prob.nseq, prob.nheads, prob.headdim, prob.dstate), generator=gb).to(dev)
+
+        def bstep(wsb=None):
+            return binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, dy,
+                                   dfin, D=d["D"], dt_bias=d["dt_bias"], initial_states=d["init"],
+                                   cu_seqlens=d["cu_seqlens"], workspace=wsb)
+        wsb = bstep()["workspace"]
+        bstep(wsb)
+        torch.cuda.synchronize()
+        try:
+            torch.cuda._sleep(20_000_000)
+        except Exception:
+            pass
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(cur)
+        for _ in range(args.backward_reps):
+            bstep(wsb)
+        b1.record(cur)
+        torch.cuda.synchronize()
+        bus = b0.elapsed_time(b1) * 1e3 / args.backward_reps
+        e = 2 if prob.dtype == "bf16" else 4
+        H, P, N, G = prob.nheads, prob.headdim, prob.dstate, prob.ngroups
+        # the fused minimum: x, dy read and dx written; dt read and ddt
+        # written; B, C read and dB, dC written; init, dfinal read, dinit written
+        bbytes = (3 * e * tokens * H * P + 8 * tokens * H + 4 * e * tokens * G * N
+                  + 12 * prob.nseq * H * P * N)
+        backward = {"us": round(bus, 1), "tokens_per_s": round(tokens / (bus * 1e-6), 1),
+                    "alg_bytes_fused_minimum": int(bbytes),
+                    "hbm_frac_of_fused_minimum": round(bbytes / (bus * 1e-6) / 1e9 / HBM_PEAK_GBS, 5),
+                    "reps": args.backward_reps,
+                    "note": "ssd_bwd: gradients of every input; recomputes the forward's "
+                            "stages 0-4; per-kernel times in profiles/"}
+        del wsb
+
     # --- CPU baseline: the fp64 oracle on this host's cores, same workload
     cpu = None
     if not args.no_cpu_baseline:
@@ -333,6 +377,7 @@ def main():
                    "key": tuning.shape_key(cprob), "choice": tuned or {}},
         "stages": stages,
         "stages_unfused": singles,
+        "backward": backward,
         "step_alg_bytes": int(total_bytes),
         "step_alg_gbs": round(total_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "timing": "HIP-graph replays back to back (warm caches); per launch: "

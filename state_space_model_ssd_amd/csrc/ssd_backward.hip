@@ -43,24 +43,71 @@ constexpr int kBwdThreads = 256;
 template <typename T>
 __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
 
-// 1. Q_j[p,n]; grid (ceil(P*N / 256), H, chunk slots).
-template <typename T, int P, int N>
-__global__ __launch_bounds__(kBwdThreads) void bwd_q_kernel(ChunkMap cm, const T* __restrict__ dy,
-                                                           const T* __restrict__ C,
-                                                           const float* __restrict__ dAcs, int H,
-                                                           int G, int L, float* __restrict__ Q) {
-  const int o = blockIdx.x * kBwdThreads + threadIdx.x;
-  if (o >= P * N) return;
-  const int h = blockIdx.y, j = blockIdx.z, g = h / (H / G);
-  const int p = o / N, n = o - (o / N) * N;
-  const ChunkDesc d = cm.desc(j);
-  const float* a = dAcs + ((int64_t)j * H + h) * L;
-  float acc = 0.f;
-  for (int l = 0; l < d.len; ++l) {
-    const int64_t t = d.start + l;
-    acc += expf(a[l]) * ld(dy + (t * H + h) * P + p) * ld(C + (t * G + g) * N + n);
+// A 64 x 64 fp32 output tile of sum_k A(m, k) B(k, n) for k in [k0, k1),
+// accumulated into acc (4 x 4 per thread of 256).  Operand tiles of 32
+// k-values pass through LDS: As[k][m] and Bs[k][n] (row pitch 68 floats).
+// A_KFAST: A(m, k) is contiguous in k (else in m); B(k, n) is read with n
+// fastest.  The loaders return 0 outside the operands.
+constexpr int kGemmPitch = 68;
+
+template <bool A_KFAST, typename LA, typename LB>
+__device__ __forceinline__ void gemm_tile(int k0, int k1, LA loadA, LB loadB, float (&acc)[4][4],
+                                          float* As, float* Bs) {
+  const int tid = threadIdx.x;
+  const int tm = (tid >> 4) * 4, tn = (tid & 15) * 4;
+  for (int kb = k0; kb < k1; kb += 32) {
+    __syncthreads();                       // previous tile consumed
+    for (int i = tid; i < 64 * 32; i += kBwdThreads) {
+      int m, k;
+      if constexpr (A_KFAST) { m = i >> 5; k = i & 31; } else { k = i >> 6; m = i & 63; }
+      As[k * kGemmPitch + m] = kb + k < k1 ? loadA(m, kb + k) : 0.f;
+      const int kk = i >> 6, n = i & 63;
+      Bs[kk * kGemmPitch + n] = kb + kk < k1 ? loadB(kb + kk, n) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(&As[k * kGemmPitch + tm]);
+      const float4 b = *reinterpret_cast<const float4*>(&Bs[k * kGemmPitch + tn]);
+      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) acc[i][jn] += av[i] * bv[jn];
+    }
   }
-  Q[((int64_t)j * H + h) * P * N + o] = acc;
+}
+
+// 1. Q_j[p,n] = sum_l exp(a_l) dy[l,p] C[l,n] as 64 x 64 tiles;
+// grid (ceil(P/64) * ceil(N/64), H, chunk slots).
+template <typename T, int P, int N, int L>
+__global__ __launch_bounds__(kBwdThreads) void bwd_q_tiled_kernel(
+    ChunkMap cm, const T* __restrict__ dy, const T* __restrict__ C,
+    const float* __restrict__ dAcs, int H, int G, float* __restrict__ Q) {
+  __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
+  __shared__ float sc[L];
+  constexpr int NT = (N + 63) / 64;
+  const int m0 = (blockIdx.x / NT) * 64, n0 = (blockIdx.x % NT) * 64;
+  const int h = blockIdx.y, j = blockIdx.z, g = h / (H / G);
+  const ChunkDesc cd = cm.desc(j);
+  const int64_t jh = (int64_t)j * H + h;
+  for (int l = threadIdx.x; l < L; l += kBwdThreads) sc[l] = expf(dAcs[jh * L + l]);
+  __syncthreads();
+  float acc[4][4] = {};
+  gemm_tile<false>(0, max(cd.len, 0),
+      [&](int m, int l) { const int p = m0 + m;
+        return p < P ? sc[l] * ld(dy + ((int64_t)(cd.start + l) * H + h) * P + p) : 0.f; },
+      [&](int l, int n) { const int nn = n0 + n;
+        return nn < N ? ld(C + ((int64_t)(cd.start + l) * G + g) * N + nn) : 0.f; },
+      acc, As, Bs);
+  const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn) {
+      const int p = m0 + tm + i, n = n0 + tn + jn;
+      if (p < P && n < N) Q[(jh * P + p) * N + n] = acc[i][jn];
+    }
 }
 
 // 2. Reverse chain; grid (ceil(P*N / 256), H, nstates).
@@ -247,35 +294,72 @@ __global__ __launch_bounds__(L) void bwd_chunk_kernel(
   }
 }
 
-// 4. Per-head dB and dC rows; grid (ceil(L*N / 256), H, chunk slots).
+// 4. Per-head dC and dB rows as 64 x 64 tiles:
+//   dC_h = dCB B (s <= l) + diag(exp(a)) dy H,
+//   dB_h = dCB^T C (l >= s) + diag(delta exp(a_last - a)) x dS_j;
+// grid (L/64 * ceil(N/64), H, chunk slots), blockIdx.x even: dC, odd: dB
+// (the x index counts (row tile, column tile, which)).
 template <typename T, int P, int N, int L>
-__global__ __launch_bounds__(kBwdThreads) void bwd_bc_kernel(
+__global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
     ChunkMap cm, const T* __restrict__ x, const T* __restrict__ B, const T* __restrict__ C,
     const T* __restrict__ dy, const float* __restrict__ delta, const float* __restrict__ dAcs,
     const T* __restrict__ states_in, const float* __restrict__ dS, const float* __restrict__ dcb,
     int H, int G, float* __restrict__ dBh, float* __restrict__ dCh) {
-  const int o = blockIdx.x * kBwdThreads + threadIdx.x;
-  if (o >= L * N) return;
+  __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
+  __shared__ float sc[L];
+  constexpr int NT = (N + 63) / 64;
+  const int which = blockIdx.x & 1, t = blockIdx.x >> 1;
+  const int m0 = (t / NT) * 64, n0 = (t % NT) * 64;
   const int h = blockIdx.y, j = blockIdx.z, g = h / (H / G);
-  const int k = o / N, n = o - (o / N) * N;
   const ChunkDesc cd = cm.desc(j);
-  if (k >= cd.len) return;
+  const int len = max(cd.len, 0);
+  if (m0 >= len) return;                   // uniform: rows past the chunk
   const int64_t jh = (int64_t)j * H + h;
   const float* a = dAcs + jh * L;
+  const float alast = a[len - 1];
+  for (int l = threadIdx.x; l < L; l += kBwdThreads)
+    sc[l] = which == 0 ? expf(a[l]) : delta[jh * L + l] * expf(alast - a[l]);
   const float* dcbj = dcb + jh * L * L;
-  const int64_t tk = cd.start + k;
-  float sc = 0.f;                          // dC_h[k, n]
-  for (int s = 0; s <= k; ++s) sc += dcbj[(int64_t)k * L + s] * ld(B + ((cd.start + s) * G + g) * N + n);
-  float yh = 0.f;
-  for (int p = 0; p < P; ++p) yh += ld(dy + (tk * H + h) * P + p) * ld(states_in + (jh * P + p) * N + n);
-  sc += expf(a[k]) * yh;
-  float sb = 0.f;                          // dB_h[k, n]
-  for (int l = k; l < cd.len; ++l) sb += dcbj[(int64_t)l * L + k] * ld(C + ((cd.start + l) * G + g) * N + n);
-  float xg = 0.f;
-  for (int p = 0; p < P; ++p) xg += ld(x + (tk * H + h) * P + p) * dS[(jh * P + p) * N + n];
-  sb += delta[jh * L + k] * expf(a[cd.len - 1] - a[k]) * xg;
-  dBh[(jh * L + k) * N + n] = sb;
-  dCh[(jh * L + k) * N + n] = sc;
+  const int64_t t0 = cd.start;
+  float acc[4][4] = {};
+  auto ldB = [&](int s, int n) { const int nn = n0 + n;
+    return nn < N ? ld(B + ((t0 + s) * G + g) * N + nn) : 0.f; };
+  auto ldC = [&](int l, int n) { const int nn = n0 + n;
+    return nn < N ? ld(C + ((t0 + l) * G + g) * N + nn) : 0.f; };
+  if (which == 0) {
+    // dC rows m0..m0+63: s runs to the tile's last row
+    gemm_tile<true>(0, min(len, m0 + 64),
+        [&](int m, int s) { const int l = m0 + m;
+          return (l < len && s <= l) ? dcbj[(int64_t)l * L + s] : 0.f; },
+        ldB, acc, As, Bs);
+    gemm_tile<true>(0, P,
+        [&](int m, int p) { const int l = m0 + m;
+          return l < len ? sc[l] * ld(dy + ((t0 + l) * H + h) * P + p) : 0.f; },
+        [&](int p, int n) { const int nn = n0 + n;
+          return nn < N ? ld(states_in + (jh * P + p) * N + nn) : 0.f; },
+        acc, As, Bs);
+  } else {
+    // dB rows m0..m0+63: l runs from the tile's first row
+    gemm_tile<false>(m0, len,
+        [&](int m, int l) { const int s = m0 + m;
+          return (s < len && l >= s) ? dcbj[(int64_t)l * L + s] : 0.f; },
+        ldC, acc, As, Bs);
+    gemm_tile<true>(0, P,
+        [&](int m, int p) { const int s = m0 + m;
+          return s < len ? sc[s] * ld(x + ((t0 + s) * H + h) * P + p) : 0.f; },
+        [&](int p, int n) { const int nn = n0 + n;
+          return nn < N ? dS[(jh * P + p) * N + nn] : 0.f; },
+        acc, As, Bs);
+  }
+  float* out = which == 0 ? dCh : dBh;
+  const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn) {
+      const int r = m0 + tm + i, n = n0 + tn + jn;
+      if (r < len && n < N) out[(jh * L + r) * N + n] = acc[i][jn];
+    }
 }
 
 // 5a. dB, dC: sums over the heads of a group; grid (ceil(L*N / 256), G, chunk slots).
@@ -341,14 +425,15 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   const T* dy = (const T*)b.dy;
   const T* cb = (const T*)a.cb;
   const T* hin = (const T*)a.states_in;
-  hipLaunchKernelGGL((bwd_q_kernel<T, P, N>), dim3((PN + kBwdThreads - 1) / kBwdThreads, H, mc),
-                     dim3(kBwdThreads), 0, s, cm, dy, C, a.dAcs, H, G, L, b.Q);
+  constexpr int NT = (N + 63) / 64;
+  hipLaunchKernelGGL((bwd_q_tiled_kernel<T, P, N, L>), dim3(((P + 63) / 64) * NT, H, mc),
+                     dim3(kBwdThreads), 0, s, cm, dy, C, a.dAcs, H, G, b.Q);
   hipLaunchKernelGGL(bwd_chain_kernel, dim3((PN + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
                      dim3(kBwdThreads), 0, s, cm, b.Q, a.dAcs, b.dfinal, H, PN, L, b.dS, b.dinit);
   hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N, L>), dim3(H, mc), dim3(L), 0, s, cm, x, a.dt,
                      a.dt_bias, a.A, B, C, a.D, dy, a.delta, a.dAcs, cb, hin, b.dS, H, G, a.dt_min,
                      a.dt_max, (T*)b.dx, b.ddt, b.dcb, b.dA_part, b.dD_part, b.dbias_part);
-  hipLaunchKernelGGL((bwd_bc_kernel<T, P, N, L>), dim3((L * N + kBwdThreads - 1) / kBwdThreads, H, mc),
+  hipLaunchKernelGGL((bwd_bc_tiled_kernel<T, P, N, L>), dim3((L / 64) * NT * 2, H, mc),
                      dim3(kBwdThreads), 0, s, cm, x, B, C, dy, a.delta, a.dAcs, hin, b.dS, b.dcb, H,
                      G, b.dBh, b.dCh);
   hipLaunchKernelGGL((bwd_bc_reduce_kernel<T, N, L>), dim3((L * N + kBwdThreads - 1) / kBwdThreads, G, mc),
