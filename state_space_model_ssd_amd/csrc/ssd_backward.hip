@@ -50,7 +50,7 @@ __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
 // fastest.  The loaders return 0 outside the operands.
 constexpr int kGemmPitch = 68;
 
-template <bool A_KFAST, typename LA, typename LB>
+template <bool A_KFAST, bool B_KFAST = false, typename LA, typename LB>
 __device__ __forceinline__ void gemm_tile(int k0, int k1, LA loadA, LB loadB, float (&acc)[4][4],
                                           float* As, float* Bs) {
   const int tid = threadIdx.x;
@@ -61,7 +61,8 @@ __device__ __forceinline__ void gemm_tile(int k0, int k1, LA loadA, LB loadB, fl
       int m, k;
       if constexpr (A_KFAST) { m = i >> 5; k = i & 31; } else { k = i >> 6; m = i & 63; }
       As[k * kGemmPitch + m] = kb + k < k1 ? loadA(m, kb + k) : 0.f;
-      const int kk = i >> 6, n = i & 63;
+      int kk, n;
+      if constexpr (B_KFAST) { n = i >> 5; kk = i & 31; } else { kk = i >> 6; n = i & 63; }
       Bs[kk * kGemmPitch + n] = kb + kk < k1 ? loadB(kb + kk, n) : 0.f;
     }
     __syncthreads();
@@ -76,6 +77,14 @@ __device__ __forceinline__ void gemm_tile(int k0, int k1, LA loadA, LB loadB, fl
         for (int jn = 0; jn < 4; ++jn) acc[i][jn] += av[i] * bv[jn];
     }
   }
+}
+
+// Sum of v over the 16 threads that share a row of the 4 x 4 blocks (lanes
+// differing in their low 4 bits); every one of them gets it.
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+  return v;
 }
 
 // 1. Q_j[p,n] = sum_l exp(a_l) dy[l,p] C[l,n] as 64 x 64 tiles;
@@ -151,22 +160,238 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
-// 3. Per (chunk, head), one thread per token: dx, ddt, the dCB rows, and the
-// chunk's parts of dA, dD and dt_bias.  grid (H, chunk slots), L threads.
+// 3a. V[l,s] = exp(a_l - a_s) (dy_l . x_s) for s <= l (so dCB = delta_s V),
+// as 64 x 64 tiles on or below the diagonal, with each tile's partial sums
+//   rowpart[st][l] = sum_s CB[l,s] delta_s V[l,s]   (s in column tile st)
+//   colpart[lt][s] = sum_l CB[l,s] V[l,s]           (l in row tile lt);
+// grid ((L/64)^2, H, chunk slots).
 template <typename T, int P, int N, int L>
-__global__ __launch_bounds__(L) void bwd_chunk_kernel(
+__global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
+    ChunkMap cm, const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ cb,
+    const float* __restrict__ delta, const float* __restrict__ dAcs, int H, int G,
+    float* __restrict__ V, float* __restrict__ rowpart, float* __restrict__ colpart) {
+  __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
+  __shared__ float cpart[16][64];
+  constexpr int LT = L / 64;
+  const int lt = blockIdx.x / LT, st = blockIdx.x % LT;
+  if (st > lt) return;                     // above the diagonal: nothing
+  const int h = blockIdx.y, j = blockIdx.z, g = h / (H / G);
+  const ChunkDesc cd = cm.desc(j);
+  const int len = max(cd.len, 0);
+  const int l0 = lt * 64, s0 = st * 64;
+  if (l0 >= len) return;
+  const int64_t jh = (int64_t)j * H + h, t0 = cd.start;
+  const float* a = dAcs + jh * L;
+  float acc[4][4] = {};
+  gemm_tile<true, true>(0, P,
+      [&](int m, int p) { const int l = l0 + m;
+        return l < len ? ld(dy + ((t0 + l) * H + h) * P + p) : 0.f; },
+      [&](int p, int n) { const int sx = s0 + n;
+        return sx < len ? ld(x + ((t0 + sx) * H + h) * P + p) : 0.f; },
+      acc, As, Bs);
+  const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+  const T* cbj = cb + ((int64_t)j * G + g) * L * L;
+  float* Vj = V + jh * L * L;
+  float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn) {
+      const int l = l0 + tm + i, sx = s0 + tn + jn;
+      if (l < len && sx <= l) {
+        const float v = expf(a[l] - a[sx]) * acc[i][jn];
+        Vj[(int64_t)l * L + sx] = v;
+        const float m = ld(cbj + (int64_t)l * L + sx) * v;
+        rsum[i] += delta[jh * L + sx] * m;
+        csum[jn] += m;
+      }
+    }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float r = row16_sum(rsum[i]);
+    if ((threadIdx.x & 15) == 0) rowpart[(jh * LT + st) * L + l0 + tm + i] = r;
+  }
+#pragma unroll
+  for (int jn = 0; jn < 4; ++jn) cpart[threadIdx.x >> 4][tn + jn] = csum[jn];
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    float c = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c += cpart[r][threadIdx.x];
+    colpart[(jh * LT + lt) * L + s0 + threadIdx.x] = c;
+  }
+}
+
+// 3b. dx as 64 x 64 tiles of (token s, p):
+//   dx_s = delta_s [ sum_{l>=s} CB[l,s] exp(a_l - a_s) dy_l + exp(a_last - a_s) dS_j B_s ]
+//          + D dy_s;
+// grid (L/64 * ceil(P/64), H, chunk slots).
+template <typename T, int P, int N, int L>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
+    ChunkMap cm, const T* __restrict__ B, const T* __restrict__ dy, const T* __restrict__ cb,
+    const float* __restrict__ delta, const float* __restrict__ dAcs, const float* __restrict__ dS,
+    const float* __restrict__ D, int H, int G, T* __restrict__ dx) {
+  __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
+  __shared__ float es[L];
+  constexpr int PT = (P + 63) / 64;
+  const int s0 = (blockIdx.x / PT) * 64, p0 = (blockIdx.x % PT) * 64;
+  const int h = blockIdx.y, j = blockIdx.z, g = h / (H / G);
+  const ChunkDesc cd = cm.desc(j);
+  const int len = max(cd.len, 0);
+  if (s0 >= len) return;
+  const int64_t jh = (int64_t)j * H + h, t0 = cd.start;
+  const float* a = dAcs + jh * L;
+  const float alast = a[len - 1];
+  for (int l = threadIdx.x; l < L; l += kBwdThreads) es[l] = expf(alast - a[l]);
+  const T* cbj = cb + ((int64_t)j * G + g) * L * L;
+  float acc[4][4] = {};
+  gemm_tile<false>(s0, len,
+      [&](int m, int l) { const int sx = s0 + m;
+        return (sx < len && l >= sx) ? ld(cbj + (int64_t)l * L + sx) * expf(a[l] - a[sx]) : 0.f; },
+      [&](int l, int n) { const int pp = p0 + n;
+        return pp < P ? ld(dy + ((t0 + l) * H + h) * P + pp) : 0.f; },
+      acc, As, Bs);
+  gemm_tile<true, true>(0, N,
+      [&](int m, int n) { const int sx = s0 + m;
+        return sx < len ? es[sx] * ld(B + ((t0 + sx) * G + g) * N + n) : 0.f; },
+      [&](int n, int c) { const int pp = p0 + c;
+        return pp < P ? dS[(jh * P + pp) * N + n] : 0.f; },
+      acc, As, Bs);
+  const float Dh = D ? D[h] : 0.f;
+  const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sx = s0 + tm + i;
+    if (sx >= len) continue;
+    const float dsx = delta[jh * L + sx];
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn) {
+      const int pp = p0 + tn + jn;
+      if (pp < P) {
+        const int64_t o = ((t0 + sx) * H + h) * P + pp;
+        dx[o] = from_f32<T>(dsx * acc[i][jn] + Dh * ld(dy + o));
+      }
+    }
+  }
+}
+
+// 4. Per-head dC and dB rows as 64 x 64 tiles:
+//   dC_h = diag(exp(a)) dy H + dCB B (s <= l),
+//   dB_h = diag(delta exp(a_last - a)) x dS_j + dCB^T C (l >= s),
+// with dCB[l,s] = delta_s V[l,s].  Between its two products each tile takes
+// a partial row dot product for the per-token pass:
+//   interpart[nt][l] = sum_n C[l,n] exp(a_l) (dy_l H)[n],
+//   vxpart[nt][s]    = sum_n B[s,n] exp(a_last - a_s) (x_s dS_j)[n]
+// over its 64 columns n.  grid (L/64 * ceil(N/64) * 2, H, chunk slots);
+// even x: dC, odd: dB.
+template <typename T, int P, int N, int L>
+__global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
+    ChunkMap cm, const T* __restrict__ x, const T* __restrict__ B, const T* __restrict__ C,
+    const T* __restrict__ dy, const float* __restrict__ delta, const float* __restrict__ dAcs,
+    const T* __restrict__ states_in, const float* __restrict__ dS, const float* __restrict__ V,
+    int H, int G, float* __restrict__ dBh, float* __restrict__ dCh, float* __restrict__ interpart,
+    float* __restrict__ vxpart) {
+  __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
+  __shared__ float sc[L], ds[L];
+  constexpr int NT = (N + 63) / 64;
+  const int which = blockIdx.x & 1, t = blockIdx.x >> 1;
+  const int m0 = (t / NT) * 64, nt = t % NT, n0 = nt * 64;
+  const int h = blockIdx.y, j = blockIdx.z, g = h / (H / G);
+  const ChunkDesc cd = cm.desc(j);
+  const int len = max(cd.len, 0);
+  if (m0 >= len) return;                   // uniform: rows past the chunk
+  const int64_t jh = (int64_t)j * H + h;
+  const float* a = dAcs + jh * L;
+  const float alast = a[len - 1];
+  for (int l = threadIdx.x; l < L; l += kBwdThreads) {
+    sc[l] = which == 0 ? expf(a[l]) : expf(alast - a[l]);
+    ds[l] = delta[jh * L + l];
+  }
+  const float* Vj = V + jh * L * L;
+  const int64_t t0 = cd.start;
+  const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+  float acc[4][4] = {};
+  auto row_dot = [&](const T* M, float* part) {   // sum_n M[row, n] acc[row, n] over the tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = m0 + tm + i;
+      float v = 0.f;
+      if (r < len) {
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) {
+          const int nn = n0 + tn + jn;
+          if (nn < N) v += ld(M + ((t0 + r) * G + g) * N + nn) * acc[i][jn];
+        }
+      }
+      v = row16_sum(v);
+      if ((threadIdx.x & 15) == 0 && r < L) part[(jh * NT + nt) * L + r] = v;
+    }
+  };
+  if (which == 0) {
+    gemm_tile<true>(0, P,
+        [&](int m, int p) { const int l = m0 + m;
+          return l < len ? sc[l] * ld(dy + ((t0 + l) * H + h) * P + p) : 0.f; },
+        [&](int p, int n) { const int nn = n0 + n;
+          return nn < N ? ld(states_in + (jh * P + p) * N + nn) : 0.f; },
+        acc, As, Bs);
+    row_dot(C, interpart);
+    // dC rows m0..m0+63: s runs to the tile's last row
+    gemm_tile<true>(0, min(len, m0 + 64),
+        [&](int m, int sx) { const int l = m0 + m;
+          return (l < len && sx <= l) ? ds[sx] * Vj[(int64_t)l * L + sx] : 0.f; },
+        [&](int sx, int n) { const int nn = n0 + n;
+          return nn < N ? ld(B + ((t0 + sx) * G + g) * N + nn) : 0.f; },
+        acc, As, Bs);
+  } else {
+    gemm_tile<true>(0, P,
+        [&](int m, int p) { const int sx = m0 + m;
+          return sx < len ? sc[sx] * ld(x + ((t0 + sx) * H + h) * P + p) : 0.f; },
+        [&](int p, int n) { const int nn = n0 + n;
+          return nn < N ? dS[(jh * P + p) * N + nn] : 0.f; },
+        acc, As, Bs);
+    row_dot(B, vxpart);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sx = m0 + tm + i;
+      const float f = sx < L ? ds[sx] : 0.f;
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) acc[i][jn] *= f;
+    }
+    // dB rows m0..m0+63: l runs from the tile's first row
+    gemm_tile<false>(m0, len,
+        [&](int m, int l) { const int sx = m0 + m;
+          return (sx < len && l >= sx) ? ds[sx] * Vj[(int64_t)l * L + sx] : 0.f; },
+        [&](int l, int n) { const int nn = n0 + n;
+          return nn < N ? ld(C + ((t0 + l) * G + g) * N + nn) : 0.f; },
+        acc, As, Bs);
+  }
+  float* out = which == 0 ? dCh : dBh;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn) {
+      const int r = m0 + tm + i, n = n0 + tn + jn;
+      if (r < len && n < N) out[(jh * L + r) * N + n] = acc[i][jn];
+    }
+}
+
+// 3c. Per (chunk, head), one thread per token: da from the partial sums,
+// its suffix sums, ddelta and ddt, and the chunk's parts of dA, dD and
+// dt_bias.  grid (H, chunk slots), L threads.
+template <typename T, int P, int N, int L>
+__global__ __launch_bounds__(L) void bwd_token_kernel(
     ChunkMap cm, const T* __restrict__ x, const float* __restrict__ dt,
-    const float* __restrict__ dt_bias, const float* __restrict__ A, const T* __restrict__ B,
-    const T* __restrict__ C, const float* __restrict__ D, const T* __restrict__ dy,
-    const float* __restrict__ delta, const float* __restrict__ dAcs, const T* __restrict__ cb,
-    const T* __restrict__ states_in, const float* __restrict__ dS, int H, int G, float dt_min,
-    float dt_max, T* __restrict__ dx, float* __restrict__ ddt, float* __restrict__ dcb,
-    float* __restrict__ dA_part, float* __restrict__ dD_part, float* __restrict__ dbias_part) {
-  __shared__ float Gs[P * N];     // dS_j
-  __shared__ float Hs[P * N];     // H entering chunk j
-  __shared__ float as[L], ds[L], das[L];
+    const float* __restrict__ dt_bias, const float* __restrict__ A, const T* __restrict__ dy,
+    const float* __restrict__ delta, const float* __restrict__ dAcs,
+    const T* __restrict__ states_in, const float* __restrict__ dS,
+    const float* __restrict__ rowpart, const float* __restrict__ colpart,
+    const float* __restrict__ interpart, const float* __restrict__ vxpart, int H, float dt_min,
+    float dt_max, float* __restrict__ ddt, float* __restrict__ dA_part,
+    float* __restrict__ dD_part, float* __restrict__ dbias_part) {
+  __shared__ float das[L];
   __shared__ float red[L / kWave];
-  const int h = blockIdx.x, j = blockIdx.y, g = h / (H / G), k = threadIdx.x;
+  constexpr int LT = L / 64, NT = (N + 63) / 64;
+  const int h = blockIdx.x, j = blockIdx.y, k = threadIdx.x;
   const ChunkDesc cd = cm.desc(j);
   const int64_t jh = (int64_t)j * H + h;
   if (cd.len <= 0) {                       // uniform over the workgroup
@@ -178,103 +403,33 @@ __global__ __launch_bounds__(L) void bwd_chunk_kernel(
     return;
   }
   const int len = cd.len;
-  for (int i = k; i < P * N; i += L) {
-    Gs[i] = dS[jh * P * N + i];
-    Hs[i] = ld(states_in + jh * P * N + i);
-  }
-  as[k] = dAcs[jh * L + k];
-  ds[k] = delta[jh * L + k];
-  __syncthreads();
   const bool valid = k < len;
-  const float ak = as[k], dk = ds[k], alast = as[len - 1];
-  const T* cbj = cb + ((int64_t)j * G + g) * L * L;
+  const float* a = dAcs + jh * L;
+  const float alast = a[len - 1];
+  const float dk = delta[jh * L + k];
   const int64_t tk = cd.start + k;
-  const float Dh = D ? D[h] : 0.f;
-
-  float ddir = 0.f, colsum = 0.f, vs = 0.f, dd = 0.f, rowsum = 0.f, inter = 0.f;
+  float rowsum = 0.f, sdir = 0.f, inter = 0.f, vxe = 0.f, dd = 0.f;
   if (valid) {
-    // ---- with x_k held: dx_k, the column sums, the state term
-    float xk[P], acc[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      xk[p] = ld(x + (tk * H + h) * P + p);
-      acc[p] = 0.f;
+    for (int st = 0; st <= k / 64; ++st) rowsum += rowpart[(jh * LT + st) * L + k];
+    for (int lt = k / 64; lt < LT && lt * 64 < len; ++lt) sdir += colpart[(jh * LT + lt) * L + k];
+    for (int nt = 0; nt < NT; ++nt) {
+      inter += interpart[(jh * NT + nt) * L + k];
+      vxe += vxpart[(jh * NT + nt) * L + k];
     }
-    float sdir = 0.f;
-    for (int l = k; l < len; ++l) {
-      const float c = ld(cbj + (int64_t)l * L + k) * expf(as[l] - ak);
-      const T* dyl = dy + ((cd.start + l) * H + h) * P;
-      float u = 0.f;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const float v = ld(dyl + p);
-        u += v * xk[p];
-        acc[p] += c * v;
-      }
-      sdir += c * u;
-    }
-#pragma unroll
-    for (int p = 0; p < P; ++p) acc[p] *= dk;
-    const float fs = dk * expf(alast - ak);
-    float vx = 0.f;
-    for (int n = 0; n < N; ++n) {
-      const float b = ld(B + (tk * G + g) * N + n);
-      const float fb = fs * b;
-      float xg = 0.f;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const float gv = Gs[p * N + n];
-        xg += xk[p] * gv;
-        acc[p] += fb * gv;
-      }
-      vx += b * xg;
-    }
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const float dyk = ld(dy + (tk * H + h) * P + p);
-      dd += dyk * xk[p];
-      dx[(tk * H + h) * P + p] = from_f32<T>(acc[p] + Dh * dyk);
-    }
-    ddir = sdir + expf(alast - ak) * vx;
-    colsum = dk * sdir;
-    vs = fs * vx;
-
-    // ---- with dy_k held: the row sums (and the dCB row), the inter term
-    float yk[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) yk[p] = ld(dy + (tk * H + h) * P + p);
-    float* dcbk = dcb + (jh * L + k) * L;
-    for (int s = 0; s <= k; ++s) {
-      const T* xs = x + ((cd.start + s) * H + h) * P;
-      float u = 0.f;
-#pragma unroll
-      for (int p = 0; p < P; ++p) u += yk[p] * ld(xs + p);
-      const float w = expf(ak - as[s]) * ds[s] * u;
-      dcbk[s] = w;
-      rowsum += ld(cbj + (int64_t)k * L + s) * w;
-    }
-    float it = 0.f;
-    for (int n = 0; n < N; ++n) {
-      float yh = 0.f;
-#pragma unroll
-      for (int p = 0; p < P; ++p) yh += yk[p] * Hs[p * N + n];
-      it += ld(C + (tk * G + g) * N + n) * yh;
-    }
-    inter = expf(ak) * it;
+    for (int p = 0; p < P; ++p) dd += ld(dy + (tk * H + h) * P + p) * ld(x + (tk * H + h) * P + p);
   }
-
-  // ---- da, its suffix sums, and the parts reduced over the chunk
+  const float vs = dk * vxe;
   float gh = 0.f;
-  for (int i = k; i < P * N; i += L) gh += Gs[i] * Hs[i];
+  for (int i = k; i < P * N; i += L) gh += dS[jh * P * N + i] * ld(states_in + jh * P * N + i);
   gh = block_sum<L>(gh, red);
   const float t1 = block_sum<L>(valid ? vs : 0.f, red);
-  float da = valid ? rowsum - colsum + inter - vs : 0.f;
+  float da = valid ? rowsum - dk * sdir + inter - vs : 0.f;
   if (k == len - 1) da += t1 + expf(alast) * gh;
   das[k] = da;
   __syncthreads();
   float rc = 0.f;
   for (int l = L - 1; l >= k; --l) rc += das[l];
-  const float ddelta = ddir + A[h] * rc;
+  const float ddelta = sdir + vxe + A[h] * rc;
   float dbias = 0.f;
   if (valid) {
     const float u = dt[tk * H + h] + (dt_bias ? dt_bias[h] : 0.f);
@@ -292,74 +447,6 @@ __global__ __launch_bounds__(L) void bwd_chunk_kernel(
     dD_part[jh] = dd_sum;
     dbias_part[jh] = db_sum;
   }
-}
-
-// 4. Per-head dC and dB rows as 64 x 64 tiles:
-//   dC_h = dCB B (s <= l) + diag(exp(a)) dy H,
-//   dB_h = dCB^T C (l >= s) + diag(delta exp(a_last - a)) x dS_j;
-// grid (L/64 * ceil(N/64), H, chunk slots), blockIdx.x even: dC, odd: dB
-// (the x index counts (row tile, column tile, which)).
-template <typename T, int P, int N, int L>
-__global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
-    ChunkMap cm, const T* __restrict__ x, const T* __restrict__ B, const T* __restrict__ C,
-    const T* __restrict__ dy, const float* __restrict__ delta, const float* __restrict__ dAcs,
-    const T* __restrict__ states_in, const float* __restrict__ dS, const float* __restrict__ dcb,
-    int H, int G, float* __restrict__ dBh, float* __restrict__ dCh) {
-  __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
-  __shared__ float sc[L];
-  constexpr int NT = (N + 63) / 64;
-  const int which = blockIdx.x & 1, t = blockIdx.x >> 1;
-  const int m0 = (t / NT) * 64, n0 = (t % NT) * 64;
-  const int h = blockIdx.y, j = blockIdx.z, g = h / (H / G);
-  const ChunkDesc cd = cm.desc(j);
-  const int len = max(cd.len, 0);
-  if (m0 >= len) return;                   // uniform: rows past the chunk
-  const int64_t jh = (int64_t)j * H + h;
-  const float* a = dAcs + jh * L;
-  const float alast = a[len - 1];
-  for (int l = threadIdx.x; l < L; l += kBwdThreads)
-    sc[l] = which == 0 ? expf(a[l]) : delta[jh * L + l] * expf(alast - a[l]);
-  const float* dcbj = dcb + jh * L * L;
-  const int64_t t0 = cd.start;
-  float acc[4][4] = {};
-  auto ldB = [&](int s, int n) { const int nn = n0 + n;
-    return nn < N ? ld(B + ((t0 + s) * G + g) * N + nn) : 0.f; };
-  auto ldC = [&](int l, int n) { const int nn = n0 + n;
-    return nn < N ? ld(C + ((t0 + l) * G + g) * N + nn) : 0.f; };
-  if (which == 0) {
-    // dC rows m0..m0+63: s runs to the tile's last row
-    gemm_tile<true>(0, min(len, m0 + 64),
-        [&](int m, int s) { const int l = m0 + m;
-          return (l < len && s <= l) ? dcbj[(int64_t)l * L + s] : 0.f; },
-        ldB, acc, As, Bs);
-    gemm_tile<true>(0, P,
-        [&](int m, int p) { const int l = m0 + m;
-          return l < len ? sc[l] * ld(dy + ((t0 + l) * H + h) * P + p) : 0.f; },
-        [&](int p, int n) { const int nn = n0 + n;
-          return nn < N ? ld(states_in + (jh * P + p) * N + nn) : 0.f; },
-        acc, As, Bs);
-  } else {
-    // dB rows m0..m0+63: l runs from the tile's first row
-    gemm_tile<false>(m0, len,
-        [&](int m, int l) { const int s = m0 + m;
-          return (s < len && l >= s) ? dcbj[(int64_t)l * L + s] : 0.f; },
-        ldC, acc, As, Bs);
-    gemm_tile<true>(0, P,
-        [&](int m, int p) { const int s = m0 + m;
-          return s < len ? sc[s] * ld(x + ((t0 + s) * H + h) * P + p) : 0.f; },
-        [&](int p, int n) { const int nn = n0 + n;
-          return nn < N ? dS[(jh * P + p) * N + nn] : 0.f; },
-        acc, As, Bs);
-  }
-  float* out = which == 0 ? dCh : dBh;
-  const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
-      const int r = m0 + tm + i, n = n0 + tn + jn;
-      if (r < len && n < N) out[(jh * L + r) * N + n] = acc[i][jn];
-    }
 }
 
 // 5a. dB, dC: sums over the heads of a group; grid (ceil(L*N / 256), G, chunk slots).
@@ -430,12 +517,19 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
                      dim3(kBwdThreads), 0, s, cm, dy, C, a.dAcs, H, G, b.Q);
   hipLaunchKernelGGL(bwd_chain_kernel, dim3((PN + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
                      dim3(kBwdThreads), 0, s, cm, b.Q, a.dAcs, b.dfinal, H, PN, L, b.dS, b.dinit);
-  hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N, L>), dim3(H, mc), dim3(L), 0, s, cm, x, a.dt,
-                     a.dt_bias, a.A, B, C, a.D, dy, a.delta, a.dAcs, cb, hin, b.dS, H, G, a.dt_min,
-                     a.dt_max, (T*)b.dx, b.ddt, b.dcb, b.dA_part, b.dD_part, b.dbias_part);
-  hipLaunchKernelGGL((bwd_bc_tiled_kernel<T, P, N, L>), dim3((L / 64) * NT * 2, H, mc),
+  constexpr int LT = L / 64;
+  hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(LT * LT, H, mc), dim3(kBwdThreads), 0, s,
+                     cm, x, dy, cb, a.delta, a.dAcs, H, G, b.dcb, b.rowpart, b.colpart);
+  hipLaunchKernelGGL((bwd_bc_tiled_kernel<T, P, N, L>), dim3(LT * NT * 2, H, mc),
                      dim3(kBwdThreads), 0, s, cm, x, B, C, dy, a.delta, a.dAcs, hin, b.dS, b.dcb, H,
-                     G, b.dBh, b.dCh);
+                     G, b.dBh, b.dCh, b.interpart, b.vxpart);
+  hipLaunchKernelGGL((bwd_dx_tiled_kernel<T, P, N, L>), dim3(LT * ((P + 63) / 64), H, mc),
+                     dim3(kBwdThreads), 0, s, cm, B, dy, cb, a.delta, a.dAcs, b.dS, a.D, H, G,
+                     (T*)b.dx);
+  hipLaunchKernelGGL((bwd_token_kernel<T, P, N, L>), dim3(H, mc), dim3(L), 0, s, cm, x, a.dt,
+                     a.dt_bias, a.A, dy, a.delta, a.dAcs, hin, b.dS, b.rowpart, b.colpart,
+                     b.interpart, b.vxpart, H, a.dt_min, a.dt_max, b.ddt, b.dA_part, b.dD_part,
+                     b.dbias_part);
   hipLaunchKernelGGL((bwd_bc_reduce_kernel<T, N, L>), dim3((L * N + kBwdThreads - 1) / kBwdThreads, G, mc),
                      dim3(kBwdThreads), 0, s, cm, b.dBh, b.dCh, H, G, (T*)b.dB, (T*)b.dC);
   hipLaunchKernelGGL(bwd_head_reduce_kernel, dim3((H + kBwdThreads - 1) / kBwdThreads), dim3(kBwdThreads),

@@ -68,7 +68,11 @@ struct BwdArgs {
   float* dinit;             // nullable
   float* Q;                 // [max_chunks][H][P*N]
   float* dS;                // [max_chunks][H][P*N]
-  float* dcb;               // [max_chunks][H][L][L]
+  float* dcb;               // [max_chunks][H][L][L]: exp(a_l - a_s) dy_l . x_s, s <= l
+  float* rowpart;           // [max_chunks][H][L/64][L]
+  float* colpart;           // [max_chunks][H][L/64][L]
+  float* interpart;         // [max_chunks][H][ceil(N/64)][L]
+  float* vxpart;            // [max_chunks][H][ceil(N/64)][L]
   float* dBh;               // [max_chunks][H][L][N]
   float* dCh;               // [max_chunks][H][L][N]
   float* dA_part;           // [max_chunks][H]
