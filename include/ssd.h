@@ -190,8 +190,11 @@ ssd_status_t ssd_fwd_stages(const ssd_problem_t* p,
  * they move rounding only where noted.
  *   scan_kernel  chunk_scan for bf16: 1 = one workgroup per (chunk, head)
  *                tile (its rescaled path rounds differently from the
- *                masked one), 2 = the persistent walk over tiles.  Must be 0
- *                for fp32.
+ *                masked one), 2 = the persistent walk over tiles, 3 = one
+ *                workgroup of four waves per tile (bitwise the same results
+ *                as 1; with 256-token chunks each wave owns four 16-row
+ *                groups instead of two, so three workgroups fit on a CU).
+ *                Must be 0 for fp32.
  *   sp_vec       consecutive state elements per state_passing thread: 1, 2
  *                or 4 (identical results).
  *   front        bf16 stages 1-3: 1 = one fused launch, 2 = one launch per

@@ -125,7 +125,7 @@ ssd_status_t check_tuning(const ssd_problem_t* p, const ssd_tuning_t& t, int64_t
       t.sp_blocks != 8 && t.sp_blocks != 16)
     return SSD_ERR_INVALID_ARG;
   if (t.sp_blocks > ws_blocks) return SSD_ERR_INVALID_ARG;
-  if (t.scan_kernel < 0 || t.scan_kernel > 2 || (!bf16 && t.scan_kernel != 0)) return SSD_ERR_INVALID_ARG;
+  if (t.scan_kernel < 0 || t.scan_kernel > 3 || (!bf16 && t.scan_kernel != 0)) return SSD_ERR_INVALID_ARG;
   if (t.sp_vec != 0 && t.sp_vec != 1 && t.sp_vec != 2 && t.sp_vec != 4) return SSD_ERR_INVALID_ARG;
   if (t.front < 0 || t.front > 2 || (!bf16 && t.front != 0)) return SSD_ERR_INVALID_ARG;
   return SSD_OK;

@@ -22,9 +22,11 @@
 //  - the inter-chunk term is the entering state times the C rows on MFMA,
 //    scaled by exp(a_l) per token;
 //  - all global traffic goes through buffer resources bounded by the tile.
-// Two kernels; the launcher picks by tiles per resident workgroup (or as a
-// caller pins it):
-//  - one workgroup of 8 waves per (chunk, head) tile.  Each tile takes the
+// Two kernels, the first in two sizes; the launcher picks by tiles per
+// resident workgroup (or as a caller pins it):
+//  - one workgroup per (chunk, head) tile, of 8 waves (two 16-row groups per
+//    wave; 4 waves for chunks of 128 tokens or fewer) or of 4 waves (four
+//    row groups per wave, three workgroups per CU).  Each tile takes the
 //    rescaled path when its whole decay is within 2^64 (x staged as
 //    x delta 2^(-a), CB rows used as loaded, one row factor 2^(a_l) at the
 //    end), else the masked path; the two are compiled as separate bodies;
@@ -664,12 +666,15 @@ __device__ __forceinline__ void scan_tile_inter(f32x4 (&acc)[RGW][P / 16],
 }
 
 template <int L> constexpr int kTileWaves = (L / 16) / 2 < 4 ? 4 : (L / 16) / 2;
+// Waves per SIMD the tile kernel is compiled for: two workgroups per CU with
+// 8-wave tiles; three with 4-wave tiles of four row groups per wave.
+template <int L, int NW> constexpr int kTileWavesPerEU = (L / 16) / NW == 4 ? 3 : 4;
 
 // One tile of the bf16 chunk_scan.  FAST: the chunk's whole decay is within
 // 2^kScanFastMaxLog2, and the rescaled path runs; otherwise the masked one.
 // The two paths share their loads and the inter-chunk term but are compiled
 // as separate bodies, so that neither carries the other's registers.
-template <int P, int N, int L, bool FAST>
+template <int P, int N, int L, int NW, bool FAST>
 __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __restrict__ x,
                                                const bf16* __restrict__ C, const bf16* __restrict__ cb,
                                                const float* __restrict__ delta,
@@ -678,12 +683,11 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
                                                const float* __restrict__ D, int H, int G, bf16* __restrict__ out,
                                                bf16* xs, bf16* hsm, float* dal2, float* dls, float* cfs) {
   using M = Mfma<bf16>;
-  constexpr int NW = kTileWaves<L>;
   constexpr int NT = 64 * NW;            // threads
   constexpr int HP = N + 8;              // state tile pitch: conflict-free 16-byte row reads
   constexpr int RG = L / 16;             // 16-row groups of the chunk
-  constexpr int RGW = RG / NW;           // row groups per wave: 1 or 2
-  static_assert(RGW * NW == RG && (RGW == 1 || RGW == 2), "row-group split");
+  constexpr int RGW = RG / NW;           // row groups per wave: 1, 2 or 4
+  static_assert(RGW * NW == RG && (RGW == 1 || RGW == 2 || RGW == 4), "row-group split");
   constexpr int PT = P / 16;
   constexpr int NK = N / 32;             // k-steps of the inter-chunk term
   constexpr int NQ = RG / 2;             // most intra-chunk k-steps of one row group
@@ -699,10 +703,16 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
   const bool has_d = D != nullptr;
   const float Dh = has_d ? D[h] : 0.f;
   // Row groups of this wave; with two per wave they pair from both ends of
-  // the chunk, so every wave carries the same causal work.
+  // the chunk, with four from both ends of each half, so every wave carries
+  // the same causal work (the last one listed reaches furthest).
   int mg[RGW];
   mg[0] = w;
   if constexpr (RGW == 2) mg[1] = RG - 1 - w;
+  if constexpr (RGW == 4) {
+    mg[1] = 2 * NW - 1 - w;
+    mg[2] = 2 * NW + w;
+    mg[3] = RG - 1 - w;
+  }
   int lrow[RGW], nq[RGW];
 #pragma unroll
   for (int i = 0; i < RGW; ++i) {
@@ -726,9 +736,13 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
   const float dA_t = buf_load4(buf_rsrc(dAcs + jhl * L, L * 4), tid * 4);
   const float dl_t = buf_load4(buf_rsrc(delta + jhl * L, L * 4), tid * 4);
   const auto rc = buf_rsrc(C + ((int64_t)T.start * G + g) * N, ((uint32_t)(T.len - 1) * GN + N) * 2u);
-  bf16x8 fc[RGW][NK];                      // C rows of this lane, all n-steps
+  // C rows of this lane, all n-steps.  With four row groups per wave the
+  // last two groups' rows are issued once x and the state are staged, so
+  // that they do not share registers with the staging loads.
+  constexpr int RGE = RGW == 4 ? 2 : RGW;
+  bf16x8 fc[RGW][NK];
 #pragma unroll
-  for (int i = 0; i < RGW; ++i)
+  for (int i = 0; i < RGE; ++i)
 #pragma unroll
     for (int k = 0; k < NK; ++k)
       fc[i][k] = __builtin_bit_cast(bf16x8, buf_load16(rc, ((uint32_t)lrow[i] * GN + 32 * k + kq) * 2u));
@@ -755,6 +769,11 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
       cfs[tid] = dl_t * exp2_fast(a2r - a2);
     }
   }
+#pragma unroll
+  for (int i = RGE; i < RGW; ++i)
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+      fc[i][k] = __builtin_bit_cast(bf16x8, buf_load16(rc, ((uint32_t)lrow[i] * GN + 32 * k + kq) * 2u));
   const int xrow = 8 * kg + (lr >> 2);
   const int xsl = tile_sw<CPR>(xrow) >> 1;
   const int xcol = ((lr & 3) >> 1) * 8 + (lr & 1) * 4;
@@ -792,17 +811,18 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
         }
       }
     }
-    // CB pieces stream through a ring of three per row group, and enter the
+    // CB pieces stream through a ring of RD per row group, and enter the
     // MFMAs as loaded (the stored CB is 0 above the diagonal, so the diagonal
-    // step needs no mask): the first two steps' pieces are in flight while x
-    // is rescaled, and each step issues the pieces two steps ahead (the loop
-    // is unrolled, so the slots are fixed registers).  Steps past a row
+    // step needs no mask): the first RD - 1 steps' pieces are in flight while
+    // x is rescaled, and each step issues the pieces RD - 1 steps ahead (the
+    // loop is unrolled, so the slots are fixed registers).  Steps past a row
     // group's last load nothing.
-    bf16x8 ring[RGW][3];
+    constexpr int RD = RGW == 4 ? 2 : 3;   // ring slots (registers) per row group
+    bf16x8 ring[RGW][RD];
 #pragma unroll
     for (int i = 0; i < RGW; ++i)
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int q = 0; q < RD - 1; ++q)
         if (q < nq[i])                     // wave-uniform
           ring[i][q] = __builtin_bit_cast(bf16x8, buf_load16(rcb, ((uint32_t)lrow[i] * L + kq + 32 * q) * 2u));
     __syncthreads();                       // x as loaded is no longer read
@@ -830,12 +850,12 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
         if (q >= nq_wave) break;           // wave-uniform
 #pragma unroll
         for (int i = 0; i < RGW; ++i)
-          if (q + 2 < nq[i])               // wave-uniform
-            ring[i][(q + 2) % 3] = __builtin_bit_cast(
-                bf16x8, buf_load16(rcb, ((uint32_t)lrow[i] * L + kq + 32 * (q + 2)) * 2u));
+          if (q + RD - 1 < nq[i])          // wave-uniform
+            ring[i][(q + RD - 1) % RD] = __builtin_bit_cast(
+                bf16x8, buf_load16(rcb, ((uint32_t)lrow[i] * L + kq + 32 * (q + RD - 1)) * 2u));
 #pragma unroll
         for (int i = 0; i < RGW; ++i)
-          if (q < nq[i]) fb[i] = ring[i][q % 3];
+          if (q < nq[i]) fb[i] = ring[i][q % RD];
       }
 #pragma unroll
       for (int i = 0; i < RGW; ++i)
@@ -851,38 +871,45 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
   } else {
     // ---- exact path: each CB piece is masked with its decay
     // exp(a_l - a_s) delta_s; the next step's CB rows are in flight while
-    // one is multiplied.
-    uint32_t cbo[RGW];
-    bf16x8 cur[RGW];                       // CB rows of the current k-step
-#pragma unroll
-    for (int i = 0; i < RGW; ++i) {
-      cbo[i] = ((uint32_t)lrow[i] * L + kq) * 2u;
-      cur[i] = __builtin_bit_cast(bf16x8, buf_load16(rcb, cbo[i]));
-    }
+    // one is multiplied.  With four row groups per wave, two passes over the
+    // k-steps take two row groups each (the pairs mirror inside each half of
+    // the chunk, so the second of a pass reaches furthest).
+    constexpr int RP = RGW == 4 ? 2 : RGW;   // row groups per pass
 #pragma unroll
     for (int i = 0; i < RGW; ++i) {
       const float rsc = exp2_fast(dal2[lrow[i]]);
 #pragma unroll
       for (int a = 0; a < PT; ++a) acc[i][a] *= rsc;
     }
-    for (int q = 0; q < nq_wave; ++q) {
-      const int sn = min(32 * q + 32, L - 32);   // next step (clamped: always in the row)
-      bf16x8 nxt[RGW];
 #pragma unroll
-      for (int i = 0; i < RGW; ++i) nxt[i] = __builtin_bit_cast(bf16x8, buf_load16(rcb, cbo[i] + sn * 2));
-      bf16x8 fm[RGW];
+    for (int i0 = 0; i0 < RGW; i0 += RP) {
+      uint32_t cbo[RP];
+      bf16x8 cur[RP];                      // CB rows of the current k-step
 #pragma unroll
-      for (int i = 0; i < RGW; ++i)
-        if (q < nq[i]) fm[i] = scan_masked_cb(mg[i], q, cur[i], lr, kq, dal2, dls, cfs);
-#pragma unroll
-      for (int a = 0; a < PT; ++a) {
-        const bf16x8 fx = scan_x_operand<P>(xs, q, a, xrow, xsl, xcol);
-#pragma unroll
-        for (int i = 0; i < RGW; ++i)
-          if (q < nq[i]) acc[i][a] = M::mma(fx, fm[i], acc[i][a]);   // wave-uniform
+      for (int r = 0; r < RP; ++r) {
+        cbo[r] = ((uint32_t)lrow[i0 + r] * L + kq) * 2u;
+        cur[r] = __builtin_bit_cast(bf16x8, buf_load16(rcb, cbo[r]));
       }
+      const int nqp = nq[i0 + RP - 1];
+      for (int q = 0; q < nqp; ++q) {
+        const int sn = min(32 * q + 32, L - 32);   // next step (clamped: always in the row)
+        bf16x8 nxt[RP];
 #pragma unroll
-      for (int i = 0; i < RGW; ++i) cur[i] = nxt[i];
+        for (int r = 0; r < RP; ++r) nxt[r] = __builtin_bit_cast(bf16x8, buf_load16(rcb, cbo[r] + sn * 2));
+        bf16x8 fm[RP];
+#pragma unroll
+        for (int r = 0; r < RP; ++r)
+          if (q < nq[i0 + r]) fm[r] = scan_masked_cb(mg[i0 + r], q, cur[r], lr, kq, dal2, dls, cfs);
+#pragma unroll
+        for (int a = 0; a < PT; ++a) {
+          const bf16x8 fx = scan_x_operand<P>(xs, q, a, xrow, xsl, xcol);
+#pragma unroll
+          for (int r = 0; r < RP; ++r)
+            if (q < nq[i0 + r]) acc[i0 + r][a] = M::mma(fx, fm[r], acc[i0 + r][a]);   // wave-uniform
+        }
+#pragma unroll
+        for (int r = 0; r < RP; ++r) cur[r] = nxt[r];
+      }
     }
     // y = acc + D x, written over x (each element read and written by one lane)
     __syncthreads();
@@ -935,8 +962,8 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
   }
 }
 
-template <int P, int N, int L>
-__global__ __launch_bounds__(64 * kTileWaves<L>) __attribute__((amdgpu_waves_per_eu(4))) void
+template <int P, int N, int L, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kTileWavesPerEU<L, NW>))) void
 chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
                             const bf16* __restrict__ C, const bf16* __restrict__ cb,
                             const float* __restrict__ delta, const float* __restrict__ dAcs,
@@ -966,15 +993,18 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
   }
   if (T.len <= 0) return;
   if (fabsf(last) * kLog2e <= kScanFastMaxLog2)   // uniform over the workgroup
-    scan_tile_body<P, N, L, true>(T, x, C, cb, delta, dAcs, states_in, D, H, G, out, xs, hsm, dal2, dls, cfs);
+    scan_tile_body<P, N, L, NW, true>(T, x, C, cb, delta, dAcs, states_in, D, H, G, out, xs, hsm, dal2, dls, cfs);
   else
-    scan_tile_body<P, N, L, false>(T, x, C, cb, delta, dAcs, states_in, D, H, G, out, xs, hsm, dal2, dls, cfs);
+    scan_tile_body<P, N, L, NW, false>(T, x, C, cb, delta, dAcs, states_in, D, H, G, out, xs, hsm, dal2, dls, cfs);
 }
 
 }  // namespace
 
-// The persistent kernel pays off once each resident workgroup has this many
-// tiles to walk; below that, one workgroup per tile.
+// Below this many tiles per resident persistent workgroup, one 8-wave (or
+// 4-wave for short chunks) workgroup per tile is fastest.  Above it, with
+// 256-token chunks, 4-wave tiles (three workgroups per CU) beat the
+// persistent walk by about 2.5% on long and packed sequences and tie on the
+// training batch; with shorter chunks the persistent walk is used.
 constexpr int kPersistentMinTiles = 6;
 
 // Workgroups that stay resident per CU times the CU count, cached per device.
@@ -1002,13 +1032,20 @@ hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s) {
     const int ntiles = xcd_grid(a.max_chunks, a.H);
     const int g = persistent_grid(kern, 4 * L, 0);
     if (g <= 0) return hipErrorInvalidDevice;
-    const bool persistent = a.scan_kernel == 2 || (a.scan_kernel == 0 && ntiles >= kPersistentMinTiles * g);
-    if (persistent) {
+    int choice = a.scan_kernel;
+    if (choice == 0)
+      choice = ntiles < kPersistentMinTiles * g ? 1 : (kTileWaves<L> == 8 ? 3 : 2);
+    if (choice == 2) {
       hipLaunchKernelGGL(kern, dim3(g), dim3(4 * L), 0, s, a.cmap(), a.max_chunks, ntiles,
                          (const bf16*)a.x, (const bf16*)a.C, (const bf16*)a.cb, a.delta, a.dAcs,
                          (const bf16*)a.states_in, a.D, a.H, a.G, (bf16*)a.out);
+    } else if (choice == 3) {
+      hipLaunchKernelGGL((chunk_scan_bf16_tile_kernel<P, N, L, 4>), dim3(ntiles), dim3(64 * 4), 0, s,
+                         a.cmap(), a.max_chunks, (const bf16*)a.x, (const bf16*)a.C,
+                         (const bf16*)a.cb, a.delta, a.dAcs, (const bf16*)a.states_in, a.D, a.H,
+                         a.G, (bf16*)a.out);
     } else {
-      hipLaunchKernelGGL((chunk_scan_bf16_tile_kernel<P, N, L>), dim3(ntiles),
+      hipLaunchKernelGGL((chunk_scan_bf16_tile_kernel<P, N, L, kTileWaves<L>>), dim3(ntiles),
                          dim3(64 * kTileWaves<L>), 0, s, a.cmap(), a.max_chunks, (const bf16*)a.x,
                          (const bf16*)a.C, (const bf16*)a.cb, a.delta, a.dAcs,
                          (const bf16*)a.states_in, a.D, a.H, a.G, (bf16*)a.out);

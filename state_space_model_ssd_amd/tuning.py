@@ -12,7 +12,8 @@ hardware space").  Here the choices are the ones the library has more than
 one kernel for:
 
   scan_kernel  chunk_scan, bf16: 1 = one workgroup per (chunk, head) tile,
-               2 = the persistent walk over tiles
+               2 = the persistent walk over tiles, 3 = one workgroup of
+               four waves per tile
   sp_vec       state elements per state_passing thread: 1, 2 or 4
   front        bf16 stages 1-3: 1 = one fused launch, 2 = three launches
   sp_blocks    state_passing: 1 = one chain per sequence, 2..16 = blocks of
@@ -97,7 +98,7 @@ def candidates(prob: binding.ProblemC) -> list:
     vecs = [v for v in (1, 2, 4) if (prob.headdim * prob.dstate) % v == 0]
     if prob.dtype == binding.SSD_BF16:
         out = [dict(scan_kernel=s, sp_vec=v, front=f)
-               for s, v, f in itertools.product((1, 2), vecs, (1, 2))]
+               for s, v, f in itertools.product((1, 2, 3), vecs, (1, 2))]
     else:
         out = [dict(sp_vec=v) for v in vecs]
     if binding.workspace_layout(prob).sp_blocks > 1:

@@ -30,8 +30,8 @@ def test_shape_key_names_what_the_choices_depend_on():
 
 def test_candidates_cover_every_choice():
     bf = tuning.candidates(_prob())
-    assert len(bf) == 12 and len({json.dumps(c, sort_keys=True) for c in bf}) == 12
-    assert {c["scan_kernel"] for c in bf} == {1, 2}
+    assert len(bf) == 18 and len({json.dumps(c, sort_keys=True) for c in bf}) == 18
+    assert {c["scan_kernel"] for c in bf} == {1, 2, 3}
     assert {c["sp_vec"] for c in bf} == {1, 2, 4}
     assert {c["front"] for c in bf} == {1, 2}
     f32 = tuning.candidates(_prob(dtype=binding.SSD_F32, headdim=32, dstate=16, chunk_size=64))
@@ -93,7 +93,7 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails on the h
 
 
 @pytest.mark.parametrize("dtype,fields", [
-    (binding.SSD_BF16, dict(scan_kernel=3)),
+    (binding.SSD_BF16, dict(scan_kernel=4)),
     (binding.SSD_BF16, dict(scan_kernel=-1)),
     (binding.SSD_BF16, dict(sp_vec=3)),
     (binding.SSD_BF16, dict(sp_vec=8)),
