@@ -308,9 +308,11 @@ __global__ __launch_bounds__(kStateThreads) void front_bf16_kernel(
   constexpr size_t kState = sizeof(StateSmem<P, N, L>);
   __shared__ __align__(16) unsigned char smem[kBmm > kState ? kBmm : kState];
   const int b = blockIdx.x;
-  if (b >= nstate) {                      // nstate is a multiple of 8: XCD order kept above
-    const int tile = (b - nstate) % NTRI, jg = (b - nstate) / NTRI;
-    const int j = jg / G, g = jg - (jg / G) * G;
+  if (b >= nstate) {
+    // nstate is a multiple of 8, so the bmm tiles of chunk j run on the XCD
+    // of its chunk_state workgroups, and one L2 fetches its B and C rows
+    const int2 jt = xcd_chunk_head(b - nstate, G * NTRI);
+    const int j = jt.x, g = jt.y / NTRI, tile = jt.y - (jt.y / NTRI) * NTRI;
     if (j >= nslots) return;
     const int2 t = tri_tile(tile);
     const ChunkDesc d = cm.desc(j);
@@ -351,7 +353,7 @@ hipError_t launch_front(const FwdArgs& a, hipStream_t s) {
   } else {
     if (a.max_chunks <= 0) return hipSuccess;
     constexpr int ntri = (L / 64) * (L / 64 + 1) / 2;
-    const int nbmm = a.max_chunks * a.G * ntri;
+    const int nbmm = xcd_grid(a.max_chunks, a.G * ntri);
     const int nstate = xcd_grid(a.max_chunks, a.H);
     hipLaunchKernelGGL((front_bf16_kernel<P, N, L>), dim3(nstate + nbmm),
                        dim3(kStateThreads), 0, s, a.cmap(), a.max_chunks, nstate, a.G, (const bf16*)a.x,
