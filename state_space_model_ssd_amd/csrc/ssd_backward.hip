@@ -23,15 +23,17 @@
 //      + exp(a_last) <dS_j, H>; then a = cumsum(delta A) gives
 //      ddelta_k += A sum_{l>=k} da_l and dA += sum_k delta_k sum_{l>=k} da_l,
 //      and ddt = ddelta softplus'(dt + dt_bias) where the clamp passes it.
-//   4. per head: dC_h[l] = sum_{s<=l} dCB[l,s] B_s + exp(a_l) dy_l H,
-//      dB_h[s] = sum_{l>=s} dCB[l,s] C_l + delta_s exp(a_last - a_s) x_s dS_j;
-//   5. dB, dC: sums of dB_h, dC_h over the heads of each group; dA, dD and
-//      dt_bias: sums over chunks.
+//   4. per group g (B and C are shared by its heads, so the intra-chunk
+//      parts contract dCB summed over the heads, once per group):
+//      dC[l] = sum_{s<=l} (sum_h dCB_h[l,s]) B_s + sum_h exp(a_l) dy_l H,
+//      dB[s] = sum_{l>=s} (sum_h dCB_h[l,s]) C_l
+//              + sum_h delta_s exp(a_last - a_s) x_s dS_j;
+//   5. dA, dD and dt_bias: sums over chunks.
 // Everything accumulates in fp32; dx, dB and dC are rounded once to x's
 // dtype.  Deterministic: fixed loop orders, no atomics.
 //
-// This first version is direct loops over global memory (the operands stay
-// in L2) with the states in LDS: correctness first, MFMA tiling later.
+// The contractions are 64 x 64 fp32 tiles on the vector ALUs, with operand
+// slices staged through LDS by element-wise loads (the operands stay in L2).
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -39,6 +41,9 @@ namespace ssd {
 namespace {
 
 constexpr int kBwdThreads = 256;
+// Most blocks a group's heads are split into for the summed dCB (more blocks:
+// more workgroups in 3a, more partial sums read in 4b).
+constexpr int kBwdHeadBlocks = 8;
 
 template <typename T>
 __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
@@ -160,66 +165,85 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
-// 3a. V[l,s] = exp(a_l - a_s) (dy_l . x_s) for s <= l (so dCB = delta_s V),
-// as 64 x 64 tiles on or below the diagonal, with each tile's partial sums
+// 3a. For each head, V[l,s] = exp(a_l - a_s) (dy_l . x_s) for s <= l as
+// 64 x 64 tiles on or below the diagonal, with each tile's partial sums
 //   rowpart[st][l] = sum_s CB[l,s] delta_s V[l,s]   (s in column tile st)
-//   colpart[lt][s] = sum_l CB[l,s] V[l,s]           (l in row tile lt);
-// grid ((L/64)^2, H, chunk slots).
+//   colpart[lt][s] = sum_l CB[l,s] V[l,s]           (l in row tile lt),
+// and dCB[l,s] = delta_s V[l,s] summed over a block of the group's heads:
+// B and C are shared by the group, so dB and dC need dCB only summed over
+// its heads.  Workgroup (lt, st, g, hb) walks the heads of block hb of group
+// g (HB blocks per group) and writes that block's sum to dcbp[j][g][hb].
+// grid ((L/64)^2, G * HB, chunk slots).
 template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
     ChunkMap cm, const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ cb,
-    const float* __restrict__ delta, const float* __restrict__ dAcs, int H, int G,
-    float* __restrict__ V, float* __restrict__ rowpart, float* __restrict__ colpart) {
+    const float* __restrict__ delta, const float* __restrict__ dAcs, int H, int G, int HB,
+    float* __restrict__ dcbp, float* __restrict__ rowpart, float* __restrict__ colpart) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   __shared__ float cpart[16][64];
   constexpr int LT = L / 64;
   const int lt = blockIdx.x / LT, st = blockIdx.x % LT;
   if (st > lt) return;                     // above the diagonal: nothing
-  const int h = blockIdx.y, j = blockIdx.z, g = h / (H / G);
+  const int g = blockIdx.y / HB, hb = blockIdx.y - (blockIdx.y / HB) * HB, j = blockIdx.z;
+  const int hpg = H / G, h0 = g * hpg + hb * hpg / HB, h1 = g * hpg + (hb + 1) * hpg / HB;
   const ChunkDesc cd = cm.desc(j);
   const int len = max(cd.len, 0);
   const int l0 = lt * 64, s0 = st * 64;
   if (l0 >= len) return;
-  const int64_t jh = (int64_t)j * H + h, t0 = cd.start;
-  const float* a = dAcs + jh * L;
-  float acc[4][4] = {};
-  gemm_tile<true, true>(0, P,
-      [&](int m, int p) { const int l = l0 + m;
-        return l < len ? ld(dy + ((t0 + l) * H + h) * P + p) : 0.f; },
-      [&](int p, int n) { const int sx = s0 + n;
-        return sx < len ? ld(x + ((t0 + sx) * H + h) * P + p) : 0.f; },
-      acc, As, Bs);
+  const int64_t t0 = cd.start;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
   const T* cbj = cb + ((int64_t)j * G + g) * L * L;
-  float* Vj = V + jh * L * L;
-  float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum[4] = {0.f, 0.f, 0.f, 0.f};
+  float w[4][4] = {};                      // this block's sum of delta_s V[l,s]
+  for (int h = h0; h < h1; ++h) {
+    const int64_t jh = (int64_t)j * H + h;
+    const float* a = dAcs + jh * L;
+    float acc[4][4] = {};
+    gemm_tile<true, true>(0, P,
+        [&](int m, int p) { const int l = l0 + m;
+          return l < len ? ld(dy + ((t0 + l) * H + h) * P + p) : 0.f; },
+        [&](int p, int n) { const int sx = s0 + n;
+          return sx < len ? ld(x + ((t0 + sx) * H + h) * P + p) : 0.f; },
+        acc, As, Bs);
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) {
+        const int l = l0 + tm + i, sx = s0 + tn + jn;
+        if (l < len && sx <= l) {
+          const float v = expf(a[l] - a[sx]) * acc[i][jn];
+          const float dv = delta[jh * L + sx] * v;
+          w[i][jn] += dv;
+          const float c = ld(cbj + (int64_t)l * L + sx);
+          rsum[i] += c * dv;
+          csum[jn] += c * v;
+        }
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float r = row16_sum(rsum[i]);
+      if ((threadIdx.x & 15) == 0) rowpart[(jh * LT + st) * L + l0 + tm + i] = r;
+    }
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn) cpart[threadIdx.x >> 4][tn + jn] = csum[jn];
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      float c = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c += cpart[r][threadIdx.x];
+      colpart[(jh * LT + lt) * L + s0 + threadIdx.x] = c;
+    }
+    // the next head's gemm_tile starts with a barrier, so cpart is read
+    // before it is written again
+  }
+  float* W = dcbp + (((int64_t)j * G + g) * HB + hb) * L * L;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) {
       const int l = l0 + tm + i, sx = s0 + tn + jn;
-      if (l < len && sx <= l) {
-        const float v = expf(a[l] - a[sx]) * acc[i][jn];
-        Vj[(int64_t)l * L + sx] = v;
-        const float m = ld(cbj + (int64_t)l * L + sx) * v;
-        rsum[i] += delta[jh * L + sx] * m;
-        csum[jn] += m;
-      }
+      if (l < len && sx <= l) W[(int64_t)l * L + sx] = w[i][jn];
     }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float r = row16_sum(rsum[i]);
-    if ((threadIdx.x & 15) == 0) rowpart[(jh * LT + st) * L + l0 + tm + i] = r;
-  }
-#pragma unroll
-  for (int jn = 0; jn < 4; ++jn) cpart[threadIdx.x >> 4][tn + jn] = csum[jn];
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    float c = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) c += cpart[r][threadIdx.x];
-    colpart[(jh * LT + lt) * L + s0 + threadIdx.x] = c;
-  }
 }
 
 // 3b. dx as 64 x 64 tiles of (token s, p):
@@ -275,11 +299,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
   }
 }
 
-// 4. Per-head dC and dB rows as 64 x 64 tiles:
-//   dC_h = diag(exp(a)) dy H + dCB B (s <= l),
-//   dB_h = diag(delta exp(a_last - a)) x dS_j + dCB^T C (l >= s),
-// with dCB[l,s] = delta_s V[l,s].  Between its two products each tile takes
-// a partial row dot product for the per-token pass:
+// 4a. The per-head state terms of dC and dB as 64 x 64 tiles of rows x n:
+//   dC_h = diag(exp(a)) dy H,   dB_h = diag(delta exp(a_last - a)) x dS_j.
+// Between the product and its store each tile takes a partial row dot
+// product for the per-token pass:
 //   interpart[nt][l] = sum_n C[l,n] exp(a_l) (dy_l H)[n],
 //   vxpart[nt][s]    = sum_n B[s,n] exp(a_last - a_s) (x_s dS_j)[n]
 // over its 64 columns n.  grid (L/64 * ceil(N/64) * 2, H, chunk slots);
@@ -288,8 +311,8 @@ template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
     ChunkMap cm, const T* __restrict__ x, const T* __restrict__ B, const T* __restrict__ C,
     const T* __restrict__ dy, const float* __restrict__ delta, const float* __restrict__ dAcs,
-    const T* __restrict__ states_in, const float* __restrict__ dS, const float* __restrict__ V,
-    int H, int G, float* __restrict__ dBh, float* __restrict__ dCh, float* __restrict__ interpart,
+    const T* __restrict__ states_in, const float* __restrict__ dS, int H, int G,
+    float* __restrict__ dBh, float* __restrict__ dCh, float* __restrict__ interpart,
     float* __restrict__ vxpart) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   __shared__ float sc[L], ds[L];
@@ -307,7 +330,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
     sc[l] = which == 0 ? expf(a[l]) : expf(alast - a[l]);
     ds[l] = delta[jh * L + l];
   }
-  const float* Vj = V + jh * L * L;
   const int64_t t0 = cd.start;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
   float acc[4][4] = {};
@@ -335,13 +357,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
           return nn < N ? ld(states_in + (jh * P + p) * N + nn) : 0.f; },
         acc, As, Bs);
     row_dot(C, interpart);
-    // dC rows m0..m0+63: s runs to the tile's last row
-    gemm_tile<true>(0, min(len, m0 + 64),
-        [&](int m, int sx) { const int l = m0 + m;
-          return (l < len && sx <= l) ? ds[sx] * Vj[(int64_t)l * L + sx] : 0.f; },
-        [&](int sx, int n) { const int nn = n0 + n;
-          return nn < N ? ld(B + ((t0 + sx) * G + g) * N + nn) : 0.f; },
-        acc, As, Bs);
   } else {
     gemm_tile<true>(0, P,
         [&](int m, int p) { const int sx = m0 + m;
@@ -357,13 +372,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
 #pragma unroll
       for (int jn = 0; jn < 4; ++jn) acc[i][jn] *= f;
     }
-    // dB rows m0..m0+63: l runs from the tile's first row
-    gemm_tile<false>(m0, len,
-        [&](int m, int l) { const int sx = m0 + m;
-          return (sx < len && l >= sx) ? ds[sx] * Vj[(int64_t)l * L + sx] : 0.f; },
-        [&](int l, int n) { const int nn = n0 + n;
-          return nn < N ? ld(C + ((t0 + l) * G + g) * N + nn) : 0.f; },
-        acc, As, Bs);
   }
   float* out = which == 0 ? dCh : dBh;
 #pragma unroll
@@ -372,6 +380,90 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
     for (int jn = 0; jn < 4; ++jn) {
       const int r = m0 + tm + i, n = n0 + tn + jn;
       if (r < len && n < N) out[(jh * L + r) * N + n] = acc[i][jn];
+    }
+}
+
+// 3b'. The group's dCB: the HB partial sums of 3a added into the first,
+// four floats per thread (entries above the diagonal or past the chunk are
+// summed too and never read).  grid (ceil(L*L / 1024), G, chunk slots).
+template <int L>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dcb_sum_kernel(int G, int HB,
+                                                                  float* __restrict__ dcbp) {
+  const int e = blockIdx.x * kBwdThreads + threadIdx.x;
+  if (e >= L * L / 4) return;
+  const int64_t LL4 = (int64_t)L * L / 4;
+  float4* W = reinterpret_cast<float4*>(dcbp) + ((int64_t)blockIdx.z * G + blockIdx.y) * HB * LL4 + e;
+  float4 v = W[0];
+  for (int k = 1; k < HB; ++k) {
+    const float4 u = W[k * LL4];
+    v.x += u.x;
+    v.y += u.y;
+    v.z += u.z;
+    v.w += u.w;
+  }
+  W[0] = v;
+}
+
+// 4b. dC and dB of a group as 64 x 64 tiles of rows x n: the group's summed
+// dCB (3b') times B or C, plus the per-head state
+// terms of 4a summed over the group's heads, rounded once to the dtype:
+//   dC[l] = sum_{s<=l} dCB[l,s] B_s + sum_h dC_h[l],
+//   dB[s] = sum_{l>=s} dCB[l,s] C_l + sum_h dB_h[s].
+// grid (L/64 * ceil(N/64) * 2, G, chunk slots); even x: dC, odd: dB.
+template <typename T, int N, int L>
+__global__ __launch_bounds__(kBwdThreads) void bwd_bc_group_kernel(
+    ChunkMap cm, const T* __restrict__ B, const T* __restrict__ C,
+    const float* __restrict__ dcbp, const float* __restrict__ dBh, const float* __restrict__ dCh,
+    int H, int G, int HB, T* __restrict__ dB, T* __restrict__ dC) {
+  __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
+  constexpr int NT = (N + 63) / 64;
+  const int which = blockIdx.x & 1, t = blockIdx.x >> 1;
+  const int m0 = (t / NT) * 64, n0 = (t % NT) * 64;
+  const int g = blockIdx.y, j = blockIdx.z;
+  const ChunkDesc cd = cm.desc(j);
+  const int len = max(cd.len, 0);
+  if (m0 >= len) return;                   // uniform: rows past the chunk
+  const int64_t t0 = cd.start;
+  const float* W = dcbp + ((int64_t)j * G + g) * HB * L * L;   // the summed slot
+  float acc[4][4] = {};
+  if (which == 0) {                        // dC rows m0..m0+63: s runs to the tile's last row
+    gemm_tile<true>(0, min(len, m0 + 64),
+        [&](int m, int sx) { const int l = m0 + m;
+          return (l < len && sx <= l) ? W[(int64_t)l * L + sx] : 0.f; },
+        [&](int sx, int n) { const int nn = n0 + n;
+          return nn < N ? ld(B + ((t0 + sx) * G + g) * N + nn) : 0.f; },
+        acc, As, Bs);
+  } else {                                 // dB rows m0..m0+63: l runs from the tile's first row
+    gemm_tile<false>(m0, len,
+        [&](int m, int l) { const int sx = m0 + m;
+          return (sx < len && l >= sx) ? W[(int64_t)l * L + sx] : 0.f; },
+        [&](int l, int n) { const int nn = n0 + n;
+          return nn < N ? ld(C + ((t0 + l) * G + g) * N + nn) : 0.f; },
+        acc, As, Bs);
+  }
+  // the heads' state terms: per head, the tile's 16 values of this thread
+  // are independent loads (rows past the chunk read row 0 and are dropped)
+  const float* part = which == 0 ? dCh : dBh;
+  T* out = which == 0 ? dC : dB;
+  const int hpg = H / G;
+  const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+#pragma unroll 2
+  for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+    const float* ph = part + ((int64_t)j * H + h) * L * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) {
+        const int r = m0 + tm + i, n = n0 + tn + jn;
+        acc[i][jn] += ph[(int64_t)(r < len ? r : 0) * N + (n < N ? n : 0)];
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn) {
+      const int r = m0 + tm + i, n = n0 + tn + jn;
+      if (r < len && n < N) out[((t0 + r) * G + g) * N + n] = from_f32<T>(acc[i][jn]);
     }
 }
 
@@ -449,30 +541,7 @@ __global__ __launch_bounds__(L) void bwd_token_kernel(
   }
 }
 
-// 5a. dB, dC: sums over the heads of a group; grid (ceil(L*N / 256), G, chunk slots).
-template <typename T, int N, int L>
-__global__ __launch_bounds__(kBwdThreads) void bwd_bc_reduce_kernel(
-    ChunkMap cm, const float* __restrict__ dBh, const float* __restrict__ dCh, int H, int G,
-    T* __restrict__ dB, T* __restrict__ dC) {
-  const int o = blockIdx.x * kBwdThreads + threadIdx.x;
-  if (o >= L * N) return;
-  const int g = blockIdx.y, j = blockIdx.z;
-  const int k = o / N, n = o - (o / N) * N;
-  const ChunkDesc cd = cm.desc(j);
-  if (k >= cd.len) return;
-  const int hpg = H / G;
-  float sb = 0.f, sc = 0.f;
-  for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
-    const int64_t i = (((int64_t)j * H + h) * L + k) * N + n;
-    sb += dBh[i];
-    sc += dCh[i];
-  }
-  const int64_t t = cd.start + k;
-  dB[(t * G + g) * N + n] = from_f32<T>(sb);
-  dC[(t * G + g) * N + n] = from_f32<T>(sc);
-}
-
-// 5b. dA, dD, dt_bias: sums over the chunk slots; one thread per head.
+// 5. dA, dD, dt_bias: sums over the chunk slots; one thread per head.
 __global__ __launch_bounds__(kBwdThreads) void bwd_head_reduce_kernel(
     const float* __restrict__ dA_part, const float* __restrict__ dD_part,
     const float* __restrict__ dbias_part, int H, int nslots, float* __restrict__ dA,
@@ -518,11 +587,19 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   hipLaunchKernelGGL(bwd_chain_kernel, dim3((PN + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
                      dim3(kBwdThreads), 0, s, cm, b.Q, a.dAcs, b.dfinal, H, PN, L, b.dS, b.dinit);
   constexpr int LT = L / 64;
-  hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(LT * LT, H, mc), dim3(kBwdThreads), 0, s,
-                     cm, x, dy, cb, a.delta, a.dAcs, H, G, b.dcb, b.rowpart, b.colpart);
+  // head blocks per group for the summed dCB (their partial sums fit the
+  // workspace's H L^2 floats per chunk: G * HB <= H)
+  const int hpg = H / G, HB = hpg < kBwdHeadBlocks ? hpg : kBwdHeadBlocks;
+  hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(LT * LT, G * HB, mc), dim3(kBwdThreads),
+                     0, s, cm, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb, b.rowpart, b.colpart);
   hipLaunchKernelGGL((bwd_bc_tiled_kernel<T, P, N, L>), dim3(LT * NT * 2, H, mc),
-                     dim3(kBwdThreads), 0, s, cm, x, B, C, dy, a.delta, a.dAcs, hin, b.dS, b.dcb, H,
-                     G, b.dBh, b.dCh, b.interpart, b.vxpart);
+                     dim3(kBwdThreads), 0, s, cm, x, B, C, dy, a.delta, a.dAcs, hin, b.dS, H, G,
+                     b.dBh, b.dCh, b.interpart, b.vxpart);
+  if (HB > 1)
+    hipLaunchKernelGGL((bwd_dcb_sum_kernel<L>), dim3((L * L / 4 + kBwdThreads - 1) / kBwdThreads, G, mc),
+                       dim3(kBwdThreads), 0, s, G, HB, b.dcb);
+  hipLaunchKernelGGL((bwd_bc_group_kernel<T, N, L>), dim3(LT * NT * 2, G, mc), dim3(kBwdThreads), 0,
+                     s, cm, B, C, b.dcb, b.dBh, b.dCh, H, G, HB, (T*)b.dB, (T*)b.dC);
   hipLaunchKernelGGL((bwd_dx_tiled_kernel<T, P, N, L>), dim3(LT * ((P + 63) / 64), H, mc),
                      dim3(kBwdThreads), 0, s, cm, B, dy, cb, a.delta, a.dAcs, b.dS, a.D, H, G,
                      (T*)b.dx);
@@ -530,8 +607,6 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
                      a.dt_bias, a.A, dy, a.delta, a.dAcs, hin, b.dS, b.rowpart, b.colpart,
                      b.interpart, b.vxpart, H, a.dt_min, a.dt_max, b.ddt, b.dA_part, b.dD_part,
                      b.dbias_part);
-  hipLaunchKernelGGL((bwd_bc_reduce_kernel<T, N, L>), dim3((L * N + kBwdThreads - 1) / kBwdThreads, G, mc),
-                     dim3(kBwdThreads), 0, s, cm, b.dBh, b.dCh, H, G, (T*)b.dB, (T*)b.dC);
   hipLaunchKernelGGL(bwd_head_reduce_kernel, dim3((H + kBwdThreads - 1) / kBwdThreads), dim3(kBwdThreads),
                      0, s, b.dA_part, b.dD_part, b.dbias_part, H, mc, b.dA, b.dD, b.ddt_bias);
   return hipGetLastError();

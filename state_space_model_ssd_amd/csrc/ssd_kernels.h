@@ -68,7 +68,8 @@ struct BwdArgs {
   float* dinit;             // nullable
   float* Q;                 // [max_chunks][H][P*N]
   float* dS;                // [max_chunks][H][P*N]
-  float* dcb;               // [max_chunks][H][L][L]: exp(a_l - a_s) dy_l . x_s, s <= l
+  float* dcb;               // [max_chunks][H][L][L] floats; holds [max_chunks][G][HB][L][L]: sums
+                            // of delta_s exp(a_l - a_s) dy_l . x_s (s <= l) over head blocks
   float* rowpart;           // [max_chunks][H][L/64][L]
   float* colpart;           // [max_chunks][H][L/64][L]
   float* interpart;         // [max_chunks][H][ceil(N/64)][L]
