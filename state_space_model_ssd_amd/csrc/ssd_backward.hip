@@ -181,6 +181,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
     float* __restrict__ dcbp, float* __restrict__ rowpart, float* __restrict__ colpart) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   __shared__ float cpart[16][64];
+  __shared__ float cbt[64][65];            // the CB tile, shared by the group's heads
+  __shared__ float al[64], as[64], dls[64];   // the head's running sums (rows, columns), steps
   constexpr int LT = L / 64;
   const int lt = blockIdx.x / LT, st = blockIdx.x % LT;
   if (st > lt) return;                     // above the diagonal: nothing
@@ -193,10 +195,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
   const int64_t t0 = cd.start;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
   const T* cbj = cb + ((int64_t)j * G + g) * L * L;
+  for (int i = threadIdx.x; i < 64 * 64; i += kBwdThreads) {
+    const int r = i >> 6, c = i & 63;
+    cbt[r][c] = ld(cbj + (int64_t)(l0 + r) * L + s0 + c);   // rows past the chunk: never used
+  }
   float w[4][4] = {};                      // this block's sum of delta_s V[l,s]
   for (int h = h0; h < h1; ++h) {
     const int64_t jh = (int64_t)j * H + h;
-    const float* a = dAcs + jh * L;
+    if (threadIdx.x < 64) {                // read after gemm_tile's barriers
+      al[threadIdx.x] = dAcs[jh * L + l0 + threadIdx.x];
+      as[threadIdx.x] = dAcs[jh * L + s0 + threadIdx.x];
+      dls[threadIdx.x] = delta[jh * L + s0 + threadIdx.x];
+    }
     float acc[4][4] = {};
     gemm_tile<true, true>(0, P,
         [&](int m, int p) { const int l = l0 + m;
@@ -211,10 +221,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
       for (int jn = 0; jn < 4; ++jn) {
         const int l = l0 + tm + i, sx = s0 + tn + jn;
         if (l < len && sx <= l) {
-          const float v = expf(a[l] - a[sx]) * acc[i][jn];
-          const float dv = delta[jh * L + sx] * v;
+          const float v = expf(al[tm + i] - as[tn + jn]) * acc[i][jn];
+          const float dv = dls[tn + jn] * v;
           w[i][jn] += dv;
-          const float c = ld(cbj + (int64_t)l * L + sx);
+          const float c = cbt[tm + i][tn + jn];
           rsum[i] += c * dv;
           csum[jn] += c * v;
         }
@@ -233,8 +243,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
       for (int r = 0; r < 16; ++r) c += cpart[r][threadIdx.x];
       colpart[(jh * LT + lt) * L + s0 + threadIdx.x] = c;
     }
-    // the next head's gemm_tile starts with a barrier, so cpart is read
-    // before it is written again
+    __syncthreads();                       // cpart, al, as, dls read before the next head writes them
   }
   float* W = dcbp + (((int64_t)j * G + g) * HB + hb) * L * L;
 #pragma unroll
@@ -256,7 +265,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
     const float* __restrict__ delta, const float* __restrict__ dAcs, const float* __restrict__ dS,
     const float* __restrict__ D, int H, int G, T* __restrict__ dx) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
-  __shared__ float es[L];
+  __shared__ float es[L], av[L];
   constexpr int PT = (P + 63) / 64;
   const int s0 = (blockIdx.x / PT) * 64, p0 = (blockIdx.x % PT) * 64;
   const int h = blockIdx.y, j = blockIdx.z, g = h / (H / G);
@@ -266,12 +275,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
   const int64_t jh = (int64_t)j * H + h, t0 = cd.start;
   const float* a = dAcs + jh * L;
   const float alast = a[len - 1];
-  for (int l = threadIdx.x; l < L; l += kBwdThreads) es[l] = expf(alast - a[l]);
+  for (int l = threadIdx.x; l < L; l += kBwdThreads) {
+    es[l] = expf(alast - a[l]);
+    av[l] = a[l];
+  }
   const T* cbj = cb + ((int64_t)j * G + g) * L * L;
   float acc[4][4] = {};
   gemm_tile<false>(s0, len,
       [&](int m, int l) { const int sx = s0 + m;
-        return (sx < len && l >= sx) ? ld(cbj + (int64_t)l * L + sx) * expf(a[l] - a[sx]) : 0.f; },
+        return (sx < len && l >= sx) ? ld(cbj + (int64_t)l * L + sx) * expf(av[l] - av[sx]) : 0.f; },
       [&](int l, int n) { const int pp = p0 + n;
         return pp < P ? ld(dy + ((t0 + l) * H + h) * P + pp) : 0.f; },
       acc, As, Bs);
