@@ -49,28 +49,63 @@ template <typename T>
 __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
 
 // A 64 x 64 fp32 output tile of sum_k A(m, k) B(k, n) for k in [k0, k1),
-// accumulated into acc (4 x 4 per thread of 256).  Operand tiles of 32
-// k-values pass through LDS: As[k][m] and Bs[k][n] (row pitch 68 floats).
+// accumulated into acc (4 x 4 per thread of 256).  Operand slices of 32
+// k-values pass through registers into LDS: As[k][m] and Bs[k][n] (row pitch
+// 68 floats).  PF: the next slice is loaded while the current one is
+// multiplied (more registers; pays off where occupancy has room).
 // A_KFAST: A(m, k) is contiguous in k (else in m); B(k, n) is read with n
 // fastest.  The loaders return 0 outside the operands.
 constexpr int kGemmPitch = 68;
 
-template <bool A_KFAST, bool B_KFAST = false, typename LA, typename LB>
+template <bool A_KFAST, bool B_KFAST = false, bool PF = false, typename LA, typename LB>
 __device__ __forceinline__ void gemm_tile(int k0, int k1, LA loadA, LB loadB, float (&acc)[4][4],
                                           float* As, float* Bs) {
   const int tid = threadIdx.x;
   const int tm = (tid >> 4) * 4, tn = (tid & 15) * 4;
-  for (int kb = k0; kb < k1; kb += 32) {
-    __syncthreads();                       // previous tile consumed
-    for (int i = tid; i < 64 * 32; i += kBwdThreads) {
+  constexpr int E = 64 * 32 / kBwdThreads;   // operand elements per thread and slice
+  float ra[E], rb[E];
+  auto fetch = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const int i = tid + kBwdThreads * u;
       int m, k;
       if constexpr (A_KFAST) { m = i >> 5; k = i & 31; } else { k = i >> 6; m = i & 63; }
-      As[k * kGemmPitch + m] = kb + k < k1 ? loadA(m, kb + k) : 0.f;
+      ra[u] = kb + k < k1 ? loadA(m, kb + k) : 0.f;
       int kk, n;
       if constexpr (B_KFAST) { n = i >> 5; kk = i & 31; } else { kk = i >> 6; n = i & 63; }
-      Bs[kk * kGemmPitch + n] = kb + kk < k1 ? loadB(kb + kk, n) : 0.f;
+      rb[u] = kb + kk < k1 ? loadB(kb + kk, n) : 0.f;
+    }
+  };
+  if constexpr (PF) {
+    __syncthreads();                       // what the caller staged for the loaders
+    if (k0 < k1) fetch(k0);
+  }
+  for (int kb = k0; kb < k1; kb += 32) {
+    __syncthreads();                       // previous slice consumed
+    if constexpr (PF) {
+#pragma unroll
+      for (int u = 0; u < E; ++u) {
+        const int i = tid + kBwdThreads * u;
+        int m, k;
+        if constexpr (A_KFAST) { m = i >> 5; k = i & 31; } else { k = i >> 6; m = i & 63; }
+        As[k * kGemmPitch + m] = ra[u];
+        int kk, n;
+        if constexpr (B_KFAST) { n = i >> 5; kk = i & 31; } else { kk = i >> 6; n = i & 63; }
+        Bs[kk * kGemmPitch + n] = rb[u];
+      }
+    } else {
+      for (int i = tid; i < 64 * 32; i += kBwdThreads) {
+        int m, k;
+        if constexpr (A_KFAST) { m = i >> 5; k = i & 31; } else { k = i >> 6; m = i & 63; }
+        As[k * kGemmPitch + m] = kb + k < k1 ? loadA(m, kb + k) : 0.f;
+        int kk, n;
+        if constexpr (B_KFAST) { n = i >> 5; kk = i & 31; } else { kk = i >> 6; n = i & 63; }
+        Bs[kk * kGemmPitch + n] = kb + kk < k1 ? loadB(kb + kk, n) : 0.f;
+      }
     }
     __syncthreads();
+    if constexpr (PF)
+      if (kb + 32 < k1) fetch(kb + 32);
 #pragma unroll 8
     for (int k = 0; k < 32; ++k) {
       const float4 a = *reinterpret_cast<const float4*>(&As[k * kGemmPitch + tm]);
@@ -362,7 +397,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
     }
   };
   if (which == 0) {
-    gemm_tile<true>(0, P,
+    gemm_tile<true, false, true>(0, P,
         [&](int m, int p) { const int l = m0 + m;
           return l < len ? sc[l] * ld(dy + ((t0 + l) * H + h) * P + p) : 0.f; },
         [&](int p, int n) { const int nn = n0 + n;
@@ -370,7 +405,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
         acc, As, Bs);
     row_dot(C, interpart);
   } else {
-    gemm_tile<true>(0, P,
+    gemm_tile<true, false, true>(0, P,
         [&](int m, int p) { const int sx = m0 + m;
           return sx < len ? sc[sx] * ld(x + ((t0 + sx) * H + h) * P + p) : 0.f; },
         [&](int p, int n) { const int nn = n0 + n;
@@ -439,14 +474,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_group_kernel(
   const float* W = dcbp + ((int64_t)j * G + g) * HB * L * L;   // the summed slot
   float acc[4][4] = {};
   if (which == 0) {                        // dC rows m0..m0+63: s runs to the tile's last row
-    gemm_tile<true>(0, min(len, m0 + 64),
+    gemm_tile<true, false, true>(0, min(len, m0 + 64),
         [&](int m, int sx) { const int l = m0 + m;
           return (l < len && sx <= l) ? W[(int64_t)l * L + sx] : 0.f; },
         [&](int sx, int n) { const int nn = n0 + n;
           return nn < N ? ld(B + ((t0 + sx) * G + g) * N + nn) : 0.f; },
         acc, As, Bs);
   } else {                                 // dB rows m0..m0+63: l runs from the tile's first row
-    gemm_tile<false>(m0, len,
+    gemm_tile<false, false, true>(m0, len,
         [&](int m, int l) { const int sx = m0 + m;
           return (sx < len && l >= sx) ? W[(int64_t)l * L + sx] : 0.f; },
         [&](int l, int n) { const int nn = n0 + n;
