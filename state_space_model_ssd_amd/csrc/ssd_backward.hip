@@ -119,6 +119,58 @@ __device__ __forceinline__ void gemm_tile(int k0, int k1, LA loadA, LB loadB, fl
   }
 }
 
+// As gemm_tile for A(m, p) = arow[m * stride + p] and B(p, n) = brow[n * stride + p]
+// (64 rows each of P contiguous values; rows at or past na, nb read as 0),
+// staged with one 16-byte load per row piece.  Same products, same order.
+template <typename T>
+__device__ __forceinline__ void load16_f32(const T* p, bool ok, float* v);
+template <>
+__device__ __forceinline__ void load16_f32<float>(const float* p, bool ok, float* v) {
+  const float4 t = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+  v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+template <>
+__device__ __forceinline__ void load16_f32<bf16>(const bf16* p, bool ok, float* v) {
+  const uint4 t = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
+  const bf16x8 b = __builtin_bit_cast(bf16x8, t);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(b[e]);
+}
+
+template <typename T, int P>
+__device__ __forceinline__ void gemm_rows_tile(const T* arow, const T* brow, int64_t stride, int na,
+                                               int nb, float (&acc)[4][4], float* As, float* Bs) {
+  constexpr int V = 16 / sizeof(T);
+  static_assert(P % 32 == 0, "row length");
+  const int tid = threadIdx.x;
+  const int tm = (tid >> 4) * 4, tn = (tid & 15) * 4;
+  for (int kb = 0; kb < P; kb += 32) {
+    __syncthreads();                       // previous slice consumed
+    for (int i = tid; i < 64 * (32 / V); i += kBwdThreads) {
+      const int r = i & 63, c = i >> 6;    // consecutive threads: consecutive rows
+      float va[V], vb[V];
+      load16_f32<T>(arow + r * stride + kb + c * V, r < na, va);
+      load16_f32<T>(brow + r * stride + kb + c * V, r < nb, vb);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        As[(c * V + e) * kGemmPitch + r] = va[e];
+        Bs[(c * V + e) * kGemmPitch + r] = vb[e];
+      }
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(&As[k * kGemmPitch + tm]);
+      const float4 b = *reinterpret_cast<const float4*>(&Bs[k * kGemmPitch + tn]);
+      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) acc[i][jn] += av[i] * bv[jn];
+    }
+  }
+}
+
 // Sum of v over the 16 threads that share a row of the 4 x 4 blocks (lanes
 // differing in their low 4 bits); every one of them gets it.
 __device__ __forceinline__ float row16_sum(float v) {
@@ -243,12 +295,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
       dls[threadIdx.x] = delta[jh * L + s0 + threadIdx.x];
     }
     float acc[4][4] = {};
-    gemm_tile<true, true>(0, P,
-        [&](int m, int p) { const int l = l0 + m;
-          return l < len ? ld(dy + ((t0 + l) * H + h) * P + p) : 0.f; },
-        [&](int p, int n) { const int sx = s0 + n;
-          return sx < len ? ld(x + ((t0 + sx) * H + h) * P + p) : 0.f; },
-        acc, As, Bs);
+    gemm_rows_tile<T, P>(dy + ((t0 + l0) * H + h) * P, x + ((t0 + s0) * H + h) * P, (int64_t)H * P,
+                         len - l0, len - s0, acc, As, Bs);
     float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
