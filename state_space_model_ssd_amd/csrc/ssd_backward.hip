@@ -119,9 +119,10 @@ __device__ __forceinline__ void gemm_tile(int k0, int k1, LA loadA, LB loadB, fl
   }
 }
 
-// As gemm_tile for A(m, p) = arow[m * stride + p] and B(p, n) = brow[n * stride + p]
-// (64 rows each of P contiguous values; rows at or past na, nb read as 0),
-// staged with one 16-byte load per row piece.  Same products, same order.
+// As gemm_tile for A(m, k) = ascale[m] arow[m * astride + k] (ascale: LDS, or
+// null for 1) and B(k, n) = brow[n * bstride + k], k in [0, K): 64 rows of K
+// contiguous values each, rows at or past na, nb read as 0, staged with one
+// 16-byte load per row piece.  Same products, same order.
 template <typename T>
 __device__ __forceinline__ void load16_f32(const T* p, bool ok, float* v);
 template <>
@@ -137,29 +138,36 @@ __device__ __forceinline__ void load16_f32<bf16>(const bf16* p, bool ok, float* 
   for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(b[e]);
 }
 
-template <typename T, int P>
-__device__ __forceinline__ void gemm_rows_tile(const T* arow, const T* brow, int64_t stride, int na,
-                                               int nb, float (&acc)[4][4], float* As, float* Bs) {
-  constexpr int V = 16 / sizeof(T);
-  static_assert(P % 32 == 0, "row length");
+template <typename TA, typename TB, int K>
+__device__ __forceinline__ void gemm_rows_tile(const TA* arow, int64_t astride, int na,
+                                               const float* ascale, const TB* brow,
+                                               int64_t bstride, int nb, float (&acc)[4][4],
+                                               float* As, float* Bs) {
+  constexpr int VA = 16 / sizeof(TA), VB = 16 / sizeof(TB);
+  constexpr int KS = K < 32 ? K : 32;      // slice length
+  static_assert(K % KS == 0 && KS % VA == 0 && KS % VB == 0, "row length");
   const int tid = threadIdx.x;
   const int tm = (tid >> 4) * 4, tn = (tid & 15) * 4;
-  for (int kb = 0; kb < P; kb += 32) {
-    __syncthreads();                       // previous slice consumed
-    for (int i = tid; i < 64 * (32 / V); i += kBwdThreads) {
+  for (int kb = 0; kb < K; kb += KS) {
+    __syncthreads();                       // previous slice consumed (and the caller's staging done)
+    for (int i = tid; i < 64 * (KS / VA); i += kBwdThreads) {
       const int r = i & 63, c = i >> 6;    // consecutive threads: consecutive rows
-      float va[V], vb[V];
-      load16_f32<T>(arow + r * stride + kb + c * V, r < na, va);
-      load16_f32<T>(brow + r * stride + kb + c * V, r < nb, vb);
+      float v[VA];
+      load16_f32<TA>(arow + r * astride + kb + c * VA, r < na, v);
+      const float sc = ascale ? ascale[r] : 1.f;
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        As[(c * V + e) * kGemmPitch + r] = va[e];
-        Bs[(c * V + e) * kGemmPitch + r] = vb[e];
-      }
+      for (int e = 0; e < VA; ++e) As[(c * VA + e) * kGemmPitch + r] = ascale ? sc * v[e] : v[e];
+    }
+    for (int i = tid; i < 64 * (KS / VB); i += kBwdThreads) {
+      const int r = i & 63, c = i >> 6;
+      float v[VB];
+      load16_f32<TB>(brow + r * bstride + kb + c * VB, r < nb, v);
+#pragma unroll
+      for (int e = 0; e < VB; ++e) Bs[(c * VB + e) * kGemmPitch + r] = v[e];
     }
     __syncthreads();
 #pragma unroll 8
-    for (int k = 0; k < 32; ++k) {
+    for (int k = 0; k < KS; ++k) {
       const float4 a = *reinterpret_cast<const float4*>(&As[k * kGemmPitch + tm]);
       const float4 b = *reinterpret_cast<const float4*>(&Bs[k * kGemmPitch + tn]);
       const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
@@ -295,8 +303,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
       dls[threadIdx.x] = delta[jh * L + s0 + threadIdx.x];
     }
     float acc[4][4] = {};
-    gemm_rows_tile<T, P>(dy + ((t0 + l0) * H + h) * P, x + ((t0 + s0) * H + h) * P, (int64_t)H * P,
-                         len - l0, len - s0, acc, As, Bs);
+    gemm_rows_tile<T, T, P>(dy + ((t0 + l0) * H + h) * P, (int64_t)H * P, len - l0, nullptr,
+                            x + ((t0 + s0) * H + h) * P, (int64_t)H * P, len - s0, acc, As, Bs);
     float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -364,18 +372,42 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
   }
   const T* cbj = cb + ((int64_t)j * G + g) * L * L;
   float acc[4][4] = {};
-  gemm_tile<false>(s0, len,
-      [&](int m, int l) { const int sx = s0 + m;
-        return (sx < len && l >= sx) ? ld(cbj + (int64_t)l * L + sx) * expf(av[l] - av[sx]) : 0.f; },
-      [&](int l, int n) { const int pp = p0 + n;
-        return pp < P ? ld(dy + ((t0 + l) * H + h) * P + pp) : 0.f; },
-      acc, As, Bs);
-  gemm_tile<true, true>(0, N,
-      [&](int m, int n) { const int sx = s0 + m;
-        return sx < len ? es[sx] * ld(B + ((t0 + sx) * G + g) * N + n) : 0.f; },
-      [&](int n, int c) { const int pp = p0 + c;
-        return pp < P ? dS[(jh * P + pp) * N + n] : 0.f; },
-      acc, As, Bs);
+  // sum_{l >= s} CB[l,s] exp(a_l - a_s) dy_l: slices of 32 tokens l, each a
+  // CB row (columns s) and a dy row (columns p) in 16-byte pieces
+  {
+    constexpr int V = 16 / sizeof(T), PC = 64 / V;   // pieces per 64-wide row
+    const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+    for (int kb = s0; kb < len; kb += 32) {
+      __syncthreads();                     // previous slice consumed (es, av staged)
+      for (int i = threadIdx.x; i < 32 * PC; i += kBwdThreads) {
+        const int kr = i / PC, c = (i - (i / PC) * PC) * V, l = kb + kr;
+        const bool lok = l < len;
+        float va[V], vb[V];
+        load16_f32<T>(cbj + (int64_t)l * L + s0 + c, lok, va);
+        load16_f32<T>(dy + ((t0 + l) * H + h) * P + p0 + c, lok && p0 + c < P, vb);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const int sx = s0 + c + e;
+          As[kr * kGemmPitch + c + e] = (lok && sx < len && l >= sx) ? va[e] * expf(av[l] - av[sx]) : 0.f;
+          Bs[kr * kGemmPitch + c + e] = vb[e];
+        }
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int k = 0; k < 32; ++k) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&As[k * kGemmPitch + tm]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&Bs[k * kGemmPitch + tn]);
+        const float avv[4] = {a4.x, a4.y, a4.z, a4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int jn = 0; jn < 4; ++jn) acc[i][jn] += avv[i] * bv[jn];
+      }
+    }
+  }
+  // + exp(a_last - a_s) B_s . dS_j[p, :]: rows s of B (scaled), rows p of dS
+  gemm_rows_tile<T, float, N>(B + ((t0 + s0) * G + g) * N, (int64_t)G * N, len - s0, es + s0,
+                              dS + (jh * P + p0) * N, N, P - p0, acc, As, Bs);
   const float Dh = D ? D[h] : 0.f;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
 #pragma unroll
