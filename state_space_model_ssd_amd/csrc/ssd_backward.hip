@@ -119,10 +119,6 @@ __device__ __forceinline__ void gemm_tile(int k0, int k1, LA loadA, LB loadB, fl
   }
 }
 
-// As gemm_tile for A(m, k) = ascale[m] arow[m * astride + k] (ascale: LDS, or
-// null for 1) and B(k, n) = brow[n * bstride + k], k in [0, K): 64 rows of K
-// contiguous values each, rows at or past na, nb read as 0, staged with one
-// 16-byte load per row piece.  Same products, same order.
 template <typename T>
 __device__ __forceinline__ void load16_f32(const T* p, bool ok, float* v);
 template <>
@@ -138,33 +134,61 @@ __device__ __forceinline__ void load16_f32<bf16>(const bf16* p, bool ok, float* 
   for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(b[e]);
 }
 
-template <typename TA, typename TB, int K>
-__device__ __forceinline__ void gemm_rows_tile(const TA* arow, int64_t astride, int na,
-                                               const float* ascale, const TB* brow,
-                                               int64_t bstride, int nb, float (&acc)[4][4],
-                                               float* As, float* Bs) {
-  constexpr int VA = 16 / sizeof(TA), VB = 16 / sizeof(TB);
-  constexpr int KS = K < 32 ? K : 32;      // slice length
-  static_assert(K % KS == 0 && KS % VA == 0 && KS % VB == 0, "row length");
+// One KS-long slice (k in [kb, kb + KS)) of a 64-wide GEMM operand staged in
+// LDS as S[k * kGemmPitch + i], read from memory rows with 16-byte loads.
+// KCONTIG: element (i, k) is at p[i * stride + k] (a row per i, k
+// contiguous); otherwise at p[k * stride + i] (a row per k, i contiguous).
+// Elements with i >= ni or k >= k1 are 0 (a piece that straddles either
+// bound must still lie inside the buffer).  TRI keeps only k <= i + ioff
+// (1) or k >= i + ioff (2).  scale (LDS, or null for 1): each stored row is
+// multiplied by scale[row], row = i (KCONTIG) or k.
+template <typename T, bool KCONTIG, int KS, int TRI = 0>
+__device__ __forceinline__ void stage_slice(const T* p, int64_t stride, int ni, int kb, int k1,
+                                            const float* scale, float* S, int ioff = 0) {
+  constexpr int V = 16 / sizeof(T);
+  static_assert(KS % V == 0 && 64 % V == 0, "piece size");
+  auto keep = [&](int i, int k) {
+    return i < ni && k < k1 && (TRI == 0 || (TRI == 1 ? k <= i + ioff : k >= i + ioff));
+  };
+  if constexpr (KCONTIG) {
+    for (int t = threadIdx.x; t < 64 * (KS / V); t += kBwdThreads) {
+      const int r = t & 63, c = (t >> 6) * V;   // consecutive threads: consecutive rows
+      const bool ok = r < ni && kb + c < k1;
+      float v[V];
+      load16_f32<T>(p + r * stride + kb + c, ok, v);
+      const float sc = (scale && ok) ? scale[r] : 1.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        S[(c + e) * kGemmPitch + r] = keep(r, kb + c + e) ? (scale ? sc * v[e] : v[e]) : 0.f;
+    }
+  } else {
+    constexpr int PR = 64 / V;             // pieces per row
+    for (int t = threadIdx.x; t < KS * PR; t += kBwdThreads) {
+      const int kr = t / PR, c = (t - kr * PR) * V;
+      const bool ok = kb + kr < k1 && c < ni;
+      float v[V];
+      load16_f32<T>(p + (int64_t)(kb + kr) * stride + c, ok, v);
+      const float sc = (scale && ok) ? scale[kb + kr] : 1.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        S[kr * kGemmPitch + c + e] = keep(c + e, kb + kr) ? (scale ? sc * v[e] : v[e]) : 0.f;
+    }
+  }
+}
+
+// acc += A B over k in [k0, k1) for a 64 x 64 tile, both operands staged
+// per slice by stage_slice (A's i = m, B's i = n; TRI and ioff mask A).
+// Products and their order are those of gemm_tile.
+template <typename TA, bool AK, typename TB, bool BK, int KS = 32, int TRI = 0>
+__device__ __forceinline__ void gemm_staged(const TA* pa, int64_t sa, int na, const float* scale_a,
+                                            const TB* pb, int64_t sb, int nb, int k0, int k1,
+                                            float (&acc)[4][4], float* As, float* Bs, int ioff = 0) {
   const int tid = threadIdx.x;
   const int tm = (tid >> 4) * 4, tn = (tid & 15) * 4;
-  for (int kb = 0; kb < K; kb += KS) {
+  for (int kb = k0; kb < k1; kb += KS) {
     __syncthreads();                       // previous slice consumed (and the caller's staging done)
-    for (int i = tid; i < 64 * (KS / VA); i += kBwdThreads) {
-      const int r = i & 63, c = i >> 6;    // consecutive threads: consecutive rows
-      float v[VA];
-      load16_f32<TA>(arow + r * astride + kb + c * VA, r < na, v);
-      const float sc = ascale ? ascale[r] : 1.f;
-#pragma unroll
-      for (int e = 0; e < VA; ++e) As[(c * VA + e) * kGemmPitch + r] = ascale ? sc * v[e] : v[e];
-    }
-    for (int i = tid; i < 64 * (KS / VB); i += kBwdThreads) {
-      const int r = i & 63, c = i >> 6;
-      float v[VB];
-      load16_f32<TB>(brow + r * bstride + kb + c * VB, r < nb, v);
-#pragma unroll
-      for (int e = 0; e < VB; ++e) Bs[(c * VB + e) * kGemmPitch + r] = v[e];
-    }
+    stage_slice<TA, AK, KS, TRI>(pa, sa, na, kb, k1, scale_a, As, ioff);
+    stage_slice<TB, BK, KS>(pb, sb, nb, kb, k1, nullptr, Bs);
     __syncthreads();
 #pragma unroll 8
     for (int k = 0; k < KS; ++k) {
@@ -203,12 +227,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_tiled_kernel(
   for (int l = threadIdx.x; l < L; l += kBwdThreads) sc[l] = expf(dAcs[jh * L + l]);
   __syncthreads();
   float acc[4][4] = {};
-  gemm_tile<false>(0, max(cd.len, 0),
-      [&](int m, int l) { const int p = m0 + m;
-        return p < P ? sc[l] * ld(dy + ((int64_t)(cd.start + l) * H + h) * P + p) : 0.f; },
-      [&](int l, int n) { const int nn = n0 + n;
-        return nn < N ? ld(C + ((int64_t)(cd.start + l) * G + g) * N + nn) : 0.f; },
-      acc, As, Bs);
+  // rows l of dy (columns p, scaled by exp(a_l)) and of C (columns n)
+  gemm_staged<T, false, T, false>(dy + ((int64_t)cd.start * H + h) * P + m0, (int64_t)H * P, P - m0, sc,
+                                  C + ((int64_t)cd.start * G + g) * N + n0, (int64_t)G * N, N - n0, 0,
+                                  max(cd.len, 0), acc, As, Bs);
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -303,8 +325,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
       dls[threadIdx.x] = delta[jh * L + s0 + threadIdx.x];
     }
     float acc[4][4] = {};
-    gemm_rows_tile<T, T, P>(dy + ((t0 + l0) * H + h) * P, (int64_t)H * P, len - l0, nullptr,
-                            x + ((t0 + s0) * H + h) * P, (int64_t)H * P, len - s0, acc, As, Bs);
+    gemm_staged<T, true, T, true>(dy + ((t0 + l0) * H + h) * P, (int64_t)H * P, len - l0, nullptr,
+                                  x + ((t0 + s0) * H + h) * P, (int64_t)H * P, len - s0, 0, P, acc,
+                                  As, Bs);
     float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -406,8 +429,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
     }
   }
   // + exp(a_last - a_s) B_s . dS_j[p, :]: rows s of B (scaled), rows p of dS
-  gemm_rows_tile<T, float, N>(B + ((t0 + s0) * G + g) * N, (int64_t)G * N, len - s0, es + s0,
-                              dS + (jh * P + p0) * N, N, P - p0, acc, As, Bs);
+  gemm_staged<T, true, float, true, (N < 32 ? N : 32)>(B + ((t0 + s0) * G + g) * N, (int64_t)G * N,
+                                                       len - s0, es + s0, dS + (jh * P + p0) * N, N,
+                                                       P - p0, 0, N, acc, As, Bs);
   const float Dh = D ? D[h] : 0.f;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
 #pragma unroll
@@ -477,20 +501,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
     }
   };
   if (which == 0) {
-    gemm_tile<true, false, true>(0, P,
-        [&](int m, int p) { const int l = m0 + m;
-          return l < len ? sc[l] * ld(dy + ((t0 + l) * H + h) * P + p) : 0.f; },
-        [&](int p, int n) { const int nn = n0 + n;
-          return nn < N ? ld(states_in + (jh * P + p) * N + nn) : 0.f; },
-        acc, As, Bs);
+    // rows l of dy (scaled by exp(a_l)), rows p of the entering state
+    gemm_staged<T, true, T, false>(dy + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0, sc + m0,
+                                   states_in + jh * P * N + n0, N, N - n0, 0, P, acc, As, Bs);
     row_dot(C, interpart);
   } else {
-    gemm_tile<true, false, true>(0, P,
-        [&](int m, int p) { const int sx = m0 + m;
-          return sx < len ? sc[sx] * ld(x + ((t0 + sx) * H + h) * P + p) : 0.f; },
-        [&](int p, int n) { const int nn = n0 + n;
-          return nn < N ? dS[(jh * P + p) * N + nn] : 0.f; },
-        acc, As, Bs);
+    // rows s of x (scaled by exp(a_last - a_s)), rows p of dS_j
+    gemm_staged<T, true, float, false>(x + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0, sc + m0,
+                                       dS + jh * P * N + n0, N, N - n0, 0, P, acc, As, Bs);
     row_dot(B, vxpart);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -554,19 +572,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_group_kernel(
   const float* W = dcbp + ((int64_t)j * G + g) * HB * L * L;   // the summed slot
   float acc[4][4] = {};
   if (which == 0) {                        // dC rows m0..m0+63: s runs to the tile's last row
-    gemm_tile<true, false, true>(0, min(len, m0 + 64),
-        [&](int m, int sx) { const int l = m0 + m;
-          return (l < len && sx <= l) ? W[(int64_t)l * L + sx] : 0.f; },
-        [&](int sx, int n) { const int nn = n0 + n;
-          return nn < N ? ld(B + ((t0 + sx) * G + g) * N + nn) : 0.f; },
-        acc, As, Bs);
+    // rows l of the summed dCB (columns s <= l), rows s of B
+    gemm_staged<float, true, T, false, 32, 1>(W + (int64_t)m0 * L, L, len - m0, nullptr,
+                                              B + (t0 * G + g) * N + n0, (int64_t)G * N, N - n0, 0,
+                                              min(len, m0 + 64), acc, As, Bs, m0);
   } else {                                 // dB rows m0..m0+63: l runs from the tile's first row
-    gemm_tile<false, false, true>(m0, len,
-        [&](int m, int l) { const int sx = m0 + m;
-          return (sx < len && l >= sx) ? W[(int64_t)l * L + sx] : 0.f; },
-        [&](int l, int n) { const int nn = n0 + n;
-          return nn < N ? ld(C + ((t0 + l) * G + g) * N + nn) : 0.f; },
-        acc, As, Bs);
+    // rows l of the summed dCB (columns s <= l), rows l of C
+    gemm_staged<float, false, T, false, 32, 2>(W + m0, L, len - m0, nullptr,
+                                               C + (t0 * G + g) * N + n0, (int64_t)G * N, N - n0, m0,
+                                               len, acc, As, Bs, m0);
   }
   // the heads' state terms: per head, the tile's 16 values of this thread
   // are independent loads (rows past the chunk read row 0 and are dropped)
