@@ -203,6 +203,63 @@ __device__ __forceinline__ void gemm_staged(const TA* pa, int64_t sa, int na, co
   }
 }
 
+// acc[i][jn] = sum_k arow[(tm + i) * astride + k] brow[(tn + jn) * bstride + k]
+// over k < K for bf16 rows on MFMA: the products are exact in fp32, as in
+// the vector tiles, and only the order of the fp32 sums differs.  Rows at
+// or past na (nb) read as 0.  Each wave computes a 32 x 32 quarter from
+// 16-byte loads; the tile passes through LDS (rows 0-31 in lo, 32-63 in hi,
+// pitch kGemmPitch) into the 4 x 4 block of the thread.  Ends with a
+// barrier; the caller keeps lo and hi unread before the call.
+template <int K>
+__device__ __forceinline__ void mfma_rows_tile(const bf16* arow, int64_t astride, int na,
+                                               const bf16* brow, int64_t bstride, int nb,
+                                               float (&acc)[4][4], float* lo, float* hi) {
+  using M = Mfma<bf16>;
+  static_assert(K % M::K == 0, "row length");
+  const int w = wave_id(), lane = threadIdx.x & (kWave - 1);
+  const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+  const int lr = lane & 15, kq = (lane >> 4) * M::KPL;
+  f32x4 d[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) d[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += M::K) {
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int r = wr + mi * 16 + lr;
+      a[mi] = __builtin_bit_cast(bf16x8, load16(arow + r * astride + k0 + kq, r < na));
+    }
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int c = wc + ni * 16 + lr;
+      b[ni] = __builtin_bit_cast(bf16x8, load16(brow + c * bstride + k0 + kq, c < nb));
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) d[mi][ni] = M::mma(a[mi], b[ni], d[mi][ni]);
+  }
+  float* dst = wr == 0 ? lo : hi;          // wave-uniform
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dst[(mi * 16 + (lane >> 4) * 4 + r) * kGemmPitch + wc + ni * 16 + lr] = d[mi][ni][r];
+  __syncthreads();
+  const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+  const float* src = tm < 32 ? lo : hi;    // wave-uniform
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = *reinterpret_cast<const float4*>(&src[((tm + i) & 31) * kGemmPitch + tn]);
+    acc[i][0] = v.x; acc[i][1] = v.y; acc[i][2] = v.z; acc[i][3] = v.w;
+  }
+}
+
 // Sum of v over the 16 threads that share a row of the 4 x 4 blocks (lanes
 // differing in their low 4 bits); every one of them gets it.
 __device__ __forceinline__ float row16_sum(float v) {
@@ -325,9 +382,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
       dls[threadIdx.x] = delta[jh * L + s0 + threadIdx.x];
     }
     float acc[4][4] = {};
-    gemm_staged<T, true, T, true>(dy + ((t0 + l0) * H + h) * P, (int64_t)H * P, len - l0, nullptr,
-                                  x + ((t0 + s0) * H + h) * P, (int64_t)H * P, len - s0, 0, P, acc,
-                                  As, Bs);
+    if constexpr (sizeof(T) == 2)          // dy_l . x_s: bf16 rows, exact products on MFMA
+      mfma_rows_tile<P>(dy + ((t0 + l0) * H + h) * P, (int64_t)H * P, len - l0,
+                        x + ((t0 + s0) * H + h) * P, (int64_t)H * P, len - s0, acc, As, Bs);
+    else
+      gemm_staged<T, true, T, true>(dy + ((t0 + l0) * H + h) * P, (int64_t)H * P, len - l0, nullptr,
+                                    x + ((t0 + s0) * H + h) * P, (int64_t)H * P, len - s0, 0, P, acc,
+                                    As, Bs);
     float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
