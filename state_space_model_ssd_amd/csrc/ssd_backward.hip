@@ -203,53 +203,59 @@ __device__ __forceinline__ void gemm_staged(const TA* pa, int64_t sa, int na, co
   }
 }
 
-// acc[i][jn] = sum_k arow[(tm + i) * astride + k] brow[(tn + jn) * bstride + k]
-// over k < K for bf16 rows on MFMA: the products are exact in fp32, as in
-// the vector tiles, and only the order of the fp32 sums differs.  Rows at
-// or past na (nb) read as 0.  Each wave computes a 32 x 32 quarter from
-// 16-byte loads; the tile passes through LDS (rows 0-31 in lo, 32-63 in hi,
-// pitch kGemmPitch) into the 4 x 4 block of the thread.  Ends with a
-// barrier; the caller keeps lo and hi unread before the call.
-template <int K>
-__device__ __forceinline__ void mfma_rows_tile(const bf16* arow, int64_t astride, int na,
-                                               const bf16* brow, int64_t bstride, int nb,
-                                               float (&acc)[4][4], float* lo, float* hi) {
-  using M = Mfma<bf16>;
-  static_assert(K % M::K == 0, "row length");
-  const int w = wave_id(), lane = threadIdx.x & (kWave - 1);
-  const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
-  const int lr = lane & 15, kq = (lane >> 4) * M::KPL;
-  f32x4 d[2][2];
+// bf16 MFMA tiles (16x16x32, fp32 sums) for 64 x 64 outputs: each of the 4
+// waves computes a 32 x 32 quarter d[mi][ni] (rows wr + 16 mi + 4 (lane/16)
+// + r, columns wc + 16 ni + lane%16); quarter_to_thread then moves the tile
+// through LDS into the 4 x 4 block of the vector epilogues.
+struct MfmaQuarter {
+  int lane, wr, wc, lr, kq;
+  __device__ __forceinline__ MfmaQuarter() {
+    const int w = wave_id();
+    lane = threadIdx.x & (kWave - 1);
+    wr = (w >> 1) * 32;
+    wc = (w & 1) * 32;
+    lr = lane & 15;
+    kq = (lane >> 4) * 8;
+  }
+  // row (column) of d[mi][ni][r] within the tile
+  __device__ __forceinline__ int row(int mi, int r) const { return wr + mi * 16 + (lane >> 4) * 4 + r; }
+  __device__ __forceinline__ int col(int ni) const { return wc + ni * 16 + lr; }
+};
+
+__device__ __forceinline__ void zero_quarter(f32x4 (&d)[2][2]) {
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) d[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int k0 = 0; k0 < K; k0 += M::K) {
-    bf16x8 a[2], b[2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int r = wr + mi * 16 + lr;
-      a[mi] = __builtin_bit_cast(bf16x8, load16(arow + r * astride + k0 + kq, r < na));
-    }
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int c = wc + ni * 16 + lr;
-      b[ni] = __builtin_bit_cast(bf16x8, load16(brow + c * bstride + k0 + kq, c < nb));
-    }
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) d[mi][ni] = M::mma(a[mi], b[ni], d[mi][ni]);
-  }
-  float* dst = wr == 0 ? lo : hi;          // wave-uniform
+}
+
+// 8 consecutive values of an fp32 row as a bf16 operand (rounded once).
+__device__ __forceinline__ bf16x8 frag_f32(const float* p, bool ok) {
+  float v[8];
+  const float4 a = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 b = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  return Mfma<bf16>::pack(v);
+}
+__device__ __forceinline__ bf16x8 frag_row(const bf16* p, bool ok) {
+  return __builtin_bit_cast(bf16x8, load16(p, ok));
+}
+__device__ __forceinline__ bf16x8 frag_row(const float* p, bool ok) { return frag_f32(p, ok); }
+
+// The quarters of the waves into acc[i][jn] (tile row tm + i, column tn + jn)
+// through LDS: rows 0-31 in lo, 32-63 in hi (32 x kGemmPitch floats each).
+// Begins and ends with a barrier.
+__device__ __forceinline__ void quarter_to_thread(const MfmaQuarter& q, const f32x4 (&d)[2][2],
+                                                  float (&acc)[4][4], float* lo, float* hi) {
+  __syncthreads();                         // lo and hi free
+  float* dst = q.wr == 0 ? lo : hi;        // wave-uniform
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        dst[(mi * 16 + (lane >> 4) * 4 + r) * kGemmPitch + wc + ni * 16 + lr] = d[mi][ni][r];
+        dst[(q.row(mi, r) & 31) * kGemmPitch + q.col(ni)] = d[mi][ni][r];
   __syncthreads();
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
   const float* src = tm < 32 ? lo : hi;    // wave-uniform
@@ -257,6 +263,76 @@ __device__ __forceinline__ void mfma_rows_tile(const bf16* arow, int64_t astride
   for (int i = 0; i < 4; ++i) {
     const float4 v = *reinterpret_cast<const float4*>(&src[((tm + i) & 31) * kGemmPitch + tn]);
     acc[i][0] = v.x; acc[i][1] = v.y; acc[i][2] = v.z; acc[i][3] = v.w;
+  }
+}
+
+// d += A B^T over k < K, A(m, k) = arow[m * astride + k] (bf16 rows) and
+// B^T(n, k) = brow[n * bstride + k] (bf16 or fp32 rows, fp32 rounded once to
+// bf16), both from 16-byte loads; rows at or past na (nb) read as 0.
+template <int K, typename TB>
+__device__ __forceinline__ void mfma_rows(const MfmaQuarter& q, const bf16* arow, int64_t astride,
+                                          int na, const TB* brow, int64_t bstride, int nb,
+                                          f32x4 (&d)[2][2]) {
+  using M = Mfma<bf16>;
+  static_assert(K % M::K == 0, "row length");
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += M::K) {
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int r = q.wr + mi * 16 + q.lr;
+      a[mi] = frag_row(arow + r * astride + k0 + q.kq, r < na);
+    }
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int c = q.wc + ni * 16 + q.lr;
+      b[ni] = frag_row(brow + c * bstride + k0 + q.kq, c < nb);
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) d[mi][ni] = M::mma(a[mi], b[ni], d[mi][ni]);
+  }
+}
+
+// d += A B over the 32-long k-slice held in LDS as k-major bf16 tiles
+// at[k * kKtPitch + m] and bt[k * kKtPitch + n] (read by transpose reads).
+constexpr int kKtPitch = 80;               // 160-byte rows: a transpose read's 16 lanes hit distinct banks
+__device__ __forceinline__ void mfma_kmajor(const MfmaQuarter& q, const bf16* at, const bf16* bt,
+                                            f32x4 (&d)[2][2]) {
+  using M = Mfma<bf16>;
+  bf16x8 a[2], b[2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) a[mi] = lds_operand_kmajor(at, kKtPitch, 0, q.wr + mi * 16, q.lane);
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) b[ni] = lds_operand_kmajor(bt, kKtPitch, 0, q.wc + ni * 16, q.lane);
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) d[mi][ni] = M::mma(a[mi], b[ni], d[mi][ni]);
+}
+
+// d += A B with A^T(m, k) = arow rows as in mfma_rows and B(k, n) from the
+// k-major bf16 LDS tile bt[k * kKtPitch + n], k < K.
+template <int K>
+__device__ __forceinline__ void mfma_rows_kmajor(const MfmaQuarter& q, const bf16* arow,
+                                                 int64_t astride, int na, const bf16* bt,
+                                                 f32x4 (&d)[2][2]) {
+  using M = Mfma<bf16>;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += M::K) {
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int r = q.wr + mi * 16 + q.lr;
+      a[mi] = frag_row(arow + r * astride + k0 + q.kq, r < na);
+    }
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) b[ni] = lds_operand_kmajor(bt, kKtPitch, k0, q.wc + ni * 16, q.lane);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) d[mi][ni] = M::mma(a[mi], b[ni], d[mi][ni]);
   }
 }
 
@@ -283,19 +359,54 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_tiled_kernel(
   const int64_t jh = (int64_t)j * H + h;
   for (int l = threadIdx.x; l < L; l += kBwdThreads) sc[l] = expf(dAcs[jh * L + l]);
   __syncthreads();
-  float acc[4][4] = {};
-  // rows l of dy (columns p, scaled by exp(a_l)) and of C (columns n)
-  gemm_staged<T, false, T, false>(dy + ((int64_t)cd.start * H + h) * P + m0, (int64_t)H * P, P - m0, sc,
-                                  C + ((int64_t)cd.start * G + g) * N + n0, (int64_t)G * N, N - n0, 0,
-                                  max(cd.len, 0), acc, As, Bs);
-  const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+  if constexpr (sizeof(T) == 2) {
+    // bf16 MFMA over slices of 32 tokens l: exp(a_l) dy_l (rounded once) and
+    // C_l staged k-major in LDS
+    __shared__ __align__(16) bf16 yt[32 * kKtPitch], ct[32 * kKtPitch];
+    static_assert(32 * 8 == kBwdThreads, "one 8-wide piece of each slice tile per thread");
+    const MfmaQuarter q;
+    f32x4 d[2][2];
+    zero_quarter(d);
+    const int len = max(cd.len, 0), kr = threadIdx.x >> 3, c = (threadIdx.x & 7) * 8;
+    for (int kb = 0; kb < len; kb += 32) {
+      const int l = kb + kr;
+      const bool lok = l < len;
+      const bf16x8 yv = frag_row(dy + ((int64_t)(cd.start + l) * H + h) * P + m0 + c, lok && m0 + c < P);
+      const bf16x8 cv = frag_row(C + ((int64_t)(cd.start + l) * G + g) * N + n0 + c, lok && n0 + c < N);
+      const float f = lok ? sc[l] : 0.f;
+      float v[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
-      const int p = m0 + tm + i, n = n0 + tn + jn;
-      if (p < P && n < N) Q[(jh * P + p) * N + n] = acc[i][jn];
+      for (int e = 0; e < 8; ++e) v[e] = f * static_cast<float>(yv[e]);
+      __syncthreads();                     // previous slice consumed
+      *reinterpret_cast<bf16x8*>(&yt[kr * kKtPitch + c]) = Mfma<bf16>::pack(v);
+      *reinterpret_cast<bf16x8*>(&ct[kr * kKtPitch + c]) = cv;
+      __syncthreads();
+      mfma_kmajor(q, yt, ct, d);
     }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int p = m0 + q.row(mi, r), n = n0 + q.col(ni);
+          if (p < P && n < N) Q[(jh * P + p) * N + n] = d[mi][ni][r];
+        }
+  } else {
+    float acc[4][4] = {};
+    // rows l of dy (columns p, scaled by exp(a_l)) and of C (columns n)
+    gemm_staged<T, false, T, false>(dy + ((int64_t)cd.start * H + h) * P + m0, (int64_t)H * P, P - m0, sc,
+                                    C + ((int64_t)cd.start * G + g) * N + n0, (int64_t)G * N, N - n0, 0,
+                                    max(cd.len, 0), acc, As, Bs);
+    const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) {
+        const int p = m0 + tm + i, n = n0 + tn + jn;
+        if (p < P && n < N) Q[(jh * P + p) * N + n] = acc[i][jn];
+      }
+  }
 }
 
 // 2. Reverse chain; grid (ceil(P*N / 256), H, nstates).
@@ -382,10 +493,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
       dls[threadIdx.x] = delta[jh * L + s0 + threadIdx.x];
     }
     float acc[4][4] = {};
-    if constexpr (sizeof(T) == 2)          // dy_l . x_s: bf16 rows, exact products on MFMA
-      mfma_rows_tile<P>(dy + ((t0 + l0) * H + h) * P, (int64_t)H * P, len - l0,
-                        x + ((t0 + s0) * H + h) * P, (int64_t)H * P, len - s0, acc, As, Bs);
-    else
+    if constexpr (sizeof(T) == 2) {        // dy_l . x_s: bf16 rows, exact products on MFMA
+      const MfmaQuarter q;
+      f32x4 d[2][2];
+      zero_quarter(d);
+      mfma_rows<P>(q, dy + ((t0 + l0) * H + h) * P, (int64_t)H * P, len - l0,
+                   x + ((t0 + s0) * H + h) * P, (int64_t)H * P, len - s0, d);
+      quarter_to_thread(q, d, acc, As, Bs);
+    } else
       gemm_staged<T, true, T, true>(dy + ((t0 + l0) * H + h) * P, (int64_t)H * P, len - l0, nullptr,
                                     x + ((t0 + s0) * H + h) * P, (int64_t)H * P, len - s0, 0, P, acc,
                                     As, Bs);
@@ -456,6 +571,49 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
   }
   const T* cbj = cb + ((int64_t)j * G + g) * L * L;
   float acc[4][4] = {};
+  if constexpr (sizeof(T) == 2) {
+    // bf16 MFMA.  exp(a_last - a_s) B_s . dS_j[p, :] first (B rows exact,
+    // dS rounded once to bf16), times its row factor; then the slices of 32
+    // tokens l of sum_{l >= s} CB[l,s] exp(a_l - a_s) dy_l, the decay-masked
+    // CB (rounded once) and dy staged k-major in LDS (in As and Bs).
+    static_assert(32 * kKtPitch * sizeof(bf16) <= 32 * kGemmPitch * sizeof(float), "slice tiles");
+    bf16* mt = reinterpret_cast<bf16*>(As);
+    bf16* yt = reinterpret_cast<bf16*>(Bs);
+    const MfmaQuarter q;
+    f32x4 d[2][2];
+    zero_quarter(d);
+    mfma_rows<N>(q, B + ((t0 + s0) * G + g) * N, (int64_t)G * N, len - s0, dS + (jh * P + p0) * N, N,
+                 P - p0, d);
+    __syncthreads();                       // es, av staged
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = es[s0 + q.row(mi, r)];
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) d[mi][ni][r] *= f;
+      }
+    static_assert(32 * 8 == kBwdThreads, "one 8-wide piece of each slice tile per thread");
+    const int kr = threadIdx.x >> 3, c = (threadIdx.x & 7) * 8;
+    for (int kb = s0; kb < len; kb += 32) {
+      const int l = kb + kr;
+      const bool lok = l < len;
+      const bf16x8 cv = frag_row(cbj + (int64_t)l * L + s0 + c, lok);
+      const bf16x8 yv = frag_row(dy + ((t0 + l) * H + h) * P + p0 + c, lok && p0 + c < P);
+      float mv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sx = s0 + c + e;
+        mv[e] = (lok && l >= sx) ? static_cast<float>(cv[e]) * expf(av[l] - av[sx]) : 0.f;
+      }
+      __syncthreads();                     // previous slice consumed
+      *reinterpret_cast<bf16x8*>(&mt[kr * kKtPitch + c]) = Mfma<bf16>::pack(mv);
+      *reinterpret_cast<bf16x8*>(&yt[kr * kKtPitch + c]) = yv;
+      __syncthreads();
+      mfma_kmajor(q, mt, yt, d);
+    }
+    quarter_to_thread(q, d, acc, As, Bs);
+  } else {
   // sum_{l >= s} CB[l,s] exp(a_l - a_s) dy_l: slices of 32 tokens l, each a
   // CB row (columns s) and a dy row (columns p) in 16-byte pieces
   {
@@ -493,6 +651,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
   gemm_staged<T, true, float, true, (N < 32 ? N : 32)>(B + ((t0 + s0) * G + g) * N, (int64_t)G * N,
                                                        len - s0, es + s0, dS + (jh * P + p0) * N, N,
                                                        P - p0, 0, N, acc, As, Bs);
+  }
   const float Dh = D ? D[h] : 0.f;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
 #pragma unroll
@@ -561,15 +720,43 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
       if ((threadIdx.x & 15) == 0 && r < L) part[(jh * NT + nt) * L + r] = v;
     }
   };
-  if (which == 0) {
+  if constexpr (sizeof(T) == 2) {
+    // bf16 MFMA: rows of dy (dC) or x (dB) times the entering state (bf16)
+    // or dS_j (rounded once to bf16), staged k-major (rows p) in LDS; the
+    // row factor exp(a_l) or exp(a_last - a_s) multiplies the product.
+    __shared__ __align__(16) bf16 kt[P * kKtPitch];
+    for (int i = threadIdx.x; i < P * 8; i += kBwdThreads) {
+      const int r = i >> 3, c = (i & 7) * 8;
+      const bool ok = n0 + c < N;
+      const bf16x8 v = which == 0 ? frag_row(states_in + (jh * P + r) * N + n0 + c, ok)
+                                  : frag_f32(dS + (jh * P + r) * N + n0 + c, ok);
+      *reinterpret_cast<bf16x8*>(&kt[r * kKtPitch + c]) = v;
+    }
+    __syncthreads();
+    const MfmaQuarter q;
+    f32x4 d[2][2];
+    zero_quarter(d);
+    mfma_rows_kmajor<P>(q, (which == 0 ? dy : x) + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0,
+                        kt, d);
+    quarter_to_thread(q, d, acc, As, Bs);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f = sc[m0 + tm + i];
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) acc[i][jn] *= f;
+    }
+  } else if (which == 0) {
     // rows l of dy (scaled by exp(a_l)), rows p of the entering state
     gemm_staged<T, true, T, false>(dy + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0, sc + m0,
                                    states_in + jh * P * N + n0, N, N - n0, 0, P, acc, As, Bs);
-    row_dot(C, interpart);
   } else {
     // rows s of x (scaled by exp(a_last - a_s)), rows p of dS_j
     gemm_staged<T, true, float, false>(x + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0, sc + m0,
                                        dS + jh * P * N + n0, N, N - n0, 0, P, acc, As, Bs);
+  }
+  if (which == 0) {
+    row_dot(C, interpart);
+  } else {
     row_dot(B, vxpart);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
