@@ -670,41 +670,83 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
   }
 }
 
-// 4a. The per-head state terms of dC and dB as 64 x 64 tiles of rows x n:
-//   dC_h = diag(exp(a)) dy H,   dB_h = diag(delta exp(a_last - a)) x dS_j.
-// Between the product and its store each tile takes a partial row dot
-// product for the per-token pass:
+// 4a. The state terms of dC and dB as 64 x 64 tiles of rows x n, per head
+//   dC_h = diag(exp(a)) dy H,   dB_h = diag(delta exp(a_last - a)) x dS_j,
+// summed over a block of the group's heads (HB blocks per group, as in 3a):
+// only the group's sum enters dB and dC.  Between each head's product and
+// the sum, a partial row dot product for the per-token pass:
 //   interpart[nt][l] = sum_n C[l,n] exp(a_l) (dy_l H)[n],
 //   vxpart[nt][s]    = sum_n B[s,n] exp(a_last - a_s) (x_s dS_j)[n]
-// over its 64 columns n.  grid (L/64 * ceil(N/64) * 2, H, chunk slots);
-// even x: dC, odd: dB.
+// over the tile's 64 columns n.  Block hb of group g writes its sum to
+// slot (j, g, hb) of dBh / dCh.  grid (L/64 * ceil(N/64) * 2, G * HB, chunk
+// slots); even x: dC, odd: dB.
 template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
     ChunkMap cm, const T* __restrict__ x, const T* __restrict__ B, const T* __restrict__ C,
     const T* __restrict__ dy, const float* __restrict__ delta, const float* __restrict__ dAcs,
-    const T* __restrict__ states_in, const float* __restrict__ dS, int H, int G,
+    const T* __restrict__ states_in, const float* __restrict__ dS, int H, int G, int HB,
     float* __restrict__ dBh, float* __restrict__ dCh, float* __restrict__ interpart,
     float* __restrict__ vxpart) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
-  __shared__ float sc[L], ds[L];
+  __shared__ float sc[64], ds[64];         // the head's row factors and steps
   constexpr int NT = (N + 63) / 64;
   const int which = blockIdx.x & 1, t = blockIdx.x >> 1;
   const int m0 = (t / NT) * 64, nt = t % NT, n0 = nt * 64;
-  const int h = blockIdx.y, j = blockIdx.z, g = h / (H / G);
+  const int g = blockIdx.y / HB, hb = blockIdx.y - (blockIdx.y / HB) * HB, j = blockIdx.z;
+  const int hpg = H / G, h0 = g * hpg + hb * hpg / HB, h1 = g * hpg + (hb + 1) * hpg / HB;
   const ChunkDesc cd = cm.desc(j);
   const int len = max(cd.len, 0);
   if (m0 >= len) return;                   // uniform: rows past the chunk
-  const int64_t jh = (int64_t)j * H + h;
-  const float* a = dAcs + jh * L;
-  const float alast = a[len - 1];
-  for (int l = threadIdx.x; l < L; l += kBwdThreads) {
-    sc[l] = which == 0 ? expf(a[l]) : expf(alast - a[l]);
-    ds[l] = delta[jh * L + l];
-  }
   const int64_t t0 = cd.start;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
-  float acc[4][4] = {};
-  auto row_dot = [&](const T* M, float* part) {   // sum_n M[row, n] acc[row, n] over the tile
+  const T* M = which == 0 ? C : B;         // the row dot's group rows
+  float tot[4][4] = {};
+  for (int h = h0; h < h1; ++h) {
+    const int64_t jh = (int64_t)j * H + h;
+    __syncthreads();                       // the previous head's sc, ds and LDS tiles consumed
+    if (threadIdx.x < 64) {
+      const float* a = dAcs + jh * L;
+      const int r = m0 + threadIdx.x;
+      sc[threadIdx.x] = which == 0 ? expf(a[r]) : expf(a[len - 1] - a[r]);
+      ds[threadIdx.x] = delta[jh * L + r];
+    }
+    float acc[4][4] = {};
+    if constexpr (sizeof(T) == 2) {
+      // bf16 MFMA: rows of dy (dC) or x (dB) times the entering state (bf16)
+      // or dS_j (rounded once to bf16), staged k-major (rows p) in LDS; the
+      // row factor exp(a_l) or exp(a_last - a_s) multiplies the product.
+      __shared__ __align__(16) bf16 kt[P * kKtPitch];
+      for (int i = threadIdx.x; i < P * 8; i += kBwdThreads) {
+        const int r = i >> 3, c = (i & 7) * 8;
+        const bool ok = n0 + c < N;
+        const bf16x8 v = which == 0 ? frag_row(states_in + (jh * P + r) * N + n0 + c, ok)
+                                    : frag_f32(dS + (jh * P + r) * N + n0 + c, ok);
+        *reinterpret_cast<bf16x8*>(&kt[r * kKtPitch + c]) = v;
+      }
+      __syncthreads();
+      const MfmaQuarter q;
+      f32x4 d[2][2];
+      zero_quarter(d);
+      mfma_rows_kmajor<P>(q, (which == 0 ? dy : x) + ((t0 + m0) * H + h) * P, (int64_t)H * P,
+                          len - m0, kt, d);
+      quarter_to_thread(q, d, acc, As, Bs);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = sc[tm + i];
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) acc[i][jn] *= f;
+      }
+    } else if (which == 0) {
+      // rows l of dy (scaled by exp(a_l)), rows p of the entering state
+      gemm_staged<T, true, T, false>(dy + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0, sc,
+                                     states_in + jh * P * N + n0, N, N - n0, 0, P, acc, As, Bs);
+    } else {
+      // rows s of x (scaled by exp(a_last - a_s)), rows p of dS_j
+      gemm_staged<T, true, float, false>(x + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0, sc,
+                                         dS + jh * P * N + n0, N, N - n0, 0, P, acc, As, Bs);
+    }
+    // sum_n M[row, n] acc[row, n] over the tile
+    float* part = which == 0 ? interpart : vxpart;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = m0 + tm + i;
@@ -717,62 +759,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
         }
       }
       v = row16_sum(v);
-      if ((threadIdx.x & 15) == 0 && r < L) part[(jh * NT + nt) * L + r] = v;
+      if ((threadIdx.x & 15) == 0) part[(jh * NT + nt) * L + r] = v;
     }
-  };
-  if constexpr (sizeof(T) == 2) {
-    // bf16 MFMA: rows of dy (dC) or x (dB) times the entering state (bf16)
-    // or dS_j (rounded once to bf16), staged k-major (rows p) in LDS; the
-    // row factor exp(a_l) or exp(a_last - a_s) multiplies the product.
-    __shared__ __align__(16) bf16 kt[P * kKtPitch];
-    for (int i = threadIdx.x; i < P * 8; i += kBwdThreads) {
-      const int r = i >> 3, c = (i & 7) * 8;
-      const bool ok = n0 + c < N;
-      const bf16x8 v = which == 0 ? frag_row(states_in + (jh * P + r) * N + n0 + c, ok)
-                                  : frag_f32(dS + (jh * P + r) * N + n0 + c, ok);
-      *reinterpret_cast<bf16x8*>(&kt[r * kKtPitch + c]) = v;
-    }
-    __syncthreads();
-    const MfmaQuarter q;
-    f32x4 d[2][2];
-    zero_quarter(d);
-    mfma_rows_kmajor<P>(q, (which == 0 ? dy : x) + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0,
-                        kt, d);
-    quarter_to_thread(q, d, acc, As, Bs);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float f = sc[m0 + tm + i];
+      const float f = which == 0 ? 1.f : ds[tm + i];
 #pragma unroll
-      for (int jn = 0; jn < 4; ++jn) acc[i][jn] *= f;
-    }
-  } else if (which == 0) {
-    // rows l of dy (scaled by exp(a_l)), rows p of the entering state
-    gemm_staged<T, true, T, false>(dy + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0, sc + m0,
-                                   states_in + jh * P * N + n0, N, N - n0, 0, P, acc, As, Bs);
-  } else {
-    // rows s of x (scaled by exp(a_last - a_s)), rows p of dS_j
-    gemm_staged<T, true, float, false>(x + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0, sc + m0,
-                                       dS + jh * P * N + n0, N, N - n0, 0, P, acc, As, Bs);
-  }
-  if (which == 0) {
-    row_dot(C, interpart);
-  } else {
-    row_dot(B, vxpart);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sx = m0 + tm + i;
-      const float f = sx < L ? ds[sx] : 0.f;
-#pragma unroll
-      for (int jn = 0; jn < 4; ++jn) acc[i][jn] *= f;
+      for (int jn = 0; jn < 4; ++jn) tot[i][jn] += f * acc[i][jn];
     }
   }
-  float* out = which == 0 ? dCh : dBh;
+  float* out = (which == 0 ? dCh : dBh) + (((int64_t)j * G + g) * HB + hb) * L * N;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) {
       const int r = m0 + tm + i, n = n0 + tn + jn;
-      if (r < len && n < N) out[(jh * L + r) * N + n] = acc[i][jn];
+      if (r < len && n < N) out[(int64_t)r * N + n] = tot[i][jn];
     }
 }
 
@@ -830,15 +832,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_group_kernel(
                                                C + (t0 * G + g) * N + n0, (int64_t)G * N, N - n0, m0,
                                                len, acc, As, Bs, m0);
   }
-  // the heads' state terms: per head, the tile's 16 values of this thread
-  // are independent loads (rows past the chunk read row 0 and are dropped)
+  // the state terms of the group's HB head blocks: per block, the tile's 16
+  // values of this thread are independent loads (rows past the chunk read
+  // row 0 and are dropped)
   const float* part = which == 0 ? dCh : dBh;
   T* out = which == 0 ? dC : dB;
-  const int hpg = H / G;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
 #pragma unroll 2
-  for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
-    const float* ph = part + ((int64_t)j * H + h) * L * N;
+  for (int b = 0; b < HB; ++b) {
+    const float* ph = part + (((int64_t)j * G + g) * HB + b) * L * N;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -976,13 +978,14 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   hipLaunchKernelGGL(bwd_chain_kernel, dim3((PN + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
                      dim3(kBwdThreads), 0, s, cm, b.Q, a.dAcs, b.dfinal, H, PN, L, b.dS, b.dinit);
   constexpr int LT = L / 64;
-  // head blocks per group for the summed dCB (their partial sums fit the
-  // workspace's H L^2 floats per chunk: G * HB <= H)
+  // head blocks per group for the summed dCB and dB/dC state terms (their
+  // partial sums fit the workspace's H L^2 and H L N floats per chunk:
+  // G * HB <= H)
   const int hpg = H / G, HB = hpg < kBwdHeadBlocks ? hpg : kBwdHeadBlocks;
   hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(LT * LT, G * HB, mc), dim3(kBwdThreads),
                      0, s, cm, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb, b.rowpart, b.colpart);
-  hipLaunchKernelGGL((bwd_bc_tiled_kernel<T, P, N, L>), dim3(LT * NT * 2, H, mc),
-                     dim3(kBwdThreads), 0, s, cm, x, B, C, dy, a.delta, a.dAcs, hin, b.dS, H, G,
+  hipLaunchKernelGGL((bwd_bc_tiled_kernel<T, P, N, L>), dim3(LT * NT * 2, G * HB, mc),
+                     dim3(kBwdThreads), 0, s, cm, x, B, C, dy, a.delta, a.dAcs, hin, b.dS, H, G, HB,
                      b.dBh, b.dCh, b.interpart, b.vxpart);
   if (HB > 1)
     hipLaunchKernelGGL((bwd_dcb_sum_kernel<L>), dim3((L * L / 4 + kBwdThreads - 1) / kBwdThreads, G, mc),

@@ -74,8 +74,8 @@ struct BwdArgs {
   float* colpart;           // [max_chunks][H][L/64][L]
   float* interpart;         // [max_chunks][H][ceil(N/64)][L]
   float* vxpart;            // [max_chunks][H][ceil(N/64)][L]
-  float* dBh;               // [max_chunks][H][L][N]
-  float* dCh;               // [max_chunks][H][L][N]
+  float* dBh;               // [max_chunks][G * head blocks <= H][L][N]
+  float* dCh;               // [max_chunks][G * head blocks <= H][L][N]
   float* dA_part;           // [max_chunks][H]
   float* dD_part;           // [max_chunks][H]
   float* dbias_part;        // [max_chunks][H]

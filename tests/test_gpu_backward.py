@@ -68,6 +68,9 @@ SHAPES = [
     (1, 520, 4, 64, 128, 2, 256, "bf16"),
     (1, 300, 2, 64, 128, 1, 128, "bf16"),
     (2, 100, 2, 64, 128, 1, 64, "bf16"),
+    # more heads per group than head blocks: blocks of one and two heads
+    (1, 300, 12, 32, 32, 1, 64, "bf16"),
+    (1, 200, 20, 32, 16, 2, 64, "f32"),
 ]
 
 
