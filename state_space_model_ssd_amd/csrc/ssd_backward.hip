@@ -41,9 +41,12 @@ namespace ssd {
 namespace {
 
 constexpr int kBwdThreads = 256;
-// Most blocks a group's heads are split into for the summed dCB (more blocks:
-// more workgroups in 3a, more partial sums read in 4b).
+// Most blocks a group's heads are split into for the summed dCB and the
+// dB/dC state terms.  More blocks: more workgroups in 3a and 4a, but more
+// partial sums written there and read in 3b' and 4b; the launcher takes the
+// fewest that give kBwdMinWgPerCu workgroups per CU.
 constexpr int kBwdHeadBlocks = 8;
+constexpr int kBwdMinWgPerCu = 2;
 
 template <typename T>
 __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
@@ -952,6 +955,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_head_reduce_kernel(
 
 }  // namespace
 
+// Head blocks per group: the fewest (at most hpg and kBwdHeadBlocks) for
+// which `wg_per_block` workgroups per block give kBwdMinWgPerCu workgroups
+// per CU of the current device (CU count cached per device).
+static int bwd_head_blocks(int hpg, int64_t wg_per_block) {
+  static int cus_cached[64] = {0};
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    if (cus_cached[dev] <= 0)
+      hipDeviceGetAttribute(&cus_cached[dev], hipDeviceAttributeMultiprocessorCount, dev);
+    cus = cus_cached[dev];
+  }
+  const int cap = hpg < kBwdHeadBlocks ? hpg : kBwdHeadBlocks;
+  if (cus <= 0) return cap;
+  int hb = 1;
+  while (hb < cap && wg_per_block * hb < (int64_t)kBwdMinWgPerCu * cus) ++hb;
+  return hb;
+}
+
 template <typename T, int P, int N, int L>
 hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   const int mc = a.max_chunks, H = a.H, G = a.G, PN = P * N;
@@ -978,10 +999,10 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   hipLaunchKernelGGL(bwd_chain_kernel, dim3((PN + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
                      dim3(kBwdThreads), 0, s, cm, b.Q, a.dAcs, b.dfinal, H, PN, L, b.dS, b.dinit);
   constexpr int LT = L / 64;
-  // head blocks per group for the summed dCB and dB/dC state terms (their
-  // partial sums fit the workspace's H L^2 and H L N floats per chunk:
-  // G * HB <= H)
-  const int hpg = H / G, HB = hpg < kBwdHeadBlocks ? hpg : kBwdHeadBlocks;
+  // head blocks per group for the summed dCB and dB/dC state terms: the
+  // fewest that fill the GPU with 3a's workgroups (their partial sums fit
+  // the workspace's H L^2 and H L N floats per chunk: G * HB <= H)
+  const int hpg = H / G, HB = bwd_head_blocks(hpg, (int64_t)(LT * (LT + 1) / 2) * G * mc);
   hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(LT * LT, G * HB, mc), dim3(kBwdThreads),
                      0, s, cm, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb, b.rowpart, b.colpart);
   hipLaunchKernelGGL((bwd_bc_tiled_kernel<T, P, N, L>), dim3(LT * NT * 2, G * HB, mc),

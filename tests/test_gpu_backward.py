@@ -94,6 +94,15 @@ def test_backward_packed(lens, L, dt):
     _grads_case(prob, Recipe(init_std=0.4), seed=len(lens))
 
 
+def test_backward_one_head_block_per_group():
+    # 64 sequences of 256 tokens in 64-token chunks: 512 workgroups per head
+    # block in the dCB launch, so on a GPU of up to 256 CUs each group's two
+    # heads are walked by one workgroup and no partial dCB sums are added
+    lens = (256,) * 64
+    prob = Problem(1, sum(lens), 4, 32, 32, 2, 64, "bf16", seq_lens=lens)
+    _grads_case(prob, Recipe(init_std=0.4), seed=11)
+
+
 def test_backward_without_optional_inputs():
     prob = Problem(1, 140, 2, 32, 16, 1, 64, "f32")
     inp_rec = Recipe()                      # no initial state
