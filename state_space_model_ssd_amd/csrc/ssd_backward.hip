@@ -32,8 +32,12 @@
 // Everything accumulates in fp32; dx, dB and dC are rounded once to x's
 // dtype.  Deterministic: fixed loop orders, no atomics.
 //
-// The contractions are 64 x 64 fp32 tiles on the vector ALUs, with operand
-// slices staged through LDS by element-wise loads (the operands stay in L2).
+// The contractions are 64 x 64 output tiles.  With bf16 inputs, 1, 3a, 3b
+// and 4a run on the bf16 MFMA: rows read with 16-byte loads, or k-major
+// slices staged in LDS as bf16 and read with the gfx950 transpose read; an
+// operand that is scaled or fp32 is rounded to bf16 once, and row factors
+// are applied to the product where they can be.  4b and the fp32 path use
+// fp32 tiles on the vector ALUs, staged through LDS with 16-byte loads.
 #include "ssd_kernels.h"
 
 namespace ssd {
