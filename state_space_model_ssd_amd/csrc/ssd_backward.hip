@@ -443,18 +443,73 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_pass_final_kernel(const float
   if (i < n) dinit[i] = dfinal ? dfinal[i] : 0.f;
 }
 
-// Sum over the workgroup (L threads, L a multiple of 64); every thread gets it.
+// Three sums over the workgroup (L threads, L a multiple of 64) at once;
+// every thread gets them.
 template <int L>
-__device__ __forceinline__ float block_sum(float v, float* red) {
+__device__ __forceinline__ float3 block_sum3(float3 v, float* red) {
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    v.x += __shfl_xor(v.x, off);
+    v.y += __shfl_xor(v.y, off);
+    v.z += __shfl_xor(v.z, off);
+  }
   __syncthreads();
-  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    red[3 * (threadIdx.x / kWave)] = v.x;
+    red[3 * (threadIdx.x / kWave) + 1] = v.y;
+    red[3 * (threadIdx.x / kWave) + 2] = v.z;
+  }
   __syncthreads();
-  float t = 0.f;
+  float3 t = make_float3(0.f, 0.f, 0.f);
 #pragma unroll
-  for (int w = 0; w < L / kWave; ++w) t += red[w];
+  for (int w = 0; w < L / kWave; ++w) {
+    t.x += red[3 * w];
+    t.y += red[3 * w + 1];
+    t.z += red[3 * w + 2];
+  }
   return t;
+}
+
+// Inclusive suffix sum over the workgroup (L threads): thread k gets the sum
+// of v over threads k .. L-1.  wred: L / kWave floats of LDS.
+template <int L>
+__device__ __forceinline__ float block_suffix_sum(float v, float* wred) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float u = __shfl_down(v, off);
+    if (lane + off < kWave) v += u;
+  }
+  __syncthreads();
+  if (lane == 0) wred[w] = v;              // the wave's total
+  __syncthreads();
+#pragma unroll
+  for (int w2 = L / kWave - 1; w2 > 0; --w2)
+    if (w2 > w) v += wred[w2];
+  return v;
+}
+
+// 16 bytes of T as fp32 values.
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& u, float* v);
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4& u, float* v) {
+  v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+  v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+}
+template <>
+__device__ __forceinline__ void unpack16<bf16>(const uint4& u, float* v) {
+  const bf16x8 b = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(b[e]);
+}
+
+// Four consecutive values of T as fp32 (8- or 16-byte load).
+__device__ __forceinline__ float4 load4_f32(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4_f32(const bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
 // 3a. For each head, V[l,s] = exp(a_l - a_s) (dy_l . x_s) for s <= l as
@@ -878,8 +933,8 @@ __global__ __launch_bounds__(L) void bwd_token_kernel(
     const float* __restrict__ interpart, const float* __restrict__ vxpart, int H, float dt_min,
     float dt_max, float* __restrict__ ddt, float* __restrict__ dA_part,
     float* __restrict__ dD_part, float* __restrict__ dbias_part) {
-  __shared__ float das[L];
-  __shared__ float red[L / kWave];
+  __shared__ float red[3 * (L / kWave)];
+  __shared__ float dds[L];                 // dy . x per token
   constexpr int LT = L / 64, NT = (N + 63) / 64;
   const int h = blockIdx.x, j = blockIdx.y, k = threadIdx.x;
   const ChunkDesc cd = cm.desc(j);
@@ -906,19 +961,49 @@ __global__ __launch_bounds__(L) void bwd_token_kernel(
       inter += interpart[(jh * NT + nt) * L + k];
       vxe += vxpart[(jh * NT + nt) * L + k];
     }
-    for (int p = 0; p < P; ++p) dd += ld(dy + (tk * H + h) * P + p) * ld(x + (tk * H + h) * P + p);
+  }
+  // dy_k . x_k per token: the PPR 16-byte pieces of a row are read by PPR
+  // consecutive lanes (coalesced rows), every load issued before use, and
+  // summed across those lanes
+  {
+    constexpr int V = 16 / sizeof(T), PPR = P / V, UB = PPR < 8 ? PPR : 8;
+    static_assert(P % V == 0 && kWave % PPR == 0, "row pieces");
+    for (int u0 = 0; u0 < PPR; u0 += UB) {
+      uint4 ry[UB], rx[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int i = k + L * (u0 + u), tok = i / PPR, pc = i % PPR;
+        const int64_t o = ((int64_t)(cd.start + tok) * H + h) * P + pc * V;
+        ry[u] = load16(dy + o, tok < len);
+        rx[u] = load16(x + o, tok < len);
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int i = k + L * (u0 + u), tok = i / PPR;
+        float vy[V], vx[V], part = 0.f;
+        unpack16<T>(ry[u], vy);
+        unpack16<T>(rx[u], vx);
+#pragma unroll
+        for (int e = 0; e < V; ++e) part += vy[e] * vx[e];
+#pragma unroll
+        for (int off = 1; off < PPR; off <<= 1) part += __shfl_xor(part, off);
+        if (i % PPR == 0) dds[tok] = part;
+      }
+    }
+    __syncthreads();
+    dd = valid ? dds[k] : 0.f;
   }
   const float vs = dk * vxe;
   float gh = 0.f;
-  for (int i = k; i < P * N; i += L) gh += dS[jh * P * N + i] * ld(states_in + jh * P * N + i);
-  gh = block_sum<L>(gh, red);
-  const float t1 = block_sum<L>(valid ? vs : 0.f, red);
+  static_assert((P * N) % (4 * L) == 0, "state elements per thread");
+  for (int i = 4 * k; i < P * N; i += 4 * L) {
+    const float4 u = load4_f32(dS + jh * P * N + i), w = load4_f32(states_in + jh * P * N + i);
+    gh += u.x * w.x + u.y * w.y + u.z * w.z + u.w * w.w;
+  }
+  const float3 gt = block_sum3<L>(make_float3(gh, valid ? vs : 0.f, 0.f), red);
   float da = valid ? rowsum - dk * sdir + inter - vs : 0.f;
-  if (k == len - 1) da += t1 + expf(alast) * gh;
-  das[k] = da;
-  __syncthreads();
-  float rc = 0.f;
-  for (int l = L - 1; l >= k; --l) rc += das[l];
+  if (k == len - 1) da += gt.y + expf(alast) * gt.x;
+  const float rc = block_suffix_sum<L>(da, red);
   const float ddelta = sdir + vxe + A[h] * rc;
   float dbias = 0.f;
   if (valid) {
@@ -929,13 +1014,11 @@ __global__ __launch_bounds__(L) void bwd_token_kernel(
     dbias = ddelta * sig * pass;
     ddt[tk * H + h] = dbias;
   }
-  const float da_sum = block_sum<L>(valid ? dk * rc : 0.f, red);
-  const float dd_sum = block_sum<L>(dd, red);
-  const float db_sum = block_sum<L>(dbias, red);
+  const float3 sums = block_sum3<L>(make_float3(valid ? dk * rc : 0.f, dd, dbias), red);
   if (k == 0) {
-    dA_part[jh] = da_sum;
-    dD_part[jh] = dd_sum;
-    dbias_part[jh] = db_sum;
+    dA_part[jh] = sums.x;
+    dD_part[jh] = sums.y;
+    dbias_part[jh] = sums.z;
   }
 }
 
@@ -967,7 +1050,7 @@ static int bwd_head_blocks(int hpg, int64_t wg_per_block) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
     if (cus_cached[dev] <= 0)
-      hipDeviceGetAttribute(&cus_cached[dev], hipDeviceAttributeMultiprocessorCount, dev);
+      (void)hipDeviceGetAttribute(&cus_cached[dev], hipDeviceAttributeMultiprocessorCount, dev);
     cus = cus_cached[dev];
   }
   const int cap = hpg < kBwdHeadBlocks ? hpg : kBwdHeadBlocks;
