@@ -542,9 +542,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
   const int64_t t0 = cd.start;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
   const T* cbj = cb + ((int64_t)j * G + g) * L * L;
-  for (int i = threadIdx.x; i < 64 * 64; i += kBwdThreads) {
-    const int r = i >> 6, c = i & 63;
-    cbt[r][c] = ld(cbj + (int64_t)(l0 + r) * L + s0 + c);   // rows past the chunk: never used
+  {                                        // rows past the chunk: never used
+    constexpr int V = 16 / sizeof(T), PR = 64 / V;
+    for (int i = threadIdx.x; i < 64 * PR; i += kBwdThreads) {
+      const int r = i / PR, c = (i - (i / PR) * PR) * V;
+      float v[V];
+      load16_f32<T>(cbj + (int64_t)(l0 + r) * L + s0 + c, true, v);
+#pragma unroll
+      for (int e = 0; e < V; ++e) cbt[r][c + e] = v[e];
+    }
   }
   float w[4][4] = {};                      // this block's sum of delta_s V[l,s]
   for (int h = h0; h < h1; ++h) {
@@ -761,7 +767,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
   if (m0 >= len) return;                   // uniform: rows past the chunk
   const int64_t t0 = cd.start;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
-  const T* M = which == 0 ? C : B;         // the row dot's group rows
+  // the row dot's group rows (C for dC, B for dB): this thread's 4 x 4
+  // values, the same for every head
+  float mv[4][4];
+  {
+    const T* M = which == 0 ? C : B;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) {
+        const int r = m0 + tm + i, nn = n0 + tn + jn;
+        mv[i][jn] = (r < len && nn < N) ? ld(M + ((t0 + r) * G + g) * N + nn) : 0.f;
+      }
+  }
   float tot[4][4] = {};
   for (int h = h0; h < h1; ++h) {
     const int64_t jh = (int64_t)j * H + h;
@@ -813,13 +831,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
     for (int i = 0; i < 4; ++i) {
       const int r = m0 + tm + i;
       float v = 0.f;
-      if (r < len) {
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn) {
-          const int nn = n0 + tn + jn;
-          if (nn < N) v += ld(M + ((t0 + r) * G + g) * N + nn) * acc[i][jn];
-        }
-      }
+      for (int jn = 0; jn < 4; ++jn) v += mv[i][jn] * acc[i][jn];
       v = row16_sum(v);
       if ((threadIdx.x & 15) == 0) part[(jh * NT + nt) * L + r] = v;
     }
@@ -894,22 +907,30 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_group_kernel(
                                                C + (t0 * G + g) * N + n0, (int64_t)G * N, N - n0, m0,
                                                len, acc, As, Bs, m0);
   }
-  // the state terms of the group's HB head blocks: per block, the tile's 16
-  // values of this thread are independent loads (rows past the chunk read
-  // row 0 and are dropped)
+  // the state terms of the group's HB head blocks: per block, four 16-byte
+  // loads of this thread's 4 x 4 values (rows past the chunk read row 0 and
+  // columns past N read column 0; both are dropped)
   const float* part = which == 0 ? dCh : dBh;
   T* out = which == 0 ? dC : dB;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+  static_assert(N % 4 == 0, "16-byte pieces of a row");
+  const int ncol = n0 + tn < N ? n0 + tn : 0;
 #pragma unroll 2
   for (int b = 0; b < HB; ++b) {
     const float* ph = part + (((int64_t)j * G + g) * HB + b) * L * N;
+    float4 v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int r = m0 + tm + i;
+      v[i] = *reinterpret_cast<const float4*>(ph + (int64_t)(r < len ? r : 0) * N + ncol);
+    }
 #pragma unroll
-      for (int jn = 0; jn < 4; ++jn) {
-        const int r = m0 + tm + i, n = n0 + tn + jn;
-        acc[i][jn] += ph[(int64_t)(r < len ? r : 0) * N + (n < N ? n : 0)];
-      }
+    for (int i = 0; i < 4; ++i) {
+      acc[i][0] += v[i].x;
+      acc[i][1] += v[i].y;
+      acc[i][2] += v[i].z;
+      acc[i][3] += v[i].w;
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
