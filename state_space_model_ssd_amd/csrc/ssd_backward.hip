@@ -32,12 +32,12 @@
 // Everything accumulates in fp32; dx, dB and dC are rounded once to x's
 // dtype.  Deterministic: fixed loop orders, no atomics.
 //
-// The contractions are 64 x 64 output tiles.  With bf16 inputs, 1, 3a, 3b
-// and 4a run on the bf16 MFMA: rows read with 16-byte loads, or k-major
-// slices staged in LDS as bf16 and read with the gfx950 transpose read; an
-// operand that is scaled or fp32 is rounded to bf16 once, and row factors
-// are applied to the product where they can be.  4b and the fp32 path use
-// fp32 tiles on the vector ALUs, staged through LDS with 16-byte loads.
+// The contractions are 64 x 64 output tiles.  With bf16 inputs they run on
+// the bf16 MFMA: rows read with 16-byte loads, or k-major slices staged in
+// LDS as bf16 and read with the gfx950 transpose read; an operand that is
+// scaled or fp32 is rounded to bf16 once, and row factors are applied to
+// the product where they can be.  The fp32 path uses fp32 tiles on the
+// vector ALUs, staged through LDS with 16-byte loads.
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -896,7 +896,66 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_group_kernel(
   const int64_t t0 = cd.start;
   const float* W = dcbp + ((int64_t)j * G + g) * HB * L * L;   // the summed slot
   float acc[4][4] = {};
-  if (which == 0) {                        // dC rows m0..m0+63: s runs to the tile's last row
+  if constexpr (sizeof(T) == 2) {
+    // bf16 MFMA over 32-long k-slices, the summed dCB rounded once to bf16
+    // (masked to s <= l); B (dC) or C (dB) rows staged k-major in LDS
+    __shared__ __align__(16) bf16 at[32 * kKtPitch], bt[32 * kKtPitch];
+    static_assert(32 * 8 == kBwdThreads, "one 8-wide piece of each slice tile per thread");
+    const int kr = threadIdx.x >> 3, c = (threadIdx.x & 7) * 8;
+    const MfmaQuarter q;
+    f32x4 d[2][2];
+    zero_quarter(d);
+    const int k0 = which == 0 ? 0 : m0, k1 = which == 0 ? min(len, m0 + 64) : len;
+    const T* R = which == 0 ? B : C;       // rows k of the second operand
+    for (int kb = k0; kb < k1; kb += 32) {
+      const int k = kb + kr;
+      const bf16x8 rv = frag_row(R + ((t0 + k) * G + g) * N + n0 + c, k < k1 && n0 + c < N);
+      bf16x8 av[2];
+      if (which == 0) {
+        // A rows l = m0 + row: dCB[l, kb + kq ..] for s <= l, straight from W
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          const int l = m0 + q.wr + mi * 16 + q.lr, s1 = kb + q.kq;
+          const bool ok = l < len && s1 < k1;
+          const float* pw = W + (int64_t)l * L + s1;
+          const float4 u0 = ok ? *reinterpret_cast<const float4*>(pw) : make_float4(0.f, 0.f, 0.f, 0.f);
+          const float4 u1 = ok ? *reinterpret_cast<const float4*>(pw + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+          const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (s1 + e <= l && s1 + e < k1) ? u[e] : 0.f;
+          av[mi] = Mfma<bf16>::pack(v);
+        }
+      } else {
+        // rows l = k of W, columns s = m0 + c ..: dCB[l, s] for s <= l, k-major
+        const bool ok = k < k1;
+        const float* pw = W + (int64_t)k * L + m0 + c;
+        const float4 u0 = ok ? *reinterpret_cast<const float4*>(pw) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 u1 = ok ? *reinterpret_cast<const float4*>(pw + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (m0 + c + e <= k && m0 + c + e < len) ? u[e] : 0.f;
+        av[0] = Mfma<bf16>::pack(v);
+      }
+      __syncthreads();                     // previous slice consumed
+      *reinterpret_cast<bf16x8*>(&bt[kr * kKtPitch + c]) = rv;
+      if (which != 0) *reinterpret_cast<bf16x8*>(&at[kr * kKtPitch + c]) = av[0];
+      __syncthreads();
+      if (which == 0) {
+        bf16x8 b[2];
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) b[ni] = lds_operand_kmajor(bt, kKtPitch, 0, q.wc + ni * 16, q.lane);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) d[mi][ni] = Mfma<bf16>::mma(av[mi], b[ni], d[mi][ni]);
+      } else {
+        mfma_kmajor(q, at, bt, d);
+      }
+    }
+    quarter_to_thread(q, d, acc, As, Bs);
+  } else if (which == 0) {                 // dC rows m0..m0+63: s runs to the tile's last row
     // rows l of the summed dCB (columns s <= l), rows s of B
     gemm_staged<float, true, T, false, 32, 1>(W + (int64_t)m0 * L, L, len - m0, nullptr,
                                               B + (t0 * G + g) * N + n0, (int64_t)G * N, N - n0, 0,
