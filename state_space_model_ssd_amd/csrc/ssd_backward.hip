@@ -511,6 +511,17 @@ __device__ __forceinline__ float4 load4_f32(const bf16* p) {
   return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
+// Four consecutive values rounded once to T (8- or 16-byte store).
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  const uint32_t lo = (uint32_t)__builtin_bit_cast(unsigned short, static_cast<bf16>(a)) |
+                      ((uint32_t)__builtin_bit_cast(unsigned short, static_cast<bf16>(b)) << 16);
+  const uint32_t hi = (uint32_t)__builtin_bit_cast(unsigned short, static_cast<bf16>(c)) |
+                      ((uint32_t)__builtin_bit_cast(unsigned short, static_cast<bf16>(d)) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
 
 // 3a. For each head, V[l,s] = exp(a_l - a_s) (dy_l . x_s) for s <= l as
 // 64 x 64 tiles on or below the diagonal, with each tile's partial sums
@@ -603,14 +614,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
     }
     __syncthreads();                       // cpart, al, as, dls read before the next head writes them
   }
+  // whole 4-wide pieces of the rows in the chunk (w is 0 above the
+  // diagonal; entries there and past the chunk are never read)
   float* W = dcbp + (((int64_t)j * G + g) * HB + hb) * L * L;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
-      const int l = l0 + tm + i, sx = s0 + tn + jn;
-      if (l < len && sx <= l) W[(int64_t)l * L + sx] = w[i][jn];
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int l = l0 + tm + i;
+    if (l < len) store4(W + (int64_t)l * L + s0 + tn, w[i][0], w[i][1], w[i][2], w[i][3]);
+  }
 }
 
 // 3b. dx as 64 x 64 tiles of (token s, p):
@@ -722,19 +733,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
   }
   const float Dh = D ? D[h] : 0.f;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+  static_assert(P % 4 == 0, "4-wide pieces of a row");
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int sx = s0 + tm + i;
-    if (sx >= len) continue;
+    if (sx >= len || p0 + tn >= P) continue;
     const float dsx = delta[jh * L + sx];
-#pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
-      const int pp = p0 + tn + jn;
-      if (pp < P) {
-        const int64_t o = ((t0 + sx) * H + h) * P + pp;
-        dx[o] = from_f32<T>(dsx * acc[i][jn] + Dh * ld(dy + o));
-      }
-    }
+    const int64_t o = ((t0 + sx) * H + h) * P + p0 + tn;
+    const float4 y = load4_f32(dy + o);
+    store4(dx + o, dsx * acc[i][0] + Dh * y.x, dsx * acc[i][1] + Dh * y.y,
+           dsx * acc[i][2] + Dh * y.z, dsx * acc[i][3] + Dh * y.w);
   }
 }
 
@@ -844,13 +852,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
     }
   }
   float* out = (which == 0 ? dCh : dBh) + (((int64_t)j * G + g) * HB + hb) * L * N;
+  static_assert(N % 4 == 0, "4-wide pieces of a row");
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
-      const int r = m0 + tm + i, n = n0 + tn + jn;
-      if (r < len && n < N) out[(int64_t)r * N + n] = tot[i][jn];
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int r = m0 + tm + i;
+    if (r < len && n0 + tn < N)
+      store4(out + (int64_t)r * N + n0 + tn, tot[i][0], tot[i][1], tot[i][2], tot[i][3]);
+  }
 }
 
 // 3b'. The group's dCB: the HB partial sums of 3a added into the first,
@@ -992,12 +1000,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_group_kernel(
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
-      const int r = m0 + tm + i, n = n0 + tn + jn;
-      if (r < len && n < N) out[((t0 + r) * G + g) * N + n] = from_f32<T>(acc[i][jn]);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int r = m0 + tm + i;
+    if (r < len && n0 + tn < N)
+      store4(out + ((t0 + r) * G + g) * N + n0 + tn, acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+  }
 }
 
 // 3c. Per (chunk, head), one thread per token: da from the partial sums,
