@@ -343,6 +343,16 @@ __device__ __forceinline__ void mfma_rows_kmajor(const MfmaQuarter& q, const bf1
   }
 }
 
+// Lower-triangular tile index t -> (row tile, column tile <= row tile).
+__device__ __forceinline__ int2 lower_tile(int t) {
+  int r = 0;
+  while (t > r) {
+    t -= r + 1;
+    ++r;
+  }
+  return make_int2(r, t);
+}
+
 // Sum of v over the 16 threads that share a row of the 4 x 4 blocks (lanes
 // differing in their low 4 bits); every one of them gets it.
 __device__ __forceinline__ float row16_sum(float v) {
@@ -352,16 +362,21 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 // 1. Q_j[p,n] = sum_l exp(a_l) dy[l,p] C[l,n] as 64 x 64 tiles;
-// grid (ceil(P/64) * ceil(N/64), H, chunk slots).
+// grid: xcd_grid(chunk slots, ceil(P/64) * ceil(N/64) * H), every tile and
+// head of a chunk on the XCD of that chunk.
 template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_q_tiled_kernel(
-    ChunkMap cm, const T* __restrict__ dy, const T* __restrict__ C,
+    ChunkMap cm, int nslots, const T* __restrict__ dy, const T* __restrict__ C,
     const float* __restrict__ dAcs, int H, int G, float* __restrict__ Q) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   __shared__ float sc[L];
   constexpr int NT = (N + 63) / 64;
-  const int m0 = (blockIdx.x / NT) * 64, n0 = (blockIdx.x % NT) * 64;
-  const int h = blockIdx.y, j = blockIdx.z, g = h / (H / G);
+  constexpr int NX = ((P + 63) / 64) * NT;
+  const int2 ci = xcd_chunk_head(blockIdx.x, NX * H);
+  if (ci.x >= nslots) return;
+  const int bx = ci.y % NX;
+  const int m0 = (bx / NT) * 64, n0 = (bx % NT) * 64;
+  const int h = ci.y / NX, j = ci.x, g = h / (H / G);
   const ChunkDesc cd = cm.desc(j);
   const int64_t jh = (int64_t)j * H + h;
   for (int l = threadIdx.x; l < L; l += kBwdThreads) sc[l] = expf(dAcs[jh * L + l]);
@@ -531,10 +546,11 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
 // B and C are shared by the group, so dB and dC need dCB only summed over
 // its heads.  Workgroup (lt, st, g, hb) walks the heads of block hb of group
 // g (HB blocks per group) and writes that block's sum to dcbp[j][g][hb].
-// grid ((L/64)^2, G * HB, chunk slots).
+// grid: xcd_grid(chunk slots, (L/64)(L/64 + 1)/2 * G * HB), the tiles on or
+// below the diagonal, every tile and head block of a chunk on its XCD.
 template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
-    ChunkMap cm, const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ cb,
+    ChunkMap cm, int nslots, const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ cb,
     const float* __restrict__ delta, const float* __restrict__ dAcs, int H, int G, int HB,
     float* __restrict__ dcbp, float* __restrict__ rowpart, float* __restrict__ colpart) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
@@ -542,9 +558,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
   __shared__ float cbt[64][65];            // the CB tile, shared by the group's heads
   __shared__ float al[64], as[64], dls[64];   // the head's running sums (rows, columns), steps
   constexpr int LT = L / 64;
-  const int lt = blockIdx.x / LT, st = blockIdx.x % LT;
-  if (st > lt) return;                     // above the diagonal: nothing
-  const int g = blockIdx.y / HB, hb = blockIdx.y - (blockIdx.y / HB) * HB, j = blockIdx.z;
+  constexpr int NX = LT * (LT + 1) / 2;   // tiles on or below the diagonal
+  const int2 ci = xcd_chunk_head(blockIdx.x, NX * G * HB);
+  if (ci.x >= nslots) return;
+  const int2 tt = lower_tile(ci.y % NX);
+  const int lt = tt.x, st = tt.y, by = ci.y / NX;
+  const int g = by / HB, hb = by - (by / HB) * HB, j = ci.x;
   const int hpg = H / G, h0 = g * hpg + hb * hpg / HB, h1 = g * hpg + (hb + 1) * hpg / HB;
   const ChunkDesc cd = cm.desc(j);
   const int len = max(cd.len, 0);
@@ -627,17 +646,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
 // 3b. dx as 64 x 64 tiles of (token s, p):
 //   dx_s = delta_s [ sum_{l>=s} CB[l,s] exp(a_l - a_s) dy_l + exp(a_last - a_s) dS_j B_s ]
 //          + D dy_s;
-// grid (L/64 * ceil(P/64), H, chunk slots).
+// grid: xcd_grid(chunk slots, L/64 * ceil(P/64) * H), a chunk's tiles on its XCD.
 template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
-    ChunkMap cm, const T* __restrict__ B, const T* __restrict__ dy, const T* __restrict__ cb,
+    ChunkMap cm, int nslots, const T* __restrict__ B, const T* __restrict__ dy, const T* __restrict__ cb,
     const float* __restrict__ delta, const float* __restrict__ dAcs, const float* __restrict__ dS,
     const float* __restrict__ D, int H, int G, T* __restrict__ dx) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   __shared__ float es[L], av[L];
   constexpr int PT = (P + 63) / 64;
-  const int s0 = (blockIdx.x / PT) * 64, p0 = (blockIdx.x % PT) * 64;
-  const int h = blockIdx.y, j = blockIdx.z, g = h / (H / G);
+  constexpr int NX = (L / 64) * PT;
+  const int2 ci = xcd_chunk_head(blockIdx.x, NX * H);
+  if (ci.x >= nslots) return;
+  const int bx = ci.y % NX;
+  const int s0 = (bx / PT) * 64, p0 = (bx % PT) * 64;
+  const int h = ci.y / NX, j = ci.x, g = h / (H / G);
   const ChunkDesc cd = cm.desc(j);
   const int len = max(cd.len, 0);
   if (s0 >= len) return;
@@ -754,11 +777,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
 //   interpart[nt][l] = sum_n C[l,n] exp(a_l) (dy_l H)[n],
 //   vxpart[nt][s]    = sum_n B[s,n] exp(a_last - a_s) (x_s dS_j)[n]
 // over the tile's 64 columns n.  Block hb of group g writes its sum to
-// slot (j, g, hb) of dBh / dCh.  grid (L/64 * ceil(N/64) * 2, G * HB, chunk
-// slots); even x: dC, odd: dB.
+// slot (j, g, hb) of dBh / dCh.  grid: xcd_grid(chunk slots, L/64 * ceil(N/64)
+// * 2 * G * HB), a chunk's tiles on its XCD; even tiles: dC, odd: dB.
 template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
-    ChunkMap cm, const T* __restrict__ x, const T* __restrict__ B, const T* __restrict__ C,
+    ChunkMap cm, int nslots, const T* __restrict__ x, const T* __restrict__ B, const T* __restrict__ C,
     const T* __restrict__ dy, const float* __restrict__ delta, const float* __restrict__ dAcs,
     const T* __restrict__ states_in, const float* __restrict__ dS, int H, int G, int HB,
     float* __restrict__ dBh, float* __restrict__ dCh, float* __restrict__ interpart,
@@ -766,9 +789,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   __shared__ float sc[64], ds[64];         // the head's row factors and steps
   constexpr int NT = (N + 63) / 64;
-  const int which = blockIdx.x & 1, t = blockIdx.x >> 1;
+  constexpr int NX = (L / 64) * NT * 2;
+  const int2 ci = xcd_chunk_head(blockIdx.x, NX * G * HB);
+  if (ci.x >= nslots) return;
+  const int bx = ci.y % NX, by = ci.y / NX;
+  const int which = bx & 1, t = bx >> 1;
   const int m0 = (t / NT) * 64, nt = t % NT, n0 = nt * 64;
-  const int g = blockIdx.y / HB, hb = blockIdx.y - (blockIdx.y / HB) * HB, j = blockIdx.z;
+  const int g = by / HB, hb = by - (by / HB) * HB, j = ci.x;
   const int hpg = H / G, h0 = g * hpg + hb * hpg / HB, h1 = g * hpg + (hb + 1) * hpg / HB;
   const ChunkDesc cd = cm.desc(j);
   const int len = max(cd.len, 0);
@@ -887,17 +914,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dcb_sum_kernel(int G, int HB,
 // terms of 4a summed over the group's heads, rounded once to the dtype:
 //   dC[l] = sum_{s<=l} dCB[l,s] B_s + sum_h dC_h[l],
 //   dB[s] = sum_{l>=s} dCB[l,s] C_l + sum_h dB_h[s].
-// grid (L/64 * ceil(N/64) * 2, G, chunk slots); even x: dC, odd: dB.
+// grid: xcd_grid(chunk slots, L/64 * ceil(N/64) * 2 * G), a chunk's tiles on
+// its XCD; even tiles: dC, odd: dB.
 template <typename T, int N, int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_bc_group_kernel(
-    ChunkMap cm, const T* __restrict__ B, const T* __restrict__ C,
+    ChunkMap cm, int nslots, const T* __restrict__ B, const T* __restrict__ C,
     const float* __restrict__ dcbp, const float* __restrict__ dBh, const float* __restrict__ dCh,
     int H, int G, int HB, T* __restrict__ dB, T* __restrict__ dC) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   constexpr int NT = (N + 63) / 64;
-  const int which = blockIdx.x & 1, t = blockIdx.x >> 1;
+  constexpr int NX = (L / 64) * NT * 2;
+  const int2 ci = xcd_chunk_head(blockIdx.x, NX * G);
+  if (ci.x >= nslots) return;
+  const int bx = ci.y % NX;
+  const int which = bx & 1, t = bx >> 1;
   const int m0 = (t / NT) * 64, n0 = (t % NT) * 64;
-  const int g = blockIdx.y, j = blockIdx.z;
+  const int g = ci.y / NX, j = ci.x;
   const ChunkDesc cd = cm.desc(j);
   const int len = max(cd.len, 0);
   if (m0 >= len) return;                   // uniform: rows past the chunk
@@ -1168,8 +1200,8 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   const T* cb = (const T*)a.cb;
   const T* hin = (const T*)a.states_in;
   constexpr int NT = (N + 63) / 64;
-  hipLaunchKernelGGL((bwd_q_tiled_kernel<T, P, N, L>), dim3(((P + 63) / 64) * NT, H, mc),
-                     dim3(kBwdThreads), 0, s, cm, dy, C, a.dAcs, H, G, b.Q);
+  hipLaunchKernelGGL((bwd_q_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, ((P + 63) / 64) * NT * H)),
+                     dim3(kBwdThreads), 0, s, cm, mc, dy, C, a.dAcs, H, G, b.Q);
   hipLaunchKernelGGL(bwd_chain_kernel, dim3((PN + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
                      dim3(kBwdThreads), 0, s, cm, b.Q, a.dAcs, b.dfinal, H, PN, L, b.dS, b.dinit);
   constexpr int LT = L / 64;
@@ -1177,18 +1209,20 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   // fewest that fill the GPU with 3a's workgroups (their partial sums fit
   // the workspace's H L^2 and H L N floats per chunk: G * HB <= H)
   const int hpg = H / G, HB = bwd_head_blocks(hpg, (int64_t)(LT * (LT + 1) / 2) * G * mc);
-  hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(LT * LT, G * HB, mc), dim3(kBwdThreads),
-                     0, s, cm, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb, b.rowpart, b.colpart);
-  hipLaunchKernelGGL((bwd_bc_tiled_kernel<T, P, N, L>), dim3(LT * NT * 2, G * HB, mc),
-                     dim3(kBwdThreads), 0, s, cm, x, B, C, dy, a.delta, a.dAcs, hin, b.dS, H, G, HB,
-                     b.dBh, b.dCh, b.interpart, b.vxpart);
+  hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * (LT + 1) / 2 * G * HB)),
+                     dim3(kBwdThreads), 0, s, cm, mc, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb,
+                     b.rowpart, b.colpart);
+  hipLaunchKernelGGL((bwd_bc_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * NT * 2 * G * HB)),
+                     dim3(kBwdThreads), 0, s, cm, mc, x, B, C, dy, a.delta, a.dAcs, hin, b.dS, H, G,
+                     HB, b.dBh, b.dCh, b.interpart, b.vxpart);
   if (HB > 1)
     hipLaunchKernelGGL((bwd_dcb_sum_kernel<L>), dim3((L * L / 4 + kBwdThreads - 1) / kBwdThreads, G, mc),
                        dim3(kBwdThreads), 0, s, G, HB, b.dcb);
-  hipLaunchKernelGGL((bwd_bc_group_kernel<T, N, L>), dim3(LT * NT * 2, G, mc), dim3(kBwdThreads), 0,
-                     s, cm, B, C, b.dcb, b.dBh, b.dCh, H, G, HB, (T*)b.dB, (T*)b.dC);
-  hipLaunchKernelGGL((bwd_dx_tiled_kernel<T, P, N, L>), dim3(LT * ((P + 63) / 64), H, mc),
-                     dim3(kBwdThreads), 0, s, cm, B, dy, cb, a.delta, a.dAcs, b.dS, a.D, H, G,
+  hipLaunchKernelGGL((bwd_bc_group_kernel<T, N, L>), dim3(xcd_grid(mc, LT * NT * 2 * G)),
+                     dim3(kBwdThreads), 0, s, cm, mc, B, C, b.dcb, b.dBh, b.dCh, H, G, HB, (T*)b.dB,
+                     (T*)b.dC);
+  hipLaunchKernelGGL((bwd_dx_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * ((P + 63) / 64) * H)),
+                     dim3(kBwdThreads), 0, s, cm, mc, B, dy, cb, a.delta, a.dAcs, b.dS, a.D, H, G,
                      (T*)b.dx);
   hipLaunchKernelGGL((bwd_token_kernel<T, P, N, L>), dim3(H, mc), dim3(L), 0, s, cm, x, a.dt,
                      a.dt_bias, a.A, dy, a.delta, a.dAcs, hin, b.dS, b.rowpart, b.colpart,
