@@ -1141,22 +1141,30 @@ __global__ __launch_bounds__(L) void bwd_token_kernel(
   }
 }
 
-// 5. dA, dD, dt_bias: sums over the chunk slots; one thread per head.
-__global__ __launch_bounds__(kBwdThreads) void bwd_head_reduce_kernel(
+// 5. dA, dD, dt_bias: sums over the chunk slots; one wave per head (lanes
+// stride the slots, then a shuffle sum).  grid (H), kWave threads.
+__global__ __launch_bounds__(kWave) void bwd_head_reduce_kernel(
     const float* __restrict__ dA_part, const float* __restrict__ dD_part,
     const float* __restrict__ dbias_part, int H, int nslots, float* __restrict__ dA,
     float* __restrict__ dD, float* __restrict__ dbias) {
-  const int h = blockIdx.x * kBwdThreads + threadIdx.x;
-  if (h >= H) return;
+  const int h = blockIdx.x;
   float sa = 0.f, sd = 0.f, sb = 0.f;
-  for (int j = 0; j < nslots; ++j) {
+  for (int j = threadIdx.x; j < nslots; j += kWave) {
     sa += dA_part[(int64_t)j * H + h];
     sd += dD_part[(int64_t)j * H + h];
     sb += dbias_part[(int64_t)j * H + h];
   }
-  dA[h] = sa;
-  if (dD) dD[h] = sd;
-  if (dbias) dbias[h] = sb;
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    sa += __shfl_xor(sa, off);
+    sd += __shfl_xor(sd, off);
+    sb += __shfl_xor(sb, off);
+  }
+  if (threadIdx.x == 0) {
+    dA[h] = sa;
+    if (dD) dD[h] = sd;
+    if (dbias) dbias[h] = sb;
+  }
 }
 
 }  // namespace
@@ -1188,9 +1196,8 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
     if (b.dinit && ne > 0)
       hipLaunchKernelGGL(bwd_pass_final_kernel, dim3((unsigned)((ne + kBwdThreads - 1) / kBwdThreads)),
                          dim3(kBwdThreads), 0, s, b.dfinal, ne, b.dinit);
-    hipLaunchKernelGGL(bwd_head_reduce_kernel, dim3((H + kBwdThreads - 1) / kBwdThreads),
-                       dim3(kBwdThreads), 0, s, b.dA_part, b.dD_part, b.dbias_part, H, 0, b.dA,
-                       b.dD, b.ddt_bias);
+    hipLaunchKernelGGL(bwd_head_reduce_kernel, dim3(H), dim3(kWave), 0, s, b.dA_part, b.dD_part,
+                       b.dbias_part, H, 0, b.dA, b.dD, b.ddt_bias);
     return hipGetLastError();
   }
   const T* x = (const T*)a.x;
@@ -1228,8 +1235,8 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
                      a.dt_bias, a.A, dy, a.delta, a.dAcs, hin, b.dS, b.rowpart, b.colpart,
                      b.interpart, b.vxpart, H, a.dt_min, a.dt_max, b.ddt, b.dA_part, b.dD_part,
                      b.dbias_part);
-  hipLaunchKernelGGL(bwd_head_reduce_kernel, dim3((H + kBwdThreads - 1) / kBwdThreads), dim3(kBwdThreads),
-                     0, s, b.dA_part, b.dD_part, b.dbias_part, H, mc, b.dA, b.dD, b.ddt_bias);
+  hipLaunchKernelGGL(bwd_head_reduce_kernel, dim3(H), dim3(kWave), 0, s, b.dA_part, b.dD_part,
+                     b.dbias_part, H, mc, b.dA, b.dD, b.ddt_bias);
   return hipGetLastError();
 }
 
