@@ -335,12 +335,32 @@ def main():
         # written; B, C read and dB, dC written; init, dfinal read, dinit written
         bbytes = (3 * e * tokens * H * P + 8 * tokens * H + 4 * e * tokens * G * N
                   + 12 * prob.nseq * H * P * N)
+        # ssd_bwd_after_fwd: the same gradients from the intermediates a
+        # forward call left in the workspace (the training order)
+        binding.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, D=d["D"],
+                        dt_bias=d["dt_bias"], initial_states=d["init"], cu_seqlens=d["cu_seqlens"],
+                        workspace=wsb, tuning=None)
+
+        def astep():
+            return binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, dy,
+                                   dfin, D=d["D"], dt_bias=d["dt_bias"], initial_states=d["init"],
+                                   cu_seqlens=d["cu_seqlens"], workspace=wsb, after_fwd=True)
+        astep()
+        torch.cuda.synchronize()
+        b0.record(cur)
+        for _ in range(args.backward_reps):
+            astep()
+        b1.record(cur)
+        torch.cuda.synchronize()
+        aus = b0.elapsed_time(b1) * 1e3 / args.backward_reps
         backward = {"us": round(bus, 1), "tokens_per_s": round(tokens / (bus * 1e-6), 1),
                     "alg_bytes_fused_minimum": int(bbytes),
                     "hbm_frac_of_fused_minimum": round(bbytes / (bus * 1e-6) / 1e9 / HBM_PEAK_GBS, 5),
+                    "us_after_fwd": round(aus, 1),
                     "reps": args.backward_reps,
                     "note": "ssd_bwd: gradients of every input; recomputes the forward's "
-                            "stages 0-4; per-kernel times in profiles/"}
+                            "stages 0-4 (us_after_fwd: ssd_bwd_after_fwd, which reuses a "
+                            "forward's intermediates); per-kernel times in profiles/"}
         del wsb
 
     # --- CPU baseline: the fp64 oracle on this host's cores, same workload

@@ -261,6 +261,28 @@ ssd_status_t ssd_bwd(const ssd_problem_t* p,
                      float* dD, float* ddt_bias, float* dinitial_states,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * As ssd_bwd, without recomputing the forward's stages 0-4: the workspace
+ * (ssd_bwd_workspace_size bytes) must hold, unchanged, what a completed
+ * ssd_fwd / ssd_fwd_stages / ssd_fwd_tuned call that ran stages 0-4 on the
+ * same problem and the same inputs wrote into its leading
+ * ssd_workspace_layout part (the steps, running sums, CB and entering
+ * states), as in training, where the backward follows its forward.  The
+ * gradients are those of that forward's intermediates; with the forward's
+ * default kernel choices they equal ssd_bwd's bit for bit.  The library
+ * cannot check that the workspace holds them: anything else in it gives
+ * wrong gradients without an error.  Arguments and errors as for ssd_bwd.
+ */
+ssd_status_t ssd_bwd_after_fwd(const ssd_problem_t* p,
+                               const void* x, const float* dt, const float* dt_bias,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const float* initial_states,
+                               const int32_t* cu_seqlens, const int32_t* seq_idx,
+                               const void* dout, const float* dfinal_states,
+                               void* dx, float* ddt, float* dA, void* dB, void* dC,
+                               float* dD, float* ddt_bias, float* dinitial_states,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* ssd_status_string(ssd_status_t s);
 

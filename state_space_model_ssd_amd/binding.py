@@ -29,6 +29,7 @@ STAGES = {"plan": STAGE_PLAN, "chunk_cumsum": STAGE_CUMSUM, "bmm_chunk": STAGE_B
 
 EXPORTED = ("ssd_fwd_workspace_size", "ssd_workspace_layout", "ssd_config_supported",
             "ssd_fwd", "ssd_fwd_stages", "ssd_fwd_tuned", "ssd_bwd_workspace_size", "ssd_bwd",
+            "ssd_bwd_after_fwd",
             "ssd_status_string")
 
 
@@ -95,6 +96,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_bwd_workspace_size.restype = sz
     lib.ssd_bwd.argtypes = [PP] + [vp] * 20 + [vp, sz, vp]
     lib.ssd_bwd.restype = ctypes.c_int
+    lib.ssd_bwd_after_fwd.argtypes = [PP] + [vp] * 20 + [vp, sz, vp]
+    lib.ssd_bwd_after_fwd.restype = ctypes.c_int
     lib.ssd_status_string.argtypes = [ctypes.c_int]
     lib.ssd_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -189,12 +192,17 @@ def bwd_workspace_size(prob: ProblemC) -> int:
 
 
 def ssd_bwd(x, dt, A, B, C, chunk_size, dout, dfinal_states=None, D=None, dt_bias=None,
-            initial_states=None, cu_seqlens=None, dt_min=0.0, dt_max=math.inf, workspace=None):
+            initial_states=None, cu_seqlens=None, dt_min=0.0, dt_max=math.inf, workspace=None,
+            after_fwd=False):
     """SSD backward on the GPU through the C ABI: gradients of
     sum(out * dout) + sum(final_states * dfinal_states) for the inputs of
     ssd_fwd (same arguments).  Returns a dict with x, dt, A, B, C, D,
     dt_bias, initial_states (gradients; D, dt_bias and initial_states always
-    computed) and the workspace."""
+    computed) and the workspace.
+
+    after_fwd: call ssd_bwd_after_fwd, which reuses the forward's
+    intermediates left in `workspace` (required, ssd_bwd_workspace_size
+    bytes) by an ssd_fwd call on the same inputs."""
     lib = load_library()
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -222,10 +230,13 @@ def ssd_bwd(x, dt, A, B, C, chunk_size, dout, dfinal_states=None, D=None, dt_bia
          "initial_states": torch.empty((nstates, H, P, N), dtype=f32, device=dev)}
     need = lib.ssd_bwd_workspace_size(ctypes.byref(prob))
     if workspace is None:
+        if after_fwd:
+            raise ValueError("after_fwd needs the workspace the forward ran with")
         workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-        code = lib.ssd_bwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B),
+        fn = lib.ssd_bwd_after_fwd if after_fwd else lib.ssd_bwd
+        code = fn(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B),
                            _ptr(C), _ptr(D), _ptr(initial_states), _ptr(cu_seqlens), None,
                            _ptr(dout), _ptr(dfinal_states), _ptr(g["x"]), _ptr(g["dt"]),
                            _ptr(g["A"]), _ptr(g["B"]), _ptr(g["C"]), _ptr(g["D"]),

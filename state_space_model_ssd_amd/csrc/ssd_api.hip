@@ -264,7 +264,8 @@ ssd_status_t run_bwd(const ssd_problem_t* p, const void* x, const float* dt, con
                      const float* initial_states, const int32_t* cu_seqlens,
                      const int32_t* seq_idx, const void* dout, const float* dfinal, void* dx,
                      float* ddt, float* dA, void* dB, void* dC, float* dD, float* ddt_bias,
-                     float* dinit, void* workspace, size_t workspace_bytes, void* stream) {
+                     float* dinit, void* workspace, size_t workspace_bytes, void* stream,
+                     bool recompute_forward) {
   ssd_status_t st = check_problem(p);
   if (st != SSD_OK) return st;
   const int64_t tokens = p->batch * p->seqlen;
@@ -281,8 +282,11 @@ ssd_status_t run_bwd(const ssd_problem_t* p, const void* x, const float* dt, con
                  nullptr, nullptr, workspace, &a);
   if (st != SSD_OK) return st;
   // the forward's stages 0-4: delta, running sums, CB, the entering states
-  st = launch_stages(p, a, SSD_STAGE_ALL & ~(uint32_t)SSD_STAGE_CHUNK_SCAN, tune, stream);
-  if (st != SSD_OK) return st;
+  // (already in the workspace when an ssd_fwd call on these inputs left them)
+  if (recompute_forward) {
+    st = launch_stages(p, a, SSD_STAGE_ALL & ~(uint32_t)SSD_STAGE_CHUNK_SCAN, tune, stream);
+    if (st != SSD_OK) return st;
+  }
   char* base = static_cast<char*>(workspace);
   BwdArgs b;
   b.dy = dout; b.dfinal = dfinal; b.dx = dx; b.ddt = ddt; b.dA = dA; b.dB = dB; b.dC = dC;
@@ -375,7 +379,20 @@ ssd_status_t ssd_bwd(const ssd_problem_t* p, const void* x, const float* dt, con
                      size_t workspace_bytes, void* stream) {
   return ssd::run_bwd(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, dout,
                       dfinal_states, dx, ddt, dA, dB, dC, dD, ddt_bias, dinitial_states,
-                      workspace, workspace_bytes, stream);
+                      workspace, workspace_bytes, stream, true);
+}
+
+ssd_status_t ssd_bwd_after_fwd(const ssd_problem_t* p, const void* x, const float* dt,
+                               const float* dt_bias, const float* A, const void* B, const void* C,
+                               const float* D, const float* initial_states,
+                               const int32_t* cu_seqlens, const int32_t* seq_idx, const void* dout,
+                               const float* dfinal_states, void* dx, float* ddt, float* dA,
+                               void* dB, void* dC, float* dD, float* ddt_bias,
+                               float* dinitial_states, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return ssd::run_bwd(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, dout,
+                      dfinal_states, dx, ddt, dA, dB, dC, dD, ddt_bias, dinitial_states,
+                      workspace, workspace_bytes, stream, false);
 }
 
 const char* ssd_status_string(ssd_status_t s) {

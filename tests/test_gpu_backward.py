@@ -121,3 +121,39 @@ def test_backward_deterministic():
     b, _ = _grads_case(prob, Recipe(init_std=0.3), seed=5)
     for k in ("x", "dt", "A", "B", "C", "D", "dt_bias", "initial_states"):
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("packed", [False, True], ids=["batch", "packed"])
+def test_backward_after_forward_reuses_its_intermediates(packed):
+    # ssd_bwd_after_fwd on the workspace an ssd_fwd call (library's own kernel
+    # choices) left: the same stages computed the same intermediates, so the
+    # gradients equal ssd_bwd's bit for bit; stale bytes past the forward's
+    # part of the workspace must not matter
+    if packed:
+        lens = (100, 300, 64, 200)
+        prob = Problem(1, sum(lens), 4, 64, 128, 2, 64, "bf16", seq_lens=lens)
+    else:
+        prob = Problem(2, 520, 4, 64, 128, 2, 256, "bf16")
+    inp = make_inputs(prob, Recipe(init_std=0.3), seed=21)
+    gen = torch.Generator().manual_seed(1021)
+    dy = torch.randn(inp["x"].shape, generator=gen, dtype=torch.float32).to(inp["x"].dtype).cuda()
+    dfin = torch.randn((prob.nseq, prob.nheads, prob.headdim, prob.dstate), generator=gen).cuda()
+    d = to_dev(inp)
+    kw = dict(D=d["D"], dt_bias=d["dt_bias"], initial_states=d["init"], cu_seqlens=d["cu_seqlens"])
+    ref = binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, dy, dfin, **kw)
+    ws = torch.full_like(ref["workspace"], 0x7f)           # stale bytes everywhere
+    binding.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, workspace=ws,
+                    tuning=None, **kw)
+    got = binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, dy, dfin,
+                          workspace=ws, after_fwd=True, **kw)
+    torch.cuda.synchronize()
+    for k in ("x", "dt", "A", "B", "C", "D", "dt_bias", "initial_states"):
+        assert torch.equal(got[k], ref[k]), k
+
+
+def test_backward_after_forward_needs_a_workspace():
+    prob = Problem(1, 100, 2, 32, 32, 1, 64, "bf16")
+    d = to_dev(make_inputs(prob, Recipe(), seed=1))
+    with pytest.raises(ValueError):
+        binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size,
+                        torch.zeros_like(d["x"]), after_fwd=True)
