@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_tiled_kernel(
   const int h = ci.y / NX, j = ci.x, g = h / (H / G);
   const ChunkDesc cd = cm.desc(j);
   const int64_t jh = (int64_t)j * H + h;
-  for (int l = threadIdx.x; l < L; l += kBwdThreads) sc[l] = expf(dAcs[jh * L + l]);
+  for (int l = threadIdx.x; l < L; l += kBwdThreads) sc[l] = exp2_fast(dAcs[jh * L + l] * kLog2e);
   __syncthreads();
   if constexpr (sizeof(T) == 2) {
     // bf16 MFMA over slices of 32 tokens l: exp(a_l) dy_l (rounded once) and
@@ -609,7 +609,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
       for (int jn = 0; jn < 4; ++jn) {
         const int l = l0 + tm + i, sx = s0 + tn + jn;
         if (l < len && sx <= l) {
-          const float v = expf(al[tm + i] - as[tn + jn]) * acc[i][jn];
+          const float v = exp2_fast((al[tm + i] - as[tn + jn]) * kLog2e) * acc[i][jn];
           const float dv = dls[tn + jn] * v;
           w[i][jn] += dv;
           const float c = cbt[tm + i][tn + jn];
@@ -668,7 +668,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
   const float* a = dAcs + jh * L;
   const float alast = a[len - 1];
   for (int l = threadIdx.x; l < L; l += kBwdThreads) {
-    es[l] = expf(alast - a[l]);
+    es[l] = exp2_fast((alast - a[l]) * kLog2e);
     av[l] = a[l];
   }
   const T* cbj = cb + ((int64_t)j * G + g) * L * L;
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int sx = s0 + c + e;
-        mv[e] = (lok && l >= sx) ? static_cast<float>(cv[e]) * expf(av[l] - av[sx]) : 0.f;
+        mv[e] = (lok && l >= sx) ? static_cast<float>(cv[e]) * exp2_fast((av[l] - av[sx]) * kLog2e) : 0.f;
       }
       __syncthreads();                     // previous slice consumed
       *reinterpret_cast<bf16x8*>(&mt[kr * kKtPitch + c]) = Mfma<bf16>::pack(mv);
@@ -732,7 +732,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           const int sx = s0 + c + e;
-          As[kr * kGemmPitch + c + e] = (lok && sx < len && l >= sx) ? va[e] * expf(av[l] - av[sx]) : 0.f;
+          As[kr * kGemmPitch + c + e] =
+              (lok && sx < len && l >= sx) ? va[e] * exp2_fast((av[l] - av[sx]) * kLog2e) : 0.f;
           Bs[kr * kGemmPitch + c + e] = vb[e];
         }
       }
@@ -822,7 +823,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
     if (threadIdx.x < 64) {
       const float* a = dAcs + jh * L;
       const int r = m0 + threadIdx.x;
-      sc[threadIdx.x] = which == 0 ? expf(a[r]) : expf(a[len - 1] - a[r]);
+      sc[threadIdx.x] = exp2_fast((which == 0 ? a[r] : a[len - 1] - a[r]) * kLog2e);
       ds[threadIdx.x] = delta[jh * L + r];
     }
     float acc[4][4] = {};
