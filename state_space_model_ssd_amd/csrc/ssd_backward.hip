@@ -555,8 +555,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
     float* __restrict__ dcbp, float* __restrict__ rowpart, float* __restrict__ colpart) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   __shared__ float cpart[16][64];
-  __shared__ float cbt[64][65];            // the CB tile, shared by the group's heads
-  __shared__ float al[64], as[64], dls[64];   // the head's running sums (rows, columns), steps
+  // the head's running sums (rows, columns) and steps
+  __shared__ __align__(16) float al[64], as[64], dls[64];
   constexpr int LT = L / 64;
   constexpr int NX = LT * (LT + 1) / 2;   // tiles on or below the diagonal
   const int2 ci = xcd_chunk_head(blockIdx.x, NX * G * HB);
@@ -572,15 +572,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
   const int64_t t0 = cd.start;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
   const T* cbj = cb + ((int64_t)j * G + g) * L * L;
-  {                                        // rows past the chunk: never used
-    constexpr int V = 16 / sizeof(T), PR = 64 / V;
-    for (int i = threadIdx.x; i < 64 * PR; i += kBwdThreads) {
-      const int r = i / PR, c = (i - (i / PR) * PR) * V;
-      float v[V];
-      load16_f32<T>(cbj + (int64_t)(l0 + r) * L + s0 + c, true, v);
+  // this thread's 4 x 4 block of the CB tile, the same for every head (rows
+  // past the chunk are read but never used)
+  float cbr[4][4];
 #pragma unroll
-      for (int e = 0; e < V; ++e) cbt[r][c + e] = v[e];
-    }
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = load4_f32(cbj + (int64_t)(l0 + tm + i) * L + s0 + tn);
+    cbr[i][0] = v.x; cbr[i][1] = v.y; cbr[i][2] = v.z; cbr[i][3] = v.w;
   }
   float w[4][4] = {};                      // this block's sum of delta_s V[l,s]
   for (int h = h0; h < h1; ++h) {
@@ -603,18 +601,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
                                     x + ((t0 + s0) * H + h) * P, (int64_t)H * P, len - s0, 0, P, acc,
                                     As, Bs);
     float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum[4] = {0.f, 0.f, 0.f, 0.f};
+    const float4 al4 = *reinterpret_cast<const float4*>(&al[tm]);
+    const float4 as4 = *reinterpret_cast<const float4*>(&as[tn]);
+    const float4 dl4 = *reinterpret_cast<const float4*>(&dls[tn]);
+    const float alv[4] = {al4.x, al4.y, al4.z, al4.w}, asv[4] = {as4.x, as4.y, as4.z, as4.w};
+    const float dlv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int jn = 0; jn < 4; ++jn) {
         const int l = l0 + tm + i, sx = s0 + tn + jn;
         if (l < len && sx <= l) {
-          const float v = exp2_fast((al[tm + i] - as[tn + jn]) * kLog2e) * acc[i][jn];
-          const float dv = dls[tn + jn] * v;
+          const float v = exp2_fast((alv[i] - asv[jn]) * kLog2e) * acc[i][jn];
+          const float dv = dlv[jn] * v;
           w[i][jn] += dv;
-          const float c = cbt[tm + i][tn + jn];
-          rsum[i] += c * dv;
-          csum[jn] += c * v;
+          rsum[i] += cbr[i][jn] * dv;
+          csum[jn] += cbr[i][jn] * v;
         }
       }
 #pragma unroll
