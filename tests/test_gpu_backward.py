@@ -157,3 +157,80 @@ def test_backward_after_forward_needs_a_workspace():
     with pytest.raises(ValueError):
         binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size,
                         torch.zeros_like(d["x"]), after_fwd=True)
+
+
+# ------------------------------------------------- full-size shapes, sampled
+# Heads are independent for every gradient but dB and dC (sums over a
+# group's heads), and batch rows for every gradient but dA, dD and ddt_bias
+# (sums over rows), so the oracle runs on sub-problems of the full inputs.
+
+def _sub_heads(inp, dy, dfin, rows, heads, groups):
+    hs = torch.tensor(heads)
+    gs = torch.tensor(groups)
+    pick = lambda v, dim, idx: None if v is None else v.index_select(dim, idx)
+    r = torch.tensor(rows)
+    return dict(x=pick(inp["x"], 0, r)[:, :, hs], dt=pick(inp["dt"], 0, r)[:, :, hs],
+                dt_bias=pick(inp["dt_bias"], 0, hs), A=inp["A"][hs],
+                B=pick(inp["B"], 0, r)[:, :, gs], C=pick(inp["C"], 0, r)[:, :, gs],
+                D=pick(inp["D"], 0, hs), dy=pick(dy, 0, r)[:, :, hs],
+                dfin=None if dfin is None else pick(dfin, 0, r)[:, hs])
+
+
+def test_backward_layer_shape_sampled_heads():
+    # the layer shape in the launch configuration the bench times; heads 0
+    # and 23 of both rows: every gradient but dB and dC
+    from state_space_model_ssd_amd.inputs import workload_inputs
+    prob, inp = workload_inputs(2)
+    gen = torch.Generator().manual_seed(2024)
+    dy = torch.randn(inp["x"].shape, generator=gen).to(inp["x"].dtype)
+    dfin = torch.randn((prob.nseq, prob.nheads, prob.headdim, prob.dstate), generator=gen)
+    d = to_dev(inp)
+    got = binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, dy.cuda(),
+                          dfin.cuda(), D=d["D"], dt_bias=d["dt_bias"], initial_states=d["init"])
+    torch.cuda.synchronize()
+    heads = [0, prob.nheads - 1]
+    s = _sub_heads(inp, dy, dfin, [0, 1], heads, [0])
+    init = torch.zeros((prob.nseq, len(heads), prob.headdim, prob.dstate))
+    ref = ssd_grads(s["x"], s["dt"], s["dt_bias"], s["A"], s["B"], s["C"], s["D"], s["dy"],
+                    s["dfin"], init=init)
+    hs = torch.tensor(heads)
+    report = {}
+    for name, key, dim in (("x", "x", 2), ("dt", "dt", 2), ("A", "A", 0), ("D", "D", 0),
+                           ("dt_bias", "dt_bias", 0), ("init", "initial_states", 1)):
+        g = got[key].float().cpu().index_select(dim, hs)
+        assert torch.isfinite(g).all(), name
+        report[name] = rel_l2(g, ref[name])
+        assert report[name] <= TOL["bf16"], (name, report)
+    print("  rel_l2 " + " ".join(f"{k}={v:.2e}" for k, v in report.items()), flush=True)
+
+
+def test_backward_training_batch_one_group():
+    # the training-batch shape: batch row 3 and group 7 (heads 56-63), so
+    # that dB and dC of that group are complete; per-head sums over rows
+    # (dA, dD, ddt_bias) are covered by the layer-shape case
+    from state_space_model_ssd_amd.inputs import workload_inputs
+    prob, inp = workload_inputs(3)
+    gen = torch.Generator().manual_seed(2025)
+    dy = torch.randn(inp["x"].shape, generator=gen).to(inp["x"].dtype)
+    d = to_dev(inp)
+    got = binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, dy.cuda(),
+                          None, D=d["D"], dt_bias=d["dt_bias"], initial_states=d["init"])
+    torch.cuda.synchronize()
+    row, g = 3, 7
+    hpg = prob.nheads // prob.ngroups
+    heads = list(range(g * hpg, (g + 1) * hpg))
+    s = _sub_heads(inp, dy, None, [row], heads, [g])
+    init = torch.zeros((1, hpg, prob.headdim, prob.dstate))
+    ref = ssd_grads(s["x"], s["dt"], s["dt_bias"], s["A"], s["B"], s["C"], s["D"], s["dy"], None,
+                    init=init)
+    hs = torch.tensor(heads)
+    cut = {"x": got["x"][row:row + 1][:, :, hs], "dt": got["dt"][row:row + 1][:, :, hs],
+           "B": got["B"][row:row + 1][:, :, g:g + 1], "C": got["C"][row:row + 1][:, :, g:g + 1],
+           "init": got["initial_states"][row:row + 1][:, hs]}
+    report = {}
+    for name, g_ in cut.items():
+        g_ = g_.float().cpu()
+        assert torch.isfinite(g_).all(), name
+        report[name] = rel_l2(g_, ref[name])
+        assert report[name] <= TOL["bf16"], (name, report)
+    print("  rel_l2 " + " ".join(f"{k}={v:.2e}" for k, v in report.items()), flush=True)
