@@ -431,24 +431,31 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_tiled_kernel(
   }
 }
 
-// 2. Reverse chain; grid (ceil(P*N / 256), H, nstates).
+// 2. Reverse chain, four consecutive state elements per thread (16-byte
+// loads and stores; the next chunk's Q is loaded before this one's dS is
+// stored); grid (ceil(P*N / 1024), H, nstates).
 __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(
     ChunkMap cm, const float* __restrict__ Q, const float* __restrict__ dAcs,
     const float* __restrict__ dfinal, int H, int PN, int L, float* __restrict__ dS,
     float* __restrict__ dinit) {
-  const int e = blockIdx.x * kBwdThreads + threadIdx.x;
-  if (e >= PN) return;
+  const int e = (blockIdx.x * kBwdThreads + threadIdx.x) * 4;
+  if (e >= PN) return;                     // PN is a multiple of 4
   const int h = blockIdx.y, s = blockIdx.z;
   const int2 r = cm.seq_range(s);
-  float g = dfinal ? dfinal[((int64_t)s * H + h) * PN + e] : 0.f;
+  float4 g = dfinal ? *reinterpret_cast<const float4*>(dfinal + ((int64_t)s * H + h) * PN + e)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (r.y > r.x) q = *reinterpret_cast<const float4*>(Q + ((int64_t)(r.y - 1) * H + h) * PN + e);
   for (int j = r.y - 1; j >= r.x; --j) {
     const int64_t jh = (int64_t)j * H + h;
-    dS[jh * PN + e] = g;
+    const float4 qj = q;
+    if (j > r.x) q = *reinterpret_cast<const float4*>(Q + (jh - H) * PN + e);
+    *reinterpret_cast<float4*>(dS + jh * PN + e) = g;
     const int len = cm.desc(j).len;
     const float dec = len > 0 ? expf(dAcs[jh * L + len - 1]) : 1.f;
-    g = dec * g + Q[jh * PN + e];
+    g = make_float4(dec * g.x + qj.x, dec * g.y + qj.y, dec * g.z + qj.z, dec * g.w + qj.w);
   }
-  if (dinit) dinit[((int64_t)s * H + h) * PN + e] = g;
+  if (dinit) *reinterpret_cast<float4*>(dinit + ((int64_t)s * H + h) * PN + e) = g;
 }
 
 // dinit = dfinal (or 0) when there are no chunks.
@@ -1212,7 +1219,8 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   constexpr int NT = (N + 63) / 64;
   hipLaunchKernelGGL((bwd_q_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, ((P + 63) / 64) * NT * H)),
                      dim3(kBwdThreads), 0, s, cm, mc, dy, C, a.dAcs, H, G, b.Q);
-  hipLaunchKernelGGL(bwd_chain_kernel, dim3((PN + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
+  static_assert((P * N) % 4 == 0, "four state elements per thread");
+  hipLaunchKernelGGL(bwd_chain_kernel, dim3((PN / 4 + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
                      dim3(kBwdThreads), 0, s, cm, b.Q, a.dAcs, b.dfinal, H, PN, L, b.dS, b.dinit);
   constexpr int LT = L / 64;
   // head blocks per group for the summed dCB and dB/dC state terms: the
