@@ -235,7 +235,7 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
 
 // The backward's regions follow the forward's in its workspace.
 struct BwdLayout {
-  size_t Q, dS, dcb, dBh, dCh, rowpart, colpart, interpart, vxpart, dA_part, dD_part, dbias_part,
+  size_t Q, dS, dcb, dBh, dCh, rowpart, colpart, interpart, vxpart, dA_part, dD_part, dbias_part, ddot,
       total;
 };
 
@@ -256,6 +256,7 @@ void bwd_layout_of(const ssd_problem_t* p, const ssd_workspace_layout_t& w, BwdL
   b->dA_part = off;    off = align_up(off + sizeof(float) * mc * H);
   b->dD_part = off;    off = align_up(off + sizeof(float) * mc * H);
   b->dbias_part = off; off = align_up(off + sizeof(float) * mc * H);
+  b->ddot = off;       off = align_up(off + sizeof(float) * mc * H * L);
   b->total = off;
 }
 
@@ -303,6 +304,7 @@ ssd_status_t run_bwd(const ssd_problem_t* p, const void* x, const float* dt, con
   b.dA_part = reinterpret_cast<float*>(base + bl.dA_part);
   b.dD_part = reinterpret_cast<float*>(base + bl.dD_part);
   b.dbias_part = reinterpret_cast<float*>(base + bl.dbias_part);
+  b.ddot = reinterpret_cast<float*>(base + bl.ddot);
   const Kernels* k = find_kernels(p->dtype, p->headdim, p->dstate, p->chunk_size);
   if (k->backward(a, b, static_cast<hipStream_t>(stream)) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;

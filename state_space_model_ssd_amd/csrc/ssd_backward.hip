@@ -559,7 +559,8 @@ template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
     ChunkMap cm, int nslots, const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ cb,
     const float* __restrict__ delta, const float* __restrict__ dAcs, int H, int G, int HB,
-    float* __restrict__ dcbp, float* __restrict__ rowpart, float* __restrict__ colpart) {
+    float* __restrict__ dcbp, float* __restrict__ rowpart, float* __restrict__ colpart,
+    float* __restrict__ ddot) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   __shared__ float cpart[16][64];
   // the head's running sums (rows, columns) and steps
@@ -630,6 +631,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
     for (int i = 0; i < 4; ++i) {
       const float r = row16_sum(rsum[i]);
       if ((threadIdx.x & 15) == 0) rowpart[(jh * LT + st) * L + l0 + tm + i] = r;
+    }
+    // on the diagonal, V[l,l] before its decay (1) is dy_l . x_l: the
+    // per-token dot of dD, taken here instead of re-reading dy and x
+    if (lt == st && tm == tn) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (l0 + tm + i < len) ddot[jh * L + l0 + tm + i] = acc[i][i];
     }
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) cpart[threadIdx.x >> 4][tn + jn] = csum[jn];
@@ -1059,11 +1067,11 @@ __global__ __launch_bounds__(L) void bwd_token_kernel(
     const float* __restrict__ delta, const float* __restrict__ dAcs,
     const T* __restrict__ states_in, const float* __restrict__ dS,
     const float* __restrict__ rowpart, const float* __restrict__ colpart,
-    const float* __restrict__ interpart, const float* __restrict__ vxpart, int H, float dt_min,
+    const float* __restrict__ interpart, const float* __restrict__ vxpart,
+    const float* __restrict__ ddot, int H, float dt_min,
     float dt_max, float* __restrict__ ddt, float* __restrict__ dA_part,
     float* __restrict__ dD_part, float* __restrict__ dbias_part) {
   __shared__ float red[3 * (L / kWave)];
-  __shared__ float dds[L];                 // dy . x per token
   constexpr int LT = L / 64, NT = (N + 63) / 64;
   const int h = blockIdx.x, j = blockIdx.y, k = threadIdx.x;
   const ChunkDesc cd = cm.desc(j);
@@ -1091,37 +1099,7 @@ __global__ __launch_bounds__(L) void bwd_token_kernel(
       vxe += vxpart[(jh * NT + nt) * L + k];
     }
   }
-  // dy_k . x_k per token: the PPR 16-byte pieces of a row are read by PPR
-  // consecutive lanes (coalesced rows), every load issued before use, and
-  // summed across those lanes
-  {
-    constexpr int V = 16 / sizeof(T), PPR = P / V, UB = PPR < 8 ? PPR : 8;
-    static_assert(P % V == 0 && kWave % PPR == 0, "row pieces");
-    for (int u0 = 0; u0 < PPR; u0 += UB) {
-      uint4 ry[UB], rx[UB];
-#pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        const int i = k + L * (u0 + u), tok = i / PPR, pc = i % PPR;
-        const int64_t o = ((int64_t)(cd.start + tok) * H + h) * P + pc * V;
-        ry[u] = load16(dy + o, tok < len);
-        rx[u] = load16(x + o, tok < len);
-      }
-#pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        const int i = k + L * (u0 + u), tok = i / PPR;
-        float vy[V], vx[V], part = 0.f;
-        unpack16<T>(ry[u], vy);
-        unpack16<T>(rx[u], vx);
-#pragma unroll
-        for (int e = 0; e < V; ++e) part += vy[e] * vx[e];
-#pragma unroll
-        for (int off = 1; off < PPR; off <<= 1) part += __shfl_xor(part, off);
-        if (i % PPR == 0) dds[tok] = part;
-      }
-    }
-    __syncthreads();
-    dd = valid ? dds[k] : 0.f;
-  }
+  dd = valid ? ddot[jh * L + k] : 0.f;    // dy_k . x_k, from the V tiles
   const float vs = dk * vxe;
   float gh = 0.f;
   static_assert((P * N) % (4 * L) == 0, "state elements per thread");
@@ -1229,7 +1207,7 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   const int hpg = H / G, HB = bwd_head_blocks(hpg, (int64_t)(LT * (LT + 1) / 2) * G * mc);
   hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * (LT + 1) / 2 * G * HB)),
                      dim3(kBwdThreads), 0, s, cm, mc, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb,
-                     b.rowpart, b.colpart);
+                     b.rowpart, b.colpart, b.ddot);
   hipLaunchKernelGGL((bwd_bc_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * NT * 2 * G * HB)),
                      dim3(kBwdThreads), 0, s, cm, mc, x, B, C, dy, a.delta, a.dAcs, hin, b.dS, H, G,
                      HB, b.dBh, b.dCh, b.interpart, b.vxpart);
@@ -1244,8 +1222,8 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
                      (T*)b.dx);
   hipLaunchKernelGGL((bwd_token_kernel<T, P, N, L>), dim3(H, mc), dim3(L), 0, s, cm, x, a.dt,
                      a.dt_bias, a.A, dy, a.delta, a.dAcs, hin, b.dS, b.rowpart, b.colpart,
-                     b.interpart, b.vxpart, H, a.dt_min, a.dt_max, b.ddt, b.dA_part, b.dD_part,
-                     b.dbias_part);
+                     b.interpart, b.vxpart, b.ddot, H, a.dt_min, a.dt_max, b.ddt, b.dA_part,
+                     b.dD_part, b.dbias_part);
   hipLaunchKernelGGL(bwd_head_reduce_kernel, dim3(H), dim3(kWave), 0, s, b.dA_part, b.dD_part,
                      b.dbias_part, H, mc, b.dA, b.dD, b.ddt_bias);
   return hipGetLastError();

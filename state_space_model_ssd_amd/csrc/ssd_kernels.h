@@ -79,6 +79,7 @@ struct BwdArgs {
   float* dA_part;           // [max_chunks][H]
   float* dD_part;           // [max_chunks][H]
   float* dbias_part;        // [max_chunks][H]
+  float* ddot;              // [max_chunks][H][L]: dy_t . x_t per token
 };
 
 // Stage 0: logical chunk table of a packed batch.
