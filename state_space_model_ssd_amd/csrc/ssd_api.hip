@@ -235,7 +235,7 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
 
 // The backward's regions follow the forward's in its workspace.
 struct BwdLayout {
-  size_t Q, dS, dcb, dBh, dCh, rowpart, colpart, interpart, vxpart, dA_part, dD_part, dbias_part, ddot,
+  size_t Q, dS, dS16, dcb, dBh, dCh, rowpart, colpart, interpart, vxpart, dA_part, dD_part, dbias_part, ddot,
       total;
 };
 
@@ -245,6 +245,7 @@ void bwd_layout_of(const ssd_problem_t* p, const ssd_workspace_layout_t& w, BwdL
   size_t off = w.total_bytes;
   b->Q = off;          off = align_up(off + sizeof(float) * mc * H * PN);
   b->dS = off;         off = align_up(off + sizeof(float) * mc * H * PN);
+  b->dS16 = off;       off = align_up(off + sizeof(uint16_t) * mc * H * PN);
   b->dcb = off;        off = align_up(off + sizeof(float) * mc * H * L * L);
   b->dBh = off;        off = align_up(off + sizeof(float) * mc * H * L * N);
   b->dCh = off;        off = align_up(off + sizeof(float) * mc * H * L * N);
@@ -294,6 +295,7 @@ ssd_status_t run_bwd(const ssd_problem_t* p, const void* x, const float* dt, con
   b.dD = dD; b.ddt_bias = ddt_bias; b.dinit = dinit;
   b.Q = reinterpret_cast<float*>(base + bl.Q);
   b.dS = reinterpret_cast<float*>(base + bl.dS);
+  b.dS16 = base + bl.dS16;
   b.dcb = reinterpret_cast<float*>(base + bl.dcb);
   b.dBh = reinterpret_cast<float*>(base + bl.dBh);
   b.dCh = reinterpret_cast<float*>(base + bl.dCh);

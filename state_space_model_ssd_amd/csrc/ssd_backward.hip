@@ -431,13 +431,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_tiled_kernel(
   }
 }
 
+// Four consecutive values rounded once to T (8- or 16-byte store).
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  const uint32_t lo = (uint32_t)__builtin_bit_cast(unsigned short, static_cast<bf16>(a)) |
+                      ((uint32_t)__builtin_bit_cast(unsigned short, static_cast<bf16>(b)) << 16);
+  const uint32_t hi = (uint32_t)__builtin_bit_cast(unsigned short, static_cast<bf16>(c)) |
+                      ((uint32_t)__builtin_bit_cast(unsigned short, static_cast<bf16>(d)) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+
 // 2. Reverse chain, four consecutive state elements per thread (16-byte
 // loads and stores; the next chunk's Q is loaded before this one's dS is
 // stored); grid (ceil(P*N / 1024), H, nstates).
 __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(
     ChunkMap cm, const float* __restrict__ Q, const float* __restrict__ dAcs,
     const float* __restrict__ dfinal, int H, int PN, int L, float* __restrict__ dS,
-    float* __restrict__ dinit) {
+    bf16* __restrict__ dS16, float* __restrict__ dinit) {
   const int e = (blockIdx.x * kBwdThreads + threadIdx.x) * 4;
   if (e >= PN) return;                     // PN is a multiple of 4
   const int h = blockIdx.y, s = blockIdx.z;
@@ -451,6 +463,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(
     const float4 qj = q;
     if (j > r.x) q = *reinterpret_cast<const float4*>(Q + (jh - H) * PN + e);
     *reinterpret_cast<float4*>(dS + jh * PN + e) = g;
+    if (dS16) store4(dS16 + jh * PN + e, g.x, g.y, g.z, g.w);   // rounded once, for the MFMA operands
     const int len = cm.desc(j).len;
     const float dec = len > 0 ? expf(dAcs[jh * L + len - 1]) : 1.f;
     g = make_float4(dec * g.x + qj.x, dec * g.y + qj.y, dec * g.z + qj.z, dec * g.w + qj.w);
@@ -532,17 +545,6 @@ __device__ __forceinline__ float4 load4_f32(const bf16* p) {
   const uint2 u = *reinterpret_cast<const uint2*>(p);
   return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-}
-// Four consecutive values rounded once to T (8- or 16-byte store).
-__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-}
-__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
-  const uint32_t lo = (uint32_t)__builtin_bit_cast(unsigned short, static_cast<bf16>(a)) |
-                      ((uint32_t)__builtin_bit_cast(unsigned short, static_cast<bf16>(b)) << 16);
-  const uint32_t hi = (uint32_t)__builtin_bit_cast(unsigned short, static_cast<bf16>(c)) |
-                      ((uint32_t)__builtin_bit_cast(unsigned short, static_cast<bf16>(d)) << 16);
-  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
 }
 
 // 3a. For each head, V[l,s] = exp(a_l - a_s) (dy_l . x_s) for s <= l as
@@ -668,6 +670,7 @@ template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
     ChunkMap cm, int nslots, const T* __restrict__ B, const T* __restrict__ dy, const T* __restrict__ cb,
     const float* __restrict__ delta, const float* __restrict__ dAcs, const float* __restrict__ dS,
+    const bf16* __restrict__ dS16,
     const float* __restrict__ D, int H, int G, T* __restrict__ dx) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   __shared__ float es[L], av[L];
@@ -701,7 +704,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
     const MfmaQuarter q;
     f32x4 d[2][2];
     zero_quarter(d);
-    mfma_rows<N>(q, B + ((t0 + s0) * G + g) * N, (int64_t)G * N, len - s0, dS + (jh * P + p0) * N, N,
+    mfma_rows<N>(q, B + ((t0 + s0) * G + g) * N, (int64_t)G * N, len - s0, dS16 + (jh * P + p0) * N, N,
                  P - p0, d);
     __syncthreads();                       // es, av staged
 #pragma unroll
@@ -801,7 +804,8 @@ template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
     ChunkMap cm, int nslots, const T* __restrict__ x, const T* __restrict__ B, const T* __restrict__ C,
     const T* __restrict__ dy, const float* __restrict__ delta, const float* __restrict__ dAcs,
-    const T* __restrict__ states_in, const float* __restrict__ dS, int H, int G, int HB,
+    const T* __restrict__ states_in, const float* __restrict__ dS, const bf16* __restrict__ dS16,
+    int H, int G, int HB,
     float* __restrict__ dBh, float* __restrict__ dCh, float* __restrict__ interpart,
     float* __restrict__ vxpart) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
@@ -853,7 +857,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
         const int r = i >> 3, c = (i & 7) * 8;
         const bool ok = n0 + c < N;
         const bf16x8 v = which == 0 ? frag_row(states_in + (jh * P + r) * N + n0 + c, ok)
-                                    : frag_f32(dS + (jh * P + r) * N + n0 + c, ok);
+                                    : frag_row(dS16 + (jh * P + r) * N + n0 + c, ok);
         *reinterpret_cast<bf16x8*>(&kt[r * kKtPitch + c]) = v;
       }
       __syncthreads();
@@ -1199,7 +1203,8 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
                      dim3(kBwdThreads), 0, s, cm, mc, dy, C, a.dAcs, H, G, b.Q);
   static_assert((P * N) % 4 == 0, "four state elements per thread");
   hipLaunchKernelGGL(bwd_chain_kernel, dim3((PN / 4 + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
-                     dim3(kBwdThreads), 0, s, cm, b.Q, a.dAcs, b.dfinal, H, PN, L, b.dS, b.dinit);
+                     dim3(kBwdThreads), 0, s, cm, b.Q, a.dAcs, b.dfinal, H, PN, L, b.dS,
+                     sizeof(T) == 2 ? static_cast<bf16*>(b.dS16) : nullptr, b.dinit);
   constexpr int LT = L / 64;
   // head blocks per group for the summed dCB and dB/dC state terms: the
   // fewest that fill the GPU with 3a's workgroups (their partial sums fit
@@ -1209,7 +1214,8 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
                      dim3(kBwdThreads), 0, s, cm, mc, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb,
                      b.rowpart, b.colpart, b.ddot);
   hipLaunchKernelGGL((bwd_bc_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * NT * 2 * G * HB)),
-                     dim3(kBwdThreads), 0, s, cm, mc, x, B, C, dy, a.delta, a.dAcs, hin, b.dS, H, G,
+                     dim3(kBwdThreads), 0, s, cm, mc, x, B, C, dy, a.delta, a.dAcs, hin, b.dS,
+                     static_cast<const bf16*>(b.dS16), H, G,
                      HB, b.dBh, b.dCh, b.interpart, b.vxpart);
   if (HB > 1)
     hipLaunchKernelGGL((bwd_dcb_sum_kernel<L>), dim3((L * L / 4 + kBwdThreads - 1) / kBwdThreads, G, mc),
@@ -1218,7 +1224,8 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
                      dim3(kBwdThreads), 0, s, cm, mc, B, C, b.dcb, b.dBh, b.dCh, H, G, HB, (T*)b.dB,
                      (T*)b.dC);
   hipLaunchKernelGGL((bwd_dx_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * ((P + 63) / 64) * H)),
-                     dim3(kBwdThreads), 0, s, cm, mc, B, dy, cb, a.delta, a.dAcs, b.dS, a.D, H, G,
+                     dim3(kBwdThreads), 0, s, cm, mc, B, dy, cb, a.delta, a.dAcs, b.dS,
+                     static_cast<const bf16*>(b.dS16), a.D, H, G,
                      (T*)b.dx);
   hipLaunchKernelGGL((bwd_token_kernel<T, P, N, L>), dim3(H, mc), dim3(L), 0, s, cm, x, a.dt,
                      a.dt_bias, a.A, dy, a.delta, a.dAcs, hin, b.dS, b.rowpart, b.colpart,

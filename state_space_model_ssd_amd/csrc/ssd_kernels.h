@@ -68,6 +68,7 @@ struct BwdArgs {
   float* dinit;             // nullable
   float* Q;                 // [max_chunks][H][P*N]
   float* dS;                // [max_chunks][H][P*N]
+  void* dS16;               // [max_chunks][H][P*N] bf16: dS rounded once (bf16 inputs)
   float* dcb;               // [max_chunks][H][L][L] floats; holds [max_chunks][G][HB][L][L]: sums
                             // of delta_s exp(a_l - a_s) dy_l . x_s (s <= l) over head blocks
   float* rowpart;           // [max_chunks][H][L/64][L]
