@@ -6,10 +6,16 @@ already resident in HBM.  Default workload: the Mamba-2 layer shape (batch 2,
 seqlen 4096, 24 heads, headdim 64, dstate 128, 1 group, chunk 256, bf16
 x/B/C, fp32 accumulation).
 
-Prints ONE JSON line.  `value` is tokens/s of back-to-back steps replayed
-from a HIP graph; `roofline` covers the slowest stage, timed live with HIP
-events on the stream its kernel runs on; `cpu_baseline` is the fp64 CPU
-oracle timed on this host's cores on the same workload.
+Prints ONE JSON line.  `value` is tokens/s over the K timed steps, replayed
+back to back from a HIP graph between two HIP events; the median, p10 and
+p90 of one step come from 20 further samples of 5 replays each (the clova.ai
+page reports the median of 100 runs after 10 warm-ups, section "So how much
+faster is it?").  `roofline` covers the slowest launch of the step, timed
+live with HIP events on the stream its kernel runs on, warm and after the
+last-level cache is evicted; `cpu_baseline` is the fp64 CPU oracle timed on
+this host's cores on the same workload.  `workloads` repeats the step and
+launch timings on the other full-size configurations (training batch, long
+context, packed batch).
 """
 from __future__ import annotations
 
@@ -31,6 +37,7 @@ F32_PEAK_TFLOPS = 157.3        # dense MFMA fp32, published
 STAGE_ORDER = ("plan", "chunk_cumsum", "bmm_chunk", "chunk_state", "state_passing", "chunk_scan")
 # What one bf16 forward step launches: stages 1-3 run as one fused launch.
 STEP_LAUNCHES = ("plan", "front", "state_passing", "chunk_scan")
+FLUSH_BYTES = 1 << 30          # written before a cold measurement: 4x the last-level cache
 
 
 def log(msg):
@@ -69,6 +76,15 @@ def algorithmic_work(prob, nchunks):
     return work
 
 
+def fused_minimum_bytes(prob):
+    """What any forward must move: x, dt, B, C and the initial states read,
+    y and the final states written."""
+    tok = prob.batch * prob.seqlen
+    H, P, N, G = prob.nheads, prob.headdim, prob.dstate, prob.ngroups
+    e = 2 if prob.dtype == "bf16" else 4
+    return 2 * e * tok * H * P + 4 * tok * H + 2 * e * tok * G * N + 8 * prob.nseq * H * P * N
+
+
 STAGE_SOURCE = {"plan": "ssd_prep.hip", "chunk_cumsum": "ssd_prep.hip", "front": "ssd_chunk_state.hip",
                 "bmm_chunk": "ssd_bmm.hip", "chunk_state": "ssd_chunk_state.hip",
                 "state_passing": "ssd_state_passing.hip", "chunk_scan": "ssd_chunk_scan.hip"}
@@ -94,7 +110,6 @@ def measured_traffic(kernel: str, workload_tag: str):
     profiles/<kernel>_<workload>_traffic.md (FETCH_SIZE and WRITE_SIZE passes,
     scaled by a plain copy of known size), or None when there is none or the
     kernel source changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_traffic.md")
     if not os.path.exists(path):
         return None
@@ -103,8 +118,7 @@ def measured_traffic(kernel: str, workload_tag: str):
         if ":" in line and not line.startswith(("|", "#", " ")):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    sha = kernel_source_hash(kernel)
-    if fields.get("kernel_source_sha256_16") != sha:
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -125,11 +139,199 @@ def env_info():
     return info
 
 
+def percentiles(vals):
+    """median, p10, p90 (nearest rank) of a list of numbers."""
+    v = sorted(vals)
+    pick = lambda q: v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    return {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9), "n": len(v)}
+
+
+class Workload:
+    """One workload's device inputs, buffers and a HIP graph of one step."""
+
+    def __init__(self, k, torch, binding, tuning_arg=None):
+        from state_space_model_ssd_amd.inputs import workload_inputs, WORKLOAD_NAMES
+        from state_space_model_ssd_amd import tuning
+        self.torch, self.binding, self.k = torch, binding, k
+        dev = torch.device("cuda:0")
+        log(f"[bench] workload {k}: drawing inputs")
+        self.prob, self.inp = workload_inputs(k)
+        prob = self.prob
+        self.name = WORKLOAD_NAMES[k]
+        self.d = {n: (v.to(dev) if isinstance(v, torch.Tensor) else v) for n, v in self.inp.items()}
+        self.cprob = binding.make_problem(prob.batch, prob.seqlen, prob.nheads, prob.headdim,
+                                          prob.dstate, prob.ngroups, prob.chunk_size,
+                                          1 if prob.dtype == "bf16" else 0,
+                                          nseq=len(prob.seq_lens) if prob.seq_lens else 0)
+        self.lay = binding.workspace_layout(self.cprob)
+        self.pinned = tuning_arg
+        self.tuned = tuning_arg if tuning_arg is not None else tuning.lookup(self.cprob)
+        self.tune_arg = tuning_arg if tuning_arg is not None else "config"
+        self.tuning_record = {"source": "pinned" if tuning_arg is not None else
+                              "tuned config" if self.tuned else "library's own choice",
+                              "key": tuning.shape_key(self.cprob), "choice": self.tuned or {},
+                              "library_choice": binding.fwd_choices(self.cprob)}
+        self.ws = torch.empty(self.lay.total_bytes, dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(self.d["x"])
+        self.fin = torch.empty((prob.nseq, prob.nheads, prob.headdim, prob.dstate),
+                               dtype=torch.float32, device=dev)
+        self.tokens = prob.batch * prob.seqlen
+        self.graph = None
+
+    def step(self, stages=None):
+        b = self.binding
+        self.binding.ssd_fwd(self.d["x"], self.d["dt"], self.d["A"], self.d["B"], self.d["C"],
+                             self.prob.chunk_size, D=self.d["D"], dt_bias=self.d["dt_bias"],
+                             initial_states=self.d["init"], cu_seqlens=self.d["cu_seqlens"],
+                             out=self.out, final_states=self.fin, workspace=self.ws,
+                             stages=b.STAGE_ALL if stages is None else stages,
+                             tuning=self.tune_arg)
+
+    def nchunks(self):
+        if self.prob.seq_lens:
+            return int(self.binding.intermediates(self.ws, self.cprob)["seq_chunks"][-1].item())
+        return self.lay.max_chunks
+
+    def capture(self, warmup):
+        torch = self.torch
+        for _ in range(max(warmup, 1)):
+            self.step()
+        torch.cuda.synchronize()
+        self.ref_out = self.out.clone()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            self.step()                  # settle on the side stream before capture
+            torch.cuda.synchronize()
+            with torch.cuda.graph(self.graph, stream=stream):
+                self.step()
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            self.graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(self.out, self.ref_out):
+            raise RuntimeError("graph replay differs from the eager forward")
+
+    def time_replays(self, steps):
+        """K replays back to back between two HIP events: (total ms, wall s)."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            self.graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), time.perf_counter() - wall0
+
+    def step_samples(self, batches, per_batch):
+        """Per-step ms of `batches` samples, each the mean of `per_batch`
+        replays back to back between two HIP events (an event recorded
+        between every two replays would add its own cost to each step)."""
+        torch = self.torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(batches):
+            for _ in range(per_batch):
+                self.graph.replay()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) / per_batch for i in range(batches)]
+
+    def time_cold(self, reps, flush, fn):
+        """Median over reps of fn() timed alone, each after a write of the
+        flush buffer evicts the last-level cache (ms list)."""
+        torch = self.torch
+        cur = torch.cuda.current_stream()
+        res = []
+        for _ in range(reps):
+            flush.fill_(1.0)
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(cur)
+            fn()
+            c1.record(cur)
+            torch.cuda.synchronize()
+            res.append(c0.elapsed_time(c1))
+        return res
+
+    def time_launches(self, names, reps):
+        """Average us of each launch: reps back-to-back launches between two
+        HIP events on the launch stream, queued behind a GPU sleep so the CPU
+        is never the limit."""
+        torch, b = self.torch, self.binding
+        cur = torch.cuda.current_stream()
+        masks = dict(b.STAGES)
+        masks["front"] = b.STAGES["chunk_cumsum"] | b.STAGES["bmm_chunk"] | b.STAGES["chunk_state"]
+        res = {}
+        for name in names:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            try:
+                torch.cuda._sleep(20_000_000)
+            except Exception:
+                pass
+            e0.record(cur)
+            for _ in range(reps):
+                self.step(masks[name])
+            e1.record(cur)
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) * 1e3 / reps
+        return res
+
+    def masks(self):
+        b = self.binding
+        m = dict(b.STAGES)
+        m["front"] = b.STAGES["chunk_cumsum"] | b.STAGES["bmm_chunk"] | b.STAGES["chunk_state"]
+        return m
+
+
+def stage_record(work, name, us, dtype):
+    nbytes, flops = work[name]
+    rec = {"us": round(us, 3), "alg_bytes": int(nbytes),
+           "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+           "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    if flops:
+        peak = BF16_PEAK_TFLOPS if dtype == "bf16" else F32_PEAK_TFLOPS
+        rec["tflops"] = round(flops / (us * 1e-6) / 1e12, 2)
+        rec["mfma_frac"] = round(flops / (us * 1e-6) / 1e12 / peak, 4)
+    return rec
+
+
+def side_workload(k, torch, binding, flush, steps, warmup, reps):
+    """Step and launch timings of another full-size workload (warm and cold)."""
+    w = Workload(k, torch, binding)
+    w.capture(warmup)
+    total, _ = w.time_replays(steps)
+    per = w.step_samples(10, 5)
+    cold = w.time_cold(5, flush, w.graph.replay)
+    nch = w.nchunks()
+    work = algorithmic_work(w.prob, nch)
+    launches = [n for n in STEP_LAUNCHES if n != "plan" or w.prob.seq_lens]
+    us = w.time_launches(launches, reps)
+    if not torch.equal(w.out, w.ref_out):
+        raise RuntimeError(f"workload {k}: stage-by-stage run differs from the eager forward")
+    step_pct = {q: round(v * 1e3, 2) for q, v in percentiles(per).items() if q != "n"}
+    cold_pct = {q: round(v * 1e3, 2) for q, v in percentiles(cold).items() if q != "n"}
+    rec = {"workload": w.name, "tokens": w.tokens, "chunks": nch,
+           "tokens_per_s": round(w.tokens / (step_pct["median"] * 1e-6), 1),
+           "step_us_warm": step_pct, "step_us_cold": cold_pct,
+           "step_us_mean_warm": round(total * 1e3 / steps, 2),
+           "fused_minimum_bytes": fused_minimum_bytes(w.prob),
+           "launches": {n: stage_record(work, n, us[n], w.prob.dtype) for n in launches},
+           "tuning": w.tuning_record}
+    del w
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, help="1..6")
     ap.add_argument("--tuning", default=None, metavar="JSON",
                     help='pin kernel choices, e.g. \'{"sp_blocks": 1}\' (default: the tuned '
@@ -140,6 +342,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward (ssd_bwd) on the same workload")
     ap.add_argument("--backward-reps", type=int, default=5)
+    ap.add_argument("--side-workloads", default="3,4,5",
+                    help="comma-separated other workloads to time after the main one "
+                         "('' for none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, copy a buffer of MIB MiB three times (a plain copy "
                          "kernel of known size, for scaling HBM byte counters)")
@@ -151,147 +356,74 @@ def main():
 
     import torch
     from state_space_model_ssd_amd import binding
-    from state_space_model_ssd_amd.inputs import workload_inputs, WORKLOAD_NAMES
 
     torch.cuda.init()
     dev = torch.device("cuda:0")
     binding.load_library()
-    log(f"[bench] workload {args.workload}: drawing inputs")
-    prob, inp = workload_inputs(args.workload)
-    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
-    cprob = binding.make_problem(prob.batch, prob.seqlen, prob.nheads, prob.headdim, prob.dstate,
-                                 prob.ngroups, prob.chunk_size, 1 if prob.dtype == "bf16" else 0,
-                                 nseq=len(prob.seq_lens) if prob.seq_lens else 0)
-    lay = binding.workspace_layout(cprob)
-    from state_space_model_ssd_amd import tuning
     pinned = json.loads(args.tuning) if args.tuning else None
-    tuned = pinned if pinned is not None else tuning.lookup(cprob)
-    tune_arg = pinned if pinned is not None else "config"   # the binding's own lookup
-    ws = torch.empty(lay.total_bytes, dtype=torch.uint8, device=dev)
-    out = torch.empty_like(d["x"])
-    fin = torch.empty((prob.nseq, prob.nheads, prob.headdim, prob.dstate), dtype=torch.float32,
-                      device=dev)
-
-    def step(stages=binding.STAGE_ALL):
-        binding.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, D=d["D"],
-                        dt_bias=d["dt_bias"], initial_states=d["init"],
-                        cu_seqlens=d["cu_seqlens"], out=out, final_states=fin, workspace=ws,
-                        stages=stages, tuning=tune_arg)
-
+    w = Workload(args.workload, torch, binding, pinned)
+    prob, inp, d = w.prob, w.inp, w.d
     log("[bench] warmup")
-    for _ in range(max(args.warmup, 1)):
-        step()
-    torch.cuda.synchronize()
-    nchunks = int(binding.intermediates(ws, cprob)["seq_chunks"][-1].item()) \
-        if prob.seq_lens else lay.max_chunks
-    ref_out = out.clone()
+    w.capture(args.warmup)
+    nchunks = w.nchunks()
 
     # --- whole step: a HIP graph of one forward, replayed back to back
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        step()                       # settle on the side stream before capture
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph, stream=stream):
-            step()
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    if not torch.equal(out, ref_out):
-        raise RuntimeError("graph replay differs from the eager forward")
     log(f"[bench] timing {args.steps} graph replays")
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record()
-    for _ in range(args.steps):
-        graph.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    tokens = prob.batch * prob.seqlen
+    total_ms, wall = w.time_replays(args.steps)
+    ms_per_step = total_ms / args.steps
+    per_ms = w.step_samples(20, 5)
+    tokens = w.tokens
     value = tokens / (ms_per_step * 1e-3)
+    step_pct = {q: round(v * 1e3, 2) for q, v in percentiles(per_ms).items() if q != "n"}
 
-    # --- context: the same step with cold caches (a 1 GiB write evicts the
-    # 256 MB last-level cache before each replay; only the replay is timed),
-    # and what a plain device copy sustains on this GPU
+    # --- the same step with cold caches (a 1 GiB write evicts the 256 MB
+    # last-level cache before each replay; only the replay is timed), and
+    # what a plain device copy sustains on this GPU
     log("[bench] cold-cache steps and copy bandwidth")
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    cold = []
-    for _ in range(10):
-        flush.fill_(1.0)
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record()
-        graph.replay()
-        c1.record()
-        torch.cuda.synchronize()
-        cold.append(c0.elapsed_time(c1))
-    ms_cold = sorted(cold)[len(cold) // 2]
-    src = flush
-    dst = torch.empty_like(src)
-    dst.copy_(src)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    cold = w.time_cold(20, flush, w.graph.replay)
+    cold_pct = {q: round(v * 1e3, 2) for q, v in percentiles(cold).items() if q != "n"}
+    dst = torch.empty_like(flush)
+    dst.copy_(flush)
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0.record()
     for _ in range(5):
-        dst.copy_(src)
+        dst.copy_(flush)
     c1.record()
     torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del flush, src, dst
+    copy_gbs = 2 * flush.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del dst
 
-    # --- per stage: R back-to-back launches between two events on the
-    # launch stream, queued behind a GPU sleep so the CPU is never the limit
-    log("[bench] per-stage timing")
+    # --- per launch, warm: R back-to-back launches between two events
+    log("[bench] per-launch timing")
     work = algorithmic_work(prob, nchunks)
-    R = args.stage_reps
-    stages, singles = {}, {}
-    cur = torch.cuda.current_stream()
     fused = prob.dtype == "bf16"
-    step_launches = STEP_LAUNCHES if fused else STAGE_ORDER
-    masks = dict(binding.STAGES)
-    masks["front"] = binding.STAGES["chunk_cumsum"] | binding.STAGES["bmm_chunk"] | \
-        binding.STAGES["chunk_state"]
-    names = list(step_launches) + ([n for n in STAGE_ORDER if n not in step_launches])
-    for name in names:
-        if name == "plan" and not prob.seq_lens:
-            continue
-        bit = masks[name]
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        try:
-            torch.cuda._sleep(20_000_000)
-        except Exception:
-            pass
-        e0.record(cur)
-        for _ in range(R):
-            step(bit)
-        e1.record(cur)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / R
-        nbytes, flops = work[name]
-        rec = {"us": round(us, 3), "alg_bytes": int(nbytes),
-               "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
-               "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        if flops:
-            peak = BF16_PEAK_TFLOPS if prob.dtype == "bf16" else F32_PEAK_TFLOPS
-            rec["tflops"] = round(flops / (us * 1e-6) / 1e12, 2)
-            rec["mfma_frac"] = round(flops / (us * 1e-6) / 1e12 / peak, 4)
-        (stages if name in step_launches else singles)[name] = rec
-    if not torch.equal(out, ref_out):
+    step_launches = [n for n in (STEP_LAUNCHES if fused else STAGE_ORDER)
+                     if n != "plan" or prob.seq_lens]
+    singles_names = [n for n in STAGE_ORDER if n not in step_launches and n != "plan"]
+    us = w.time_launches(step_launches + singles_names, args.stage_reps)
+    stages = {n: stage_record(work, n, us[n], prob.dtype) for n in step_launches}
+    singles = {n: stage_record(work, n, us[n], prob.dtype) for n in singles_names}
+    if not torch.equal(w.out, w.ref_out):
         raise RuntimeError("stage-by-stage run differs from the eager forward")
     dom = max(stages, key=lambda k: stages[k]["us"])
     ds = stages[dom]
-    wtag = WORKLOAD_NAMES[args.workload].split()[0]
+    # the dominant launch alone after the cache is evicted: what it reads
+    # comes from HBM (the stages before it have left their outputs in place)
+    masks = w.masks()
+    cold_dom = w.time_cold(20, flush, lambda: w.step(masks[dom]))
+    cold_dom_us = percentiles(cold_dom)["median"] * 1e3
+    cold_rec = stage_record(work, dom, cold_dom_us, prob.dtype)
+    wtag = w.name.split()[0]
     traffic = measured_traffic(dom, wtag)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": ds["gbs"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ds["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "unit": "GB/s", "frac": ds["hbm_frac"], "traffic": traffic,
                 "traffic_unit": "bytes per launch", "launch_us": ds["us"],
-                "alg_bytes_per_launch": ds["alg_bytes"]}
-    total_bytes = sum(work[n][0] for n in step_launches if n in work and
-                      (n != "plan" or prob.seq_lens))
+                "alg_bytes_per_launch": ds["alg_bytes"],
+                "cold": {"launch_us_median": round(cold_dom_us, 3), "achieved": cold_rec["gbs"],
+                         "frac": cold_rec["hbm_frac"]}}
+    total_bytes = sum(work[n][0] for n in step_launches)
+    del flush
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
@@ -307,14 +439,15 @@ def main():
     backward = None
     if not args.no_backward:
         log("[bench] backward")
+        cur = torch.cuda.current_stream()
         gb = torch.Generator().manual_seed(12345)
         dy = torch.randn(inp["x"].shape, generator=gb).to(inp["x"].dtype).to(dev)
         dfin = torch.randn((prob.nseq, prob.nheads, prob.headdim, prob.dstate), generator=gb).to(dev)
 
-        def bstep(wsb=None):
+        def bstep(wsb=None, after_fwd=False):
             return binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, dy,
                                    dfin, D=d["D"], dt_bias=d["dt_bias"], initial_states=d["init"],
-                                   cu_seqlens=d["cu_seqlens"], workspace=wsb)
+                                   cu_seqlens=d["cu_seqlens"], workspace=wsb, after_fwd=after_fwd)
         wsb = bstep()["workspace"]
         bstep(wsb)
         torch.cuda.synchronize()
@@ -340,16 +473,11 @@ def main():
         binding.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, D=d["D"],
                         dt_bias=d["dt_bias"], initial_states=d["init"], cu_seqlens=d["cu_seqlens"],
                         workspace=wsb, tuning=None)
-
-        def astep():
-            return binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, dy,
-                                   dfin, D=d["D"], dt_bias=d["dt_bias"], initial_states=d["init"],
-                                   cu_seqlens=d["cu_seqlens"], workspace=wsb, after_fwd=True)
-        astep()
+        bstep(wsb, True)
         torch.cuda.synchronize()
         b0.record(cur)
         for _ in range(args.backward_reps):
-            astep()
+            bstep(wsb, True)
         b1.record(cur)
         torch.cuda.synchronize()
         aus = b0.elapsed_time(b1) * 1e3 / args.backward_reps
@@ -361,7 +489,21 @@ def main():
                     "note": "ssd_bwd: gradients of every input; recomputes the forward's "
                             "stages 0-4 (us_after_fwd: ssd_bwd_after_fwd, which reuses a "
                             "forward's intermediates); per-kernel times in profiles/"}
-        del wsb
+        del wsb, dy, dfin
+    main_tuning = w.tuning_record
+    del w
+    torch.cuda.empty_cache()
+
+    # --- the other full-size workloads: warm and cold step, per launch
+    side = {}
+    for k in [int(v) for v in args.side_workloads.split(",") if v.strip()]:
+        if k == args.workload:
+            continue
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        side[str(k)] = side_workload(k, torch, binding, flush, steps=20,
+                                     warmup=3, reps=max(5, args.stage_reps // 5))
+        del flush
+        torch.cuda.empty_cache()
 
     # --- CPU baseline: the fp64 oracle on this host's cores, same workload
     cpu = None
@@ -381,6 +523,7 @@ def main():
                "sample": f"whole workload ({tokens} tokens x {prob.nheads} heads) repeated "
                          f"{reps} time(s), {t_cpu:.1f} s, each including the fp64 upcast"}
 
+    from state_space_model_ssd_amd.inputs import WORKLOAD_NAMES
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -392,24 +535,29 @@ def main():
                    "chunk_size": prob.chunk_size, "tokens": tokens, "chunks": nchunks},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "tuning": {"source": "pinned" if pinned is not None else
-                   "tuned config" if tuned else "library's own choice",
-                   "key": tuning.shape_key(cprob), "choice": tuned or {}},
+        "step_us_warm": step_pct,
+        "step_us_cold": cold_pct,
+        "tokens_per_s_median": round(tokens / (step_pct["median"] * 1e-6), 1),
+        "tuning": main_tuning,
         "stages": stages,
         "stages_unfused": singles,
         "backward": backward,
         "step_alg_bytes": int(total_bytes),
         "step_alg_gbs": round(total_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "timing": "HIP-graph replays back to back (warm caches); per launch: "
-                  f"{R} back-to-back launches between HIP events; 'stages' are the launches "
-                  "of one step, 'stages_unfused' the stages a fused launch covers, run alone",
+        "fused_minimum_bytes": fused_minimum_bytes(prob),
+        "workloads": side,
+        "timing": "value: tokens over the mean of K HIP-graph replays back to back between "
+                  "two HIP events (warm caches); step_us_warm: median/p10/p90 over 20 "
+                  "samples, each the mean of 5 replays back to back between two events; "
+                  "cold: each replay (or launch) alone after a "
+                  "1 GiB write evicts the last-level cache; per launch: "
+                  f"{args.stage_reps} back-to-back launches between HIP events; 'stages' are "
+                  "the launches of one step, 'stages_unfused' the stages a fused launch "
+                  "covers, run alone",
         "wall_s_timed_region": round(wall, 4),
-        "context": {"ms_per_step_cold_cache": round(ms_cold, 5),
-                    "tokens_per_s_cold_cache": round(tokens / (ms_cold * 1e-3), 1),
-                    "device_copy_gbs": round(copy_gbs, 1),
-                    "note": "cold: median of 10 replays, each after a 1 GiB write that evicts "
-                            "the last-level cache; copy: torch device-to-device copy of 1 GiB, "
-                            "read + write bytes (measured, not the roofline peak)"},
+        "context": {"device_copy_gbs": round(copy_gbs, 1),
+                    "note": "copy: torch device-to-device copy of 1 GiB, read + write bytes "
+                            "(measured, not the roofline peak)"},
         "env": env_info(),
     }
     print(json.dumps(res), flush=True)

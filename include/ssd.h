@@ -150,7 +150,8 @@ int ssd_config_supported(int32_t dtype, int64_t headdim, int64_t dstate, int64_t
  * batch * seqlen == 0).  dt_bias, D, initial_states, final_states are
  * optional.  A packed batch (p->nseq > 0, p->batch == 1) takes exactly one
  * of cu_seqlens (non-decreasing, from 0 to seqlen) or seq_idx (the sequence
- * id of each token, non-decreasing, in [0, nseq)); an unpacked problem takes
+ * id of each token, non-decreasing, in [0, nseq)); with seqlen == 0 it may
+ * pass neither (every sequence is then empty).  An unpacked problem takes
  * neither.  Malformed packing arrays give unspecified outputs but never an
  * access outside the given buffers.  Tokens that belong to no sequence keep
  * whatever `out` held.
@@ -226,6 +227,21 @@ ssd_status_t ssd_fwd_tuned(const ssd_problem_t* p,
                            void* out, float* final_states,
                            void* workspace, size_t workspace_bytes,
                            uint32_t stages, const ssd_tuning_t* tuning, void* stream);
+
+/*
+ * The kernel choices ssd_fwd / ssd_fwd_stages (and ssd_fwd_tuned for its
+ * fields left 0) make for this problem on the calling thread's current HIP
+ * device, in the fields of ssd_tuning_t: scan_kernel 1-3 (0 for fp32),
+ * sp_vec 1/2/4, front 1 (bf16) or 0 (fp32), sp_blocks 1-16.  They depend on
+ * the shape and on the device's compute-unit count and occupancy only, never
+ * on earlier calls, so a tuner or test can pin exactly what the default
+ * path runs (clova.ai page, section "Stage 3. Logic and heuristic
+ * refinement": launch parameters tied to the GPU's unit count belong with
+ * the device, not in the code).  Host only; enqueues nothing.  Errors:
+ * SSD_ERR_INVALID_ARG / SSD_ERR_UNSUPPORTED as for ssd_fwd, SSD_ERR_HIP if
+ * a device query fails (e.g. no device).
+ */
+ssd_status_t ssd_fwd_choices(const ssd_problem_t* p, ssd_tuning_t* choices);
 
 /*
  * The backward: gradients of loss = sum(out * dout) + sum(final_states *

@@ -29,7 +29,7 @@ STAGES = {"plan": STAGE_PLAN, "chunk_cumsum": STAGE_CUMSUM, "bmm_chunk": STAGE_B
 
 EXPORTED = ("ssd_fwd_workspace_size", "ssd_workspace_layout", "ssd_config_supported",
             "ssd_fwd", "ssd_fwd_stages", "ssd_fwd_tuned", "ssd_bwd_workspace_size", "ssd_bwd",
-            "ssd_bwd_after_fwd",
+            "ssd_bwd_after_fwd", "ssd_fwd_choices",
             "ssd_status_string")
 
 
@@ -98,6 +98,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_bwd.restype = ctypes.c_int
     lib.ssd_bwd_after_fwd.argtypes = [PP] + [vp] * 20 + [vp, sz, vp]
     lib.ssd_bwd_after_fwd.restype = ctypes.c_int
+    lib.ssd_fwd_choices.argtypes = [PP, ctypes.POINTER(TuningC)]
+    lib.ssd_fwd_choices.restype = ctypes.c_int
     lib.ssd_status_string.argtypes = [ctypes.c_int]
     lib.ssd_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -254,6 +256,14 @@ def ssd_fwd_seq_idx(x, dt, A, B, C, chunk_size, seq_idx, nseq, **kw):
                 kw.get("dt_max", math.inf), kw.get("out"), kw.get("final_states"),
                 kw.get("return_final_states", True), kw.get("workspace"),
                 kw.get("stages", STAGE_ALL), kw.get("tuning", "config"))
+
+
+def fwd_choices(prob: ProblemC) -> dict:
+    """The library's own kernel choices for this problem on the current
+    device (ssd_fwd_choices), as a dict of the ssd_tuning_t fields."""
+    t = TuningC(0, 0, 0, 0)
+    _check(load_library().ssd_fwd_choices(ctypes.byref(prob), ctypes.byref(t)))
+    return {k: int(getattr(t, k)) for k, _ in TuningC._fields_}
 
 
 def make_tuning(choice) -> TuningC:

@@ -3,10 +3,25 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "ssd.h"
 #include "ssd_kernels.h"
 
 namespace ssd {
+
+int device_cu_count() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 0;
+  cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -15,12 +30,14 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 typedef hipError_t (*launch_fn)(const FwdArgs&, hipStream_t);
 
 typedef hipError_t (*launch_bwd_fn)(const FwdArgs&, const BwdArgs&, hipStream_t);
+typedef int (*choice_fn)(const FwdArgs&);
 
 struct Kernels {
   int32_t dtype;
   int64_t P, N, L;
   launch_fn bmm, chunk_state, state_passing, chunk_scan, front;
   launch_bwd_fn backward;
+  choice_fn scan_choice;
 };
 
 template <typename T> constexpr int32_t dtype_of();
@@ -30,7 +47,8 @@ template <> constexpr int32_t dtype_of<bf16>() { return SSD_BF16; }
 #define SSD_ROW(T, P, N, L)                                                              \
   {dtype_of<T>(), P, N, L, &launch_bmm_chunk<T, N, L>, &launch_chunk_state<T, P, N, L>, \
    &launch_state_passing<T>, &launch_chunk_scan<T, P, N, L>,                          \
-   sizeof(T) == 2 ? &launch_front<T, P, N, L> : nullptr, &launch_backward<T, P, N, L>},
+   sizeof(T) == 2 ? &launch_front<T, P, N, L> : nullptr, &launch_backward<T, P, N, L>,   \
+   &chunk_scan_choice<T, P, N, L>},
 const Kernels kKernels[] = {SSD_FOR_EACH_CONFIG(SSD_ROW)};
 #undef SSD_ROW
 
@@ -74,8 +92,12 @@ int64_t max_chunks_of(const ssd_problem_t* p) {
 
 // The blocked state_passing (associative scan over blocks of chunks) is
 // for problems whose state elements, one chain each, cannot keep the HBM
-// busy: fewer than kSpBlockElems (1024 waves of 64 lanes, 4 elements each).
-constexpr int64_t kSpBlockElems = int64_t(1) << 18;
+// busy: fewer than one wave of 64 lanes, 4 elements each, per SIMD of the
+// device.  The workspace reserves the blocks' storage for problems under
+// kSpReserveElems state elements, a fixed bound (the reported workspace
+// size never depends on the device); the threshold the library uses is the
+// device's, capped at that bound.
+constexpr int64_t kSpReserveElems = int64_t(1) << 18;
 constexpr int kSpMaxBlocks = 16;
 
 int64_t state_elems(const ssd_problem_t* p) {
@@ -83,18 +105,26 @@ int64_t state_elems(const ssd_problem_t* p) {
   return nstates * p->nheads * p->headdim * p->dstate;
 }
 
+// State elements below which the library blocks the chain on this device.
+int64_t sp_block_threshold() {
+  const int cus = device_cu_count();
+  const int64_t t = cus > 0 ? (int64_t)cus * 4 * 64 * 4 : kSpReserveElems;
+  return t < kSpReserveElems ? t : kSpReserveElems;
+}
+
 // The library's own block count.  Blocking costs a second launch and a
 // second read of the chunk states, which measured slower for sequences of
 // 32 and 64 chunks and up to 37% faster from 256 chunks on; so: sequences of
-// at least 128 chunks on average, enough blocks to reach kSpBlockElems
-// chains, and blocks of at least 16 chunks.
+// at least 128 chunks on average, enough blocks to reach the device's
+// threshold in chains, and blocks of at least 16 chunks.
 int auto_sp_blocks(const ssd_problem_t* p, int64_t max_chunks) {
   const int64_t elems = state_elems(p);
   const int64_t nstates = p->nseq > 0 ? p->nseq : p->batch;
   const int64_t per_seq = max_chunks / (nstates > 0 ? nstates : 1);
-  if (elems <= 0 || elems >= kSpBlockElems || per_seq < 128) return 1;
+  const int64_t thr = sp_block_threshold();
+  if (elems <= 0 || elems >= thr || per_seq < 128) return 1;
   int kb = 1;
-  while (kb < kSpMaxBlocks && elems * kb < kSpBlockElems && per_seq >= 16 * (2 * kb)) kb *= 2;
+  while (kb < kSpMaxBlocks && elems * kb < thr && per_seq >= 16 * (2 * kb)) kb *= 2;
   return kb;
 }
 
@@ -111,7 +141,7 @@ void layout_of(const ssd_problem_t* p, ssd_workspace_layout_t* w) {
   w->cb = off;           off = align_up(off + elem_size(p->dtype) * (size_t)mc * p->ngroups * L * L);
   w->chunk_states = off; off = align_up(off + sizeof(float) * (size_t)mc * H * PN);
   w->states_in = off;    off = align_up(off + elem_size(p->dtype) * (size_t)mc * H * PN);
-  w->sp_blocks = state_elems(p) < kSpBlockElems ? kSpMaxBlocks : 1;
+  w->sp_blocks = state_elems(p) < kSpReserveElems ? kSpMaxBlocks : 1;
   const size_t kbw = w->sp_blocks > 1 ? (size_t)w->sp_blocks : 0;
   w->block_states = off;   off = align_up(off + sizeof(float) * (size_t)nstates * kbw * H * PN);
   w->block_logdecay = off; off = align_up(off + sizeof(float) * (size_t)nstates * kbw * H);
@@ -140,9 +170,12 @@ ssd_status_t fill_args(const ssd_problem_t* p, const ssd_workspace_layout_t& w,
                        const int32_t* seq_idx, void* out, float* final_states, void* workspace,
                        FwdArgs* out_args) {
   const bool packed = p->nseq > 0;
-  if (packed && ((cu_seqlens != nullptr) + (seq_idx != nullptr)) != 1) return SSD_ERR_INVALID_ARG;
-  if (!packed && (cu_seqlens || seq_idx)) return SSD_ERR_INVALID_ARG;
   const int64_t tokens = p->batch * p->seqlen;
+  // a packed batch names its sequences by exactly one of the two arrays; with
+  // no tokens (every sequence empty) it may pass neither
+  if (packed && cu_seqlens && seq_idx) return SSD_ERR_INVALID_ARG;
+  if (packed && !cu_seqlens && !seq_idx && tokens > 0) return SSD_ERR_INVALID_ARG;
+  if (!packed && (cu_seqlens || seq_idx)) return SSD_ERR_INVALID_ARG;
   if (tokens > 0 && (!x || !dt || !A || !B || !C)) return SSD_ERR_INVALID_ARG;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
 
@@ -397,6 +430,34 @@ ssd_status_t ssd_bwd_after_fwd(const ssd_problem_t* p, const void* x, const floa
   return ssd::run_bwd(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, dout,
                       dfinal_states, dx, ddt, dA, dB, dC, dD, ddt_bias, dinitial_states,
                       workspace, workspace_bytes, stream, false);
+}
+
+ssd_status_t ssd_fwd_choices(const ssd_problem_t* p, ssd_tuning_t* choices) {
+  if (!choices) return SSD_ERR_INVALID_ARG;
+  ssd_status_t st = ssd::check_problem(p);
+  if (st != SSD_OK) return st;
+  ssd_workspace_layout_t w;
+  ssd::layout_of(p, &w);
+  ssd::FwdArgs a{};
+  a.batch = (int)p->batch;
+  a.seqlen = (int)p->seqlen;
+  a.H = (int)p->nheads;
+  a.P = (int)p->headdim;
+  a.N = (int)p->dstate;
+  a.G = (int)p->ngroups;
+  a.L = (int)p->chunk_size;
+  a.nstates = (int)(p->nseq > 0 ? p->nseq : p->batch);
+  a.max_chunks = (int)w.max_chunks;
+  a.packed = p->nseq > 0;
+  a.sp_blocks = ssd::auto_sp_blocks(p, w.max_chunks);
+  const ssd::Kernels* k = ssd::find_kernels(p->dtype, p->headdim, p->dstate, p->chunk_size);
+  const int scan = k->scan_choice(a);
+  if (scan < 0 || ssd::device_cu_count() <= 0) return SSD_ERR_HIP;
+  choices->scan_kernel = scan;
+  choices->sp_vec = ssd::state_passing_vec(a);
+  choices->front = k->front ? 1 : 0;
+  choices->sp_blocks = a.sp_blocks;
+  return SSD_OK;
 }
 
 const char* ssd_status_string(ssd_status_t s) {

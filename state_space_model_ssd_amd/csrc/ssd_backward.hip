@@ -1165,13 +1165,7 @@ __global__ __launch_bounds__(kWave) void bwd_head_reduce_kernel(
 // which `wg_per_block` workgroups per block give kBwdMinWgPerCu workgroups
 // per CU of the current device (CU count cached per device).
 static int bwd_head_blocks(int hpg, int64_t wg_per_block) {
-  static int cus_cached[64] = {0};
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-    if (cus_cached[dev] <= 0)
-      (void)hipDeviceGetAttribute(&cus_cached[dev], hipDeviceAttributeMultiprocessorCount, dev);
-    cus = cus_cached[dev];
-  }
+  const int cus = device_cu_count();
   const int cap = hpg < kBwdHeadBlocks ? hpg : kBwdHeadBlocks;
   if (cus <= 0) return cap;
   int hb = 1;

@@ -45,6 +45,8 @@
 //    HBM in operand layout (n contiguous) and contracted over n; the row
 //    scale exp(dAcs[l]) is applied to that partial sum.
 //  - skip term: x of the diagonal slice is still in LDS.
+#include <atomic>
+
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -1007,20 +1009,36 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
 // training batch; with shorter chunks the persistent walk is used.
 constexpr int kPersistentMinTiles = 6;
 
-// Workgroups that stay resident per CU times the CU count, cached per device.
-template <typename K>
-static int persistent_grid(K kernel, int block, int lds_dynamic) {
-  static int cached[64] = {0};
+// Workgroups of the persistent kernel <P, N, L> that stay resident per CU,
+// times the CU count, rounded down to a multiple of the 8 XCDs; queried once
+// per (instantiation, device) and cached (0 if a query fails).
+template <int P, int N, int L>
+static int persistent_grid() {
+  static std::atomic<int> cached[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] > 0) return cached[dev];
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds_dynamic) != hipSuccess)
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  const int c = cached[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  const int cus = device_cu_count();
+  int per_cu = 0;
+  if (cus <= 0 || hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                      &per_cu, chunk_scan_bf16_kernel<P, N, L>, 4 * L, 0) != hipSuccess)
     return 0;
   const int g = (cus * per_cu) / 8 * 8;
-  cached[dev] = g;
+  cached[dev].store(g, std::memory_order_relaxed);
   return g;
+}
+
+template <typename T, int P, int N, int L>
+int chunk_scan_choice(const FwdArgs& a) {
+  if constexpr (sizeof(T) != 2) {
+    return 0;
+  } else {
+    const int g = persistent_grid<P, N, L>();
+    if (g <= 0) return -1;
+    const int ntiles = xcd_grid(a.max_chunks, a.H);
+    return ntiles < kPersistentMinTiles * g ? 1 : (kTileWaves<L> == 8 ? 3 : 2);
+  }
 }
 
 template <typename T, int P, int N, int L>
@@ -1030,12 +1048,12 @@ hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     auto kern = chunk_scan_bf16_kernel<P, N, L>;
     const int ntiles = xcd_grid(a.max_chunks, a.H);
-    const int g = persistent_grid(kern, 4 * L, 0);
-    if (g <= 0) return hipErrorInvalidDevice;
     int choice = a.scan_kernel;
-    if (choice == 0)
-      choice = ntiles < kPersistentMinTiles * g ? 1 : (kTileWaves<L> == 8 ? 3 : 2);
+    if (choice == 0) choice = chunk_scan_choice<T, P, N, L>(a);
+    if (choice < 0) return hipErrorInvalidDevice;
     if (choice == 2) {
+      const int g = persistent_grid<P, N, L>();
+      if (g <= 0) return hipErrorInvalidDevice;
       hipLaunchKernelGGL(kern, dim3(g), dim3(4 * L), 0, s, a.cmap(), a.max_chunks, ntiles,
                          (const bf16*)a.x, (const bf16*)a.C, (const bf16*)a.cb, a.delta, a.dAcs,
                          (const bf16*)a.states_in, a.D, a.H, a.G, (bf16*)a.out);
@@ -1059,7 +1077,9 @@ hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-#define SSD_INST(T, P, N, L) template hipError_t launch_chunk_scan<T, P, N, L>(const FwdArgs&, hipStream_t);
+#define SSD_INST(T, P, N, L)                                                          \
+  template hipError_t launch_chunk_scan<T, P, N, L>(const FwdArgs&, hipStream_t); \
+  template int chunk_scan_choice<T, P, N, L>(const FwdArgs&);
 SSD_FOR_EACH_CONFIG(SSD_INST)
 #undef SSD_INST
 

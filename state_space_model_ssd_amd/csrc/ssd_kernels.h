@@ -83,6 +83,22 @@ struct BwdArgs {
   float* ddot;              // [max_chunks][H][L]: dy_t . x_t per token
 };
 
+// Devices whose per-device launch parameters the library caches.
+constexpr int kMaxDevices = 64;
+
+// Compute units of the calling thread's current HIP device, queried once per
+// device and cached (0 if the query fails).  Launch heuristics size their
+// grids and thresholds from it instead of assuming a CU count.
+int device_cu_count();
+
+// The library's own chunk_scan kernel for this problem on the current device
+// (1, 2 or 3 as in ssd_tuning_t.scan_kernel; 0 for fp32, -1 if a device
+// query fails).
+template <typename T, int P, int N, int L>
+int chunk_scan_choice(const FwdArgs& a);
+// The library's own state_passing vector width (1, 2 or 4) for this problem.
+int state_passing_vec(const FwdArgs& a);
+
 // Stage 0: logical chunk table of a packed batch.
 hipError_t launch_plan(const FwdArgs& a, hipStream_t s);
 // Stage 1: delta and its chunk-local cumulative sum times A.

@@ -196,17 +196,25 @@ __global__ __launch_bounds__(kSpThreads) void state_passing_kernel(
 
 }  // namespace
 
+// Widest vector per thread that still gives every SIMD of the device a wave
+// of 64 lanes (4 SIMDs per CU); each wave keeps kSpDepth chunk loads in
+// flight, so the bytes in flight do not depend on the width, only the
+// instruction count does.
+int state_passing_vec(const FwdArgs& a) {
+  const int KB = a.sp_blocks > 1 ? a.sp_blocks : 1;
+  const int64_t lanes = (int64_t)a.nstates * KB * a.H * a.P * a.N;
+  const int cus = device_cu_count();
+  const int64_t wave_lanes = (int64_t)(cus > 0 ? cus : 256) * 4 * 64;
+  return (lanes / 4 >= wave_lanes) ? 4 : (lanes / 2 >= wave_lanes) ? 2 : 1;
+}
+
 template <typename T>
 hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s) {
   const int PN = a.P * a.N;
   if (a.nstates <= 0) return hipSuccess;
   const int KB = a.sp_blocks > 1 ? a.sp_blocks : 1;
   if (KB > 1 && (!a.block_states || !a.block_logdecay)) return hipErrorInvalidValue;
-  // Widest vector per thread that still gives every SIMD a wave (1024 waves
-  // of 64 lanes); each wave keeps kSpDepth chunk loads in flight, so the bytes
-  // in flight do not depend on the width, only the instruction count does.
-  const int64_t lanes = (int64_t)a.nstates * KB * a.H * PN;
-  int vec = (lanes / 4 >= (int64_t)1024 * 64) ? 4 : (lanes / 2 >= (int64_t)1024 * 64) ? 2 : 1;
+  int vec = state_passing_vec(a);
   if (a.sp_vec == 1 || a.sp_vec == 2 || a.sp_vec == 4) vec = a.sp_vec;   // pinned by the caller
   if (PN % vec != 0) return hipErrorInvalidValue;
   auto go = [&](auto kern, int v) {

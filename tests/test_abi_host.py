@@ -149,6 +149,10 @@ def test_packing_arguments_checked(lib):
     assert _call(lib, packed) == binding.SSD_ERR_INVALID_ARG                   # neither
     assert _call(lib, packed, cu=FAKE, sidx=FAKE) == binding.SSD_ERR_INVALID_ARG   # both
     assert _call(lib, _prob(), cu=FAKE) == binding.SSD_ERR_INVALID_ARG          # unpacked + cu
+    # no tokens: a packed batch of empty sequences may name neither (checked
+    # up to the workspace, the first check that needs no device)
+    empty = _prob(batch=1, seqlen=0, nseq=3)
+    assert _call(lib, empty, ws=None) == binding.SSD_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("null", ["x", "dt", "A", "B", "C", "out"])
@@ -184,3 +188,16 @@ def test_missing_library_fails_loudly(tmp_path):
             binding.load_library(str(tmp_path / "absent.so"))
     finally:
         binding._lib = saved
+
+
+def test_choices_query_checked_on_host(lib):
+    t = binding.TuningC(0, 0, 0, 0)
+    assert lib.ssd_fwd_choices(ctypes.byref(_prob(nheads=7, ngroups=2)), ctypes.byref(t)) == \
+        binding.SSD_ERR_INVALID_ARG
+    assert lib.ssd_fwd_choices(ctypes.byref(_prob(headdim=48)), ctypes.byref(t)) == \
+        binding.SSD_ERR_UNSUPPORTED
+    assert lib.ssd_fwd_choices(ctypes.byref(_prob()), None) == binding.SSD_ERR_INVALID_ARG
+    import torch
+    if not torch.cuda.is_available():
+        # the choices depend on the device, so without one the query fails
+        assert lib.ssd_fwd_choices(ctypes.byref(_prob()), ctypes.byref(t)) == binding.SSD_ERR_HIP
