@@ -73,7 +73,9 @@ typedef enum {
   SSD_ERR_UNSUPPORTED = 2,  /* valid, but (dtype, headdim, dstate, chunk)  */
                             /* has no compiled kernel                      */
   SSD_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than required     */
-  SSD_ERR_HIP = 4           /* a HIP launch or device query failed         */
+  SSD_ERR_HIP = 4,          /* a HIP launch or device query failed         */
+  SSD_ERR_TOO_LARGE = 5     /* ssd_fwd_noalloc: the problem's workspace is */
+                            /* larger than SSD_NOALLOC_SCRATCH_BYTES       */
 } ssd_status_t;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
@@ -298,6 +300,33 @@ ssd_status_t ssd_bwd_after_fwd(const ssd_problem_t* p,
                                void* dx, float* ddt, float* dA, void* dB, void* dC,
                                float* dD, float* ddt_bias, float* dinitial_states,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ssd_fwd
+ * without a workspace argument.  The workspace is a static device array of
+ * SSD_NOALLOC_SCRATCH_BYTES inside the library, one per device, allocated
+ * when the library's code is loaded on that device and held until the
+ * process ends; this call allocates nothing and calls no allocating routine.
+ * The caller still passes every input and output, as for ssd_fwd.
+ *   - Problems whose ssd_fwd_workspace_size exceeds SSD_NOALLOC_SCRATCH_BYTES
+ *     are rejected with SSD_ERR_TOO_LARGE before anything is enqueued.
+ *   - Every call on one device shares that device's array, whose contents
+ *     persist between calls (nothing in it needs to start at zero).  Calls
+ *     that overlap on one device, on different streams or from different
+ *     threads, race on it and give wrong results: serialise them (e.g. on
+ *     one stream).
+ * Results are bit for bit those of ssd_fwd on the same problem and inputs.
+ * Other errors as for ssd_fwd.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+ssd_status_t ssd_fwd_noalloc(const ssd_problem_t* p,
+                             const void* x, const float* dt, const float* dt_bias,
+                             const float* A, const void* B, const void* C, const float* D,
+                             const float* initial_states,
+                             const int32_t* cu_seqlens, const int32_t* seq_idx,
+                             void* out, float* final_states, void* stream);
 
 /* Static description of a status code. */
 const char* ssd_status_string(ssd_status_t s);

@@ -18,7 +18,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssd_hip.so")
 
-SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
+SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP, \
+    SSD_ERR_TOO_LARGE = range(6)
+NOALLOC_SCRATCH_BYTES = 64 << 20     # SSD_NOALLOC_SCRATCH_BYTES of include/ssd.h
 SSD_F32, SSD_BF16 = 0, 1
 STAGE_PLAN, STAGE_CUMSUM, STAGE_BMM, STAGE_CHUNK_STATE, STAGE_STATE_PASSING, STAGE_CHUNK_SCAN = \
     (1 << i for i in range(6))
@@ -29,7 +31,7 @@ STAGES = {"plan": STAGE_PLAN, "chunk_cumsum": STAGE_CUMSUM, "bmm_chunk": STAGE_B
 
 EXPORTED = ("ssd_fwd_workspace_size", "ssd_workspace_layout", "ssd_config_supported",
             "ssd_fwd", "ssd_fwd_stages", "ssd_fwd_tuned", "ssd_bwd_workspace_size", "ssd_bwd",
-            "ssd_bwd_after_fwd", "ssd_fwd_choices",
+            "ssd_bwd_after_fwd", "ssd_fwd_choices", "ssd_fwd_noalloc",
             "ssd_status_string")
 
 
@@ -98,6 +100,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_bwd.restype = ctypes.c_int
     lib.ssd_bwd_after_fwd.argtypes = [PP] + [vp] * 20 + [vp, sz, vp]
     lib.ssd_bwd_after_fwd.restype = ctypes.c_int
+    lib.ssd_fwd_noalloc.argtypes = [PP] + [vp] * 12 + [vp]
+    lib.ssd_fwd_noalloc.restype = ctypes.c_int
     lib.ssd_fwd_choices.argtypes = [PP, ctypes.POINTER(TuningC)]
     lib.ssd_fwd_choices.restype = ctypes.c_int
     lib.ssd_status_string.argtypes = [ctypes.c_int]
@@ -256,6 +260,44 @@ def ssd_fwd_seq_idx(x, dt, A, B, C, chunk_size, seq_idx, nseq, **kw):
                 kw.get("dt_max", math.inf), kw.get("out"), kw.get("final_states"),
                 kw.get("return_final_states", True), kw.get("workspace"),
                 kw.get("stages", STAGE_ALL), kw.get("tuning", "config"))
+
+
+def ssd_fwd_noalloc(x, dt, A, B, C, chunk_size, out, final_states=None, D=None, dt_bias=None,
+                    initial_states=None, cu_seqlens=None, seq_idx=None, nseq=0, dt_min=0.0,
+                    dt_max=math.inf):
+    """The forward through ssd_fwd_noalloc: the library's static scratch array
+    is the workspace, and the caller passes the outputs (`out`, and
+    `final_states` or None), so nothing is allocated here either.  For a
+    packed batch pass cu_seqlens, or seq_idx with nseq."""
+    lib = load_library()
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    f32 = torch.float32
+    if dev.type != "cuda":
+        raise ValueError("ssd_fwd_noalloc runs on the GPU only; x is on " + str(dev))
+    if cu_seqlens is not None:
+        nseq = cu_seqlens.numel() - 1
+    nstates = nseq if nseq > 0 else b
+    for t, name, dtp, shape in ((x, "x", x.dtype, (b, T, H, P)), (dt, "dt", f32, (b, T, H)),
+                                (A, "A", f32, (H,)), (B, "B", x.dtype, (b, T, G, N)),
+                                (C, "C", x.dtype, (b, T, G, N)), (D, "D", f32, (H,)),
+                                (dt_bias, "dt_bias", f32, (H,)),
+                                (initial_states, "initial_states", f32, (nstates, H, P, N)),
+                                (cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,)),
+                                (seq_idx, "seq_idx", torch.int32, (T,)),
+                                (out, "out", x.dtype, (b, T, H, P)),
+                                (final_states, "final_states", f32, (nstates, H, P, N))):
+        _need(t, name, dtp, shape, dev)
+    prob = make_problem(b, T, H, P, N, G, chunk_size, x.dtype, nseq, dt_min, dt_max)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        code = lib.ssd_fwd_noalloc(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A),
+                                   _ptr(B), _ptr(C), _ptr(D), _ptr(initial_states),
+                                   _ptr(cu_seqlens), _ptr(seq_idx), _ptr(out),
+                                   _ptr(final_states), stream)
+    _check(code)
+    return out, final_states
 
 
 def fwd_choices(prob: ProblemC) -> dict:

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "ssd.h"
 #include "ssd_kernels.h"
@@ -345,6 +346,32 @@ ssd_status_t run_bwd(const ssd_problem_t* p, const void* x, const float* dt, con
   return SSD_OK;
 }
 
+// The allocation-free forward's workspace: a static device array, one copy
+// per device the library runs on, kept until the process ends.  Host code
+// never passes the array's name to a kernel (in host code it is only a
+// stand-in): each device's address comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+static_assert(SSD_NOALLOC_SCRATCH_BYTES % kAlign == 0, "scratch size");
+__device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// This device's scratch address, or nullptr if the query fails.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot]() {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) slot.ptr = ptr;
+  });
+  return slot.ptr;
+}
+
 }  // namespace
 }  // namespace ssd
 
@@ -432,6 +459,22 @@ ssd_status_t ssd_bwd_after_fwd(const ssd_problem_t* p, const void* x, const floa
                       workspace, workspace_bytes, stream, false);
 }
 
+ssd_status_t ssd_fwd_noalloc(const ssd_problem_t* p, const void* x, const float* dt,
+                             const float* dt_bias, const float* A, const void* B, const void* C,
+                             const float* D, const float* initial_states,
+                             const int32_t* cu_seqlens, const int32_t* seq_idx, void* out,
+                             float* final_states, void* stream) {
+  ssd_status_t st = ssd::check_problem(p);
+  if (st != SSD_OK) return st;
+  ssd_workspace_layout_t w;
+  ssd::layout_of(p, &w);
+  if (w.total_bytes > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_TOO_LARGE;
+  void* ws = ssd::scratch_address();
+  if (!ws) return SSD_ERR_HIP;
+  return ssd::run(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, out,
+                  final_states, ws, SSD_NOALLOC_SCRATCH_BYTES, SSD_STAGE_ALL, nullptr, stream);
+}
+
 ssd_status_t ssd_fwd_choices(const ssd_problem_t* p, ssd_tuning_t* choices) {
   if (!choices) return SSD_ERR_INVALID_ARG;
   ssd_status_t st = ssd::check_problem(p);
@@ -467,6 +510,8 @@ const char* ssd_status_string(ssd_status_t s) {
     case SSD_ERR_UNSUPPORTED: return "unsupported (dtype, headdim, dstate, chunk_size) or size";
     case SSD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case SSD_ERR_HIP: return "HIP launch failed";
+    case SSD_ERR_TOO_LARGE:
+      return "problem needs more workspace than ssd_fwd_noalloc's static scratch buffer holds";
   }
   return "unknown status";
 }

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert binding.status_string(code)
     assert binding.status_string(99) == "unknown status"
 
