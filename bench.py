@@ -300,7 +300,22 @@ def stage_record(work, name, us, dtype):
     return rec
 
 
-def side_workload(k, torch, binding, flush, steps, warmup, reps):
+def fused_step(k, torch, binding, steps, warmup):
+    """Median step of workload k with the fused forward pinned
+    (ssd_tuning_t.fused = 2), or None where the shape has none."""
+    w = Workload(k, torch, binding, {"fused": 2})
+    if w.prob.dtype != "bf16" or w.prob.chunk_size not in (128, 256):
+        return None
+    w.capture(warmup)
+    w.time_replays(steps)
+    per = w.step_samples(10, 5)
+    med = percentiles(per)["median"] * 1e3
+    del w
+    torch.cuda.empty_cache()
+    return round(med, 2)
+
+
+def side_workload(k, torch, binding, flush, steps, warmup, reps, compare_fused=False):
     """Step and launch timings of another full-size workload (warm and cold)."""
     w = Workload(k, torch, binding)
     w.capture(warmup)
@@ -324,6 +339,8 @@ def side_workload(k, torch, binding, flush, steps, warmup, reps):
            "tuning": w.tuning_record}
     del w
     torch.cuda.empty_cache()
+    if compare_fused:
+        rec["fused_step_us_warm_median"] = fused_step(k, torch, binding, steps, warmup)
     return rec
 
 
@@ -345,6 +362,8 @@ def main():
     ap.add_argument("--side-workloads", default="3,4,5",
                     help="comma-separated other workloads to time after the main one "
                          "('' for none)")
+    ap.add_argument("--fused-workloads", default="2,4",
+                    help="workloads whose step is also timed with the fused forward pinned")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, copy a buffer of MIB MiB three times (a plain copy "
                          "kernel of known size, for scaling HBM byte counters)")
@@ -494,6 +513,13 @@ def main():
     del w
     torch.cuda.empty_cache()
 
+    # --- the fused forward (ssd_tuning_t.fused = 2) on the main workload
+    fused_list = [v.strip() for v in args.fused_workloads.split(",") if v.strip()]
+    fused_main = None
+    if str(args.workload) in fused_list and pinned is None:
+        log("[bench] fused forward")
+        fused_main = fused_step(args.workload, torch, binding, 20, 3)
+
     # --- the other full-size workloads: warm and cold step, per launch
     side = {}
     for k in [int(v) for v in args.side_workloads.split(",") if v.strip()]:
@@ -501,7 +527,8 @@ def main():
             continue
         flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
         side[str(k)] = side_workload(k, torch, binding, flush, steps=20,
-                                     warmup=3, reps=max(5, args.stage_reps // 5))
+                                     warmup=3, reps=max(5, args.stage_reps // 5),
+                                     compare_fused=str(k) in fused_list)
         del flush
         torch.cuda.empty_cache()
 
@@ -538,6 +565,7 @@ def main():
         "step_us_warm": step_pct,
         "step_us_cold": cold_pct,
         "tokens_per_s_median": round(tokens / (step_pct["median"] * 1e-6), 1),
+        "fused_step_us_warm_median": fused_main,
         "tuning": main_tuning,
         "stages": stages,
         "stages_unfused": singles,

@@ -125,11 +125,13 @@ typedef struct {
  *                state_passing's per-block end states and log decays
  *                (present, with sp_blocks = 16, only when nstates * nheads *
  *                headdim * dstate < 2^18; else sp_blocks = 1 and both are
- *                empty)                                                    */
+ *                empty)
+ *   sync         int32 counters of the fused forward (ssd_tuning_t.fused):
+ *                max_chunks * nheads + 1                                   */
 typedef struct {
   int64_t max_chunks;
   size_t chunk_table, seq_chunks, delta, dA_cumsum, cb, chunk_states, states_in;
-  size_t block_states, block_logdecay;
+  size_t block_states, block_logdecay, sync;
   int64_t sp_blocks;
   size_t total_bytes;
 } ssd_workspace_layout_t;
@@ -207,6 +209,16 @@ ssd_status_t ssd_fwd_stages(const ssd_problem_t* p,
  *                launches (rounds differently: the blocks' maps are
  *                composed in another order).  Above 1 only when the
  *                workspace layout's sp_blocks is 16.
+ *   fused        bf16 with 128- or 256-token chunks: 1 = front,
+ *                state_passing and chunk_scan as separate launches, 2 =
+ *                the front's launch, then state_passing and chunk_scan in
+ *                one persistent launch in which the scan tiles of a chunk
+ *                start once the state chain has passed it; bitwise the same
+ *                results as 1 with the one-chain state passing and the same
+ *                scan tile (scan_kernel 1 or 3, or the library's choice).
+ *                2 cannot be combined with sp_blocks > 1, front 2, sp_vec
+ *                1 or 2, or scan_kernel 2; it applies when a call runs all
+ *                of stages 1-5.
  * A field outside its range, or a choice the dtype does not have, is
  * rejected with SSD_ERR_INVALID_ARG before anything is enqueued.
  */
@@ -215,6 +227,7 @@ typedef struct {
   int32_t sp_vec;
   int32_t front;
   int32_t sp_blocks;
+  int32_t fused;
 } ssd_tuning_t;
 
 /*
@@ -234,7 +247,7 @@ ssd_status_t ssd_fwd_tuned(const ssd_problem_t* p,
  * The kernel choices ssd_fwd / ssd_fwd_stages (and ssd_fwd_tuned for its
  * fields left 0) make for this problem on the calling thread's current HIP
  * device, in the fields of ssd_tuning_t: scan_kernel 1-3 (0 for fp32),
- * sp_vec 1/2/4, front 1 (bf16) or 0 (fp32), sp_blocks 1-16.  They depend on
+ * sp_vec 1/2/4, front 1 (bf16) or 0 (fp32), sp_blocks 1-16, fused 1 or 2.  They depend on
  * the shape and on the device's compute-unit count and occupancy only, never
  * on earlier calls, so a tuner or test can pin exactly what the default
  * path runs (clova.ai page, section "Stage 3. Logic and heuristic

@@ -56,13 +56,15 @@ class LayoutC(ctypes.Structure):
                 ("dA_cumsum", ctypes.c_size_t), ("cb", ctypes.c_size_t),
                 ("chunk_states", ctypes.c_size_t), ("states_in", ctypes.c_size_t),
                 ("block_states", ctypes.c_size_t), ("block_logdecay", ctypes.c_size_t),
+                ("sync", ctypes.c_size_t),
                 ("sp_blocks", ctypes.c_int64), ("total_bytes", ctypes.c_size_t)]
 
 
 class TuningC(ctypes.Structure):
     """ssd_tuning_t: pinned kernel choices, 0 = the library's own."""
     _fields_ = [("scan_kernel", ctypes.c_int32), ("sp_vec", ctypes.c_int32),
-                ("front", ctypes.c_int32), ("sp_blocks", ctypes.c_int32)]
+                ("front", ctypes.c_int32), ("sp_blocks", ctypes.c_int32),
+                ("fused", ctypes.c_int32)]
 
 
 _lib = None
@@ -303,16 +305,17 @@ def ssd_fwd_noalloc(x, dt, A, B, C, chunk_size, out, final_states=None, D=None, 
 def fwd_choices(prob: ProblemC) -> dict:
     """The library's own kernel choices for this problem on the current
     device (ssd_fwd_choices), as a dict of the ssd_tuning_t fields."""
-    t = TuningC(0, 0, 0, 0)
+    t = TuningC(0, 0, 0, 0, 0)
     _check(load_library().ssd_fwd_choices(ctypes.byref(prob), ctypes.byref(t)))
     return {k: int(getattr(t, k)) for k, _ in TuningC._fields_}
 
 
 def make_tuning(choice) -> TuningC:
-    """TuningC from None or a dict of scan_kernel / sp_vec / front / sp_blocks."""
-    t = TuningC(0, 0, 0, 0)
+    """TuningC from None or a dict of scan_kernel / sp_vec / front / sp_blocks /
+    fused."""
+    t = TuningC(0, 0, 0, 0, 0)
     if choice:
-        unknown = set(choice) - {"scan_kernel", "sp_vec", "front", "sp_blocks"}
+        unknown = set(choice) - {"scan_kernel", "sp_vec", "front", "sp_blocks", "fused"}
         if unknown:
             raise ValueError(f"unknown tuning fields {sorted(unknown)}")
         for k, v in choice.items():

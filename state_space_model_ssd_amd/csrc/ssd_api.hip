@@ -33,12 +33,15 @@ typedef hipError_t (*launch_fn)(const FwdArgs&, hipStream_t);
 typedef hipError_t (*launch_bwd_fn)(const FwdArgs&, const BwdArgs&, hipStream_t);
 typedef int (*choice_fn)(const FwdArgs&);
 
+typedef hipError_t (*launch_fused_fn)(const FwdArgs&, int, hipStream_t);
+
 struct Kernels {
   int32_t dtype;
   int64_t P, N, L;
   launch_fn bmm, chunk_state, state_passing, chunk_scan, front;
   launch_bwd_fn backward;
   choice_fn scan_choice;
+  launch_fused_fn fused;   // nullptr: no fused forward for this configuration
 };
 
 template <typename T> constexpr int32_t dtype_of();
@@ -49,7 +52,8 @@ template <> constexpr int32_t dtype_of<bf16>() { return SSD_BF16; }
   {dtype_of<T>(), P, N, L, &launch_bmm_chunk<T, N, L>, &launch_chunk_state<T, P, N, L>, \
    &launch_state_passing<T>, &launch_chunk_scan<T, P, N, L>,                          \
    sizeof(T) == 2 ? &launch_front<T, P, N, L> : nullptr, &launch_backward<T, P, N, L>,   \
-   &chunk_scan_choice<T, P, N, L>},
+   &chunk_scan_choice<T, P, N, L>,                                                      \
+   fused_supported<T, P, N, L>() ? &launch_fused<T, P, N, L> : nullptr},
 const Kernels kKernels[] = {SSD_FOR_EACH_CONFIG(SSD_ROW)};
 #undef SSD_ROW
 
@@ -146,6 +150,7 @@ void layout_of(const ssd_problem_t* p, ssd_workspace_layout_t* w) {
   const size_t kbw = w->sp_blocks > 1 ? (size_t)w->sp_blocks : 0;
   w->block_states = off;   off = align_up(off + sizeof(float) * (size_t)nstates * kbw * H * PN);
   w->block_logdecay = off; off = align_up(off + sizeof(float) * (size_t)nstates * kbw * H);
+  w->sync = off;           off = align_up(off + fused_sync_bytes((int)nstates, (int)H, (int)p->ngroups, (int)mc));
   w->total_bytes = off;
 }
 
@@ -159,6 +164,14 @@ ssd_status_t check_tuning(const ssd_problem_t* p, const ssd_tuning_t& t, int64_t
   if (t.scan_kernel < 0 || t.scan_kernel > 3 || (!bf16 && t.scan_kernel != 0)) return SSD_ERR_INVALID_ARG;
   if (t.sp_vec != 0 && t.sp_vec != 1 && t.sp_vec != 2 && t.sp_vec != 4) return SSD_ERR_INVALID_ARG;
   if (t.front < 0 || t.front > 2 || (!bf16 && t.front != 0)) return SSD_ERR_INVALID_ARG;
+  if (t.fused < 0 || t.fused > 2) return SSD_ERR_INVALID_ARG;
+  if (t.fused == 2) {
+    const Kernels* k = find_kernels(p->dtype, p->headdim, p->dstate, p->chunk_size);
+    // the fused launch has its own state passing and its own (8-wave) scan tile
+    if (!k || !k->fused || t.sp_blocks > 1 || t.front == 2 || (t.sp_vec != 0 && t.sp_vec != 4) ||
+        t.scan_kernel == 2)
+      return SSD_ERR_INVALID_ARG;
+  }
   return SSD_OK;
 }
 
@@ -197,6 +210,7 @@ ssd_status_t fill_args(const ssd_problem_t* p, const ssd_workspace_layout_t& w,
   a.scan_kernel = tune.scan_kernel;
   a.sp_vec = tune.sp_vec;
   a.sp_blocks = tune.sp_blocks > 0 ? tune.sp_blocks : auto_sp_blocks(p, w.max_chunks);
+  a.fused = tune.fused;
   a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.D = D;
   a.init = initial_states;
   a.cu_seqlens = cu_seqlens;
@@ -213,7 +227,19 @@ ssd_status_t fill_args(const ssd_problem_t* p, const ssd_workspace_layout_t& w,
   a.states_in = base + w.states_in;
   a.block_states = w.sp_blocks > 1 ? reinterpret_cast<float*>(base + w.block_states) : nullptr;
   a.block_logdecay = w.sp_blocks > 1 ? reinterpret_cast<float*>(base + w.block_logdecay) : nullptr;
+  a.sync = reinterpret_cast<int*>(base + w.sync);
+  a.zero_ints = 0;
   return SSD_OK;
+}
+
+// 2: the fused forward, 1: separate launches.  A pinned choice wins; the
+// library's own keeps separate launches (the fused one uses the one-chain
+// state passing, so it is never picked where the blocked one is).
+int fused_choice(const ssd_problem_t* p, const FwdArgs& a, const ssd_tuning_t& tune) {
+  (void)p;
+  if (tune.fused != 0) return tune.fused;
+  if (a.sp_blocks > 1 || tune.front == 2) return 1;
+  return 1;
 }
 
 ssd_status_t launch_stages(const ssd_problem_t* p, const FwdArgs& a, uint32_t stages,
@@ -229,6 +255,16 @@ ssd_status_t launch_stages(const ssd_problem_t* p, const FwdArgs& a, uint32_t st
       {SSD_STAGE_STATE_PASSING, k->state_passing},
       {SSD_STAGE_CHUNK_SCAN, k->chunk_scan},
   };
+  // Stages 1-5 as one fused launch: when all of them are asked for and the
+  // caller pinned it (or the library picks it for the shape).
+  constexpr uint32_t kAfterPlan = SSD_STAGE_ALL & ~(uint32_t)SSD_STAGE_PLAN;
+  if (k->fused && (stages & kAfterPlan) == kAfterPlan && fused_choice(p, a, tune) == 2) {
+    if ((stages & SSD_STAGE_PLAN) && launch_plan(a, s) != hipSuccess) return SSD_ERR_HIP;
+    const int scan = tune.scan_kernel != 0 ? tune.scan_kernel : k->scan_choice(a);
+    if (scan < 0) return SSD_ERR_HIP;
+    if (k->fused(a, scan, s) != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+  }
   // The bf16 path runs stages 1-3 as one launch when all three are asked for.
   constexpr uint32_t kFront = SSD_STAGE_CUMSUM | SSD_STAGE_BMM | SSD_STAGE_CHUNK_STATE;
   const bool fuse_front = k->front && (stages & kFront) == kFront && tune.front != 2;
@@ -251,7 +287,7 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
   ssd_status_t st = check_problem(p);
   if (st != SSD_OK) return st;
   if (stages & ~(uint32_t)SSD_STAGE_ALL) return SSD_ERR_INVALID_ARG;
-  const ssd_tuning_t tune = tuning ? *tuning : ssd_tuning_t{0, 0, 0, 0};
+  const ssd_tuning_t tune = tuning ? *tuning : ssd_tuning_t{0, 0, 0, 0, 0};
   ssd_workspace_layout_t w;
   layout_of(p, &w);
   st = check_tuning(p, tune, w.sp_blocks);
@@ -312,7 +348,7 @@ ssd_status_t run_bwd(const ssd_problem_t* p, const void* x, const float* dt, con
   BwdLayout bl;
   bwd_layout_of(p, w, &bl);
   if (!workspace || workspace_bytes < bl.total) return SSD_ERR_WORKSPACE;
-  const ssd_tuning_t tune{0, 0, 0, 0};
+  const ssd_tuning_t tune{0, 0, 0, 0, 0};
   FwdArgs a;
   st = fill_args(p, w, tune, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx,
                  nullptr, nullptr, workspace, &a);
@@ -500,6 +536,7 @@ ssd_status_t ssd_fwd_choices(const ssd_problem_t* p, ssd_tuning_t* choices) {
   choices->sp_vec = ssd::state_passing_vec(a);
   choices->front = k->front ? 1 : 0;
   choices->sp_blocks = a.sp_blocks;
+  choices->fused = k->fused ? ssd::fused_choice(p, a, ssd_tuning_t{0, 0, 0, 0, 0}) : 1;
   return SSD_OK;
 }
 

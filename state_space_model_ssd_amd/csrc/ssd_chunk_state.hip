@@ -18,6 +18,7 @@
 //    LDS (k contiguous per row, 16-byte padded rows).
 #include "ssd_device.h"
 #include "ssd_kernels.h"
+#include "ssd_state_tile.h"
 
 namespace ssd {
 
@@ -130,153 +131,6 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(
 }
 
 
-// ------------------------------------------------------------- bf16 kernels
-// Threads of the bf16 chunk_state and front workgroups (8 waves).
-constexpr int kStateThreads = 512;
-
-template <int P, int N, int L>
-struct StateSmem {
-  static constexpr int KS = 64;    // tokens per slice
-  bf16 xs[KS * P];                 // weighted x slice, token-major, swizzled
-  bf16 bs[KS * N];                 // B slice, token-major, swizzled
-  float wl[L];
-  float cum[L];
-  float wave_tot[kStateThreads / 64];
-};
-
-// chunk_state for chunk j, head h (kStateThreads threads).  With CUMSUM the workgroup
-// also runs chunk_cumsum for its (chunk, head) -- the step and its running
-// sum come from dt here and are written to delta/dAcs for the later stages --
-// otherwise it reads them from delta/dAcs.
-//
-// Each 64-token slice of x (scaled by w[l] in fp32 and rounded once to bf16)
-// and of B is staged token-major in LDS; the MFMA operands come out through
-// the transpose read.  The MFMAs produce the transposed tile S^T[n][p], so a
-// lane holds four consecutive n of one p and S leaves in 16-byte stores.
-// Loads and stores go through buffer resources bounded by the chunk: tokens
-// past its end read as zeros.
-template <int P, int N, int L, bool CUMSUM>
-__device__ __forceinline__ void chunk_state_bf16_body(
-    const ChunkDesc& d, int j, int h, const bf16* __restrict__ x, const bf16* __restrict__ B,
-    float* __restrict__ delta, float* __restrict__ dAcs, const float* __restrict__ dt,
-    const float* __restrict__ dt_bias, const float* __restrict__ A, float dt_min, float dt_max,
-    int H, int G, float* __restrict__ S, StateSmem<P, N, L>& sm) {
-  static_assert(L % 64 == 0 && L <= 256 && P % 16 == 0 && N % 16 == 0, "tile shape");
-  using SM = StateSmem<P, N, L>;
-  constexpr int KS = SM::KS;
-  constexpr int XC = P / 8, BC = N / 8;   // 16-byte pieces per row
-  constexpr int TH = kStateThreads, NWV = TH / 64;
-  constexpr int XU = (KS * XC + TH - 1) / TH, BU = (KS * BC + TH - 1) / TH;
-  constexpr int PT = P / 16, NT = N / 16;
-  constexpr int WN = NT < 4 ? NT : 4;                       // waves along n
-  constexpr int WP = (NWV / WN) < PT ? (NWV / WN) : PT;     // waves along p
-  constexpr int TP = PT / WP, TN = NT / WN;
-  static_assert(PT % WP == 0 && NT % WN == 0, "tile split");
-  const int g = h / (H / G);
-  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
-  const int last = d.len - 1;
-  const uint32_t HP = (uint32_t)H * P, GN = (uint32_t)G * N;
-  const auto rx = buf_rsrc(x + ((int64_t)d.start * H + h) * P, ((uint32_t)last * HP + P) * 2u);
-  const auto rb = buf_rsrc(B + ((int64_t)d.start * G + g) * N, ((uint32_t)last * GN + N) * 2u);
-
-  uint4 xr[XU], br[BU];
-  const int nsl = (d.len + KS - 1) / KS;
-  // slice `sl` into registers (pieces past a thread's share, if any, read
-  // out of range as zeros and are never staged)
-#define SSD_STATE_FETCH(sl)                                                               \
-  {                                                                                       \
-    _Pragma("unroll") for (int u = 0; u < XU; ++u) {                                      \
-      const int i = tid + TH * u, r = (sl) * KS + i / XC, c = i % XC;                     \
-      xr[u] = buf_load16(rx, i < KS * XC ? ((uint32_t)r * HP + c * 8) * 2u : 0xFFFFFFF0u);  \
-    }                                                                                     \
-    _Pragma("unroll") for (int u = 0; u < BU; ++u) {                                      \
-      const int i = tid + TH * u, r = (sl) * KS + i / BC, c = i % BC;                     \
-      br[u] = buf_load16(rb, i < KS * BC ? ((uint32_t)r * GN + c * 8) * 2u : 0xFFFFFFF0u);  \
-    }                                                                                     \
-  }
-  SSD_STATE_FETCH(0)                      // in flight while the weights are formed
-
-  // w[l] = exp(a_last - a_l) * delta_l
-  if constexpr (CUMSUM) {
-    float step, cum;
-    chunk_cumsum_block<L>(d, tid, dt, dt_bias, A, H, h, dt_min, dt_max, sm.wave_tot, step, cum);
-    if (tid < L) {
-      const int64_t o = ((int64_t)j * H + h) * L + tid;
-      delta[o] = step;
-      dAcs[o] = cum;
-      sm.cum[tid] = cum;
-      sm.wl[tid] = step;
-    }
-    __syncthreads();
-    if (tid < L) sm.wl[tid] = exp2_fast((sm.cum[last] - sm.cum[tid]) * kLog2e) * sm.wl[tid];
-  } else {
-    const float* dA = dAcs + ((int64_t)j * H + h) * L;
-    const float* dl = delta + ((int64_t)j * H + h) * L;
-    const float lastv = dA[last];
-    for (int l = tid; l < L; l += TH)
-      sm.wl[l] = (l < d.len) ? exp2_fast((lastv - dA[l]) * kLog2e) * dl[l] : 0.f;
-  }
-
-  const int wp = w / WN, wn = w - (w / WN) * WN;
-  const bool active = w < WP * WN;
-  f32x4 acc[TN][TP];                      // S^T tiles: rows n, columns p
-#pragma unroll
-  for (int b = 0; b < TN; ++b)
-#pragma unroll
-    for (int a = 0; a < TP; ++a) acc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  __syncthreads();                        // wl ready
-  for (int sl = 0; sl < nsl; ++sl) {
-#pragma unroll
-    for (int u = 0; u < XU; ++u) {
-      const int i = tid + TH * u, r = i / XC, c = i % XC;
-      if (i < KS * XC) {
-        const bf16x8 v = __builtin_bit_cast(bf16x8, xr[u]);
-        const float wv = sm.wl[sl * KS + r];   // 0 past the chunk's end
-        bf16x8 o;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = static_cast<bf16>(static_cast<float>(v[e]) * wv);
-        *reinterpret_cast<bf16x8*>(&sm.xs[tile_at<P>(r, c * 8)]) = o;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < BU; ++u) {
-      const int i = tid + TH * u, r = i / BC, c = i % BC;
-      if (i < KS * BC) *reinterpret_cast<uint4*>(&sm.bs[tile_at<N>(r, c * 8)]) = br[u];
-    }
-    __syncthreads();
-    if (sl + 1 < nsl) SSD_STATE_FETCH(sl + 1)   // in flight while this slice multiplies
-    if (active) {
-#pragma unroll
-      for (int k0 = 0; k0 < KS; k0 += 32) {
-        bf16x8 fa[TP], fb[TN];
-#pragma unroll
-        for (int a = 0; a < TP; ++a) fa[a] = lds_operand_sw<P>(sm.xs, k0, 16 * (wp * TP + a), lane);
-#pragma unroll
-        for (int b = 0; b < TN; ++b) fb[b] = lds_operand_sw<N>(sm.bs, k0, 16 * (wn * TN + b), lane);
-#pragma unroll
-        for (int b = 0; b < TN; ++b)
-#pragma unroll
-          for (int a = 0; a < TP; ++a) acc[b][a] = Mfma<bf16>::mma(fb[b], fa[a], acc[b][a]);
-      }
-    }
-    __syncthreads();
-  }
-#undef SSD_STATE_FETCH
-
-  if (!active) return;
-  const auto rs = buf_rsrc(S + ((int64_t)j * H + h) * P * N, P * N * 4);
-  const int lr = lane & 15;
-#pragma unroll
-  for (int b = 0; b < TN; ++b)
-#pragma unroll
-    for (int a = 0; a < TP; ++a) {
-      const int p = 16 * (wp * TP + a) + lr;
-      const int n = 16 * (wn * TN + b) + (lane >> 4) * 4;
-      buf_store16(rs, ((uint32_t)p * N + n) * 4u, __builtin_bit_cast(uint4, acc[b][a]));
-    }
-}
-
 template <int P, int N, int L>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_bf16_kernel(
     ChunkMap cm, int nslots, const bf16* __restrict__ x, const bf16* __restrict__ B,
@@ -295,19 +149,27 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_bf16_kernel(
 // bmm_chunk tiles.  The three stages are independent of each other's outputs
 // here, so they share the machine instead of running back to back; the short
 // bmm workgroups come last and fill the CUs the chunk_state tail leaves idle.
+//
+// With nclear > 0 the last nclear workgroups set the `nzero` ints at `zero` to
+// 0 (the counters the fused forward's next launch counts on).
 template <int P, int N, int L>
 __global__ __launch_bounds__(kStateThreads) void front_bf16_kernel(
-    ChunkMap cm, int nslots, int nstate, int G, const bf16* __restrict__ x,
+    ChunkMap cm, int nslots, int nstate, int nbmm, int G, const bf16* __restrict__ x,
     const bf16* __restrict__ B, const bf16* __restrict__ C, const float* __restrict__ dt,
     const float* __restrict__ dt_bias, const float* __restrict__ A, float dt_min, float dt_max,
     int H, float* __restrict__ delta, float* __restrict__ dAcs, bf16* __restrict__ cb,
-    float* __restrict__ S) {
+    float* __restrict__ S, int* __restrict__ zero, int64_t nzero) {
   constexpr int LDB = N + 8;
   constexpr int NTRI = (L / 64) * (L / 64 + 1) / 2;
   constexpr size_t kBmm = 2 * 64 * LDB * sizeof(bf16);
   constexpr size_t kState = sizeof(StateSmem<P, N, L>);
   __shared__ __align__(16) unsigned char smem[kBmm > kState ? kBmm : kState];
   const int b = blockIdx.x;
+  if (b >= nstate + nbmm) {
+    const int64_t i = (int64_t)(b - nstate - nbmm) * kStateThreads + threadIdx.x;
+    if (i < nzero) zero[i] = 0;
+    return;
+  }
   if (b >= nstate) {
     // nstate is a multiple of 8, so the bmm tiles of chunk j run on the XCD
     // of its chunk_state workgroups, and one L2 fetches its B and C rows
@@ -355,10 +217,12 @@ hipError_t launch_front(const FwdArgs& a, hipStream_t s) {
     constexpr int ntri = (L / 64) * (L / 64 + 1) / 2;
     const int nbmm = xcd_grid(a.max_chunks, a.G * ntri);
     const int nstate = xcd_grid(a.max_chunks, a.H);
-    hipLaunchKernelGGL((front_bf16_kernel<P, N, L>), dim3(nstate + nbmm),
-                       dim3(kStateThreads), 0, s, a.cmap(), a.max_chunks, nstate, a.G, (const bf16*)a.x,
-                       (const bf16*)a.B, (const bf16*)a.C, a.dt, a.dt_bias, a.A, a.dt_min,
-                       a.dt_max, a.H, a.delta, a.dAcs, (bf16*)a.cb, a.chunk_states);
+    const int nclear = (int)((a.zero_ints + kStateThreads - 1) / kStateThreads);
+    hipLaunchKernelGGL((front_bf16_kernel<P, N, L>), dim3(nstate + nbmm + nclear),
+                       dim3(kStateThreads), 0, s, a.cmap(), a.max_chunks, nstate, nbmm, a.G,
+                       (const bf16*)a.x, (const bf16*)a.B, (const bf16*)a.C, a.dt, a.dt_bias,
+                       a.A, a.dt_min, a.dt_max, a.H, a.delta, a.dAcs, (bf16*)a.cb,
+                       a.chunk_states, a.sync, a.zero_ints);
     return hipGetLastError();
   }
 }

@@ -15,6 +15,30 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// threadIdx.x through an empty asm statement: values computed from it cannot
+// be hoisted out of an enclosing loop.  A persistent kernel that runs a tile
+// body per loop iteration would otherwise keep every lane offset of every
+// body in registers for the whole loop.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// threadIdx.x for a tile body of TH threads: laundered when the body runs
+// inside a persistent loop (OPQ), with its range restated so the compiler
+// keeps the code it makes for a known thread range; plain otherwise.
+template <bool OPQ, int TH>
+__device__ __forceinline__ int body_tid() {
+  if constexpr (OPQ) {
+    const int t = opaque_tid();
+    __builtin_assume(t >= 0 && t < TH);
+    return t;
+  } else {
+    return threadIdx.x;
+  }
+}
+
 // Index of the calling wave within its workgroup, as a wave-uniform (scalar)
 // value: branches and addresses derived from it stay on the scalar unit.
 __device__ __forceinline__ int wave_id() {
@@ -205,14 +229,37 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
+// Cache-policy bits of a buffer access (the aux operand): 0 is the default;
+// kSc1 makes the access coherent at device scope -- a load sees what another
+// workgroup on any XCD stored with kSc1 and waited for, and a store is
+// written through the L2 -- which is how one launch hands data from one
+// workgroup to another.
+constexpr int kSc1 = 16;
+
+template <int AUX = 0>
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
 }
+template <int AUX = 0>
 __device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX));
 }
+template <int AUX = 0>
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, AUX);
+}
+template <int AUX = 0>
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, AUX);
+}
+template <int AUX = 0>
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, AUX);
+}
+template <int AUX = 0>
+__device__ __forceinline__ void buf_store2(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16 v) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, off, 0, AUX);
 }
 
 // ---------------------------------------------------------------------------

@@ -53,7 +53,11 @@ __device__ __forceinline__ void chunk_cumsum_block(const ChunkDesc& d, int l,
 // so their CB entries are exactly 0.  A diagonal tile (ti == tj) stores 0
 // above the diagonal (s > l): the stored CB is causal, and a consumer may
 // multiply whole 32- or 64-token blocks of a row without masking them.
-template <typename T, int N, int L, int TH = 256>
+//
+// AUX: cache-policy bits of the CB stores (bf16 only; kSc1 when another
+// workgroup of the same launch reads them).  OPQ: the tile runs inside a
+// persistent loop.
+template <typename T, int N, int L, int TH = 256, int AUX = 0, bool OPQ = false>
 __device__ __forceinline__ void bmm_tile(const ChunkDesc& d, int j, int g, int ti, int tj,
                                          const T* __restrict__ C, const T* __restrict__ B, int G,
                                          T* __restrict__ cb, T* Cs, T* Bs) {
@@ -63,7 +67,7 @@ __device__ __forceinline__ void bmm_tile(const ChunkDesc& d, int j, int g, int t
   constexpr int LD = N + V;           // padded LDS row
   constexpr int VPR = N / V;
   constexpr int MI = TH == 256 ? 2 : 1;   // 16-row tiles per wave
-  const int tid = threadIdx.x;
+  const int tid = body_tid<OPQ, TH>();
   for (int i = tid; i < 64 * VPR; i += TH) {
     const int r = i / VPR, cv = i - (i / VPR) * VPR;
     const int lc = ti * 64 + r, lb = tj * 64 + r;
@@ -102,7 +106,13 @@ __device__ __forceinline__ void bmm_tile(const ChunkDesc& d, int j, int g, int t
       for (int r = 0; r < 4; ++r) {
         const int row = ti * 64 + wr + mi * 16 + (lane >> 4) * 4 + r;
         const int col = tj * 64 + wc + ni * 16 + lr;
-        out[(int64_t)row * L + col] = from_f32<T>(col <= row ? acc[mi][ni][r] : 0.f);
+        if constexpr (AUX == 0) {
+          out[(int64_t)row * L + col] = from_f32<T>(col <= row ? acc[mi][ni][r] : 0.f);
+        } else {
+          static_assert(sizeof(T) == 2, "write-through CB stores are bf16");
+          buf_store2<AUX>(buf_rsrc(out, L * L * 2), ((uint32_t)row * L + col) * 2u,
+                          from_f32<T>(col <= row ? acc[mi][ni][r] : 0.f));
+        }
       }
 }
 

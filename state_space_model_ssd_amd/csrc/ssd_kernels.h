@@ -19,6 +19,7 @@ struct FwdArgs {
   int scan_kernel;  // 0: by shape, 1: one workgroup per tile, 2: persistent (bf16)
   int sp_vec;       // 0: by shape, else state elements per state_passing thread
   int sp_blocks;    // state_passing: 1 = one chain per sequence, KB > 1 = KB blocks
+  int fused;        // 1: front, state_passing, chunk_scan as separate launches; 2: one launch
 
   const void* x;
   const float* dt;
@@ -42,8 +43,10 @@ struct FwdArgs {
   void* states_in;
   float* block_states;     // [nstates][KB][H][P*N] when sp_blocks > 1
   float* block_logdecay;   // [nstates][KB][H]
+  int* sync;               // counters of the fused forward
+  int64_t zero_ints;       // the front also clears this many ints at `sync` (0: none)
 
-  ChunkMap cmap() const {
+  __host__ __device__ ChunkMap cmap() const {
     ChunkMap m;
     m.table = packed ? table : nullptr;
     m.seq_chunks = packed ? seq_chunks : nullptr;
@@ -119,6 +122,14 @@ hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s);
 // Stage 5: outputs.
 template <typename T, int P, int N, int L>
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s);
+// Stages 1-5 of the bf16 forward as the front's launch (which clears the
+// counters at a.sync, fused_sync_bytes long) and one persistent launch of
+// state_passing and chunk_scan; scan_choice as chunk_scan_choice.
+size_t fused_sync_bytes(int nstates, int H, int G, int max_chunks);
+template <typename T, int P, int N, int L>
+bool fused_supported();
+template <typename T, int P, int N, int L>
+hipError_t launch_fused(const FwdArgs& a, int scan_choice, hipStream_t s);
 // The backward, after stages 0-4 of the forward have filled `a`'s workspace.
 template <typename T, int P, int N, int L>
 hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s);

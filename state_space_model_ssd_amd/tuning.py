@@ -19,6 +19,8 @@ one kernel for:
   sp_blocks    state_passing: 1 = one chain per sequence, 2..16 = blocks of
                chunks scanned in two launches (only for problems with few
                state elements, where the workspace reserves the blocks)
+  fused        bf16, 128- or 256-token chunks: 1 = front, state_passing and
+               chunk_scan as separate launches, 2 = one persistent launch
 
 A shape key holds everything the choices depend on: dtype, headdim, dstate,
 chunk size, ngroups, nheads, the number of logical chunks the workspace is
@@ -48,7 +50,7 @@ from state_space_model_ssd_amd import binding
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 CONFIG_PATH = os.path.join(_HERE, "tuned_configs.json")
-FIELDS = ("scan_kernel", "sp_vec", "front", "sp_blocks")
+FIELDS = ("scan_kernel", "sp_vec", "front", "sp_blocks", "fused")
 
 _cache: dict = {}
 
@@ -96,13 +98,16 @@ def candidates(prob: binding.ProblemC) -> list:
     """Every pinned combination the problem's dtype has; the state_passing
     block counts (with every vector width) where the workspace has blocks."""
     vecs = [v for v in (1, 2, 4) if (prob.headdim * prob.dstate) % v == 0]
+    fusable = prob.dtype == binding.SSD_BF16 and prob.chunk_size in (128, 256)
     if prob.dtype == binding.SSD_BF16:
-        out = [dict(scan_kernel=s, sp_vec=v, front=f)
+        out = [dict(scan_kernel=s, sp_vec=v, front=f, **(dict(fused=1) if fusable else {}))
                for s, v, f in itertools.product((1, 2, 3), vecs, (1, 2))]
     else:
         out = [dict(sp_vec=v) for v in vecs]
     if binding.workspace_layout(prob).sp_blocks > 1:
         out += [dict(sp_vec=v, sp_blocks=kb) for kb in (1, 2, 4, 8, 16) for v in vecs]
+    if fusable:
+        out.append(dict(fused=2))
     return out
 
 
@@ -169,9 +174,10 @@ def autotune(prob: binding.ProblemC, d: dict, reps: int = 20, rounds: int = 3) -
     for cand in cands[1:]:
         out, fin, _ = _forward(d, L, cand)
         bf16 = prob.dtype == binding.SSD_BF16
-        out_tol = 1e-2 if bf16 and (cand.get("scan_kernel") or cand.get("sp_blocks")) else \
-            1e-5 if cand.get("sp_blocks") else 0.0
-        fin_tol = 1e-5 if cand.get("sp_blocks") else 0.0
+        diff_chain = cand.get("sp_blocks") or cand.get("fused")   # may change the chain's order
+        out_tol = 1e-2 if bf16 and (cand.get("scan_kernel") or diff_chain) else \
+            1e-5 if diff_chain else 0.0
+        fin_tol = 1e-5 if diff_chain else 0.0
         ok = _rel_l2(out, ref_out) <= out_tol and _rel_l2(fin, ref_fin) <= fin_tol
         if not ok:
             raise RuntimeError(f"tuning candidate {cand} disagrees with the default run")

@@ -53,8 +53,10 @@ def _expected_layout(b, T, H, P, N, G, L, nseq, esize):
     mc = (min((T + nseq * (L - 1)) // L, T) if nseq else b * ((T + L - 1) // L))
     nst = nseq if nseq else b
     kb = 16 if nst * H * P * N < 2 ** 18 else 0      # blocked state_passing reserve
+    sync = 4 * (mc * H + 1)                          # counters of the fused forward
     sizes = [16 * mc, 4 * (nst + 1), 4 * mc * H * L, 4 * mc * H * L, esize * mc * G * L * L,
-             4 * mc * H * P * N, esize * mc * H * P * N, 4 * nst * kb * H * P * N, 4 * nst * kb * H]
+             4 * mc * H * P * N, esize * mc * H * P * N, 4 * nst * kb * H * P * N, 4 * nst * kb * H,
+             sync]
     offs, off = [], 0
     for s in sizes:
         offs.append(off)
@@ -77,7 +79,7 @@ def test_workspace_layout_matches_documentation(shape):
                                            p.ngroups, p.chunk_size, p.nseq, es)
     assert lay.max_chunks == mc and lay.sp_blocks == kb
     got = [lay.chunk_table, lay.seq_chunks, lay.delta, lay.dA_cumsum, lay.cb, lay.chunk_states,
-           lay.states_in, lay.block_states, lay.block_logdecay]
+           lay.states_in, lay.block_states, lay.block_logdecay, lay.sync]
     assert got == offs and lay.total_bytes == total == binding.workspace_size(p)
 
 

@@ -30,10 +30,12 @@ def test_shape_key_names_what_the_choices_depend_on():
 
 def test_candidates_cover_every_choice():
     bf = tuning.candidates(_prob())
-    assert len(bf) == 18 and len({json.dumps(c, sort_keys=True) for c in bf}) == 18
-    assert {c["scan_kernel"] for c in bf} == {1, 2, 3}
-    assert {c["sp_vec"] for c in bf} == {1, 2, 4}
-    assert {c["front"] for c in bf} == {1, 2}
+    assert len(bf) == 19 and len({json.dumps(c, sort_keys=True) for c in bf}) == 19
+    assert {c["scan_kernel"] for c in bf[:18]} == {1, 2, 3}
+    assert {c["sp_vec"] for c in bf[:18]} == {1, 2, 4}
+    assert {c["front"] for c in bf[:18]} == {1, 2}
+    assert {c["fused"] for c in bf} == {1, 2} and bf[18] == {"fused": 2}
+    assert all("fused" not in c for c in tuning.candidates(_prob(chunk_size=64)))
     f32 = tuning.candidates(_prob(dtype=binding.SSD_F32, headdim=32, dstate=16, chunk_size=64))
     assert f32[:3] == [{"sp_vec": 1}, {"sp_vec": 2}, {"sp_vec": 4}]
     # few state elements: the workspace reserves 16 blocks, so every block
@@ -51,7 +53,7 @@ def test_workspace_reserves_blocks_only_for_few_state_elements():
     assert small.total_bytes - small.block_logdecay >= 4 * nst * 16 * H
     big = binding.workspace_layout(_prob())          # 2 * 24 * 64 * 128 >= 2^18 elements
     assert big.sp_blocks == 1
-    assert big.block_logdecay == big.block_states == big.total_bytes
+    assert big.block_logdecay == big.block_states == big.sync
 
 
 def test_config_round_trip_and_fallback(tmp_path, monkeypatch):
@@ -103,6 +105,11 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails on the h
     (binding.SSD_BF16, dict(sp_blocks=2)),      # a layer-size problem reserves no blocks
     (binding.SSD_F32, dict(scan_kernel=1)),     # fp32 has one chunk_scan kernel
     (binding.SSD_F32, dict(front=1)),           # and no fused front
+    (binding.SSD_BF16, dict(fused=3)),
+    (binding.SSD_F32, dict(fused=2)),           # the fused forward is bf16 only
+    (binding.SSD_BF16, dict(fused=2, front=2)),
+    (binding.SSD_BF16, dict(fused=2, scan_kernel=2)),
+    (binding.SSD_BF16, dict(fused=2, sp_vec=2)),
 ])
 def test_out_of_range_tuning_rejected_on_host(dtype, fields):
     lib = binding.load_library()
