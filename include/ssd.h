@@ -315,6 +315,51 @@ ssd_status_t ssd_bwd_after_fwd(const ssd_problem_t* p,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The gated RMS norm that follows the SSD in a Mamba-2 layer, and its
+ * backward.  The pages name the layer's norm only through its backward
+ * kernel (clova.ai page, table "Share of compute time by kernel":
+ * _layer_norm_bwd, the largest share, memory-bound; section "How we fixed
+ * it"); the norm read here is the Mamba-2 gated RMS norm.  For every row t
+ * (token) and every group of group_size consecutive channels:
+ *
+ *   g_c   = y[t,c] * silu(z[t,c]),        silu(v) = v / (1 + exp(-v))
+ *   r     = 1 / sqrt(mean_{c in group} g_c^2 + eps)
+ *   out[t,c] = g_c * r * w[c]
+ *
+ * y is the SSD output flattened to rows of channels = nheads * headdim
+ * ([tokens][channels], the layout of ssd_fwd's out), z the gate of the same
+ * layout and dtype, w [channels] fp32.  Accumulation in fp32, one rounding of
+ * each output to the dtype.
+ *   - group_size divides channels; group_size / (16 / dtype size) is a
+ *     power of two up to 64 or a multiple of 64 (else SSD_ERR_UNSUPPORTED);
+ *     channels <= 8192 (bf16) or 4096 (fp32); eps >= 0.
+ *   - ssd_gated_norm_fwd: out (may be y itself: each element is read before
+ *     it is written, by the same thread); rstd [tokens][channels /
+ *     group_size] fp32 receives r (nullable).
+ *   - ssd_gated_norm_bwd: the gradients of sum(out * dout): dy, dz like y,
+ *     dw [channels] fp32 (required); the workspace is
+ *     ssd_gated_norm_bwd_workspace_size bytes, 256-byte aligned.  No atomics:
+ *     deterministic.
+ * Device pointers, asynchronous on `stream`; errors as for ssd_fwd.
+ */
+typedef struct {
+  int64_t tokens;      /* rows                                           */
+  int64_t channels;    /* channels per row                               */
+  int64_t group_size;  /* consecutive channels normalised together       */
+  int32_t dtype;       /* ssd_dtype_t of y, z, out, dout, dy, dz         */
+  float eps;
+} ssd_norm_problem_t;
+
+ssd_status_t ssd_gated_norm_fwd(const ssd_norm_problem_t* p, const void* y, const void* z,
+                                const float* w, void* out, float* rstd, void* stream);
+
+size_t ssd_gated_norm_bwd_workspace_size(const ssd_norm_problem_t* p);
+
+ssd_status_t ssd_gated_norm_bwd(const ssd_norm_problem_t* p, const void* y, const void* z,
+                                const float* w, const void* dout, void* dy, void* dz, float* dw,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): ssd_fwd
  * without a workspace argument.  The workspace is a static device array of

@@ -31,7 +31,8 @@ STAGES = {"plan": STAGE_PLAN, "chunk_cumsum": STAGE_CUMSUM, "bmm_chunk": STAGE_B
 
 EXPORTED = ("ssd_fwd_workspace_size", "ssd_workspace_layout", "ssd_config_supported",
             "ssd_fwd", "ssd_fwd_stages", "ssd_fwd_tuned", "ssd_bwd_workspace_size", "ssd_bwd",
-            "ssd_bwd_after_fwd", "ssd_fwd_choices", "ssd_fwd_noalloc",
+            "ssd_bwd_after_fwd", "ssd_fwd_choices", "ssd_fwd_noalloc", "ssd_gated_norm_fwd",
+            "ssd_gated_norm_bwd_workspace_size", "ssd_gated_norm_bwd",
             "ssd_status_string")
 
 
@@ -58,6 +59,12 @@ class LayoutC(ctypes.Structure):
                 ("block_states", ctypes.c_size_t), ("block_logdecay", ctypes.c_size_t),
                 ("sync", ctypes.c_size_t),
                 ("sp_blocks", ctypes.c_int64), ("total_bytes", ctypes.c_size_t)]
+
+
+class NormProblemC(ctypes.Structure):
+    """ssd_norm_problem_t: the gated RMS norm after the SSD."""
+    _fields_ = [("tokens", ctypes.c_int64), ("channels", ctypes.c_int64),
+                ("group_size", ctypes.c_int64), ("dtype", ctypes.c_int32), ("eps", ctypes.c_float)]
 
 
 class TuningC(ctypes.Structure):
@@ -102,6 +109,13 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_bwd.restype = ctypes.c_int
     lib.ssd_bwd_after_fwd.argtypes = [PP] + [vp] * 20 + [vp, sz, vp]
     lib.ssd_bwd_after_fwd.restype = ctypes.c_int
+    NP = ctypes.POINTER(NormProblemC)
+    lib.ssd_gated_norm_fwd.argtypes = [NP] + [vp] * 5 + [vp]
+    lib.ssd_gated_norm_fwd.restype = ctypes.c_int
+    lib.ssd_gated_norm_bwd_workspace_size.argtypes = [NP]
+    lib.ssd_gated_norm_bwd_workspace_size.restype = sz
+    lib.ssd_gated_norm_bwd.argtypes = [NP] + [vp] * 8 + [sz, vp]
+    lib.ssd_gated_norm_bwd.restype = ctypes.c_int
     lib.ssd_fwd_noalloc.argtypes = [PP] + [vp] * 12 + [vp]
     lib.ssd_fwd_noalloc.restype = ctypes.c_int
     lib.ssd_fwd_choices.argtypes = [PP, ctypes.POINTER(TuningC)]
@@ -300,6 +314,67 @@ def ssd_fwd_noalloc(x, dt, A, B, C, chunk_size, out, final_states=None, D=None, 
                                    _ptr(final_states), stream)
     _check(code)
     return out, final_states
+
+
+def _norm_problem(y, group_size, eps):
+    dtype = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}.get(y.dtype, -1)
+    C = y.shape[-1]
+    return NormProblemC(int(y.numel() // max(C, 1)), int(C), int(group_size), int(dtype),
+                        float(eps))
+
+
+def gated_norm_fwd(y, z, w, group_size, eps=1e-5, out=None, return_rstd=False):
+    """ssd_gated_norm_fwd: rmsnorm(y * silu(z)) * w over groups of group_size
+    consecutive channels of the last axis.  y, z: (..., channels) in fp32 or
+    bf16 on the GPU, w: (channels,) fp32.  out may be y (in place).  Returns
+    out, or (out, rstd) with rstd (rows, channels // group_size) fp32."""
+    lib = load_library()
+    dev = y.device
+    if dev.type != "cuda":
+        raise ValueError("gated_norm_fwd runs on the GPU only; y is on " + str(dev))
+    C = y.shape[-1]
+    _need(y, "y", y.dtype, tuple(y.shape), dev)
+    _need(z, "z", y.dtype, tuple(y.shape), dev)
+    _need(w, "w", torch.float32, (C,), dev)
+    if out is None:
+        out = torch.empty_like(y)
+    _need(out, "out", y.dtype, tuple(y.shape), dev)
+    p = _norm_problem(y, group_size, eps)
+    rstd = None
+    if return_rstd:
+        rstd = torch.empty((p.tokens, C // max(int(group_size), 1)), dtype=torch.float32,
+                           device=dev)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        code = lib.ssd_gated_norm_fwd(ctypes.byref(p), _ptr(y), _ptr(z), _ptr(w), _ptr(out),
+                                      _ptr(rstd), stream)
+    _check(code)
+    return (out, rstd) if return_rstd else out
+
+
+def gated_norm_bwd(y, z, w, dout, group_size, eps=1e-5, workspace=None):
+    """ssd_gated_norm_bwd: (dy, dz, dw) of sum(gated_norm_fwd(y, z, w) * dout)."""
+    lib = load_library()
+    dev = y.device
+    if dev.type != "cuda":
+        raise ValueError("gated_norm_bwd runs on the GPU only; y is on " + str(dev))
+    C = y.shape[-1]
+    for t, name in ((y, "y"), (z, "z"), (dout, "dout")):
+        _need(t, name, y.dtype, tuple(y.shape), dev)
+    _need(w, "w", torch.float32, (C,), dev)
+    p = _norm_problem(y, group_size, eps)
+    dy, dz = torch.empty_like(y), torch.empty_like(y)
+    dw = torch.empty(C, dtype=torch.float32, device=dev)
+    need = int(lib.ssd_gated_norm_bwd_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        code = lib.ssd_gated_norm_bwd(ctypes.byref(p), _ptr(y), _ptr(z), _ptr(w), _ptr(dout),
+                                      _ptr(dy), _ptr(dz), _ptr(dw), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), stream)
+    _check(code)
+    return dy, dz, dw
 
 
 def fwd_choices(prob: ProblemC) -> dict:

@@ -540,6 +540,75 @@ ssd_status_t ssd_fwd_choices(const ssd_problem_t* p, ssd_tuning_t* choices) {
   return SSD_OK;
 }
 
+}  // extern "C"
+
+namespace ssd {
+namespace {
+
+ssd_status_t check_norm(const ssd_norm_problem_t* p) {
+  if (!p) return SSD_ERR_INVALID_ARG;
+  if (p->tokens < 0 || p->channels < 1 || p->group_size < 1) return SSD_ERR_INVALID_ARG;
+  if (p->dtype != SSD_F32 && p->dtype != SSD_BF16) return SSD_ERR_INVALID_ARG;
+  if (p->channels % p->group_size != 0) return SSD_ERR_INVALID_ARG;
+  if (!(p->eps >= 0.f) || isinf(p->eps)) return SSD_ERR_INVALID_ARG;
+  const int64_t V = p->dtype == SSD_BF16 ? 8 : 4;
+  if (p->group_size % V != 0) return SSD_ERR_UNSUPPORTED;
+  const int64_t nv = p->group_size / V;
+  const bool pow2 = (nv & (nv - 1)) == 0;
+  if (!((nv <= 64 && pow2) || nv % 64 == 0)) return SSD_ERR_UNSUPPORTED;
+  if (p->channels > norm_max_channels(p->dtype)) return SSD_ERR_UNSUPPORTED;
+  if (p->tokens * p->channels > (int64_t)1 << 40) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+NormArgs norm_args(const ssd_norm_problem_t* p) {
+  NormArgs a{};
+  a.rows = p->tokens;
+  a.C = (int)p->channels;
+  a.GS = (int)p->group_size;
+  a.eps = p->eps;
+  a.bf16 = p->dtype == SSD_BF16;
+  return a;
+}
+
+}  // namespace
+}  // namespace ssd
+
+extern "C" {
+
+ssd_status_t ssd_gated_norm_fwd(const ssd_norm_problem_t* p, const void* y, const void* z,
+                                const float* w, void* out, float* rstd, void* stream) {
+  ssd_status_t st = ssd::check_norm(p);
+  if (st != SSD_OK) return st;
+  if (p->tokens > 0 && (!y || !z || !w || !out)) return SSD_ERR_INVALID_ARG;
+  ssd::NormArgs a = ssd::norm_args(p);
+  a.y = y; a.z = z; a.w = w; a.out = out; a.rstd = rstd;
+  if (ssd::launch_norm_fwd(a, static_cast<hipStream_t>(stream)) != hipSuccess) return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+size_t ssd_gated_norm_bwd_workspace_size(const ssd_norm_problem_t* p) {
+  if (ssd::check_norm(p) != SSD_OK) return 0;
+  return ssd::align_up(sizeof(float) * (size_t)ssd::norm_workspace_floats(p->channels));
+}
+
+ssd_status_t ssd_gated_norm_bwd(const ssd_norm_problem_t* p, const void* y, const void* z,
+                                const float* w, const void* dout, void* dy, void* dz, float* dw,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  ssd_status_t st = ssd::check_norm(p);
+  if (st != SSD_OK) return st;
+  if (!w || !dw) return SSD_ERR_INVALID_ARG;
+  if (p->tokens > 0 && (!y || !z || !dout || !dy || !dz)) return SSD_ERR_INVALID_ARG;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % ssd::kAlign) != 0 ||
+      workspace_bytes < ssd_gated_norm_bwd_workspace_size(p))
+    return SSD_ERR_WORKSPACE;
+  ssd::NormArgs a = ssd::norm_args(p);
+  a.y = y; a.z = z; a.w = w; a.dout = dout; a.dy = dy; a.dz = dz; a.dw = dw;
+  a.dw_part = static_cast<float*>(workspace);
+  if (ssd::launch_norm_bwd(a, static_cast<hipStream_t>(stream)) != hipSuccess) return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
 const char* ssd_status_string(ssd_status_t s) {
   switch (s) {
     case SSD_OK: return "ok";

@@ -102,6 +102,31 @@ int chunk_scan_choice(const FwdArgs& a);
 // The library's own state_passing vector width (1, 2 or 4) for this problem.
 int state_passing_vec(const FwdArgs& a);
 
+// The gated RMS norm after the SSD (forward and backward).
+struct NormArgs {
+  int64_t rows;
+  int C, GS;            // channels per row, channels per group
+  float eps;
+  bool bf16;            // dtype of y, z, out, dout, dy, dz
+  const void* y;
+  const void* z;
+  const float* w;
+  void* out;
+  float* rstd;          // nullable
+  const void* dout;
+  void* dy;
+  void* dz;
+  float* dw;
+  float* dw_part;       // norm_workspace_floats(C) floats
+};
+// Most channels per row the norm kernels take for a dtype.
+int norm_max_channels(int32_t dtype);
+// Floats of the backward's workspace (partial rows of dw and their first
+// sums) for rows of C channels: a bound that does not depend on the device.
+int64_t norm_workspace_floats(int64_t C);
+hipError_t launch_norm_fwd(const NormArgs& a, hipStream_t s);
+hipError_t launch_norm_bwd(const NormArgs& a, hipStream_t s);
+
 // Stage 0: logical chunk table of a packed batch.
 hipError_t launch_plan(const FwdArgs& a, hipStream_t s);
 // Stage 1: delta and its chunk-local cumulative sum times A.

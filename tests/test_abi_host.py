@@ -203,3 +203,31 @@ def test_choices_query_checked_on_host(lib):
     if not torch.cuda.is_available():
         # the choices depend on the device, so without one the query fails
         assert lib.ssd_fwd_choices(ctypes.byref(_prob()), ctypes.byref(t)) == binding.SSD_ERR_HIP
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(channels=96, group_size=32), binding.SSD_OK),                 # 4 vectors per group
+    (dict(channels=1536, group_size=1536), binding.SSD_OK),             # 3 chunks of 64 vectors
+    (dict(channels=100, group_size=30), binding.SSD_ERR_INVALID_ARG),   # does not divide
+    (dict(channels=96, group_size=12), binding.SSD_ERR_UNSUPPORTED),    # not whole vectors
+    (dict(channels=96, group_size=48), binding.SSD_ERR_UNSUPPORTED),    # 6 vectors: not 2^k
+    (dict(channels=16384, group_size=64), binding.SSD_ERR_UNSUPPORTED), # too wide a row
+    (dict(eps=-1.0), binding.SSD_ERR_INVALID_ARG),
+    (dict(tokens=-1), binding.SSD_ERR_INVALID_ARG),
+    (dict(dtype=5), binding.SSD_ERR_INVALID_ARG),
+])
+def test_norm_problems_checked_on_host(lib, kw, code):
+    base = dict(tokens=10, channels=128, group_size=64, dtype=binding.SSD_BF16, eps=1e-5)
+    base.update(kw)
+    p = binding.NormProblemC(base["tokens"], base["channels"], base["group_size"], base["dtype"],
+                             base["eps"])
+    size = lib.ssd_gated_norm_bwd_workspace_size(ctypes.byref(p))
+    assert (size > 0) == (code == binding.SSD_OK)
+    if code != binding.SSD_OK:
+        assert lib.ssd_gated_norm_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None) == code
+    else:
+        # required pointers, then the workspace, are checked before any launch
+        assert lib.ssd_gated_norm_fwd(ctypes.byref(p), None, FAKE, FAKE, FAKE, None, None) == \
+            binding.SSD_ERR_INVALID_ARG
+        assert lib.ssd_gated_norm_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, size - 1, None) == binding.SSD_ERR_WORKSPACE
