@@ -360,6 +360,33 @@ ssd_status_t ssd_gated_norm_bwd(const ssd_norm_problem_t* p, const void* y, cons
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The forward followed by the gated RMS norm of its output (the same norm as
+ * ssd_gated_norm_fwd, over rows of nheads * headdim channels): `out`
+ * receives rmsnorm(y * silu(z)) * weight, not y.  Where the norm's groups lie
+ * inside a head (group_size divides headdim; bf16) and chunk_scan runs a
+ * one-tile-per-workgroup kernel (the library's choice for most shapes), the
+ * norm is applied in chunk_scan's store and y never reaches memory;
+ * otherwise the forward writes y into `out` and the norm runs over it in
+ * place.  Either way the result equals ssd_fwd followed by
+ * ssd_gated_norm_fwd bit for bit.  final_states and the workspace are as
+ * for ssd_fwd.
+ */
+typedef struct {
+  const void* z;        /* gate, layout and dtype of x and out           */
+  const float* weight;  /* [nheads * headdim]                            */
+  float eps;
+  int64_t group_size;   /* channels normalised together (see ssd_norm_problem_t) */
+} ssd_gate_t;
+
+ssd_status_t ssd_fwd_gated(const ssd_problem_t* p,
+                           const void* x, const float* dt, const float* dt_bias,
+                           const float* A, const void* B, const void* C, const float* D,
+                           const float* initial_states,
+                           const int32_t* cu_seqlens, const int32_t* seq_idx,
+                           const ssd_gate_t* gate, void* out, float* final_states,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): ssd_fwd
  * without a workspace argument.  The workspace is a static device array of

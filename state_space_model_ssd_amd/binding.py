@@ -32,7 +32,7 @@ STAGES = {"plan": STAGE_PLAN, "chunk_cumsum": STAGE_CUMSUM, "bmm_chunk": STAGE_B
 EXPORTED = ("ssd_fwd_workspace_size", "ssd_workspace_layout", "ssd_config_supported",
             "ssd_fwd", "ssd_fwd_stages", "ssd_fwd_tuned", "ssd_bwd_workspace_size", "ssd_bwd",
             "ssd_bwd_after_fwd", "ssd_fwd_choices", "ssd_fwd_noalloc", "ssd_gated_norm_fwd",
-            "ssd_gated_norm_bwd_workspace_size", "ssd_gated_norm_bwd",
+            "ssd_gated_norm_bwd_workspace_size", "ssd_gated_norm_bwd", "ssd_fwd_gated",
             "ssd_status_string")
 
 
@@ -65,6 +65,12 @@ class NormProblemC(ctypes.Structure):
     """ssd_norm_problem_t: the gated RMS norm after the SSD."""
     _fields_ = [("tokens", ctypes.c_int64), ("channels", ctypes.c_int64),
                 ("group_size", ctypes.c_int64), ("dtype", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+class GateC(ctypes.Structure):
+    """ssd_gate_t: the gated RMS norm ssd_fwd_gated applies to its output."""
+    _fields_ = [("z", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("group_size", ctypes.c_int64)]
 
 
 class TuningC(ctypes.Structure):
@@ -116,6 +122,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_gated_norm_bwd_workspace_size.restype = sz
     lib.ssd_gated_norm_bwd.argtypes = [NP] + [vp] * 8 + [sz, vp]
     lib.ssd_gated_norm_bwd.restype = ctypes.c_int
+    lib.ssd_fwd_gated.argtypes = [PP] + [vp] * 10 + [ctypes.POINTER(GateC), vp, vp, vp, sz, vp]
+    lib.ssd_fwd_gated.restype = ctypes.c_int
     lib.ssd_fwd_noalloc.argtypes = [PP] + [vp] * 12 + [vp]
     lib.ssd_fwd_noalloc.restype = ctypes.c_int
     lib.ssd_fwd_choices.argtypes = [PP, ctypes.POINTER(TuningC)]
@@ -375,6 +383,53 @@ def gated_norm_bwd(y, z, w, dout, group_size, eps=1e-5, workspace=None):
                                       workspace.numel() * workspace.element_size(), stream)
     _check(code)
     return dy, dz, dw
+
+
+def ssd_fwd_gated(x, dt, A, B, C, chunk_size, z, norm_weight, group_size, eps=1e-5, D=None,
+                  dt_bias=None, initial_states=None, cu_seqlens=None, out=None,
+                  final_states=None, workspace=None):
+    """ssd_fwd_gated: the forward, then rmsnorm(y * silu(z)) * norm_weight over
+    groups of group_size channels of each token's nheads * headdim channels.
+    Returns (out, final_states, workspace) like ssd_fwd, out being the
+    normalised output."""
+    lib = load_library()
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_fwd_gated runs on the GPU only; x is on " + str(dev))
+    f32 = torch.float32
+    nseq = cu_seqlens.numel() - 1 if cu_seqlens is not None else 0
+    nstates = nseq if nseq > 0 else b
+    for t, name, dtp, shape in ((x, "x", x.dtype, (b, T, H, P)), (dt, "dt", f32, (b, T, H)),
+                                (A, "A", f32, (H,)), (B, "B", x.dtype, (b, T, G, N)),
+                                (C, "C", x.dtype, (b, T, G, N)), (D, "D", f32, (H,)),
+                                (dt_bias, "dt_bias", f32, (H,)),
+                                (initial_states, "initial_states", f32, (nstates, H, P, N)),
+                                (cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,)),
+                                (z, "z", x.dtype, (b, T, H, P)),
+                                (norm_weight, "norm_weight", f32, (H * P,))):
+        _need(t, name, dtp, shape, dev)
+    prob = make_problem(b, T, H, P, N, G, chunk_size, x.dtype, nseq)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", x.dtype, (b, T, H, P), dev)
+    if final_states is None:
+        final_states = torch.empty((nstates, H, P, N), dtype=f32, device=dev)
+    _need(final_states, "final_states", f32, (nstates, H, P, N), dev)
+    need = lib.ssd_fwd_workspace_size(ctypes.byref(prob))
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
+    gate = GateC(_ptr(z), _ptr(norm_weight), float(eps), int(group_size))
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        code = lib.ssd_fwd_gated(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A),
+                                 _ptr(B), _ptr(C), _ptr(D), _ptr(initial_states), _ptr(cu_seqlens),
+                                 None, ctypes.byref(gate), _ptr(out), _ptr(final_states),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 stream)
+    _check(code)
+    return out, final_states, workspace
 
 
 def fwd_choices(prob: ProblemC) -> dict:

@@ -229,6 +229,10 @@ ssd_status_t fill_args(const ssd_problem_t* p, const ssd_workspace_layout_t& w,
   a.block_logdecay = w.sp_blocks > 1 ? reinterpret_cast<float*>(base + w.block_logdecay) : nullptr;
   a.sync = reinterpret_cast<int*>(base + w.sync);
   a.zero_ints = 0;
+  a.gate_z = nullptr;
+  a.gate_w = nullptr;
+  a.gate_eps = 0.f;
+  a.gate_gs = 0;
   return SSD_OK;
 }
 
@@ -279,11 +283,15 @@ ssd_status_t launch_stages(const ssd_problem_t* p, const FwdArgs& a, uint32_t st
   return SSD_OK;
 }
 
+ssd_status_t check_norm(const ssd_norm_problem_t* p);
+NormArgs norm_args(const ssd_norm_problem_t* p);
+
 ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias,
                  const float* A, const void* B, const void* C, const float* D,
                  const float* initial_states, const int32_t* cu_seqlens, const int32_t* seq_idx,
                  void* out, float* final_states, void* workspace, size_t workspace_bytes,
-                 uint32_t stages, const ssd_tuning_t* tuning, void* stream) {
+                 uint32_t stages, const ssd_tuning_t* tuning, void* stream,
+                 const ssd_gate_t* gate = nullptr) {
   ssd_status_t st = check_problem(p);
   if (st != SSD_OK) return st;
   if (stages & ~(uint32_t)SSD_STAGE_ALL) return SSD_ERR_INVALID_ARG;
@@ -299,7 +307,35 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
   st = fill_args(p, w, tune, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, out,
                  final_states, workspace, &a);
   if (st != SSD_OK) return st;
-  return launch_stages(p, a, stages, tune, stream);
+  if (!gate) return launch_stages(p, a, stages, tune, stream);
+  // the gated RMS norm after the forward: fused into chunk_scan's store when
+  // its groups lie inside a head and a one-tile-per-workgroup scan kernel
+  // runs, else a launch of its own over `out` in place
+  const ssd_norm_problem_t np{tokens, p->nheads * p->headdim, gate->group_size, p->dtype, gate->eps};
+  st = check_norm(&np);
+  if (st != SSD_OK) return st;
+  if (tokens > 0 && (!gate->z || !gate->weight)) return SSD_ERR_INVALID_ARG;
+  const Kernels* k = find_kernels(p->dtype, p->headdim, p->dstate, p->chunk_size);
+  const int scan = tune.scan_kernel != 0 ? tune.scan_kernel : k->scan_choice(a);
+  if (scan < 0) return SSD_ERR_HIP;
+  const bool fusable = p->dtype == SSD_BF16 && p->headdim % gate->group_size == 0 &&
+                       (scan == 1 || scan == 3) && fused_choice(p, a, tune) != 2;
+  if (fusable) {
+    a.gate_z = gate->z;
+    a.gate_w = gate->weight;
+    a.gate_eps = gate->eps;
+    a.gate_gs = (int)gate->group_size;
+    return launch_stages(p, a, stages, tune, stream);
+  }
+  st = launch_stages(p, a, stages, tune, stream);
+  if (st != SSD_OK || tokens == 0) return st;
+  NormArgs na = norm_args(&np);
+  na.y = out;
+  na.z = gate->z;
+  na.w = gate->weight;
+  na.out = out;
+  if (launch_norm_fwd(na, static_cast<hipStream_t>(stream)) != hipSuccess) return SSD_ERR_HIP;
+  return SSD_OK;
 }
 
 
@@ -509,6 +545,17 @@ ssd_status_t ssd_fwd_noalloc(const ssd_problem_t* p, const void* x, const float*
   if (!ws) return SSD_ERR_HIP;
   return ssd::run(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, out,
                   final_states, ws, SSD_NOALLOC_SCRATCH_BYTES, SSD_STAGE_ALL, nullptr, stream);
+}
+
+ssd_status_t ssd_fwd_gated(const ssd_problem_t* p, const void* x, const float* dt,
+                           const float* dt_bias, const float* A, const void* B, const void* C,
+                           const float* D, const float* initial_states,
+                           const int32_t* cu_seqlens, const int32_t* seq_idx,
+                           const ssd_gate_t* gate, void* out, float* final_states,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!gate) return SSD_ERR_INVALID_ARG;
+  return ssd::run(p, x, dt, dt_bias, A, B, C, D, initial_states, cu_seqlens, seq_idx, out,
+                  final_states, workspace, workspace_bytes, SSD_STAGE_ALL, nullptr, stream, gate);
 }
 
 ssd_status_t ssd_fwd_choices(const ssd_problem_t* p, ssd_tuning_t* choices) {

@@ -527,13 +527,13 @@ __global__ __launch_bounds__(4 * L) __attribute__((amdgpu_waves_per_eu(4))) void
 }
 
 
-template <int P, int N, int L, int NW>
+template <int P, int N, int L, int NW, bool GATE = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kTileWavesPerEU<L, NW>))) void
 chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
                             const bf16* __restrict__ C, const bf16* __restrict__ cb,
                             const float* __restrict__ delta, const float* __restrict__ dAcs,
                             const bf16* __restrict__ states_in, const float* __restrict__ D, int H,
-                            int G, bf16* __restrict__ out) {
+                            int G, bf16* __restrict__ out, ScanGate gate) {
   static_assert(L % 64 == 0 && P % 32 == 0 && N % 32 == 0, "tile shape");
   constexpr int HP = N + 8;
   __shared__ __align__(16) bf16 xs[L * P];
@@ -558,9 +558,11 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
   }
   if (T.len <= 0) return;
   if (fabsf(last) * kLog2e <= kScanFastMaxLog2)   // uniform over the workgroup
-    scan_tile_body<P, N, L, NW, true>(T, x, C, cb, delta, dAcs, states_in, D, H, G, out, xs, hsm, dal2, dls, cfs);
+    scan_tile_body<P, N, L, NW, true, 0, 0, false, GATE>(T, x, C, cb, delta, dAcs, states_in, D, H, G,
+                                                        out, xs, hsm, dal2, dls, cfs, gate);
   else
-    scan_tile_body<P, N, L, NW, false>(T, x, C, cb, delta, dAcs, states_in, D, H, G, out, xs, hsm, dal2, dls, cfs);
+    scan_tile_body<P, N, L, NW, false, 0, 0, false, GATE>(T, x, C, cb, delta, dAcs, states_in, D, H, G,
+                                                         out, xs, hsm, dal2, dls, cfs, gate);
 }
 
 }  // namespace
@@ -614,22 +616,37 @@ hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s) {
     int choice = a.scan_kernel;
     if (choice == 0) choice = chunk_scan_choice<T, P, N, L>(a);
     if (choice < 0) return hipErrorInvalidDevice;
+    if (choice == 2 && a.gate_z) return hipErrorInvalidValue;   // the caller picks a tile kernel
     if (choice == 2) {
       const int g = persistent_grid<P, N, L>();
       if (g <= 0) return hipErrorInvalidDevice;
       hipLaunchKernelGGL(kern, dim3(g), dim3(4 * L), 0, s, a.cmap(), a.max_chunks, ntiles,
                          (const bf16*)a.x, (const bf16*)a.C, (const bf16*)a.cb, a.delta, a.dAcs,
                          (const bf16*)a.states_in, a.D, a.H, a.G, (bf16*)a.out);
-    } else if (choice == 3) {
-      hipLaunchKernelGGL((chunk_scan_bf16_tile_kernel<P, N, L, 4>), dim3(ntiles), dim3(64 * 4), 0, s,
-                         a.cmap(), a.max_chunks, (const bf16*)a.x, (const bf16*)a.C,
-                         (const bf16*)a.cb, a.delta, a.dAcs, (const bf16*)a.states_in, a.D, a.H,
-                         a.G, (bf16*)a.out);
     } else {
-      hipLaunchKernelGGL((chunk_scan_bf16_tile_kernel<P, N, L, kTileWaves<L>>), dim3(ntiles),
-                         dim3(64 * kTileWaves<L>), 0, s, a.cmap(), a.max_chunks, (const bf16*)a.x,
-                         (const bf16*)a.C, (const bf16*)a.cb, a.delta, a.dAcs,
-                         (const bf16*)a.states_in, a.D, a.H, a.G, (bf16*)a.out);
+      // one workgroup per tile: 4 waves (choice 3) or the chunk size's default;
+      // with a gate the tile's store applies the gated RMS norm
+      ScanGate gate{};
+      if (a.gate_z) {
+        gate.z = static_cast<const bf16*>(a.gate_z);
+        gate.w = a.gate_w;
+        gate.eps = a.gate_eps;
+        gate.inv_gs = 1.f / (float)a.gate_gs;
+        gate.gpl = a.gate_gs / 8;
+      }
+      auto go = [&](auto kern, int nw) {
+        hipLaunchKernelGGL(kern, dim3(ntiles), dim3(64 * nw), 0, s, a.cmap(), a.max_chunks,
+                           (const bf16*)a.x, (const bf16*)a.C, (const bf16*)a.cb, a.delta, a.dAcs,
+                           (const bf16*)a.states_in, a.D, a.H, a.G, (bf16*)a.out, gate);
+      };
+      if (choice == 3) {
+        if (a.gate_z) go(chunk_scan_bf16_tile_kernel<P, N, L, 4, true>, 4);
+        else go(chunk_scan_bf16_tile_kernel<P, N, L, 4, false>, 4);
+      } else {
+        constexpr int NW = kTileWaves<L>;
+        if (a.gate_z) go(chunk_scan_bf16_tile_kernel<P, N, L, NW, true>, NW);
+        else go(chunk_scan_bf16_tile_kernel<P, N, L, NW, false>, NW);
+      }
     }
   } else {
     dim3 grid(a.max_chunks * (L / 64), a.H);

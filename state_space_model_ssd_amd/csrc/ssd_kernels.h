@@ -43,6 +43,11 @@ struct FwdArgs {
   void* states_in;
   float* block_states;     // [nstates][KB][H][P*N] when sp_blocks > 1
   float* block_logdecay;   // [nstates][KB][H]
+  // gated RMS norm fused into chunk_scan's store (gate_z nullptr: none)
+  const void* gate_z;
+  const float* gate_w;
+  float gate_eps;
+  int gate_gs;
   int* sync;               // counters of the fused forward
   int64_t zero_ints;       // the front also clears this many ints at `sync` (0: none)
 

@@ -30,6 +30,7 @@
 // over the rows its workgroup visits and writes one partial row per
 // workgroup; a second kernel sums the partials in workgroup order.  No
 // atomics: results are deterministic.
+#include "ssd_gate.h"
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -68,21 +69,6 @@ template <> struct NormVec<float> {
                       __builtin_bit_cast(uint32_t, f[2]), __builtin_bit_cast(uint32_t, f[3]));
   }
 };
-
-// silu(z) = z sigma(z), with sigma through the hardware reciprocal (about one
-// unit in the last place of fp32): sigma -> 0 for z -> -inf (exp overflows to
-// inf, whose reciprocal is 0) and -> 1 for z -> +inf.
-__device__ __forceinline__ float silu_sig(float z, float& sig) {
-  sig = __builtin_amdgcn_rcpf(1.f + __expf(-z));
-  return z * sig;
-}
-
-// Sum of v over the lanes of an aligned run of n lanes (n a power of two
-// <= 64), offsets from 1 up.
-__device__ __forceinline__ float run_sum(float v, int n) {
-  for (int off = 1; off < n; off <<= 1) v += __shfl_xor(v, off);
-  return v;
-}
 
 // Group sums of s[k] (this thread's vector t + 256 k), in place.  `chunk`
 // is LDS scratch of KT * 4 floats, nchunks (<= 4 KT) the row's 64-vector
@@ -164,20 +150,14 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_fwd_kernel(
       float yf[V], zf[V];
       NVc::unpack(yv[k], yf);
       NVc::unpack(zv[k], zf);
-      s[k] = 0.f;
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        float sig;
-        g[k][e] = yf[e] * silu_sig(zf[e], sig);
-        s[k] += g[k][e] * g[k][e];
-      }
+      s[k] = gate_values<V>(yf, zf, g[k]);
     }
     group_sums<KT>(s, NV, (nvec + 63) / 64, chunk + par * 4 * KT);
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
       const int v = t + kNormThreads * k;
       if (v >= nvec) continue;
-      const float rs = rsqrtf(s[k] * inv_gs + eps);
+      const float rs = gate_rstd(s[k], inv_gs, eps);
       float wv[V], o[V];
       load_w(w, v, nvec, wv, V);
 #pragma unroll
@@ -220,20 +200,14 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_bwd_kernel(
       float yf[V], zf[V];
       NVc::unpack(yv[k], yf);
       NVc::unpack(zv[k], zf);
-      s[k] = 0.f;
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        float sig;
-        u[k][e] = yf[e] * silu_sig(zf[e], sig);
-        s[k] += u[k][e] * u[k][e];
-      }
+      s[k] = gate_values<V>(yf, zf, u[k]);
     }
     group_sums<KT>(s, NV, (nvec + 63) / 64, chunk);
     // u = g r; dw += dout u; the group sums of du u with du = dout w
     float p[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-      s[k] = rsqrtf(s[k] * inv_gs + eps);  // s now holds r
+      s[k] = gate_rstd(s[k], inv_gs, eps);  // s now holds r
       float df[V];
       NVc::unpack(dv[k], df);
       p[k] = 0.f;
@@ -267,7 +241,7 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_bwd_kernel(
       for (int e = 0; e < V; ++e) {
         const float dg = s[k] * (df[e] * wr[k][e] - u[k][e] * mp);
         float sig;
-        const float gate = silu_sig(zf[e], sig);
+        const float gate = gate_silu(zf[e], sig);
         ody[e] = dg * gate;
         odz[e] = dg * yf[e] * sig * (1.f + zf[e] * (1.f - sig));
       }

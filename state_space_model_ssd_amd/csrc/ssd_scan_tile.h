@@ -5,6 +5,7 @@
 #pragma once
 
 #include "ssd_common.h"
+#include "ssd_gate.h"
 
 // Multiply-adds are fused into FMAs only inside one expression (not by the
 // code generator across statements), so every kernel that inlines these
@@ -159,6 +160,55 @@ __device__ __forceinline__ void scan_tile_inter(f32x4 (&acc)[RGW][P / 16],
   }
 }
 
+// The gated RMS norm fused into the tile's store: out = rmsnorm(y * silu(z))
+// * w over groups of `gpl` 16-byte pieces (8 channels each) of one head's
+// row, for norm groups that lie inside a head.  y is the tile's output as
+// rounded to bf16 in LDS, so the result equals the standalone norm kernel
+// run on the stored y (same arithmetic, same order of the group sum).
+struct ScanGate {
+  const bf16* z;       // like x and y
+  const float* w;      // [H * P]
+  float eps, inv_gs;
+  int gpl;             // pieces per norm group: 1, 2, 4 or 8 (a power of two, <= P / 8)
+};
+
+// z piece u of this thread's rows (the rows the store loop writes).  The
+// first min(XU, 4) pieces are loaded before the workgroup meets, the rest
+// inside the store loop, four pieces ahead.
+template <int P, int NT>
+__device__ __forceinline__ uint4 gate_load_z(const ScanGate& gate, const ScanTile& T, int H,
+                                             uint32_t HPx, int tid, int u) {
+  constexpr int CPR = P / 8;
+  const auto rz = rows_rsrc(gate.z, T, H, P, HPx);
+  const int i = tid + NT * u, r = i / CPR, c = i % CPR;
+  return buf_load16(rz, ((uint32_t)r * HPx + c * 8) * 2u);
+}
+template <int XU> constexpr int kGateRing = XU < 4 ? XU : 4;
+
+// One 16-byte piece of the gated, normalised output from the y piece and the
+// z piece of (row, piece c) of head h.  Every lane calls it (the group sum
+// shuffles); the 8 pieces of a row are 8 consecutive lanes.
+template <int P>
+__device__ __forceinline__ uint4 gate_piece(uint4 yq, uint4 zq, const ScanGate& gate, int h,
+                                            int c) {
+  const bf16x8 yb = __builtin_bit_cast(bf16x8, yq), zb = __builtin_bit_cast(bf16x8, zq);
+  float yf[8], zf[8], g[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    yf[e] = static_cast<float>(yb[e]);
+    zf[e] = static_cast<float>(zb[e]);
+  }
+  const float sum = run_sum(gate_values<8>(yf, zf, g), gate.gpl);
+  const float rs = gate_rstd(sum, gate.inv_gs, gate.eps);
+  const float4 w0 = *reinterpret_cast<const float4*>(gate.w + h * P + c * 8);
+  const float4 w1 = *reinterpret_cast<const float4*>(gate.w + h * P + c * 8 + 4);
+  const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  bf16x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = static_cast<bf16>((g[e] * rs) * wv[e]);
+  return __builtin_bit_cast(uint4, o);
+}
+
 template <int L> constexpr int kTileWaves = (L / 16) / 2 < 4 ? 4 : (L / 16) / 2;
 // Waves per SIMD the tile kernel is compiled for: two workgroups per CU with
 // 8-wave tiles; three with 4-wave tiles of four row groups per wave.
@@ -172,14 +222,17 @@ template <int L, int NW> constexpr int kTileWavesPerEU = (L / 16) / NW == 4 ? 3 
 // AUX: cache-policy bits of the loads of the entering state, the running sums
 // and the steps; CBAUX: of the CB loads (kSc1 when another workgroup of the
 // same launch wrote them).  OPQ: the body runs inside a persistent loop.
-template <int P, int N, int L, int NW, bool FAST, int AUX = 0, int CBAUX = 0, bool OPQ = false>
+// GATE: the stored output is the gated RMS norm of y (`gate`).
+template <int P, int N, int L, int NW, bool FAST, int AUX = 0, int CBAUX = 0, bool OPQ = false,
+          bool GATE = false>
 __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __restrict__ x,
                                                const bf16* __restrict__ C, const bf16* __restrict__ cb,
                                                const float* __restrict__ delta,
                                                const float* __restrict__ dAcs,
                                                const bf16* __restrict__ states_in,
                                                const float* __restrict__ D, int H, int G, bf16* __restrict__ out,
-                                               bf16* xs, bf16* hsm, float* dal2, float* dls, float* cfs) {
+                                               bf16* xs, bf16* hsm, float* dal2, float* dls, float* cfs,
+                                               const ScanGate& gate = ScanGate{}) {
   using M = Mfma<bf16>;
   constexpr int NT = 64 * NW;            // threads
   constexpr int HP = N + 8;              // state tile pitch: conflict-free 16-byte row reads
@@ -423,13 +476,24 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
         for (int r = 0; r < 4; ++r) yo[r] = static_cast<bf16>(acc[i][a][r] + Dh * static_cast<float>(xo[r]));
         *e = yo;
       }
+    constexpr int ZR = GATE ? kGateRing<XU> : 1;
+    uint4 zv[ZR];
+    if constexpr (GATE) {
+#pragma unroll
+      for (int u = 0; u < ZR; ++u) zv[u] = gate_load_z<P, NT>(gate, T, H, HPx, tid, u);
+    }
     __syncthreads();
     const auto ry = rows_rsrc(out, T, H, P, HPx);
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
       const int i = tid + NT * u, r = i / CPR, c = i % CPR;
-      buf_store16(ry, ((uint32_t)r * HPx + c * 8) * 2u,
-                  *reinterpret_cast<const uint4*>(&xs[r * P + ((c ^ tile_sw<CPR>(r)) << 3)]));
+      uint4 yq = *reinterpret_cast<const uint4*>(&xs[r * P + ((c ^ tile_sw<CPR>(r)) << 3)]);
+      if constexpr (GATE) {
+        const uint4 zq = zv[u % ZR];
+        if (u + ZR < XU) zv[u % ZR] = gate_load_z<P, NT>(gate, T, H, HPx, tid, u + ZR);
+        yq = gate_piece<P>(yq, zq, gate, h, c);
+      }
+      buf_store16(ry, ((uint32_t)r * HPx + c * 8) * 2u, yq);
     }
     return;
   }
@@ -448,6 +512,12 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
       for (int r = 0; r < 4; ++r) yo[r] = static_cast<bf16>(acc[i][a][r]);
       *reinterpret_cast<bf16x4*>(&xs[l * P + ((4 * a + kg) ^ out_sw<P>(l)) * 4]) = yo;
     }
+  constexpr int ZR = GATE ? kGateRing<XU> : 1;
+  uint4 zv[ZR];
+  if constexpr (GATE) {
+#pragma unroll
+    for (int u = 0; u < ZR; ++u) zv[u] = gate_load_z<P, NT>(gate, T, H, HPx, tid, u);
+  }
   __syncthreads();
   const auto ry = rows_rsrc(out, T, H, P, HPx);
 #pragma unroll
@@ -456,7 +526,13 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
     const int sw = out_sw<P>(r);
     const uint2 v0 = *reinterpret_cast<const uint2*>(&xs[r * P + ((2 * c) ^ sw) * 4]);
     const uint2 v1 = *reinterpret_cast<const uint2*>(&xs[r * P + ((2 * c + 1) ^ sw) * 4]);
-    buf_store16(ry, ((uint32_t)r * HPx + c * 8) * 2u, make_uint4(v0.x, v0.y, v1.x, v1.y));
+    uint4 yq = make_uint4(v0.x, v0.y, v1.x, v1.y);
+    if constexpr (GATE) {
+      const uint4 zq = zv[u % ZR];
+      if (u + ZR < XU) zv[u % ZR] = gate_load_z<P, NT>(gate, T, H, HPx, tid, u + ZR);
+      yq = gate_piece<P>(yq, zq, gate, h, c);
+    }
+    buf_store16(ry, ((uint32_t)r * HPx + c * 8) * 2u, yq);
   }
 }
 
