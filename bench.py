@@ -85,19 +85,23 @@ def fused_minimum_bytes(prob):
     return 2 * e * tok * H * P + 4 * tok * H + 2 * e * tok * G * N + 8 * prob.nseq * H * P * N
 
 
-STAGE_SOURCE = {"plan": "ssd_prep.hip", "chunk_cumsum": "ssd_prep.hip", "front": "ssd_chunk_state.hip",
-                "bmm_chunk": "ssd_bmm.hip", "chunk_state": "ssd_chunk_state.hip",
-                "state_passing": "ssd_state_passing.hip", "chunk_scan": "ssd_chunk_scan.hip"}
+STAGE_SOURCE = {"plan": ("ssd_prep.hip",), "chunk_cumsum": ("ssd_prep.hip",),
+                "front": ("ssd_chunk_state.hip", "ssd_state_tile.h"),
+                "bmm_chunk": ("ssd_bmm.hip",),
+                "chunk_state": ("ssd_chunk_state.hip", "ssd_state_tile.h"),
+                "state_passing": ("ssd_state_passing.hip",),
+                "chunk_scan": ("ssd_chunk_scan.hip", "ssd_scan_tile.h", "ssd_gate.h")}
+COMMON_HEADERS = ("ssd_common.h", "ssd_device.h", "ssd_kernels.h")
 
 
 def kernel_source_hash(kernel: str) -> str:
     """Hash of the code (comments and blank space removed) of a kernel's
-    source file and of the headers every kernel includes."""
+    source files and of the headers every kernel includes."""
     import hashlib
     import re
     csrc = os.path.join(ROOT, "state_space_model_ssd_amd", "csrc")
     h = hashlib.sha256()
-    for f in (STAGE_SOURCE[kernel], "ssd_common.h", "ssd_device.h", "ssd_kernels.h"):
+    for f in STAGE_SOURCE[kernel] + COMMON_HEADERS:
         text = open(os.path.join(csrc, f)).read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
@@ -315,6 +319,64 @@ def fused_step(k, torch, binding, steps, warmup):
     return round(med, 2)
 
 
+def gated_norm_record(w, torch, binding, reps):
+    """The gated RMS norm after the forward on workload w's output: the
+    standalone forward and backward kernels over rows of H*P channels (one
+    group per token, and one group per head), and the forward step with the
+    norm fused into chunk_scan's store (groups of one head) against the plain
+    step.  Algorithmic bytes: y, z read and out written (forward); y, z, dout
+    read and dy, dz written (backward)."""
+    prob = w.prob
+    if prob.dtype != "bf16":
+        return None
+    tokens, C, P = w.tokens, prob.nheads * prob.headdim, prob.headdim
+    gen = torch.Generator().manual_seed(77)
+    z = torch.randn(w.d["x"].shape, generator=gen).to(torch.bfloat16).to(w.d["x"].device)
+    wt = torch.ones(C, device=z.device)
+    y = w.out.view(tokens, C)
+    zz = z.view(tokens, C)
+    dout = torch.randn((tokens, C), generator=gen).to(torch.bfloat16).to(z.device)
+    cur = torch.cuda.current_stream()
+    res = {"rows": tokens, "channels": C}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(reps):
+            fn()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    nb = 2 * tokens * C
+    for gs in (C, P):
+        out = torch.empty_like(y)
+        ws = torch.empty(1 << 26, dtype=torch.uint8, device=z.device)
+        fus = timed(lambda: binding.gated_norm_fwd(y, zz, wt, gs, out=out))
+        bus = timed(lambda: binding.gated_norm_bwd(y, zz, wt, dout, gs, workspace=ws))
+        res[f"group{gs}"] = {
+            "fwd_us": round(fus, 2), "fwd_alg_bytes": 3 * nb,
+            "fwd_hbm_frac": round(3 * nb / (fus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "bwd_us": round(bus, 2), "bwd_alg_bytes": 5 * nb,
+            "bwd_hbm_frac": round(5 * nb / (bus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    d = w.d
+    gout = torch.empty_like(d["x"])
+
+    def gated_step():
+        binding.ssd_fwd_gated(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, z, wt, P,
+                              D=d["D"], dt_bias=d["dt_bias"], initial_states=d["init"],
+                              cu_seqlens=d["cu_seqlens"], out=gout, final_states=w.fin,
+                              workspace=w.ws)
+    g_us = timed(gated_step)
+    plain_us = timed(lambda: w.step())
+    res["fused_epilogue"] = {"group_size": P, "step_us": round(g_us, 2),
+                             "plain_step_us": round(plain_us, 2),
+                             "note": "eager back-to-back calls (not graph replays)"}
+    return res
+
+
 def side_workload(k, torch, binding, flush, steps, warmup, reps, compare_fused=False):
     """Step and launch timings of another full-size workload (warm and cold)."""
     w = Workload(k, torch, binding)
@@ -509,6 +571,8 @@ def main():
                             "stages 0-4 (us_after_fwd: ssd_bwd_after_fwd, which reuses a "
                             "forward's intermediates); per-kernel times in profiles/"}
         del wsb, dy, dfin
+    log("[bench] gated norm")
+    gnorm = gated_norm_record(w, torch, binding, max(5, args.stage_reps // 5))
     main_tuning = w.tuning_record
     del w
     torch.cuda.empty_cache()
@@ -566,6 +630,7 @@ def main():
         "step_us_cold": cold_pct,
         "tokens_per_s_median": round(tokens / (step_pct["median"] * 1e-6), 1),
         "fused_step_us_warm_median": fused_main,
+        "gated_norm": gnorm,
         "tuning": main_tuning,
         "stages": stages,
         "stages_unfused": singles,
