@@ -567,11 +567,12 @@ chunk_scan_bf16_tile_kernel(ChunkMap cm, int nslots, const bf16* __restrict__ x,
 
 }  // namespace
 
-// Below this many tiles per resident persistent workgroup, one 8-wave (or
-// 4-wave for short chunks) workgroup per tile is fastest.  Above it, with
-// 256-token chunks, 4-wave tiles (three workgroups per CU) beat the
-// persistent walk by about 2.5% on long and packed sequences and tie on the
-// training batch; with shorter chunks the persistent walk is used.
+// With 256-token chunks one 8-wave workgroup per tile is fastest at every
+// grid size measured (5-7% ahead of 4-wave tiles, three workgroups per CU,
+// and of the persistent walk on the training batch, long and packed
+// sequences).  With shorter chunks, below this many tiles per resident
+// persistent workgroup one workgroup per tile is used, above it the
+// persistent walk.
 constexpr int kPersistentMinTiles = 6;
 
 // Workgroups of the persistent kernel <P, N, L> that stay resident per CU,
@@ -602,7 +603,8 @@ int chunk_scan_choice(const FwdArgs& a) {
     const int g = persistent_grid<P, N, L>();
     if (g <= 0) return -1;
     const int ntiles = xcd_grid(a.max_chunks, a.H);
-    return ntiles < kPersistentMinTiles * g ? 1 : (kTileWaves<L> == 8 ? 3 : 2);
+    if constexpr (kTileWaves<L> == 8) return 1;
+    return ntiles < kPersistentMinTiles * g ? 1 : 2;
   }
 }
 

@@ -325,6 +325,15 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
 #pragma unroll
     for (int k = 0; k < NK; ++k)
       fc[i][k] = __builtin_bit_cast(bf16x8, buf_load16(rc, ((uint32_t)lrow[i] * GN + 32 * k + kq) * 2u));
+  // Masked path with one or two row groups per wave, one tile per
+  // workgroup: CB pieces stream through a ring of RM registers per row
+  // group, RM - 1 k-steps ahead of their use, the first RM - 1 issued once
+  // the inter-chunk term has released the C rows' registers.  (Inside a
+  // persistent loop the registers are not there: one step ahead.)  The order
+  // of the MFMAs is the same either way.
+  constexpr bool MRING = !FAST && RGW <= 2 && !OPQ;
+  constexpr int RM = GATE ? 3 : 4;         // the gate's store loop needs registers too
+  bf16x8 mring[RGW][MRING ? RM : 1];
   const int xrow = 8 * kg + (lr >> 2);
   const int xsl = tile_sw<CPR>(xrow) >> 1;
   const int xcol = ((lr & 3) >> 1) * 8 + (lr & 1) * 4;
@@ -336,6 +345,14 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
     for (int a = 0; a < PT; ++a) acc[i][a] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   scan_tile_inter<P, N, RGW, HP>(acc, fc, hsm, lr, kq);
+  if constexpr (MRING) {
+#pragma unroll
+    for (int i = 0; i < RGW; ++i)
+#pragma unroll
+      for (int q = 0; q < RM - 1; ++q)
+        if (q < nq[i])                     // wave-uniform
+          mring[i][q] = __builtin_bit_cast(bf16x8, buf_load16<CBAUX>(rcb, ((uint32_t)lrow[i] * L + kq + 32 * q) * 2u));
+  }
 
   if constexpr (FAST) {
     // Every term of the chunk is accumulated without its row factor 2^(a_l),
@@ -432,8 +449,30 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
 #pragma unroll
       for (int a = 0; a < PT; ++a) acc[i][a] *= rsc;
     }
+    if constexpr (MRING) {
 #pragma unroll
-    for (int i0 = 0; i0 < RGW; i0 += RP) {
+      for (int q = 0; q < NQ; ++q) {
+        if (q >= nq_wave) break;           // wave-uniform
+#pragma unroll
+        for (int i = 0; i < RGW; ++i)
+          if (q + RM - 1 < nq[i])          // wave-uniform
+            mring[i][(q + RM - 1) % RM] = __builtin_bit_cast(
+                bf16x8, buf_load16<CBAUX>(rcb, ((uint32_t)lrow[i] * L + kq + 32 * (q + RM - 1)) * 2u));
+        bf16x8 fm[RGW];
+#pragma unroll
+        for (int i = 0; i < RGW; ++i)
+          if (q < nq[i]) fm[i] = scan_masked_cb(mg[i], q, mring[i][q % RM], lr, kq, dal2, dls, cfs);
+#pragma unroll
+        for (int a = 0; a < PT; ++a) {
+          const bf16x8 fx = scan_x_operand<P>(xs, q, a, xrow, xsl, xcol);
+#pragma unroll
+          for (int i = 0; i < RGW; ++i)
+            if (q < nq[i]) acc[i][a] = M::mma(fx, fm[i], acc[i][a]);   // wave-uniform
+        }
+      }
+    }
+#pragma unroll
+    for (int i0 = 0; i0 < (MRING ? 0 : RGW); i0 += RP) {
       uint32_t cbo[RP];
       bf16x8 cur[RP];                      // CB rows of the current k-step
 #pragma unroll

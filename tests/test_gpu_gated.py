@@ -81,12 +81,12 @@ def test_gated_both_scan_paths(L):
         check_oracle(prob, inp, out, z, w, gs)
 
 
-def test_gated_four_wave_tiles_and_packed():
-    # enough tiles that the library runs the 4-wave scan tile
+def test_gated_many_tiles_and_packed():
+    # a grid of many tiles per CU (8-wave tiles with the gate in their store)
     prob = Problem(1, 65536 + 77, 8, 64, 128, 1, 256, "bf16")
     inp = make_inputs(prob, Recipe(init_std=0.1), seed=2)
     cp = binding.make_problem(1, prob.seqlen, 8, 64, 128, 1, 256, binding.SSD_BF16)
-    assert binding.fwd_choices(cp)["scan_kernel"] == 3
+    assert binding.fwd_choices(cp)["scan_kernel"] == 1
     out, fin, ref, fin2, z, w = run(prob, inp, 64)
     assert torch.equal(out, ref) and torch.equal(fin, fin2)
     check_oracle(prob, inp, out, z, w, 64)
