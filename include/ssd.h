@@ -2,11 +2,13 @@
  * ssd.h: C ABI of the Mamba-2 SSD (state-space duality) chunked-scan
  * forward on one AMD Instinct MI355X (gfx950).
  *
- * What the library computes.  The Mamba-2 layer keeps a fixed-size state per
- * head that every token updates (clova.ai, "Unlocking the potential of the
- * latest GPUs: optimizing Mamba-2 kernels for the B200", section "Why
- * optimize Mamba-2? Long context and hybrid architectures").  For each
- * sequence s, head h (B/C group g = h / (nheads / ngroups)) and token t:
+ * What the library computes.  A Mamba-2 layer updates a fixed-size hidden
+ * state per head with every token, and the chunkwise form processes it
+ * chunk by chunk (aiproviderindex.com, item on CUDA Tile Mamba-2 kernels,
+ * "Mamba-2 offers a different scaling path").  The pages do not write the
+ * update out; this library reads it as the plain Mamba-2 selective
+ * state-space update.  For each sequence s, head h (B/C group g =
+ * h / (nheads / ngroups)) and token t:
  *
  *   delta_t  = clamp(softplus(dt[t,h] + dt_bias[h]), dt_min, dt_max)
  *   h_t      = exp(delta_t * A[h]) * h_{t-1} + delta_t * x[t,h,:] (outer) B[t,g,:]
@@ -137,14 +139,18 @@ typedef struct {
 } ssd_workspace_layout_t;
 
 /* Workspace bytes ssd_fwd needs for this problem (0 if the problem is
- * invalid or unsupported). */
+ * invalid or unsupported): the intermediates the stages above hand to one
+ * another, stored in the layout their consumer reads (aiproviderindex.com,
+ * "Memory layout is part of the algorithm").  Library bookkeeping: no
+ * passage of the pages defines it. */
 size_t ssd_fwd_workspace_size(const ssd_problem_t* p);
 
 /* Fills *layout for this problem.  SSD_ERR_INVALID_ARG / SSD_ERR_UNSUPPORTED
  * as for ssd_fwd. */
 ssd_status_t ssd_workspace_layout(const ssd_problem_t* p, ssd_workspace_layout_t* layout);
 
-/* 1 if (dtype, headdim, dstate, chunk_size) has compiled kernels, else 0. */
+/* 1 if (dtype, headdim, dstate, chunk_size) has compiled kernels, else 0
+ * (library bookkeeping, not from the pages). */
 int ssd_config_supported(int32_t dtype, int64_t headdim, int64_t dstate, int64_t chunk_size);
 
 /*
@@ -413,7 +419,8 @@ ssd_status_t ssd_fwd_noalloc(const ssd_problem_t* p,
                              const int32_t* cu_seqlens, const int32_t* seq_idx,
                              void* out, float* final_states, void* stream);
 
-/* Static description of a status code. */
+/* Static description of a status code (library bookkeeping, not from the
+ * pages). */
 const char* ssd_status_string(ssd_status_t s);
 
 #ifdef __cplusplus

@@ -1,8 +1,8 @@
 """TEST INFRASTRUCTURE ONLY: Python entry to the fp64 C recurrence oracle.
 
-The arithmetic lives in ssd_recurrence.c (per-token state update of the
-Mamba-2 selective state-space layer; clova.ai page, section "Why optimize
-Mamba-2? Long context and hybrid architectures").  This wrapper only
+The arithmetic lives in ssd_recurrence.c (per-token update of the Mamba-2
+layer's fixed-size hidden state; aiproviderindex page, "Mamba-2 offers a
+different scaling path").  This wrapper only
 selects heads, upcasts inputs exactly to fp64 and marshals pointers.
 """
 from __future__ import annotations

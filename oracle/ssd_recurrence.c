@@ -4,12 +4,12 @@
  * the product path never does.  It shares no code with the HIP library.
  *
  * What it computes: the selective state-space recurrence that the SSD
- * chunked scan reaches exactly in exact arithmetic (clova.ai, "Unlocking the
- * potential of the latest GPUs: optimizing Mamba-2 kernels for the B200",
- * section "Why optimize Mamba-2? Long context and hybrid architectures":
- * a fixed-size state updated once per token; aiproviderindex.com, "Mamba-2
- * offers a different scaling path": the state update, chunk-wise cumulative
- * parameters, state propagation and output construction).  For each
+ * chunked scan reaches exactly in exact arithmetic.  The pages describe a
+ * fixed-size hidden state updated with every token and its chunkwise form
+ * (aiproviderindex.com, item on CUDA Tile Mamba-2 kernels, "Mamba-2 offers a
+ * different scaling path": the state update, chunk-wise cumulative
+ * parameters, state propagation and output construction) without writing
+ * the update out; it is read as the plain Mamba-2 selective update.  For each
  * sequence s, head h (group g = h / (H / G)) and token t of the sequence:
  *
  *   delta_t   = clamp(softplus(dt[t,h] + dt_bias[h]), dt_min, dt_max)
