@@ -127,6 +127,32 @@ def measured_traffic(kernel: str, workload_tag: str):
     return int(fields["traffic_bytes_per_launch"])
 
 
+def measured_counters(kernel: str, workload_tag: str):
+    """Counter figures of one launch (matrix-core busy fraction of SIMD time,
+    LDS bank-conflict cycles per active LDS cycle, L2 hit rate) from the
+    committed summary profiles/counters_<workload>.md, or None when there is
+    none or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload_tag}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        parts = line.split(":", 1)
+        if len(parts) != 2:
+            continue
+        key = parts[0].split()
+        if len(key) == 2 and key[1] == kernel:
+            vals[key[0]] = parts[1].strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
+        return None
+    try:
+        return {"mfma_busy": float(vals["mfma_busy"]),
+                "lds_conflict_ratio": float(vals["lds_conflict_ratio"]),
+                "l2_hit": float(vals["l2_hit"]), "source": f"profiles/counters_{workload_tag}.md"}
+    except (KeyError, ValueError):
+        return None
+
+
 def env_info():
     info = {"host": platform.node(), "nproc": os.cpu_count()}
     try:
@@ -397,7 +423,9 @@ def side_workload(k, torch, binding, flush, steps, warmup, reps, compare_fused=F
            "step_us_warm": step_pct, "step_us_cold": cold_pct,
            "step_us_mean_warm": round(total * 1e3 / steps, 2),
            "fused_minimum_bytes": fused_minimum_bytes(w.prob),
-           "launches": {n: stage_record(work, n, us[n], w.prob.dtype) for n in launches},
+           "launches": {n: dict(stage_record(work, n, us[n], w.prob.dtype),
+                                counters=measured_counters(n, w.name.split()[0]))
+                        for n in launches},
            "tuning": w.tuning_record}
     del w
     torch.cuda.empty_cache()
@@ -485,6 +513,9 @@ def main():
     us = w.time_launches(step_launches + singles_names, args.stage_reps)
     stages = {n: stage_record(work, n, us[n], prob.dtype) for n in step_launches}
     singles = {n: stage_record(work, n, us[n], prob.dtype) for n in singles_names}
+    wtag = w.name.split()[0]
+    for n in stages:
+        stages[n]["counters"] = measured_counters(n, wtag)
     if not torch.equal(w.out, w.ref_out):
         raise RuntimeError("stage-by-stage run differs from the eager forward")
     dom = max(stages, key=lambda k: stages[k]["us"])
@@ -495,12 +526,11 @@ def main():
     cold_dom = w.time_cold(20, flush, lambda: w.step(masks[dom]))
     cold_dom_us = percentiles(cold_dom)["median"] * 1e3
     cold_rec = stage_record(work, dom, cold_dom_us, prob.dtype)
-    wtag = w.name.split()[0]
     traffic = measured_traffic(dom, wtag)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": ds["gbs"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ds["hbm_frac"], "traffic": traffic,
                 "traffic_unit": "bytes per launch", "launch_us": ds["us"],
-                "alg_bytes_per_launch": ds["alg_bytes"],
+                "alg_bytes_per_launch": ds["alg_bytes"], "counters": ds["counters"],
                 "cold": {"launch_us_median": round(cold_dom_us, 3), "achieved": cold_rec["gbs"],
                          "frac": cold_rec["hbm_frac"]}}
     total_bytes = sum(work[n][0] for n in step_launches)
