@@ -22,8 +22,7 @@
 //  - the inter-chunk term is the entering state times the C rows on MFMA,
 //    scaled by exp(a_l) per token;
 //  - all global traffic goes through buffer resources bounded by the tile.
-// Two kernels, the first in two sizes; the launcher picks by tiles per
-// resident workgroup (or as a caller pins it):
+// Two kernels, the first in two sizes (a caller may pin any of them):
 //  - one workgroup per (chunk, head) tile, of 8 waves (two 16-row groups per
 //    wave; 4 waves for chunks of 128 tokens or fewer) or of 4 waves (four
 //    row groups per wave, three workgroups per CU).  Each tile takes the
@@ -32,6 +31,9 @@
 //    end), else the masked path; the two are compiled as separate bodies;
 //  - a persistent workgroup of 4 L threads per resident slot, walking the
 //    tiles with the next tile's inputs in flight (masked path).
+// The library runs the 8-wave tile for 256-token chunks, and for shorter
+// chunks the one-tile-per-workgroup kernel on small grids and the persistent
+// walk on large ones (chunk_scan_choice).
 // The y = acc + D x epilogue stages y in LDS and stores coalesced rows.
 //
 // fp32 kernel (exactness path): one workgroup per (chunk, 64-row tile, head);
