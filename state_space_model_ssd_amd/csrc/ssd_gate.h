@@ -33,6 +33,19 @@ __device__ __forceinline__ float gate_values(const float* yf, const float* zf, f
   return s;
 }
 
+// gate_values that also hands out each sigmoid (the same arithmetic).
+template <int V>
+__device__ __forceinline__ float gate_values_sig(const float* yf, const float* zf, float* g,
+                                                 float* sg) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    g[e] = yf[e] * gate_silu(zf[e], sg[e]);
+    s += g[e] * g[e];
+  }
+  return s;
+}
+
 // 1 / sqrt(mean + eps) from a group's sum of squares.
 __device__ __forceinline__ float gate_rstd(float sum, float inv_gs, float eps) {
   return rsqrtf(sum * inv_gs + eps);

@@ -13,10 +13,10 @@
 //   dg_c = r (du_c - u_c mean_{c' in group}(du_c' u_c'))
 //   dy_c = dg_c silu(z_c),  dz_c = dg_c y_c sigma(z_c) (1 + z_c (1 - sigma(z_c)))
 //
-// One workgroup of 256 threads per row at a time; thread t owns the row's
-// 16-byte vectors t, t + 256, ... (KT of them), so every access is a
-// coalesced 16-byte load and a thread's channels never change from row to
-// row.  A group spans NV = group_size / V consecutive vectors: for NV <= 64 (a
+// One workgroup of TH threads (64 to 256: the row's 16-byte vectors rounded
+// up to a wave, at most 256) per row at a time; thread t owns the row's
+// vectors t, t + TH, ... (KT of them), so every access is a coalesced
+// 16-byte load and a thread's channels never change from row to row.  A group spans NV = group_size / V consecutive vectors: for NV <= 64 (a
 // power of two) a group is an aligned run of NV lanes of one wave and reduces
 // with xor shuffles inside the run; for NV a multiple of 64 a group is NV / 64
 // consecutive 64-vector chunks, each reduced over its wave, and the chunk
@@ -37,8 +37,7 @@ namespace ssd {
 
 namespace {
 
-constexpr int kNormThreads = 256;
-constexpr int kNormWaves = kNormThreads / 64;
+constexpr int kNormThreads = 256;  // most threads of a norm workgroup
 constexpr int kNormMaxKT = 4;    // vectors per thread: channels <= 1024 V
 
 template <typename T> struct NormVec;
@@ -70,13 +69,14 @@ template <> struct NormVec<float> {
   }
 };
 
-// Group sums of s[k] (this thread's vector t + 256 k), in place.  `chunk`
-// is LDS scratch of KT * 4 floats, nchunks (<= 4 KT) the row's 64-vector
-// chunks; every thread of the workgroup must call it (it holds a barrier when
-// groups span waves).  Callers alternate between two scratch buffers, so the
-// barrier of the next call also frees this one.
-template <int KT>
+// Group sums of s[k] (this thread's vector t + TH k), in place.  `chunk`
+// is LDS scratch of KT * TH / 64 floats, nchunks (<= KT * TH / 64) the row's
+// 64-vector chunks; every thread of the workgroup must call it (it holds a
+// barrier when groups span waves).  Callers alternate between two scratch
+// buffers, so the barrier of the next call also frees this one.
+template <int KT, int TH>
 __device__ __forceinline__ void group_sums(float (&s)[KT], int NV, int nchunks, float* chunk) {
+  constexpr int NW = TH / 64;
   if (NV <= 64) {
 #pragma unroll
     for (int k = 0; k < KT; ++k) s[k] = run_sum(s[k], NV);
@@ -85,8 +85,8 @@ __device__ __forceinline__ void group_sums(float (&s)[KT], int NV, int nchunks, 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
-    const float c = run_sum(s[k], 64);      // chunk q = 4 k + w
-    if (lane == 0) chunk[4 * k + w] = c;
+    const float c = run_sum(s[k], 64);      // chunk q = NW k + w
+    if (lane == 0) chunk[NW * k + w] = c;
   }
   __syncthreads();
   const int cpg = NV / 64;                  // chunks per group
@@ -94,7 +94,7 @@ __device__ __forceinline__ void group_sums(float (&s)[KT], int NV, int nchunks, 
   for (int k = 0; k < KT; ++k) {
     // chunks past the row's last (idle threads) stay as they are: the
     // group would reach past the chunks written
-    const int q0 = (4 * k + w) / cpg * cpg;
+    const int q0 = (NW * k + w) / cpg * cpg;
     if (q0 + cpg > nchunks) continue;
     float g = 0.f;
     for (int q = q0; q < q0 + cpg; ++q) g += chunk[q];
@@ -110,13 +110,13 @@ __device__ __forceinline__ void launder(uint4& q) {
 
 // Row r's vectors of y, z (and d, if given) owned by thread t; zeros for a
 // row past the end or a vector past the row's last.
-template <int KT, int V, typename T>
+template <int KT, int TH, int V, typename T>
 __device__ __forceinline__ void load_row(const T* y, const T* z, const T* d, int64_t r,
                                          int64_t rows, int C, int nvec, int t, uint4 (&yv)[KT],
                                          uint4 (&zv)[KT], uint4* dv) {
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
-    const int v = t + 256 * k;
+    const int v = t + TH * k;
     const bool ok = r < rows && v < nvec;
     const int64_t o = r * C + (int64_t)v * V;
     yv[k] = ok ? *reinterpret_cast<const uint4*>(y + o) : make_uint4(0, 0, 0, 0);
@@ -129,13 +129,13 @@ __device__ __forceinline__ void load_w(const float* w, int v, int nvec, float* w
   for (int e = 0; e < V; ++e) wv[e] = v < nvec ? w[v * V + e] : 0.f;
 }
 
-template <typename T, int KT>
-__global__ __launch_bounds__(kNormThreads) void gated_norm_fwd_kernel(
+template <typename T, int KT, int TH>
+__global__ __launch_bounds__(TH) void gated_norm_fwd_kernel(
     const T* __restrict__ y, const T* __restrict__ z, const float* __restrict__ w, int64_t rows,
     int C, int GS, float eps, T* __restrict__ out, float* __restrict__ rstd) {
   using NVc = NormVec<T>;
-  constexpr int V = NVc::V;
-  __shared__ float chunk[2 * 4 * KT];   // two buffers, used alternately
+  constexpr int V = NVc::V, NCH = KT * TH / 64;
+  __shared__ float chunk[2 * NCH];      // two buffers, used alternately
   const int t = threadIdx.x;
   const int nvec = C / V, NV = GS / V, ng = C / GS;
   const float inv_gs = 1.f / (float)GS;
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_fwd_kernel(
 #pragma unroll 1
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x, par ^= 1) {
     uint4 yv[KT], zv[KT];
-    load_row<KT, V>(y, z, static_cast<const T*>(nullptr), r, rows, C, nvec, t, yv, zv, nullptr);
+    load_row<KT, TH, V>(y, z, static_cast<const T*>(nullptr), r, rows, C, nvec, t, yv, zv, nullptr);
     float g[KT][V], s[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
@@ -152,10 +152,10 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_fwd_kernel(
       NVc::unpack(zv[k], zf);
       s[k] = gate_values<V>(yf, zf, g[k]);
     }
-    group_sums<KT>(s, NV, (nvec + 63) / 64, chunk + par * 4 * KT);
+    group_sums<KT, TH>(s, NV, (nvec + 63) / 64, chunk + par * NCH);
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-      const int v = t + kNormThreads * k;
+      const int v = t + TH * k;
       if (v >= nvec) continue;
       const float rs = gate_rstd(s[k], inv_gs, eps);
       float wv[V], o[V];
@@ -168,41 +168,46 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_fwd_kernel(
   }
 }
 
-template <typename T, int KT>
-__global__ __launch_bounds__(kNormThreads) void gated_norm_bwd_kernel(
+template <typename T, int KT, int TH>
+__global__ __launch_bounds__(TH) void gated_norm_bwd_kernel(
     const T* __restrict__ y, const T* __restrict__ z, const float* __restrict__ w,
     const T* __restrict__ dout, int64_t rows, int C, int GS, float eps, T* __restrict__ dy,
     T* __restrict__ dz, float* __restrict__ dw_part) {
   using NVc = NormVec<T>;
-  constexpr int V = NVc::V;
-  __shared__ float chunk[2 * 4 * KT];   // two buffers, used alternately
+  constexpr int V = NVc::V, NCH = KT * TH / 64;
+  // With up to two vectors per thread the sigmoids of the first pass stay in
+  // registers for the second; with more, they are computed again there (the
+  // same values either way).
+  constexpr bool KEEP = KT <= 2;
+  __shared__ float chunk[2 * NCH];      // two buffers, used alternately
   const int t = threadIdx.x;
   const int nvec = C / V, NV = GS / V;
   const float inv_gs = 1.f / (float)GS;
   float dwa[KT][V], wr[KT][V];             // dw sums and the weights of this thread's channels
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
-    load_w(w, t + kNormThreads * k, nvec, wr[k], V);
+    load_w(w, t + TH * k, nvec, wr[k], V);
 #pragma unroll
     for (int e = 0; e < V; ++e) dwa[k][e] = 0.f;
   }
   // the next row's inputs are loaded while this row is processed
   uint4 yv[KT], zv[KT], dv[KT];
-  load_row<KT, V>(y, z, dout, (int64_t)blockIdx.x, rows, C, nvec, t, yv, zv, dv);
+  load_row<KT, TH, V>(y, z, dout, (int64_t)blockIdx.x, rows, C, nvec, t, yv, zv, dv);
 #pragma unroll 1
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
     uint4 ny[KT], nz[KT], nd[KT];
-    load_row<KT, V>(y, z, dout, r + gridDim.x, rows, C, nvec, t, ny, nz, nd);
+    load_row<KT, TH, V>(y, z, dout, r + gridDim.x, rows, C, nvec, t, ny, nz, nd);
     // g = y silu(z) and the group sums of g^2
-    float u[KT][V], s[KT];
+    float u[KT][V], s[KT], sg[KEEP ? KT : 1][V];
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
       float yf[V], zf[V];
       NVc::unpack(yv[k], yf);
       NVc::unpack(zv[k], zf);
-      s[k] = gate_values<V>(yf, zf, u[k]);
+      if constexpr (KEEP) s[k] = gate_values_sig<V>(yf, zf, u[k], sg[k]);
+      else s[k] = gate_values<V>(yf, zf, u[k]);
     }
-    group_sums<KT>(s, NV, (nvec + 63) / 64, chunk);
+    group_sums<KT, TH>(s, NV, (nvec + 63) / 64, chunk);
     // u = g r; dw += dout u; the group sums of du u with du = dout w
     float p[KT];
 #pragma unroll
@@ -218,9 +223,9 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_bwd_kernel(
         p[k] += (df[e] * wr[k][e]) * u[k][e];
       }
     }
-    group_sums<KT>(p, NV, (nvec + 63) / 64, chunk + 4 * KT);
-    // unpacking and silu again from the packed registers (the laundering
-    // keeps the compiler from holding them across the sums)
+    group_sums<KT, TH>(p, NV, (nvec + 63) / 64, chunk + NCH);
+    // unpacking again from the packed registers (the laundering keeps the
+    // compiler from holding the unpacked values across the sums)
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
       launder(yv[k]);
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_bwd_kernel(
     }
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-      const int v = t + kNormThreads * k;
+      const int v = t + TH * k;
       if (v >= nvec) continue;
       float yf[V], zf[V], df[V];
       NVc::unpack(yv[k], yf);
@@ -241,7 +246,13 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_bwd_kernel(
       for (int e = 0; e < V; ++e) {
         const float dg = s[k] * (df[e] * wr[k][e] - u[k][e] * mp);
         float sig;
-        const float gate = gate_silu(zf[e], sig);
+        float gate;
+        if constexpr (KEEP) {
+          sig = sg[k][e];
+          gate = zf[e] * sig;                // gate_silu's product, from the kept sigmoid
+        } else {
+          gate = gate_silu(zf[e], sig);
+        }
         ody[e] = dg * gate;
         odz[e] = dg * yf[e] * sig * (1.f + zf[e] * (1.f - sig));
       }
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_bwd_kernel(
   // this workgroup's partial dw: each channel belongs to one thread
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
-    const int v = t + kNormThreads * k;
+    const int v = t + TH * k;
     if (v >= nvec) continue;
 #pragma unroll
     for (int e = 0; e < V; ++e) dw_part[(int64_t)blockIdx.x * C + v * V + e] = dwa[k][e];
@@ -323,18 +334,18 @@ hipError_t norm_dw(const NormArgs& a, int nparts, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int KT>
+template <typename T, int KT, int TH>
 hipError_t norm_fwd_kt(const NormArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gated_norm_fwd_kernel<T, KT>), dim3(norm_grid(a.rows, 8)), dim3(kNormThreads),
+  hipLaunchKernelGGL((gated_norm_fwd_kernel<T, KT, TH>), dim3(norm_grid(a.rows, 8)), dim3(TH),
                      0, s, (const T*)a.y, (const T*)a.z, a.w, a.rows, a.C, a.GS, a.eps,
                      (T*)a.out, a.rstd);
   return hipGetLastError();
 }
 
-template <typename T, int KT>
+template <typename T, int KT, int TH>
 hipError_t norm_bwd_kt(const NormArgs& a, hipStream_t s) {
   const int grid = norm_grid(a.rows, 4);
-  hipLaunchKernelGGL((gated_norm_bwd_kernel<T, KT>), dim3(grid), dim3(kNormThreads), 0, s,
+  hipLaunchKernelGGL((gated_norm_bwd_kernel<T, KT, TH>), dim3(grid), dim3(TH), 0, s,
                      (const T*)a.y, (const T*)a.z, a.w, (const T*)a.dout, a.rows, a.C, a.GS,
                      a.eps, (T*)a.dy, (T*)a.dz, a.dw_part);
   const hipError_t e = hipGetLastError();
@@ -342,13 +353,27 @@ hipError_t norm_bwd_kt(const NormArgs& a, hipStream_t s) {
   return norm_dw(a, grid, s);
 }
 
+// Threads per workgroup: the row's vectors rounded up to a wave, at most
+// kNormThreads (rows of up to 192 vectors leave no wave idle); then the
+// vectors per thread.
 template <typename T, bool BWD>
 hipError_t norm_dispatch(const NormArgs& a, hipStream_t s) {
   constexpr int V = NormVec<T>::V;
-  const int kt = (a.C / V + kNormThreads - 1) / kNormThreads;
+  const int nvec = a.C / V;
+  const int th = nvec >= kNormThreads ? kNormThreads : (nvec + 63) / 64 * 64;
+  if (th < kNormThreads) {
+    switch (th) {
+#define SSD_TH(n) \
+      case n: return BWD ? norm_bwd_kt<T, 1, n>(a, s) : norm_fwd_kt<T, 1, n>(a, s);
+      SSD_TH(64) SSD_TH(128) SSD_TH(192)
+#undef SSD_TH
+    }
+    return hipErrorInvalidValue;
+  }
+  const int kt = (nvec + kNormThreads - 1) / kNormThreads;
   switch (kt) {
 #define SSD_KT(n) \
-    case n: return BWD ? norm_bwd_kt<T, n>(a, s) : norm_fwd_kt<T, n>(a, s);
+    case n: return BWD ? norm_bwd_kt<T, n, kNormThreads>(a, s) : norm_fwd_kt<T, n, kNormThreads>(a, s);
     SSD_KT(1) SSD_KT(2) SSD_KT(3) SSD_KT(4)
 #undef SSD_KT
   }
