@@ -254,8 +254,10 @@ def ssd_bwd(x, dt, A, B, C, chunk_size, dout, dfinal_states=None, D=None, dt_bia
     _need(dout, "dout", x.dtype, (b, T, H, P), dev)
     _need(dfinal_states, "dfinal_states", f32, (nstates, H, P, N), dev)
     prob = make_problem(b, T, H, P, N, G, chunk_size, x.dtype, nseq, dt_min, dt_max)
-    g = {"x": torch.zeros_like(x), "dt": torch.zeros_like(dt), "A": torch.empty(H, dtype=f32, device=dev),
-         "B": torch.zeros_like(B), "C": torch.zeros_like(C), "D": torch.empty(H, dtype=f32, device=dev),
+    # every token lies in a sequence (cu_seqlens runs from 0 to T), so the
+    # library writes every entry of these
+    g = {"x": torch.empty_like(x), "dt": torch.empty_like(dt), "A": torch.empty(H, dtype=f32, device=dev),
+         "B": torch.empty_like(B), "C": torch.empty_like(C), "D": torch.empty(H, dtype=f32, device=dev),
          "dt_bias": torch.empty(H, dtype=f32, device=dev),
          "initial_states": torch.empty((nstates, H, P, N), dtype=f32, device=dev)}
     need = lib.ssd_bwd_workspace_size(ctypes.byref(prob))

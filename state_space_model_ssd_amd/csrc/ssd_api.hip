@@ -341,8 +341,8 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
 
 // The backward's regions follow the forward's in its workspace.
 struct BwdLayout {
-  size_t Q, dS, dS16, dcb, dBh, dCh, rowpart, colpart, interpart, vxpart, dA_part, dD_part, dbias_part, ddot,
-      total;
+  size_t Q, dS, dS16, dcb, rowpart, colpart, vxpart, interpart, ghpart, dla, dA_part, dD_part, dbias_part,
+      ddot, total;
 };
 
 void bwd_layout_of(const ssd_problem_t* p, const ssd_workspace_layout_t& w, BwdLayout* b) {
@@ -353,13 +353,13 @@ void bwd_layout_of(const ssd_problem_t* p, const ssd_workspace_layout_t& w, BwdL
   b->dS = off;         off = align_up(off + sizeof(float) * mc * H * PN);
   b->dS16 = off;       off = align_up(off + sizeof(uint16_t) * mc * H * PN);
   b->dcb = off;        off = align_up(off + sizeof(float) * mc * H * L * L);
-  b->dBh = off;        off = align_up(off + sizeof(float) * mc * H * L * N);
-  b->dCh = off;        off = align_up(off + sizeof(float) * mc * H * L * N);
-  const size_t LT = L / 64, NT = (N + 63) / 64;
+  const size_t LT = L / 64, VX = 2 * ((N + 63) / 64);
   b->rowpart = off;    off = align_up(off + sizeof(float) * mc * H * LT * L);
   b->colpart = off;    off = align_up(off + sizeof(float) * mc * H * LT * L);
-  b->interpart = off;  off = align_up(off + sizeof(float) * mc * H * NT * L);
-  b->vxpart = off;     off = align_up(off + sizeof(float) * mc * H * NT * L);
+  b->vxpart = off;     off = align_up(off + sizeof(float) * mc * H * VX * L);
+  b->interpart = off;  off = align_up(off + sizeof(float) * mc * H * VX * L);
+  b->ghpart = off;     off = align_up(off + sizeof(float) * mc * H * (PN / 256));
+  b->dla = off;        off = align_up(off + sizeof(float) * mc * H);
   b->dA_part = off;    off = align_up(off + sizeof(float) * mc * H);
   b->dD_part = off;    off = align_up(off + sizeof(float) * mc * H);
   b->dbias_part = off; off = align_up(off + sizeof(float) * mc * H);
@@ -403,12 +403,12 @@ ssd_status_t run_bwd(const ssd_problem_t* p, const void* x, const float* dt, con
   b.dS = reinterpret_cast<float*>(base + bl.dS);
   b.dS16 = base + bl.dS16;
   b.dcb = reinterpret_cast<float*>(base + bl.dcb);
-  b.dBh = reinterpret_cast<float*>(base + bl.dBh);
-  b.dCh = reinterpret_cast<float*>(base + bl.dCh);
   b.rowpart = reinterpret_cast<float*>(base + bl.rowpart);
   b.colpart = reinterpret_cast<float*>(base + bl.colpart);
-  b.interpart = reinterpret_cast<float*>(base + bl.interpart);
   b.vxpart = reinterpret_cast<float*>(base + bl.vxpart);
+  b.interpart = reinterpret_cast<float*>(base + bl.interpart);
+  b.ghpart = reinterpret_cast<float*>(base + bl.ghpart);
+  b.dla = reinterpret_cast<float*>(base + bl.dla);
   b.dA_part = reinterpret_cast<float*>(base + bl.dA_part);
   b.dD_part = reinterpret_cast<float*>(base + bl.dD_part);
   b.dbias_part = reinterpret_cast<float*>(base + bl.dbias_part);

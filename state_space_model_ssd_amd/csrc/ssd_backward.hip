@@ -249,6 +249,48 @@ __device__ __forceinline__ bf16x8 frag_row(const bf16* p, bool ok) {
 }
 __device__ __forceinline__ bf16x8 frag_row(const float* p, bool ok) { return frag_f32(p, ok); }
 
+// 16 bytes at byte offset off of a buffer resource, or zeros when !ok.  The
+// load is issued whatever ok is (the offset of a lane without data lies
+// past the resource's records, which reads zeros), so no branch surrounds
+// it and the wait before its use counts only the loads issued after it:
+// software-pipelined loops keep their prefetches in flight.  Resources of
+// these loads are under 2 GiB.
+constexpr uint32_t kPastRecords = 0x80000000u;
+
+// A value every lane reads from the same address, loaded through the vector
+// memory path.  As a scalar load it would be waited for with lgkmcnt, which
+// the LDS accesses share and which scalar loads decrement out of order: the
+// wait for any LDS store before a barrier would then wait for a prefetch of
+// the next iteration's value too.  A vector load is counted in order with
+// the other prefetches.
+__device__ __forceinline__ float ld_vmem(const float* p) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(p, 4), 0u, 0, 0));
+}
+__device__ __forceinline__ int4 ld_vmem(const int4* p) {
+  return __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(p, 16), 0u, 0, 0));
+}
+// A buffer resource whose base and size are the workgroup's (read from the
+// first lane): the compiler cannot always prove a workgroup-wide address
+// uniform, and a resource it takes for a per-lane value makes it loop over
+// the distinct values around every access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc_u(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return buf_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
+}
+
+// A store that every lane issues; lanes without !ok aim past the resource's
+// records, where the store is dropped.  Stores count in the same wait as
+// loads, so a store under a branch would also blur the waits of a
+// software-pipelined loop.
+__device__ __forceinline__ void store_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, float v, bool ok) {
+  buf_store4(r, ok ? off : kPastRecords, v);
+}
+__device__ __forceinline__ bf16x8 frag_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok = true) {
+  return __builtin_bit_cast(bf16x8, buf_load16(r, ok ? off : kPastRecords));
+}
+
 // The quarters of the waves into acc[i][jn] (tile row tm + i, column tn + jn)
 // through LDS: rows 0-31 in lo, 32-63 in hi (32 x kGemmPitch floats each).
 // Begins and ends with a barrier.
@@ -361,13 +403,38 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-// 1. Q_j[p,n] = sum_l exp(a_l) dy[l,p] C[l,n] as 64 x 64 tiles;
-// grid: xcd_grid(chunk slots, ceil(P/64) * ceil(N/64) * H), every tile and
-// head of a chunk on the XCD of that chunk.
+// Sums over lanes by DPP (a data-parallel move folded into the add: no LDS
+// traffic).  dpp_add(v, CTRL, ROWS) adds to v the value that lane pattern
+// CTRL reads, in the rows (16-lane groups) of mask ROWS; other rows add 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+// The sum over each row of 16 lanes, in every lane of the row: neighbours
+// in pairs (quad_perm 1,0,3,2), pairs of pairs (quad_perm 2,3,0,1), then the
+// half-row and row mirrors.
+__device__ __forceinline__ float row_sum16(float v) {
+  v = dpp_add<0xb1>(v);
+  v = dpp_add<0x4e>(v);
+  v = dpp_add<0x141>(v);
+  return dpp_add<0x140>(v);
+}
+// The sum over the wave, in lane 63: the row sums, then row 15's and row
+// 31's broadcasts into the rows after them.
+__device__ __forceinline__ float wave_sum_last(float v) {
+  v = row_sum16(v);
+  v = dpp_add<0x142, 0xa>(v);
+  return dpp_add<0x143, 0xc>(v);
+}
+
+// 1. Q_j[p,n] = sum_l exp(a_l) dy[l,p] C[l,n] as 64 x 64 tiles, and the
+// chunk's log-decay a_last for the reverse chain (0 for an empty chunk:
+// decay 1), dla[j][h]; grid: xcd_grid(chunk slots, ceil(P/64) * ceil(N/64)
+// * H), every tile and head of a chunk on the XCD of that chunk.
 template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_q_tiled_kernel(
     ChunkMap cm, int nslots, const T* __restrict__ dy, const T* __restrict__ C,
-    const float* __restrict__ dAcs, int H, int G, float* __restrict__ Q) {
+    const float* __restrict__ dAcs, int H, int G, float* __restrict__ Q, float* __restrict__ dla) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   __shared__ float sc[L];
   constexpr int NT = (N + 63) / 64;
@@ -380,6 +447,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_tiled_kernel(
   const ChunkDesc cd = cm.desc(j);
   const int64_t jh = (int64_t)j * H + h;
   for (int l = threadIdx.x; l < L; l += kBwdThreads) sc[l] = exp2_fast(dAcs[jh * L + l] * kLog2e);
+  if (bx == 0 && threadIdx.x == 0) dla[jh] = cd.len > 0 ? dAcs[jh * L + cd.len - 1] : 0.f;
   __syncthreads();
   if constexpr (sizeof(T) == 2) {
     // bf16 MFMA over slices of 32 tokens l: exp(a_l) dy_l (rounded once) and
@@ -443,30 +511,67 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
   *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
 }
 
+// Four consecutive values of T as fp32 (8- or 16-byte load).
+__device__ __forceinline__ float4 load4_f32(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4_f32(const bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
 // 2. Reverse chain, four consecutive state elements per thread (16-byte
-// loads and stores; the next chunk's Q is loaded before this one's dS is
-// stored); grid (ceil(P*N / 1024), H, nstates).
+// loads and stores).  Alongside, the dot <dS_j, H_j> of the gradient leaving
+// chunk j with the state entering it (the chunk's last token's da needs
+// it), as one partial sum per wave (256 state elements): ghpart[j][h][PN /
+// 256].  dS in fp32 is written only where dS32 is given (the fp32 path's
+// operands).  Two register sets hold the Q piece, entering state and
+// log-decay of the next two chunks: every load is a vector load issued
+// without a branch, so the wait before a set's use leaves the other set's
+// loads in flight.  grid (ceil(P*N / 1024), H, nstates).
+template <typename T>
 __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(
-    ChunkMap cm, const float* __restrict__ Q, const float* __restrict__ dAcs,
-    const float* __restrict__ dfinal, int H, int PN, int L, float* __restrict__ dS,
-    bf16* __restrict__ dS16, float* __restrict__ dinit) {
+    ChunkMap cm, const float* __restrict__ Q, const float* __restrict__ dla,
+    const float* __restrict__ dfinal, const T* __restrict__ states_in, int H, int PN,
+    float* __restrict__ dS32, bf16* __restrict__ dS16, float* __restrict__ ghpart,
+    float* __restrict__ dinit) {
   const int e = (blockIdx.x * kBwdThreads + threadIdx.x) * 4;
-  if (e >= PN) return;                     // PN is a multiple of 4
-  const int h = blockIdx.y, s = blockIdx.z;
+  if (e >= PN) return;                     // PN is a multiple of 256: whole waves
+  const int h = blockIdx.y, s = blockIdx.z, wv = e / (4 * kWave), nw = PN / (4 * kWave);
   const int2 r = cm.seq_range(s);
   float4 g = dfinal ? *reinterpret_cast<const float4*>(dfinal + ((int64_t)s * H + h) * PN + e)
                     : make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (r.y > r.x) q = *reinterpret_cast<const float4*>(Q + ((int64_t)(r.y - 1) * H + h) * PN + e);
-  for (int j = r.y - 1; j >= r.x; --j) {
-    const int64_t jh = (int64_t)j * H + h;
-    const float4 qj = q;
-    if (j > r.x) q = *reinterpret_cast<const float4*>(Q + (jh - H) * PN + e);
-    *reinterpret_cast<float4*>(dS + jh * PN + e) = g;
-    if (dS16) store4(dS16 + jh * PN + e, g.x, g.y, g.z, g.w);   // rounded once, for the MFMA operands
-    const int len = cm.desc(j).len;
-    const float dec = len > 0 ? expf(dAcs[jh * L + len - 1]) : 1.f;
-    g = make_float4(dec * g.x + qj.x, dec * g.y + qj.y, dec * g.z + qj.z, dec * g.w + qj.w);
+  if (r.y > r.x) {
+    float4 q[2], hv[2];
+    float la[2];
+    auto loads = [&](int set, int j) {
+      const int64_t jh = (int64_t)j * H + h;
+      q[set] = *reinterpret_cast<const float4*>(Q + jh * PN + e);
+      hv[set] = load4_f32(states_in + jh * PN + e);
+      la[set] = ld_vmem(dla + jh);
+    };
+    auto step = [&](int set, int j) {      // chunk j with set's values; then chunk j - 2's loads
+      const int64_t jh = (int64_t)j * H + h;
+      const float4 qj = q[set], hj = hv[set];
+      const float dec = expf(la[set]);
+      loads(set, max(j - 2, r.x));         // before the sequence's start: its first chunk again
+      if (dS32) *reinterpret_cast<float4*>(dS32 + jh * PN + e) = g;
+      if (dS16) store4(dS16 + jh * PN + e, g.x, g.y, g.z, g.w);   // rounded once, for the MFMA operands
+      const float gh = wave_sum_last(g.x * hj.x + g.y * hj.y + g.z * hj.z + g.w * hj.w);
+      if ((threadIdx.x & (kWave - 1)) == kWave - 1) ghpart[jh * nw + wv] = gh;
+      g = make_float4(dec * g.x + qj.x, dec * g.y + qj.y, dec * g.z + qj.z, dec * g.w + qj.w);
+    };
+    loads(0, r.y - 1);
+    __builtin_amdgcn_sched_barrier(0);     // set 0's loads first, as in the loop
+    loads(1, max(r.y - 2, r.x));
+    __builtin_amdgcn_sched_barrier(0);
+    int j = r.y - 1;
+    for (; j - 1 >= r.x; j -= 2) {         // whole pairs: every path issues the same loads
+      step(0, j);
+      __builtin_amdgcn_sched_barrier(0);
+      step(1, j - 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (j >= r.x) step(0, j);
   }
   if (dinit) *reinterpret_cast<float4*>(dinit + ((int64_t)s * H + h) * PN + e) = g;
 }
@@ -539,14 +644,6 @@ __device__ __forceinline__ void unpack16<bf16>(const uint4& u, float* v) {
   for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(b[e]);
 }
 
-// Four consecutive values of T as fp32 (8- or 16-byte load).
-__device__ __forceinline__ float4 load4_f32(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ float4 load4_f32(const bf16* p) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
-  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-}
-
 // 3a. For each head, V[l,s] = exp(a_l - a_s) (dy_l . x_s) for s <= l as
 // 64 x 64 tiles on or below the diagonal, with each tile's partial sums
 //   rowpart[st][l] = sum_s CB[l,s] delta_s V[l,s]   (s in column tile st)
@@ -565,14 +662,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
     float* __restrict__ ddot) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   __shared__ float cpart[16][64];
-  // the head's running sums (rows, columns) and steps
-  __shared__ __align__(16) float al[64], as[64], dls[64];
+  // the head's running sums at the tile's rows and columns and its steps at
+  // the columns (fac[3] repeats fac[2]: every thread loads one value)
+  __shared__ __align__(16) float fac[4][64];
+  float* al = fac[0];
+  float* as = fac[1];
+  float* dls = fac[2];
   constexpr int LT = L / 64;
   constexpr int NX = LT * (LT + 1) / 2;   // tiles on or below the diagonal
   const int2 ci = xcd_chunk_head(blockIdx.x, NX * G * HB);
   if (ci.x >= nslots) return;
   const int2 tt = lower_tile(ci.y % NX);
-  const int lt = tt.x, st = tt.y, by = ci.y / NX;
+  // the tile is the workgroup's: read it as one value (buffer resources
+  // built from it must be uniform)
+  const int lt = __builtin_amdgcn_readfirstlane(tt.x), st = __builtin_amdgcn_readfirstlane(tt.y);
+  const int by = ci.y / NX;
   const int g = by / HB, hb = by - (by / HB) * HB, j = ci.x;
   const int hpg = H / G, h0 = g * hpg + hb * hpg / HB, h1 = g * hpg + (hb + 1) * hpg / HB;
   const ChunkDesc cd = cm.desc(j);
@@ -591,25 +695,74 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
     cbr[i][0] = v.x; cbr[i][1] = v.y; cbr[i][2] = v.z; cbr[i][3] = v.w;
   }
   float w[4][4] = {};                      // this block's sum of delta_s V[l,s]
+  // The next head's loads are issued before the current head's product and
+  // wait in registers: its factor value (one per thread) and, for bf16, its
+  // MFMA fragments of the dy and x rows (buffer loads: rows past the chunk
+  // read zeros).  Every load and store in the loop is issued without a
+  // branch, so the waits leave the prefetch in flight.
+  const int fk = threadIdx.x >> 6, fi = threadIdx.x & 63;
+  auto fac_src = [&](int h) -> const float* {
+    const int64_t jh = (int64_t)j * H + h;
+    return fk == 0 ? dAcs + jh * L + l0 + fi : fk == 1 ? dAcs + jh * L + s0 + fi : delta + jh * L + s0 + fi;
+  };
+  constexpr int KS = P / 32 > 0 ? P / 32 : 1;
+  const MfmaQuarter q;
+  const __amdgpu_buffer_rsrc_t rdy =
+      buf_rsrc_u(dy + (t0 + l0) * H * P, (uint32_t)((int64_t)(len - l0) * H * P * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t rx =
+      buf_rsrc_u(x + (t0 + s0) * H * P, (uint32_t)((int64_t)(len - s0) * H * P * sizeof(T)));
+  bf16x8 fa[KS][2], fb[KS][2];
+  float fv;
+  auto fetch = [&](int h) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = q.wr + u * 16 + q.lr, c = q.wc + u * 16 + q.lr;
+          fa[ks][u] = frag_buf(rdy, (uint32_t)(((r * H + h) * P + ks * 32 + q.kq) * sizeof(T)));
+          fb[ks][u] = frag_buf(rx, (uint32_t)(((c * H + h) * P + ks * 32 + q.kq) * sizeof(T)));
+        }
+    }
+    fv = *fac_src(h);
+  };
+  // a head's fragments and factor move from the prefetch registers at the
+  // end of the previous head (a point the loop reaches only from its body,
+  // so the wait there counts this head's loads exactly)
+  bf16x8 a[KS][2], b[KS][2];
+  auto take = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        a[ks][u] = fa[ks][u];
+        b[ks][u] = fb[ks][u];
+      }
+    fac[fk][fi] = fv;                      // the previous head's reads ended at its last barrier
+  };
+  fetch(h0);
+  take();
   for (int h = h0; h < h1; ++h) {
     const int64_t jh = (int64_t)j * H + h;
-    if (threadIdx.x < 64) {                // read after gemm_tile's barriers
-      al[threadIdx.x] = dAcs[jh * L + l0 + threadIdx.x];
-      as[threadIdx.x] = dAcs[jh * L + s0 + threadIdx.x];
-      dls[threadIdx.x] = delta[jh * L + s0 + threadIdx.x];
-    }
     float acc[4][4] = {};
     if constexpr (sizeof(T) == 2) {        // dy_l . x_s: bf16 rows, exact products on MFMA
-      const MfmaQuarter q;
+      static_assert(P % 32 == 0, "k-steps of the rows");
+      fetch(min(h + 1, h1 - 1));           // past the block's last head: that head again
       f32x4 d[2][2];
       zero_quarter(d);
-      mfma_rows<P>(q, dy + ((t0 + l0) * H + h) * P, (int64_t)H * P, len - l0,
-                   x + ((t0 + s0) * H + h) * P, (int64_t)H * P, len - s0, d);
-      quarter_to_thread(q, d, acc, As, Bs);
-    } else
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) d[mi][ni] = Mfma<bf16>::mma(a[ks][mi], b[ks][ni], d[mi][ni]);
+      quarter_to_thread(q, d, acc, As, Bs);  // its barriers also publish fac
+    } else {
+      fetch(min(h + 1, h1 - 1));
       gemm_staged<T, true, T, true>(dy + ((t0 + l0) * H + h) * P, (int64_t)H * P, len - l0, nullptr,
                                     x + ((t0 + s0) * H + h) * P, (int64_t)H * P, len - s0, 0, P, acc,
                                     As, Bs);
+    }
     float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum[4] = {0.f, 0.f, 0.f, 0.f};
     const float4 al4 = *reinterpret_cast<const float4*>(&al[tm]);
     const float4 as4 = *reinterpret_cast<const float4*>(&as[tn]);
@@ -629,28 +782,29 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
           csum[jn] += cbr[i][jn] * v;
         }
       }
+    const __amdgpu_buffer_rsrc_t rrow = buf_rsrc_u(rowpart + (jh * LT + st) * L + l0, 64 * sizeof(float));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float r = row16_sum(rsum[i]);
-      if ((threadIdx.x & 15) == 0) rowpart[(jh * LT + st) * L + l0 + tm + i] = r;
+      const float r = row_sum16(rsum[i]);
+      store_buf(rrow, (tm + i) * sizeof(float), r, (threadIdx.x & 15) == 0);
     }
     // on the diagonal, V[l,l] before its decay (1) is dy_l . x_l: the
     // per-token dot of dD, taken here instead of re-reading dy and x
-    if (lt == st && tm == tn) {
+    const __amdgpu_buffer_rsrc_t rdd = buf_rsrc_u(ddot + jh * L + l0, (uint32_t)((len - l0) * sizeof(float)));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (l0 + tm + i < len) ddot[jh * L + l0 + tm + i] = acc[i][i];
-    }
+    for (int i = 0; i < 4; ++i) store_buf(rdd, (tm + i) * sizeof(float), acc[i][i], lt == st && tm == tn);
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) cpart[threadIdx.x >> 4][tn + jn] = csum[jn];
     __syncthreads();
-    if (threadIdx.x < 64) {
+    {                                      // every thread sums a column; the first 64 store it
       float c = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) c += cpart[r][threadIdx.x];
-      colpart[(jh * LT + lt) * L + s0 + threadIdx.x] = c;
+      for (int r = 0; r < 16; ++r) c += cpart[r][fi];
+      store_buf(buf_rsrc_u(colpart + (jh * LT + lt) * L + s0, 64 * sizeof(float)), fi * sizeof(float), c,
+                threadIdx.x < 64);
     }
     __syncthreads();                       // cpart, al, as, dls read before the next head writes them
+    take();
   }
   // whole 4-wide pieces of the rows in the chunk (w is 0 above the
   // diagonal; entries there and past the chunk are never read)
@@ -790,126 +944,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
   }
 }
 
-// 4a. The state terms of dC and dB as 64 x 64 tiles of rows x n, per head
-//   dC_h = diag(exp(a)) dy H,   dB_h = diag(delta exp(a_last - a)) x dS_j,
-// summed over a block of the group's heads (HB blocks per group, as in 3a):
-// only the group's sum enters dB and dC.  Between each head's product and
-// the sum, a partial row dot product for the per-token pass:
-//   interpart[nt][l] = sum_n C[l,n] exp(a_l) (dy_l H)[n],
-//   vxpart[nt][s]    = sum_n B[s,n] exp(a_last - a_s) (x_s dS_j)[n]
-// over the tile's 64 columns n.  Block hb of group g writes its sum to
-// slot (j, g, hb) of dBh / dCh.  grid: xcd_grid(chunk slots, L/64 * ceil(N/64)
-// * 2 * G * HB), a chunk's tiles on its XCD; even tiles: dC, odd: dB.
-template <typename T, int P, int N, int L>
-__global__ __launch_bounds__(kBwdThreads) void bwd_bc_tiled_kernel(
-    ChunkMap cm, int nslots, const T* __restrict__ x, const T* __restrict__ B, const T* __restrict__ C,
-    const T* __restrict__ dy, const float* __restrict__ delta, const float* __restrict__ dAcs,
-    const T* __restrict__ states_in, const float* __restrict__ dS, const bf16* __restrict__ dS16,
-    int H, int G, int HB,
-    float* __restrict__ dBh, float* __restrict__ dCh, float* __restrict__ interpart,
-    float* __restrict__ vxpart) {
-  __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
-  __shared__ float sc[64], ds[64];         // the head's row factors and steps
-  constexpr int NT = (N + 63) / 64;
-  constexpr int NX = (L / 64) * NT * 2;
-  const int2 ci = xcd_chunk_head(blockIdx.x, NX * G * HB);
-  if (ci.x >= nslots) return;
-  const int bx = ci.y % NX, by = ci.y / NX;
-  const int which = bx & 1, t = bx >> 1;
-  const int m0 = (t / NT) * 64, nt = t % NT, n0 = nt * 64;
-  const int g = by / HB, hb = by - (by / HB) * HB, j = ci.x;
-  const int hpg = H / G, h0 = g * hpg + hb * hpg / HB, h1 = g * hpg + (hb + 1) * hpg / HB;
-  const ChunkDesc cd = cm.desc(j);
-  const int len = max(cd.len, 0);
-  if (m0 >= len) return;                   // uniform: rows past the chunk
-  const int64_t t0 = cd.start;
-  const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
-  // the row dot's group rows (C for dC, B for dB): this thread's 4 x 4
-  // values, the same for every head
-  float mv[4][4];
-  {
-    const T* M = which == 0 ? C : B;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jn = 0; jn < 4; ++jn) {
-        const int r = m0 + tm + i, nn = n0 + tn + jn;
-        mv[i][jn] = (r < len && nn < N) ? ld(M + ((t0 + r) * G + g) * N + nn) : 0.f;
-      }
-  }
-  float tot[4][4] = {};
-  for (int h = h0; h < h1; ++h) {
-    const int64_t jh = (int64_t)j * H + h;
-    __syncthreads();                       // the previous head's sc, ds and LDS tiles consumed
-    if (threadIdx.x < 64) {
-      const float* a = dAcs + jh * L;
-      const int r = m0 + threadIdx.x;
-      sc[threadIdx.x] = exp2_fast((which == 0 ? a[r] : a[len - 1] - a[r]) * kLog2e);
-      ds[threadIdx.x] = delta[jh * L + r];
-    }
-    float acc[4][4] = {};
-    if constexpr (sizeof(T) == 2) {
-      // bf16 MFMA: rows of dy (dC) or x (dB) times the entering state (bf16)
-      // or dS_j (rounded once to bf16), staged k-major (rows p) in LDS; the
-      // row factor exp(a_l) or exp(a_last - a_s) multiplies the product.
-      __shared__ __align__(16) bf16 kt[P * kKtPitch];
-      for (int i = threadIdx.x; i < P * 8; i += kBwdThreads) {
-        const int r = i >> 3, c = (i & 7) * 8;
-        const bool ok = n0 + c < N;
-        const bf16x8 v = which == 0 ? frag_row(states_in + (jh * P + r) * N + n0 + c, ok)
-                                    : frag_row(dS16 + (jh * P + r) * N + n0 + c, ok);
-        *reinterpret_cast<bf16x8*>(&kt[r * kKtPitch + c]) = v;
-      }
-      __syncthreads();
-      const MfmaQuarter q;
-      f32x4 d[2][2];
-      zero_quarter(d);
-      mfma_rows_kmajor<P>(q, (which == 0 ? dy : x) + ((t0 + m0) * H + h) * P, (int64_t)H * P,
-                          len - m0, kt, d);
-      quarter_to_thread(q, d, acc, As, Bs);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float f = sc[tm + i];
-#pragma unroll
-        for (int jn = 0; jn < 4; ++jn) acc[i][jn] *= f;
-      }
-    } else if (which == 0) {
-      // rows l of dy (scaled by exp(a_l)), rows p of the entering state
-      gemm_staged<T, true, T, false>(dy + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0, sc,
-                                     states_in + jh * P * N + n0, N, N - n0, 0, P, acc, As, Bs);
-    } else {
-      // rows s of x (scaled by exp(a_last - a_s)), rows p of dS_j
-      gemm_staged<T, true, float, false>(x + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0, sc,
-                                         dS + jh * P * N + n0, N, N - n0, 0, P, acc, As, Bs);
-    }
-    // sum_n M[row, n] acc[row, n] over the tile
-    float* part = which == 0 ? interpart : vxpart;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = m0 + tm + i;
-      float v = 0.f;
-#pragma unroll
-      for (int jn = 0; jn < 4; ++jn) v += mv[i][jn] * acc[i][jn];
-      v = row16_sum(v);
-      if ((threadIdx.x & 15) == 0) part[(jh * NT + nt) * L + r] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float f = which == 0 ? 1.f : ds[tm + i];
-#pragma unroll
-      for (int jn = 0; jn < 4; ++jn) tot[i][jn] += f * acc[i][jn];
-    }
-  }
-  float* out = (which == 0 ? dCh : dBh) + (((int64_t)j * G + g) * HB + hb) * L * N;
-  static_assert(N % 4 == 0, "4-wide pieces of a row");
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = m0 + tm + i;
-    if (r < len && n0 + tn < N)
-      store4(out + (int64_t)r * N + n0 + tn, tot[i][0], tot[i][1], tot[i][2], tot[i][3]);
-  }
-}
-
 // 3b'. The group's dCB: the HB partial sums of 3a added into the first,
 // four floats per thread (entries above the diagonal or past the chunk are
 // summed too and never read).  grid (ceil(L*L / 1024), G, chunk slots).
@@ -931,18 +965,28 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dcb_sum_kernel(int G, int HB,
   W[0] = v;
 }
 
-// 4b. dC and dB of a group as 64 x 64 tiles of rows x n: the group's summed
-// dCB (3b') times B or C, plus the per-head state
-// terms of 4a summed over the group's heads, rounded once to the dtype:
-//   dC[l] = sum_{s<=l} dCB[l,s] B_s + sum_h dC_h[l],
-//   dB[s] = sum_{l>=s} dCB[l,s] C_l + sum_h dB_h[s].
-// grid: xcd_grid(chunk slots, L/64 * ceil(N/64) * 2 * G), a chunk's tiles on
-// its XCD; even tiles: dC, odd: dB.
-template <typename T, int N, int L>
-__global__ __launch_bounds__(kBwdThreads) void bwd_bc_group_kernel(
-    ChunkMap cm, int nslots, const T* __restrict__ B, const T* __restrict__ C,
-    const float* __restrict__ dcbp, const float* __restrict__ dBh, const float* __restrict__ dCh,
-    int H, int G, int HB, T* __restrict__ dB, T* __restrict__ dC) {
+// 4. dC and dB of a group as 64 x 64 tiles of rows x n, rounded once to the
+// dtype: the group's summed dCB (3b') times B or C, plus the state terms
+// summed over the group's heads h and their rows p:
+//   dC[l] = sum_{s<=l} dCB[l,s] B_s + sum_h sum_p exp(a_l) dy_l[p] H_h[p, :],
+//   dB[s] = sum_{l>=s} dCB[l,s] C_l + sum_h sum_p delta_s exp(a_last - a_s) x_s[p] dS_h[p, :]
+// (a, delta, a_last those of head h).  The state terms are one contraction
+// over (h, p) per tile: dy and x rows are laid out with a token's heads side
+// by side, the entering states and dS with a chunk's heads side by side.
+// Each head's product before the sum also gives the per-token pass two row
+// dots over the tile's 64 columns n (slot 2 nt + half of the columns):
+//   interpart[slot][l] = sum_n C[l,n] exp(a_l) (dy_l H_h)[n]          (dC tiles)
+//   vxpart[slot][s]    = sum_n B[s,n] exp(a_last - a_s) (x_s dS_h)[n] (dB tiles)
+// so the dB tiles scale each head's product by delta_s after the dot.
+// grid: xcd_grid(chunk slots, L/64 * ceil(N/64) * 2 * G), a chunk's tiles
+// on its XCD; even tiles: dC, odd: dB.
+template <typename T, int P, int N, int L>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
+    ChunkMap cm, int nslots, const T* __restrict__ x, const T* __restrict__ B, const T* __restrict__ C,
+    const T* __restrict__ dy, const float* __restrict__ delta, const float* __restrict__ dAcs,
+    const T* __restrict__ states_in, const float* __restrict__ dS, const bf16* __restrict__ dS16,
+    const float* __restrict__ dcbp, int H, int G, int HB, T* __restrict__ dB, T* __restrict__ dC,
+    float* __restrict__ interpart, float* __restrict__ vxpart) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   constexpr int NT = (N + 63) / 64;
   constexpr int NX = (L / 64) * NT * 2;
@@ -956,7 +1000,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_group_kernel(
   const int len = max(cd.len, 0);
   if (m0 >= len) return;                   // uniform: rows past the chunk
   const int64_t t0 = cd.start;
+  const int hpg = H / G, h0 = g * hpg;
   const float* W = dcbp + ((int64_t)j * G + g) * HB * L * L;   // the summed slot
+  const T* rows = which == 0 ? dy : x;     // the state term's scaled rows
+  const T* M = which == 0 ? C : B;         // the row dots' group rows
+  float* part = which == 0 ? interpart : vxpart;
+  constexpr int SL = 2 * NT;               // row-dot slots per token
+  const int nt = n0 / 64;
   float acc[4][4] = {};
   if constexpr (sizeof(T) == 2) {
     // bf16 MFMA over 32-long k-slices, the summed dCB rounded once to bf16
@@ -1016,43 +1066,181 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_group_kernel(
         mfma_kmajor(q, at, bt, d);
       }
     }
+    // The state terms, head by head: the rows (dy or x, exact bf16, 16-byte
+    // pieces straight into operand registers) times the head's P x 64
+    // operand (the entering state or dS in bf16, staged k-major in one of
+    // two LDS buffers, so one barrier per head); the row factor exp(a_l) or
+    // exp(a_last - a_s) (and delta_s for dB) multiplies the product's rows.
+    // Two register sets hold the rows, operand pieces and factors of the
+    // next two heads, loaded while the current head is multiplied.
+    constexpr int KS = P / 32;             // 32-long k-steps per head
+    constexpr int PP = P * 8 / kBwdThreads;   // 16-byte operand pieces per thread
+    static_assert(P % 32 == 0 && PP >= 1 && P * 8 % kBwdThreads == 0, "head operand pieces");
+    __shared__ __align__(16) bf16 kt[2][P * kKtPitch];
+    const bf16* K16 = which == 0 ? reinterpret_cast<const bf16*>(states_in) : dS16;
+    const int h1 = h0 + hpg;
+    // the chunk's rows (tokens past its end read zeros) and its heads'
+    // P x N operands as buffer resources
+    const __amdgpu_buffer_rsrc_t rrow =
+        buf_rsrc_u(rows + t0 * H * P, (uint32_t)((int64_t)len * H * P * sizeof(T)));
+    const __amdgpu_buffer_rsrc_t rk16 =
+        buf_rsrc_u(K16 + (int64_t)j * H * P * N, (uint32_t)((int64_t)H * P * N * sizeof(bf16)));
+    // the row dots' M[row, n] at this lane's 8 rows and 2 columns of the
+    // product (rows past the chunk and columns past N read 0)
+    float mrow[2][2][4];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + q.row(mi, r), col = n0 + q.col(ni);
+          mrow[mi][ni][r] = (row < len && col < N) ? ld(M + ((t0 + row) * G + g) * N + col) : 0.f;
+        }
+    bf16x8 ra[2][KS][2], rk[2][PP];
+    float fl[2];
+    float4 al[2][2], dl[2][2];             // a and delta at this lane's product rows
+    auto fetch = [&](int set, int h) {     // no branch: see frag_buf
+      const int64_t jh = (int64_t)j * H + h;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int m = m0 + q.wr + mi * 16 + q.lr;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          ra[set][ks][mi] = frag_buf(rrow, (uint32_t)(((m * H + h) * P + ks * 32 + q.kq) * sizeof(T)));
+        // four consecutive rows < L: inside the chunk's row of the workspace
+        al[set][mi] = *reinterpret_cast<const float4*>(dAcs + jh * L + m0 + q.row(mi, 0));
+        dl[set][mi] = *reinterpret_cast<const float4*>(delta + jh * L + m0 + q.row(mi, 0));
+      }
+      fl[set] = ld_vmem(dAcs + jh * L + len - 1);
+#pragma unroll
+      for (int u = 0; u < PP; ++u) {
+        const int i = threadIdx.x + kBwdThreads * u, r = i >> 3, cc = (i & 7) * 8;
+        rk[set][u] = frag_buf(rk16, (uint32_t)(((h * P + r) * N + n0 + cc) * sizeof(bf16)), n0 + cc < N);
+      }
+    };
+    auto step = [&](int set, int h) {      // set = (h - h0) & 1, also the LDS buffer
+      bf16* kb = kt[set];
+#pragma unroll
+      for (int u = 0; u < PP; ++u) {
+        const int i = threadIdx.x + kBwdThreads * u;
+        *reinterpret_cast<bf16x8*>(&kb[(i >> 3) * kKtPitch + (i & 7) * 8]) = rk[set][u];
+      }
+      bf16x8 aop[KS][2];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) aop[ks][mi] = ra[set][ks][mi];
+      const float4 alh[2] = {al[set][0], al[set][1]}, dlh[2] = {dl[set][0], dl[set][1]};
+      const float flh = fl[set];
+      fetch(set, min(h + 2, h1 - 1));      // past the group's last head: that head again
+      __builtin_amdgcn_sched_barrier(0);   // keep the sets' loads in issue order
+      __syncthreads();                     // this head's operand tile stored
+      f32x4 dh[2][2];                      // this head's product
+      zero_quarter(dh);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 b[2];
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) b[ni] = lds_operand_kmajor(kb, kKtPitch, ks * 32, q.wc + ni * 16, q.lane);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) dh[mi][ni] = Mfma<bf16>::mma(aop[ks][mi], b[ni], dh[mi][ni]);
+      }
+      // the row dots (a row's 16 lanes hold its columns), then the sum
+      const int64_t jh = (int64_t)j * H + h;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const float av[4] = {alh[mi].x, alh[mi].y, alh[mi].z, alh[mi].w};
+        const float dlv[4] = {dlh[mi].x, dlh[mi].y, dlh[mi].z, dlh[mi].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + q.row(mi, r);
+          // rows past the chunk: factor 0 (their a and delta are not defined)
+          const float e = exp2_fast((which == 0 ? av[r] : flh - av[r]) * kLog2e);
+          const float f = row < len ? e : 0.f;
+          const float v = f * row_sum16(mrow[mi][0][r] * dh[mi][0][r] + mrow[mi][1][r] * dh[mi][1][r]);
+          if (q.lr == 0 && row < len) part[(jh * SL + 2 * nt + (q.wc >> 5)) * L + row] = v;
+          const float fr = which == 0 ? f : (row < len ? dlv[r] : 0.f) * f;
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) d[mi][ni][r] += fr * dh[mi][ni][r];
+        }
+      }
+    };
+    fetch(0, h0);
+    __builtin_amdgcn_sched_barrier(0);     // set 0's loads first, as in the loop
+    fetch(1, min(h0 + 1, h1 - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    int h = h0;
+    for (; h + 1 < h1; h += 2) {           // whole pairs: every path through the loop
+      step(0, h);                          // issues the same loads in the same order
+      step(1, h + 1);
+    }
+    if (h < h1) step(0, h);                // an odd group's last head
     quarter_to_thread(q, d, acc, As, Bs);
-  } else if (which == 0) {                 // dC rows m0..m0+63: s runs to the tile's last row
-    // rows l of the summed dCB (columns s <= l), rows s of B
-    gemm_staged<float, true, T, false, 32, 1>(W + (int64_t)m0 * L, L, len - m0, nullptr,
-                                              B + (t0 * G + g) * N + n0, (int64_t)G * N, N - n0, 0,
-                                              min(len, m0 + 64), acc, As, Bs, m0);
-  } else {                                 // dB rows m0..m0+63: l runs from the tile's first row
-    // rows l of the summed dCB (columns s <= l), rows l of C
-    gemm_staged<float, false, T, false, 32, 2>(W + m0, L, len - m0, nullptr,
-                                               C + (t0 * G + g) * N + n0, (int64_t)G * N, N - n0, m0,
-                                               len, acc, As, Bs, m0);
+  } else {
+    if (which == 0) {                      // dC rows m0..m0+63: s runs to the tile's last row
+      // rows l of the summed dCB (columns s <= l), rows s of B
+      gemm_staged<float, true, T, false, 32, 1>(W + (int64_t)m0 * L, L, len - m0, nullptr,
+                                                B + (t0 * G + g) * N + n0, (int64_t)G * N, N - n0, 0,
+                                                min(len, m0 + 64), acc, As, Bs, m0);
+    } else {                               // dB rows m0..m0+63: l runs from the tile's first row
+      // rows l of the summed dCB (columns s <= l), rows l of C
+      gemm_staged<float, false, T, false, 32, 2>(W + m0, L, len - m0, nullptr,
+                                                 C + (t0 * G + g) * N + n0, (int64_t)G * N, N - n0, m0,
+                                                 len, acc, As, Bs, m0);
+    }
+    // the state terms, head by head: the rows scaled by their factor
+    // (staged in LDS), times the head's entering state or dS rows p; the
+    // row dots of each head's product (one slot per column tile: the
+    // tile's second slot is 0), then its sum
+    __shared__ float sc[64], dsr[64];
+    const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+    float mv[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) {
+        const int r = m0 + tm + i, nn = n0 + tn + jn;
+        mv[i][jn] = (r < len && nn < N) ? ld(M + ((t0 + r) * G + g) * N + nn) : 0.f;
+      }
+    for (int h = h0; h < h0 + hpg; ++h) {
+      const int64_t jh = (int64_t)j * H + h;
+      __syncthreads();                     // the previous head's factors consumed
+      if (threadIdx.x < 64) {
+        const int m = m0 + threadIdx.x;
+        const float* ah = dAcs + jh * L;
+        sc[threadIdx.x] = m >= len ? 0.f : exp2_fast((which == 0 ? ah[m] : ah[len - 1] - ah[m]) * kLog2e);
+        dsr[threadIdx.x] = delta[jh * L + m];
+      }
+      float ah[4][4] = {};
+      if (which == 0)
+        gemm_staged<T, true, T, false>(dy + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0, sc,
+                                       states_in + jh * P * N + n0, N, N - n0, 0, P, ah, As, Bs);
+      else
+        gemm_staged<T, true, float, false>(x + ((t0 + m0) * H + h) * P, (int64_t)H * P, len - m0, sc,
+                                           dS + jh * P * N + n0, N, N - n0, 0, P, ah, As, Bs);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = m0 + tm + i;
+        float v = 0.f;
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) v += mv[i][jn] * ah[i][jn];
+        v = row16_sum(v);
+        if ((threadIdx.x & 15) == 0 && r < len) {
+          part[(jh * SL + 2 * nt) * L + r] = v;
+          part[(jh * SL + 2 * nt + 1) * L + r] = 0.f;
+        }
+        const float fr = which == 0 ? 1.f : dsr[tm + i];
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) acc[i][jn] += fr * ah[i][jn];
+      }
+    }
   }
-  // the state terms of the group's HB head blocks: per block, four 16-byte
-  // loads of this thread's 4 x 4 values (rows past the chunk read row 0 and
-  // columns past N read column 0; both are dropped)
-  const float* part = which == 0 ? dCh : dBh;
   T* out = which == 0 ? dC : dB;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
-  static_assert(N % 4 == 0, "16-byte pieces of a row");
-  const int ncol = n0 + tn < N ? n0 + tn : 0;
-#pragma unroll 2
-  for (int b = 0; b < HB; ++b) {
-    const float* ph = part + (((int64_t)j * G + g) * HB + b) * L * N;
-    float4 v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = m0 + tm + i;
-      v[i] = *reinterpret_cast<const float4*>(ph + (int64_t)(r < len ? r : 0) * N + ncol);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i][0] += v[i].x;
-      acc[i][1] += v[i].y;
-      acc[i][2] += v[i].z;
-      acc[i][3] += v[i].w;
-    }
-  }
+  static_assert(N % 4 == 0, "4-wide pieces of a row");
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = m0 + tm + i;
@@ -1066,17 +1254,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_bc_group_kernel(
 // dt_bias.  grid (H, chunk slots), L threads.
 template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(L) void bwd_token_kernel(
-    ChunkMap cm, const T* __restrict__ x, const float* __restrict__ dt,
-    const float* __restrict__ dt_bias, const float* __restrict__ A, const T* __restrict__ dy,
-    const float* __restrict__ delta, const float* __restrict__ dAcs,
-    const T* __restrict__ states_in, const float* __restrict__ dS,
-    const float* __restrict__ rowpart, const float* __restrict__ colpart,
-    const float* __restrict__ interpart, const float* __restrict__ vxpart,
-    const float* __restrict__ ddot, int H, float dt_min,
+    ChunkMap cm, const float* __restrict__ dt, const float* __restrict__ dt_bias,
+    const float* __restrict__ A, const float* __restrict__ delta, const float* __restrict__ dAcs,
+    const float* __restrict__ ghpart, const float* __restrict__ rowpart,
+    const float* __restrict__ colpart, const float* __restrict__ vxpart,
+    const float* __restrict__ interpart, const float* __restrict__ ddot, int H, float dt_min,
     float dt_max, float* __restrict__ ddt, float* __restrict__ dA_part,
     float* __restrict__ dD_part, float* __restrict__ dbias_part) {
   __shared__ float red[3 * (L / kWave)];
-  constexpr int LT = L / 64, NT = (N + 63) / 64;
+  constexpr int LT = L / 64, VX = 2 * ((N + 63) / 64);   // row-dot slots per token
   const int h = blockIdx.x, j = blockIdx.y, k = threadIdx.x;
   const ChunkDesc cd = cm.desc(j);
   const int64_t jh = (int64_t)j * H + h;
@@ -1098,19 +1284,18 @@ __global__ __launch_bounds__(L) void bwd_token_kernel(
   if (valid) {
     for (int st = 0; st <= k / 64; ++st) rowsum += rowpart[(jh * LT + st) * L + k];
     for (int lt = k / 64; lt < LT && lt * 64 < len; ++lt) sdir += colpart[(jh * LT + lt) * L + k];
-    for (int nt = 0; nt < NT; ++nt) {
-      inter += interpart[(jh * NT + nt) * L + k];
-      vxe += vxpart[(jh * NT + nt) * L + k];
+#pragma unroll
+    for (int v = 0; v < VX; ++v) {
+      vxe += vxpart[(jh * VX + v) * L + k];
+      inter += interpart[(jh * VX + v) * L + k];
     }
   }
   dd = valid ? ddot[jh * L + k] : 0.f;    // dy_k . x_k, from the V tiles
   const float vs = dk * vxe;
-  float gh = 0.f;
-  static_assert((P * N) % (4 * L) == 0, "state elements per thread");
-  for (int i = 4 * k; i < P * N; i += 4 * L) {
-    const float4 u = load4_f32(dS + jh * P * N + i), w = load4_f32(states_in + jh * P * N + i);
-    gh += u.x * w.x + u.y * w.y + u.z * w.z + u.w * w.w;
-  }
+  // <dS_j, H_j>: the chain's partial sums, one per 256 state elements
+  constexpr int NW = P * N / (4 * kWave);
+  static_assert(NW <= L && (P * N) % (4 * kWave) == 0, "partial sums of <dS, H>");
+  const float gh = k < NW ? ghpart[jh * NW + k] : 0.f;
   const float3 gt = block_sum3<L>(make_float3(gh, valid ? vs : 0.f, 0.f), red);
   float da = valid ? rowsum - dk * sdir + inter - vs : 0.f;
   if (k == len - 1) da += gt.y + expf(alast) * gt.x;
@@ -1194,37 +1379,34 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   const T* hin = (const T*)a.states_in;
   constexpr int NT = (N + 63) / 64;
   hipLaunchKernelGGL((bwd_q_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, ((P + 63) / 64) * NT * H)),
-                     dim3(kBwdThreads), 0, s, cm, mc, dy, C, a.dAcs, H, G, b.Q);
+                     dim3(kBwdThreads), 0, s, cm, mc, dy, C, a.dAcs, H, G, b.Q, b.dla);
   static_assert((P * N) % 4 == 0, "four state elements per thread");
-  hipLaunchKernelGGL(bwd_chain_kernel, dim3((PN / 4 + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
-                     dim3(kBwdThreads), 0, s, cm, b.Q, a.dAcs, b.dfinal, H, PN, L, b.dS,
-                     sizeof(T) == 2 ? static_cast<bf16*>(b.dS16) : nullptr, b.dinit);
+  static_assert(PN % (4 * kWave) == 0, "whole waves of the chain");
+  hipLaunchKernelGGL((bwd_chain_kernel<T>), dim3((PN / 4 + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
+                     dim3(kBwdThreads), 0, s, cm, b.Q, b.dla, b.dfinal, hin, H, PN,
+                     sizeof(T) == 4 ? b.dS : nullptr, sizeof(T) == 2 ? static_cast<bf16*>(b.dS16) : nullptr,
+                     b.ghpart, b.dinit);
   constexpr int LT = L / 64;
-  // head blocks per group for the summed dCB and dB/dC state terms: the
-  // fewest that fill the GPU with 3a's workgroups (their partial sums fit
-  // the workspace's H L^2 and H L N floats per chunk: G * HB <= H)
+  // head blocks per group for the summed dCB: the fewest that fill the GPU
+  // with 3a's workgroups (their partial sums fit the workspace's H L^2
+  // floats per chunk: G * HB <= H)
   const int hpg = H / G, HB = bwd_head_blocks(hpg, (int64_t)(LT * (LT + 1) / 2) * G * mc);
   hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * (LT + 1) / 2 * G * HB)),
                      dim3(kBwdThreads), 0, s, cm, mc, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb,
                      b.rowpart, b.colpart, b.ddot);
-  hipLaunchKernelGGL((bwd_bc_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * NT * 2 * G * HB)),
-                     dim3(kBwdThreads), 0, s, cm, mc, x, B, C, dy, a.delta, a.dAcs, hin, b.dS,
-                     static_cast<const bf16*>(b.dS16), H, G,
-                     HB, b.dBh, b.dCh, b.interpart, b.vxpart);
   if (HB > 1)
     hipLaunchKernelGGL((bwd_dcb_sum_kernel<L>), dim3((L * L / 4 + kBwdThreads - 1) / kBwdThreads, G, mc),
                        dim3(kBwdThreads), 0, s, G, HB, b.dcb);
-  hipLaunchKernelGGL((bwd_bc_group_kernel<T, N, L>), dim3(xcd_grid(mc, LT * NT * 2 * G)),
-                     dim3(kBwdThreads), 0, s, cm, mc, B, C, b.dcb, b.dBh, b.dCh, H, G, HB, (T*)b.dB,
-                     (T*)b.dC);
+  hipLaunchKernelGGL((bwd_bc_group_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * NT * 2 * G)),
+                     dim3(kBwdThreads), 0, s, cm, mc, x, B, C, dy, a.delta, a.dAcs, hin, b.dS,
+                     static_cast<const bf16*>(b.dS16), b.dcb, H, G, HB, (T*)b.dB, (T*)b.dC, b.interpart,
+                     b.vxpart);
   hipLaunchKernelGGL((bwd_dx_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * ((P + 63) / 64) * H)),
                      dim3(kBwdThreads), 0, s, cm, mc, B, dy, cb, a.delta, a.dAcs, b.dS,
-                     static_cast<const bf16*>(b.dS16), a.D, H, G,
-                     (T*)b.dx);
-  hipLaunchKernelGGL((bwd_token_kernel<T, P, N, L>), dim3(H, mc), dim3(L), 0, s, cm, x, a.dt,
-                     a.dt_bias, a.A, dy, a.delta, a.dAcs, hin, b.dS, b.rowpart, b.colpart,
-                     b.interpart, b.vxpart, b.ddot, H, a.dt_min, a.dt_max, b.ddt, b.dA_part,
-                     b.dD_part, b.dbias_part);
+                     static_cast<const bf16*>(b.dS16), a.D, H, G, (T*)b.dx);
+  hipLaunchKernelGGL((bwd_token_kernel<T, P, N, L>), dim3(H, mc), dim3(L), 0, s, cm, a.dt, a.dt_bias,
+                     a.A, a.delta, a.dAcs, b.ghpart, b.rowpart, b.colpart, b.vxpart, b.interpart,
+                     b.ddot, H, a.dt_min, a.dt_max, b.ddt, b.dA_part, b.dD_part, b.dbias_part);
   hipLaunchKernelGGL(bwd_head_reduce_kernel, dim3(H), dim3(kWave), 0, s, b.dA_part, b.dD_part,
                      b.dbias_part, H, mc, b.dA, b.dD, b.ddt_bias);
   return hipGetLastError();

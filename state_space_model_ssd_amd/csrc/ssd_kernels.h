@@ -75,16 +75,16 @@ struct BwdArgs {
   float* ddt_bias;          // nullable
   float* dinit;             // nullable
   float* Q;                 // [max_chunks][H][P*N]
-  float* dS;                // [max_chunks][H][P*N]
+  float* dS;                // [max_chunks][H][P*N] (fp32 inputs only)
   void* dS16;               // [max_chunks][H][P*N] bf16: dS rounded once (bf16 inputs)
   float* dcb;               // [max_chunks][H][L][L] floats; holds [max_chunks][G][HB][L][L]: sums
                             // of delta_s exp(a_l - a_s) dy_l . x_s (s <= l) over head blocks
   float* rowpart;           // [max_chunks][H][L/64][L]
   float* colpart;           // [max_chunks][H][L/64][L]
-  float* interpart;         // [max_chunks][H][ceil(N/64)][L]
-  float* vxpart;            // [max_chunks][H][ceil(N/64)][L]
-  float* dBh;               // [max_chunks][G * head blocks <= H][L][N]
-  float* dCh;               // [max_chunks][G * head blocks <= H][L][N]
+  float* vxpart;            // [max_chunks][H][2 ceil(N/64)][L]
+  float* interpart;         // [max_chunks][H][2 ceil(N/64)][L]
+  float* ghpart;            // [max_chunks][H][P*N / 256]: <dS_j, H_j> in pieces
+  float* dla;               // [max_chunks][H]: the chunk's log-decay a_last (0 if empty)
   float* dA_part;           // [max_chunks][H]
   float* dD_part;           // [max_chunks][H]
   float* dbias_part;        // [max_chunks][H]
