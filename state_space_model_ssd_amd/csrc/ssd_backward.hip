@@ -419,6 +419,27 @@ __device__ __forceinline__ float row_sum16(float v) {
   v = dpp_add<0x141>(v);
   return dpp_add<0x140>(v);
 }
+// Eight sums over each row of 16 lanes at once: the v[i] (i < 8) of the
+// row's lanes are added, and lane lr ends with the sum of v[4 (lr >> 3) +
+// 2 ((lr >> 2) & 1) + ((lr >> 1) & 1)] (lanes lr and lr ^ 1 hold the same
+// one).  Each step pairs the lanes (rotation by 8, half-row mirror, then
+// quad_perm 2,3,0,1): a lane keeps half of its values and adds its
+// partner's copy of that half.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_sum16_x8(const float (&v)[8], int lr) {
+  const bool u8 = lr & 8, u4 = lr & 4, u2 = lr & 2;
+  float a[4], b[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) a[k] = (u8 ? v[4 + k] : v[k]) + dpp_mov<0x128>(u8 ? v[k] : v[4 + k]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) b[k] = (u4 ? a[2 + k] : a[k]) + dpp_mov<0x141>(u4 ? a[k] : a[2 + k]);
+  const float c = (u2 ? b[1] : b[0]) + dpp_mov<0x4e>(u2 ? b[0] : b[1]);
+  return c + dpp_mov<0xb1>(c);
+}
+
 // The sum over the wave, in lane 63: the row sums, then row 15's and row
 // 31's broadcasts into the rows after them.
 __device__ __forceinline__ float wave_sum_last(float v) {
@@ -1099,7 +1120,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
         }
     bf16x8 ra[2][KS][2], rk[2][PP];
     float fl[2];
-    float4 al[2][2], dl[2][2];             // a and delta at this lane's product rows
+    // the row factors: thread t loads a and delta of tile row t % 64 (rows
+    // < L: inside the chunk's row of the workspace) and at each head writes
+    // f (the product's row factor) or g (what the sum takes: f, times
+    // delta for dB) of that row to LDS, beside the head's operand tile
+    __shared__ __align__(16) float fac[2][2][64];
+    const int fr_row = threadIdx.x & 63, fr_k = (threadIdx.x >> 6) & 1;
+    float fa[2], fd[2];
     auto fetch = [&](int set, int h) {     // no branch: see frag_buf
       const int64_t jh = (int64_t)j * H + h;
 #pragma unroll
@@ -1108,10 +1135,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           ra[set][ks][mi] = frag_buf(rrow, (uint32_t)(((m * H + h) * P + ks * 32 + q.kq) * sizeof(T)));
-        // four consecutive rows < L: inside the chunk's row of the workspace
-        al[set][mi] = *reinterpret_cast<const float4*>(dAcs + jh * L + m0 + q.row(mi, 0));
-        dl[set][mi] = *reinterpret_cast<const float4*>(delta + jh * L + m0 + q.row(mi, 0));
       }
+      fa[set] = dAcs[jh * L + m0 + fr_row];
+      fd[set] = delta[jh * L + m0 + fr_row];
       fl[set] = ld_vmem(dAcs + jh * L + len - 1);
 #pragma unroll
       for (int u = 0; u < PP; ++u) {
@@ -1126,13 +1152,18 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
         const int i = threadIdx.x + kBwdThreads * u;
         *reinterpret_cast<bf16x8*>(&kb[(i >> 3) * kKtPitch + (i & 7) * 8]) = rk[set][u];
       }
+      {
+        // rows past the chunk: factor 0 (their a and delta are not defined)
+        const bool ok = m0 + fr_row < len;
+        const float f = ok ? exp2_fast((which == 0 ? fa[set] : fl[set] - fa[set]) * kLog2e) : 0.f;
+        const float gsum = which == 0 ? f : (ok ? fd[set] : 0.f) * f;
+        fac[set][fr_k][fr_row] = fr_k ? gsum : f;   // threads 128-255 repeat 0-127
+      }
       bf16x8 aop[KS][2];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) aop[ks][mi] = ra[set][ks][mi];
-      const float4 alh[2] = {al[set][0], al[set][1]}, dlh[2] = {dl[set][0], dl[set][1]};
-      const float flh = fl[set];
       fetch(set, min(h + 2, h1 - 1));      // past the group's last head: that head again
       __builtin_amdgcn_sched_barrier(0);   // keep the sets' loads in issue order
       __syncthreads();                     // this head's operand tile stored
@@ -1148,24 +1179,30 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
 #pragma unroll
           for (int ni = 0; ni < 2; ++ni) dh[mi][ni] = Mfma<bf16>::mma(aop[ks][mi], b[ni], dh[mi][ni]);
       }
-      // the row dots (a row's 16 lanes hold its columns), then the sum
+      // the row dots (a row's 16 lanes hold its columns): lane lr ends with
+      // row (mi, r) = (lr >> 3, 2 ((lr >> 2) & 1) + ((lr >> 1) & 1)), one
+      // store per head for the wave's rows; then the sum, rows scaled by g
       const int64_t jh = (int64_t)j * H + h;
+      float v[8];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[4 * mi + r] = mrow[mi][0][r] * dh[mi][0][r] + mrow[mi][1][r] * dh[mi][1][r];
+      {
+        const float sum = row_sum16_x8(v, q.lr);
+        const int rl = q.row(q.lr >> 3, 2 * ((q.lr >> 2) & 1) + ((q.lr >> 1) & 1));
+        const __amdgpu_buffer_rsrc_t rp =
+            buf_rsrc_u(part + (jh * SL + 2 * nt + (q.wc >> 5)) * L + m0, (uint32_t)((len - m0) * sizeof(float)));
+        store_buf(rp, rl * sizeof(float), fac[set][0][rl] * sum, (q.lr & 1) == 0);
+      }
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
-        const float av[4] = {alh[mi].x, alh[mi].y, alh[mi].z, alh[mi].w};
-        const float dlv[4] = {dlh[mi].x, dlh[mi].y, dlh[mi].z, dlh[mi].w};
+        const float4 g4 = *reinterpret_cast<const float4*>(&fac[set][1][q.row(mi, 0)]);
+        const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = m0 + q.row(mi, r);
-          // rows past the chunk: factor 0 (their a and delta are not defined)
-          const float e = exp2_fast((which == 0 ? av[r] : flh - av[r]) * kLog2e);
-          const float f = row < len ? e : 0.f;
-          const float v = f * row_sum16(mrow[mi][0][r] * dh[mi][0][r] + mrow[mi][1][r] * dh[mi][1][r]);
-          if (q.lr == 0 && row < len) part[(jh * SL + 2 * nt + (q.wc >> 5)) * L + row] = v;
-          const float fr = which == 0 ? f : (row < len ? dlv[r] : 0.f) * f;
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int ni = 0; ni < 2; ++ni) d[mi][ni][r] += fr * dh[mi][ni][r];
-        }
+          for (int ni = 0; ni < 2; ++ni) d[mi][ni][r] += gv[r] * dh[mi][ni][r];
       }
     };
     fetch(0, h0);
