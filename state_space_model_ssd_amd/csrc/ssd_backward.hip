@@ -479,18 +479,30 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_tiled_kernel(
     f32x4 d[2][2];
     zero_quarter(d);
     const int len = max(cd.len, 0), kr = threadIdx.x >> 3, c = (threadIdx.x & 7) * 8;
+    // the next slice's rows are loaded while the current one is multiplied
+    // (buffer loads without a branch: tokens past the chunk read zeros)
+    const __amdgpu_buffer_rsrc_t rdy =
+        buf_rsrc_u(dy + (int64_t)cd.start * H * P, (uint32_t)((int64_t)len * H * P * sizeof(T)));
+    const __amdgpu_buffer_rsrc_t rc =
+        buf_rsrc_u(C + (int64_t)cd.start * G * N, (uint32_t)((int64_t)len * G * N * sizeof(T)));
+    bf16x8 yv, cv;
+    auto fetch = [&](int kb) {
+      const int l = kb + kr;
+      yv = frag_buf(rdy, (uint32_t)(((l * H + h) * P + m0 + c) * sizeof(T)), m0 + c < P);
+      cv = frag_buf(rc, (uint32_t)(((l * G + g) * N + n0 + c) * sizeof(T)), n0 + c < N);
+    };
+    if (len > 0) fetch(0);
     for (int kb = 0; kb < len; kb += 32) {
       const int l = kb + kr;
-      const bool lok = l < len;
-      const bf16x8 yv = frag_row(dy + ((int64_t)(cd.start + l) * H + h) * P + m0 + c, lok && m0 + c < P);
-      const bf16x8 cv = frag_row(C + ((int64_t)(cd.start + l) * G + g) * N + n0 + c, lok && n0 + c < N);
-      const float f = lok ? sc[l] : 0.f;
+      const float f = l < len ? sc[l] : 0.f;
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = f * static_cast<float>(yv[e]);
+      const bf16x8 ccur = cv;
+      fetch(kb + 32);                      // past the chunk: zeros
       __syncthreads();                     // previous slice consumed
       *reinterpret_cast<bf16x8*>(&yt[kr * kKtPitch + c]) = Mfma<bf16>::pack(v);
-      *reinterpret_cast<bf16x8*>(&ct[kr * kKtPitch + c]) = cv;
+      *reinterpret_cast<bf16x8*>(&ct[kr * kKtPitch + c]) = ccur;
       __syncthreads();
       mfma_kmajor(q, yt, ct, d);
     }
@@ -842,7 +854,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
 //          + D dy_s;
 // grid: xcd_grid(chunk slots, L/64 * ceil(P/64) * H), a chunk's tiles on its XCD.
 template <typename T, int P, int N, int L>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
+__global__ __launch_bounds__(kBwdThreads, 8) void bwd_dx_tiled_kernel(
     ChunkMap cm, int nslots, const T* __restrict__ B, const T* __restrict__ dy, const T* __restrict__ cb,
     const float* __restrict__ delta, const float* __restrict__ dAcs, const float* __restrict__ dS,
     const bf16* __restrict__ dS16,
@@ -892,20 +904,36 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
       }
     static_assert(32 * 8 == kBwdThreads, "one 8-wide piece of each slice tile per thread");
     const int kr = threadIdx.x >> 3, c = (threadIdx.x & 7) * 8;
+    // The next slice's CB and dy pieces are loaded while the current slice
+    // is multiplied: buffer loads issued without a branch (rows past the
+    // chunk read zeros), so the wait before their use leaves them in flight.
+    const __amdgpu_buffer_rsrc_t rcb = buf_rsrc_u(cbj, (uint32_t)(len * L * sizeof(T)));
+    const __amdgpu_buffer_rsrc_t rdy = buf_rsrc_u(dy + t0 * H * P, (uint32_t)((int64_t)len * H * P * sizeof(T)));
+    bf16x8 cv, yv;
+    auto fetch = [&](int kb) {
+      const int l = kb + kr;
+      cv = frag_buf(rcb, (uint32_t)((l * L + s0 + c) * sizeof(T)));
+      yv = frag_buf(rdy, (uint32_t)(((l * H + h) * P + p0 + c) * sizeof(T)), p0 + c < P);
+    };
+    fetch(s0);
     for (int kb = s0; kb < len; kb += 32) {
       const int l = kb + kr;
       const bool lok = l < len;
-      const bf16x8 cv = frag_row(cbj + (int64_t)l * L + s0 + c, lok);
-      const bf16x8 yv = frag_row(dy + ((t0 + l) * H + h) * P + p0 + c, lok && p0 + c < P);
+      const float avl = av[l];
       float mv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        // the mask selects the exponent (exp2 of -inf is 0), so no branch
+        // and nothing undefined enters the product
         const int sx = s0 + c + e;
-        mv[e] = (lok && l >= sx) ? static_cast<float>(cv[e]) * exp2_fast((av[l] - av[sx]) * kLog2e) : 0.f;
+        const float arg = (lok && l >= sx) ? (avl - av[sx]) * kLog2e : -INFINITY;
+        mv[e] = static_cast<float>(cv[e]) * exp2_fast(arg);
       }
+      const bf16x8 ycur = yv;
+      fetch(kb + 32);                      // past the chunk: zeros
       __syncthreads();                     // previous slice consumed
       *reinterpret_cast<bf16x8*>(&mt[kr * kKtPitch + c]) = Mfma<bf16>::pack(mv);
-      *reinterpret_cast<bf16x8*>(&yt[kr * kKtPitch + c]) = yv;
+      *reinterpret_cast<bf16x8*>(&yt[kr * kKtPitch + c]) = ycur;
       __syncthreads();
       mfma_kmajor(q, mt, yt, d);
     }
@@ -953,15 +981,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dx_tiled_kernel(
   const float Dh = D ? D[h] : 0.f;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
   static_assert(P % 4 == 0, "4-wide pieces of a row");
+  // the rows' loads first (rows past the chunk read its last row, columns
+  // past P its first piece; neither is stored), then the stores
+  float dsv[4];
+  float4 yv4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sx = min(s0 + tm + i, len - 1), pc = p0 + tn < P ? p0 + tn : 0;
+    dsv[i] = delta[jh * L + sx];
+    yv4[i] = load4_f32(dy + ((t0 + sx) * H + h) * P + pc);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int sx = s0 + tm + i;
     if (sx >= len || p0 + tn >= P) continue;
-    const float dsx = delta[jh * L + sx];
     const int64_t o = ((t0 + sx) * H + h) * P + p0 + tn;
-    const float4 y = load4_f32(dy + o);
-    store4(dx + o, dsx * acc[i][0] + Dh * y.x, dsx * acc[i][1] + Dh * y.y,
-           dsx * acc[i][2] + Dh * y.z, dsx * acc[i][3] + Dh * y.w);
+    const float4 y = yv4[i];
+    store4(dx + o, dsv[i] * acc[i][0] + Dh * y.x, dsv[i] * acc[i][1] + Dh * y.y,
+           dsv[i] * acc[i][2] + Dh * y.z, dsv[i] * acc[i][3] + Dh * y.w);
   }
 }
 
