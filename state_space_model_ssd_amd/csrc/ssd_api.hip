@@ -354,8 +354,8 @@ void bwd_layout_of(const ssd_problem_t* p, const ssd_workspace_layout_t& w, BwdL
   b->dS16 = off;       off = align_up(off + sizeof(uint16_t) * mc * H * PN);
   b->dcb = off;        off = align_up(off + sizeof(float) * mc * H * L * L);
   const size_t LT = L / 64, VX = 2 * ((N + 63) / 64);
-  b->rowpart = off;    off = align_up(off + sizeof(float) * mc * H * LT * L);
-  b->colpart = off;    off = align_up(off + sizeof(float) * mc * H * LT * L);
+  b->rowpart = off;    off = align_up(off + sizeof(float) * mc * H * 2 * LT * L);
+  b->colpart = off;    off = align_up(off + sizeof(float) * mc * H * 2 * LT * L);
   b->vxpart = off;     off = align_up(off + sizeof(float) * mc * H * VX * L);
   b->interpart = off;  off = align_up(off + sizeof(float) * mc * H * VX * L);
   b->ghpart = off;     off = align_up(off + sizeof(float) * mc * H * (PN / 256));

@@ -849,6 +849,194 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_tiled_kernel(
   }
 }
 
+// 3a, bf16 inputs: the same sums with the epilogue in the MFMA result
+// layout (each wave's 32 x 32 quarter: a lane holds rows wr + 16 mi +
+// 4 (lane / 16) + r of columns wc + 16 ni + lane % 16), so a head needs no
+// pass of the tile through LDS.  The partial sums go to two slots per tile,
+// one per half of its columns (rows) held by a wave:
+//   rowpart[2 st + wc / 32][l],  colpart[2 lt + wr / 32][s].
+// The head's dy and x rows of the tile and its running sums and steps are
+// staged in LDS, alternating between two buffers: one barrier per head.
+// The next head's rows (16-byte pieces, eight lanes per 128-byte row) and
+// factor values are loaded during the current head (buffer loads without
+// branches; rows past the chunk read zeros).
+template <int P, int L>
+__global__ __launch_bounds__(kBwdThreads) void bwd_v_mfma_kernel(
+    ChunkMap cm, int nslots, const bf16* __restrict__ x, const bf16* __restrict__ dy,
+    const bf16* __restrict__ cb, const float* __restrict__ delta, const float* __restrict__ dAcs, int H,
+    int G, int HB, float* __restrict__ dcbp, float* __restrict__ rowpart, float* __restrict__ colpart,
+    float* __restrict__ ddot) {
+  // per head: a at the tile's rows, a at its columns, delta at its columns
+  __shared__ __align__(16) float fac[2][3][64];
+  // per head: the tile's dy rows and x rows (P bf16 each, padded rows)
+  constexpr int RP = P + 8;
+  __shared__ __align__(16) bf16 ty[2][64 * RP], tx[2][64 * RP];
+  constexpr int LT = L / 64;
+  constexpr int NX = LT * (LT + 1) / 2;   // tiles on or below the diagonal
+  constexpr int KS = P / 32;
+  static_assert(P % 32 == 0, "k-steps of the rows");
+  const int2 ci = xcd_chunk_head(blockIdx.x, NX * G * HB);
+  if (ci.x >= nslots) return;
+  const int2 tt = lower_tile(ci.y % NX);
+  const int lt = __builtin_amdgcn_readfirstlane(tt.x), st = __builtin_amdgcn_readfirstlane(tt.y);
+  const int by = ci.y / NX;
+  const int g = by / HB, hb = by - (by / HB) * HB, j = ci.x;
+  const int hpg = H / G, h0 = g * hpg + hb * hpg / HB, h1 = g * hpg + (hb + 1) * hpg / HB;
+  const ChunkDesc cd = cm.desc(j);
+  const int len = max(cd.len, 0);
+  const int l0 = lt * 64, s0 = st * 64;
+  if (l0 >= len) return;
+  const int64_t t0 = cd.start;
+  const MfmaQuarter q;
+  const int lg = q.lane >> 4;
+  const bf16* cbj = cb + ((int64_t)j * G + g) * L * L;
+  // CB at this lane's 16 elements, 0 where V is not summed (s > l, rows past
+  // the chunk): the same for every head
+  float cbq[2][2][4];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int l = l0 + q.row(mi, r), sx = s0 + q.col(ni);
+        cbq[mi][ni][r] = (l < len && sx <= l) ? static_cast<float>(cbj[(int64_t)l * L + sx]) : 0.f;
+      }
+  f32x4 w[2][2];                           // this block's sum of delta_s V[l,s]
+  zero_quarter(w);
+  const __amdgpu_buffer_rsrc_t rdy =
+      buf_rsrc_u(dy + (t0 + l0) * H * P, (uint32_t)((int64_t)(len - l0) * H * P * sizeof(bf16)));
+  const __amdgpu_buffer_rsrc_t rx =
+      buf_rsrc_u(x + (t0 + s0) * H * P, (uint32_t)((int64_t)(len - s0) * H * P * sizeof(bf16)));
+  const int fk = min(threadIdx.x >> 6, 2), fi = threadIdx.x & 63;   // threads 192-255 repeat delta
+  constexpr int PR = P / 8;                // 16-byte pieces per row
+  constexpr int NP = 64 * PR / kBwdThreads;   // pieces of each tile per thread
+  static_assert(64 * PR % kBwdThreads == 0, "pieces of the row tiles");
+  bf16x8 py[NP], px[NP];
+  float fv;
+  auto fetch = [&](int h) {
+    const int64_t jh = (int64_t)j * H + h;
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int i = threadIdx.x + kBwdThreads * u, r = i / PR, c = (i % PR) * 8;
+      py[u] = frag_buf(rdy, (uint32_t)(((r * H + h) * P + c) * sizeof(bf16)));
+      px[u] = frag_buf(rx, (uint32_t)(((r * H + h) * P + c) * sizeof(bf16)));
+    }
+    fv = fk == 0 ? dAcs[jh * L + l0 + fi] : fk == 1 ? dAcs[jh * L + s0 + fi] : delta[jh * L + s0 + fi];
+  };
+  auto take = [&](int set) {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int i = threadIdx.x + kBwdThreads * u, r = i / PR, c = (i % PR) * 8;
+      *reinterpret_cast<bf16x8*>(&ty[set][r * RP + c]) = py[u];
+      *reinterpret_cast<bf16x8*>(&tx[set][r * RP + c]) = px[u];
+    }
+    fac[set][fk][fi] = fv;
+  };
+  const int RS = 2 * LT;                   // partial-sum slots per token
+  fetch(h0);
+  take(0);
+  for (int h = h0; h < h1; ++h) {
+    const int set = (h - h0) & 1;
+    const int64_t jh = (int64_t)j * H + h;
+    fetch(min(h + 1, h1 - 1));             // past the block's last head: that head again
+    // fac[set] written; the previous head's reads of fac[set ^ 1] are done
+    __syncthreads();
+    f32x4 d[2][2];
+    zero_quarter(d);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        a[u] = *reinterpret_cast<const bf16x8*>(&ty[set][(q.wr + u * 16 + q.lr) * RP + ks * 32 + q.kq]);
+        b[u] = *reinterpret_cast<const bf16x8*>(&tx[set][(q.wc + u * 16 + q.lr) * RP + ks * 32 + q.kq]);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) d[mi][ni] = Mfma<bf16>::mma(a[mi], b[ni], d[mi][ni]);
+    }
+    float rs[8], cs[2] = {0.f, 0.f};
+    float asv[2], dlv[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      asv[ni] = fac[set][1][q.col(ni)];
+      dlv[ni] = fac[set][2][q.col(ni)];
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const float4 al4 = *reinterpret_cast<const float4*>(&fac[set][0][q.row(mi, 0)]);
+      const float alv[4] = {al4.x, al4.y, al4.z, al4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int l = l0 + q.row(mi, r);
+        float rsum = 0.f;
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int sx = s0 + q.col(ni);
+          // the mask selects the exponent (exp2 of -inf is 0): no branch,
+          // and nothing undefined enters the sums
+          const float arg = (l < len && sx <= l) ? (alv[r] - asv[ni]) * kLog2e : -INFINITY;
+          const float v = exp2_fast(arg) * d[mi][ni][r];
+          const float dv = dlv[ni] * v;
+          w[mi][ni][r] += dv;
+          rsum += cbq[mi][ni][r] * dv;
+          cs[ni] += cbq[mi][ni][r] * v;
+        }
+        rs[4 * mi + r] = rsum;
+      }
+    }
+    // row sums over the wave's 32 columns: lane lr ends with one row
+    {
+      const float sum = row_sum16_x8(rs, q.lr);
+      const int rl = q.row(q.lr >> 3, 2 * ((q.lr >> 2) & 1) + ((q.lr >> 1) & 1));
+      const __amdgpu_buffer_rsrc_t rp =
+          buf_rsrc_u(rowpart + (jh * RS + 2 * st + (q.wc >> 5)) * L + l0, 64 * sizeof(float));
+      store_buf(rp, rl * sizeof(float), sum, (q.lr & 1) == 0);
+    }
+    // column sums over the wave's 32 rows: the lane groups hold 8 rows
+    // each; pairing across groups 0-1 / 2-3, lanes of group 2 lg' keep
+    // column ni = lg' / 2 ... one column per lane pair of groups
+    {
+      const bool hi = lg & 2;
+      float t = (hi ? cs[1] : cs[0]) + __shfl_xor(hi ? cs[0] : cs[1], 32);
+      t += __shfl_xor(t, 16);
+      const int cl = q.col(hi ? 1 : 0);
+      const __amdgpu_buffer_rsrc_t rc =
+          buf_rsrc_u(colpart + (jh * RS + 2 * lt + (q.wr >> 5)) * L + s0, 64 * sizeof(float));
+      store_buf(rc, cl * sizeof(float), t, (lg & 1) == 0);
+    }
+    // on the diagonal, V[l,l] before its decay (1) is dy_l . x_l: the
+    // per-token dot of dD (lanes whose column is one of their rows)
+    {
+      const __amdgpu_buffer_rsrc_t rdd = buf_rsrc_u(ddot + jh * L + l0, (uint32_t)((len - l0) * sizeof(float)));
+      const int rr = q.lr & 3;
+      const bool on = lt == st && q.wr == q.wc && (q.lr >> 2) == lg;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const f32x4 dd = d[mi][mi];
+        const float v = rr == 0 ? dd[0] : rr == 1 ? dd[1] : rr == 2 ? dd[2] : dd[3];
+        store_buf(rdd, q.row(mi, rr) * sizeof(float), v, on);
+      }
+    }
+    take(set ^ 1);                         // the next head's rows and factors
+  }
+  // the block's sum, rows in the chunk (w is 0 above the diagonal; entries
+  // there and past the chunk are never read)
+  float* W = dcbp + (((int64_t)j * G + g) * HB + hb) * L * L;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int l = l0 + q.row(mi, r);
+      if (l < len) {
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) W[(int64_t)l * L + s0 + q.col(ni)] = w[mi][ni][r];
+      }
+    }
+}
+
 // 3b. dx as 64 x 64 tiles of (token s, p):
 //   dx_s = delta_s [ sum_{l>=s} CB[l,s] exp(a_l - a_s) dy_l + exp(a_last - a_s) dS_j B_s ]
 //          + D dy_s;
@@ -1337,6 +1525,7 @@ __global__ __launch_bounds__(L) void bwd_token_kernel(
     float* __restrict__ dD_part, float* __restrict__ dbias_part) {
   __shared__ float red[3 * (L / kWave)];
   constexpr int LT = L / 64, VX = 2 * ((N + 63) / 64);   // row-dot slots per token
+  constexpr int RH = sizeof(T) == 2 ? 2 : 1;              // V partial-sum slots per tile
   const int h = blockIdx.x, j = blockIdx.y, k = threadIdx.x;
   const ChunkDesc cd = cm.desc(j);
   const int64_t jh = (int64_t)j * H + h;
@@ -1356,8 +1545,12 @@ __global__ __launch_bounds__(L) void bwd_token_kernel(
   const int64_t tk = cd.start + k;
   float rowsum = 0.f, sdir = 0.f, inter = 0.f, vxe = 0.f, dd = 0.f;
   if (valid) {
-    for (int st = 0; st <= k / 64; ++st) rowsum += rowpart[(jh * LT + st) * L + k];
-    for (int lt = k / 64; lt < LT && lt * 64 < len; ++lt) sdir += colpart[(jh * LT + lt) * L + k];
+    for (int st = 0; st <= k / 64; ++st)
+#pragma unroll
+      for (int u = 0; u < RH; ++u) rowsum += rowpart[(jh * LT * RH + st * RH + u) * L + k];
+    for (int lt = k / 64; lt < LT && lt * 64 < len; ++lt)
+#pragma unroll
+      for (int u = 0; u < RH; ++u) sdir += colpart[(jh * LT * RH + lt * RH + u) * L + k];
 #pragma unroll
     for (int v = 0; v < VX; ++v) {
       vxe += vxpart[(jh * VX + v) * L + k];
@@ -1465,9 +1658,14 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   // with 3a's workgroups (their partial sums fit the workspace's H L^2
   // floats per chunk: G * HB <= H)
   const int hpg = H / G, HB = bwd_head_blocks(hpg, (int64_t)(LT * (LT + 1) / 2) * G * mc);
-  hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * (LT + 1) / 2 * G * HB)),
-                     dim3(kBwdThreads), 0, s, cm, mc, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb,
-                     b.rowpart, b.colpart, b.ddot);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((bwd_v_mfma_kernel<P, L>), dim3(xcd_grid(mc, LT * (LT + 1) / 2 * G * HB)),
+                       dim3(kBwdThreads), 0, s, cm, mc, (const bf16*)x, (const bf16*)dy, (const bf16*)cb,
+                       a.delta, a.dAcs, H, G, HB, b.dcb, b.rowpart, b.colpart, b.ddot);
+  else
+    hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * (LT + 1) / 2 * G * HB)),
+                       dim3(kBwdThreads), 0, s, cm, mc, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb,
+                       b.rowpart, b.colpart, b.ddot);
   if (HB > 1)
     hipLaunchKernelGGL((bwd_dcb_sum_kernel<L>), dim3((L * L / 4 + kBwdThreads - 1) / kBwdThreads, G, mc),
                        dim3(kBwdThreads), 0, s, G, HB, b.dcb);

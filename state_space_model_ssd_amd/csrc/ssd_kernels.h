@@ -79,8 +79,8 @@ struct BwdArgs {
   void* dS16;               // [max_chunks][H][P*N] bf16: dS rounded once (bf16 inputs)
   float* dcb;               // [max_chunks][H][L][L] floats; holds [max_chunks][G][HB][L][L]: sums
                             // of delta_s exp(a_l - a_s) dy_l . x_s (s <= l) over head blocks
-  float* rowpart;           // [max_chunks][H][L/64][L]
-  float* colpart;           // [max_chunks][H][L/64][L]
+  float* rowpart;           // [max_chunks][H][L/64][halves][L] (halves: 2 for bf16, 1 for fp32)
+  float* colpart;           // [max_chunks][H][L/64][halves][L]
   float* vxpart;            // [max_chunks][H][2 ceil(N/64)][L]
   float* interpart;         // [max_chunks][H][2 ceil(N/64)][L]
   float* ghpart;            // [max_chunks][H][P*N / 256]: <dS_j, H_j> in pieces
