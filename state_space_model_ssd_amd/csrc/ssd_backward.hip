@@ -1312,10 +1312,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
         mfma_kmajor(q, at, bt, d);
       }
     }
-    // The state terms, head by head: the rows (dy or x, exact bf16, 16-byte
-    // pieces straight into operand registers) times the head's P x 64
-    // operand (the entering state or dS in bf16, staged k-major in one of
-    // two LDS buffers, so one barrier per head); the row factor exp(a_l) or
+    // The state terms, head by head: the rows (dy or x, exact bf16, staged
+    // in LDS from whole-line loads) times the head's P x 64 operand (the
+    // entering state or dS in bf16, staged k-major); both alternate between
+    // two LDS buffers, so one barrier per head; the row factor exp(a_l) or
     // exp(a_last - a_s) (and delta_s for dB) multiplies the product's rows.
     // Two register sets hold the rows, operand pieces and factors of the
     // next two heads, loaded while the current head is multiplied.
@@ -1323,6 +1323,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
     constexpr int PP = P * 8 / kBwdThreads;   // 16-byte operand pieces per thread
     static_assert(P % 32 == 0 && PP >= 1 && P * 8 % kBwdThreads == 0, "head operand pieces");
     __shared__ __align__(16) bf16 kt[2][P * kKtPitch];
+    // the head's rows (dy or x) of the tile, P bf16 each (padded rows)
+    constexpr int RPA = P + 8, PRA = P / 8, NPA = 64 * PRA / kBwdThreads;
+    static_assert(64 * PRA % kBwdThreads == 0, "pieces of the row tile");
+    __shared__ __align__(16) bf16 ta[2][64 * RPA];
     const bf16* K16 = which == 0 ? reinterpret_cast<const bf16*>(states_in) : dS16;
     const int h1 = h0 + hpg;
     // the chunk's rows (tokens past its end read zeros) and its heads'
@@ -1343,7 +1347,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
           const int row = m0 + q.row(mi, r), col = n0 + q.col(ni);
           mrow[mi][ni][r] = (row < len && col < N) ? ld(M + ((t0 + row) * G + g) * N + col) : 0.f;
         }
-    bf16x8 ra[2][KS][2], rk[2][PP];
+    bf16x8 ra[2][NPA], rk[2][PP];
     float fl[2];
     // the row factors: thread t loads a and delta of tile row t % 64 (rows
     // < L: inside the chunk's row of the workspace) and at each head writes
@@ -1355,11 +1359,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
     auto fetch = [&](int set, int h) {     // no branch: see frag_buf
       const int64_t jh = (int64_t)j * H + h;
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int m = m0 + q.wr + mi * 16 + q.lr;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ra[set][ks][mi] = frag_buf(rrow, (uint32_t)(((m * H + h) * P + ks * 32 + q.kq) * sizeof(T)));
+      for (int u = 0; u < NPA; ++u) {      // 16-byte pieces, PRA lanes per row
+        const int i = threadIdx.x + kBwdThreads * u, r = m0 + i / PRA, c = (i % PRA) * 8;
+        ra[set][u] = frag_buf(rrow, (uint32_t)(((r * H + h) * P + c) * sizeof(T)));
       }
       fa[set] = dAcs[jh * L + m0 + fr_row];
       fd[set] = delta[jh * L + m0 + fr_row];
@@ -1384,11 +1386,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
         const float gsum = which == 0 ? f : (ok ? fd[set] : 0.f) * f;
         fac[set][fr_k][fr_row] = fr_k ? gsum : f;   // threads 128-255 repeat 0-127
       }
-      bf16x8 aop[KS][2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) aop[ks][mi] = ra[set][ks][mi];
+      for (int u = 0; u < NPA; ++u) {
+        const int i = threadIdx.x + kBwdThreads * u;
+        *reinterpret_cast<bf16x8*>(&ta[set][(i / PRA) * RPA + (i % PRA) * 8]) = ra[set][u];
+      }
       fetch(set, min(h + 2, h1 - 1));      // past the group's last head: that head again
       __builtin_amdgcn_sched_barrier(0);   // keep the sets' loads in issue order
       __syncthreads();                     // this head's operand tile stored
@@ -1396,13 +1398,16 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
       zero_quarter(dh);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 b[2];
+        bf16x8 aop[2], b[2];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+          aop[mi] = *reinterpret_cast<const bf16x8*>(&ta[set][(q.wr + mi * 16 + q.lr) * RPA + ks * 32 + q.kq]);
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) b[ni] = lds_operand_kmajor(kb, kKtPitch, ks * 32, q.wc + ni * 16, q.lane);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-          for (int ni = 0; ni < 2; ++ni) dh[mi][ni] = Mfma<bf16>::mma(aop[ks][mi], b[ni], dh[mi][ni]);
+          for (int ni = 0; ni < 2; ++ni) dh[mi][ni] = Mfma<bf16>::mma(aop[mi], b[ni], dh[mi][ni]);
       }
       // the row dots (a row's 16 lanes hold its columns): lane lr ends with
       // row (mi, r) = (lr >> 3, 2 ((lr >> 2) & 1) + ((lr >> 1) & 1)), one
