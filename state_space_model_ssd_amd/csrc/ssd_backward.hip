@@ -1265,36 +1265,56 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
     zero_quarter(d);
     const int k0 = which == 0 ? 0 : m0, k1 = which == 0 ? min(len, m0 + 64) : len;
     const T* R = which == 0 ? B : C;       // rows k of the second operand
+    // The next slice's pieces are loaded while the current one is
+    // multiplied: buffer loads issued without a branch whichever the tile
+    // (a load a tile does not need aims past the records and reads zeros).
+    // dC: rows l = m0 + row of W, columns s = kb + kq ..; dB: rows l = k of
+    // W, columns s = m0 + c ..
+    const __amdgpu_buffer_rsrc_t rR = buf_rsrc_u(R + t0 * G * N, (uint32_t)((int64_t)len * G * N * sizeof(T)));
+    const __amdgpu_buffer_rsrc_t rW = buf_rsrc_u(W, (uint32_t)(L * L * sizeof(float)));
+    bf16x8 rvp;
+    uint4 wv[2][2];
+    auto fetch_intra = [&](int kb) {
+      const int k = kb + kr;
+      rvp = frag_buf(rR, (uint32_t)(((k * G + g) * N + n0 + c) * sizeof(T)), k < k1 && n0 + c < N);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int l = m0 + q.wr + mi * 16 + q.lr, s1 = kb + q.kq;
+        const uint32_t off = which == 0 ? (uint32_t)((l * L + s1) * sizeof(float))
+                                        : (uint32_t)((k * L + m0 + c) * sizeof(float));
+        const bool ok = which == 0 ? (l < len && s1 < k1) : (mi == 0 && k < k1);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) wv[mi][hf] = buf_load16(rW, ok ? off + 16 * hf : kPastRecords);
+      }
+    };
+    fetch_intra(k0);
     for (int kb = k0; kb < k1; kb += 32) {
       const int k = kb + kr;
-      const bf16x8 rv = frag_row(R + ((t0 + k) * G + g) * N + n0 + c, k < k1 && n0 + c < N);
-      bf16x8 av[2];
-      if (which == 0) {
-        // A rows l = m0 + row: dCB[l, kb + kq ..] for s <= l, straight from W
+      const bf16x8 rv = rvp;
+      uint4 wc[2][2];
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) wc[mi][hf] = wv[mi][hf];
+      fetch_intra(kb + 32);                // past k1: zeros
+      bf16x8 av[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        float u[8];
+        unpack16<float>(wc[mi][0], u);
+        unpack16<float>(wc[mi][1], u + 4);
+        float v[8];
+        if (which == 0) {
+          // A rows l = m0 + row: dCB[l, kb + kq ..] for s <= l
           const int l = m0 + q.wr + mi * 16 + q.lr, s1 = kb + q.kq;
-          const bool ok = l < len && s1 < k1;
-          const float* pw = W + (int64_t)l * L + s1;
-          const float4 u0 = ok ? *reinterpret_cast<const float4*>(pw) : make_float4(0.f, 0.f, 0.f, 0.f);
-          const float4 u1 = ok ? *reinterpret_cast<const float4*>(pw + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-          const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-          float v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = (s1 + e <= l && s1 + e < k1) ? u[e] : 0.f;
-          av[mi] = Mfma<bf16>::pack(v);
-        }
-      } else {
-        // rows l = k of W, columns s = m0 + c ..: dCB[l, s] for s <= l, k-major
-        const bool ok = k < k1;
-        const float* pw = W + (int64_t)k * L + m0 + c;
-        const float4 u0 = ok ? *reinterpret_cast<const float4*>(pw) : make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 u1 = ok ? *reinterpret_cast<const float4*>(pw + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-        float v[8];
+        } else {
+          // rows l = k: dCB[l, s] for s <= l, k-major
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (m0 + c + e <= k && m0 + c + e < len) ? u[e] : 0.f;
-        av[0] = Mfma<bf16>::pack(v);
+          for (int e = 0; e < 8; ++e) v[e] = (m0 + c + e <= k && m0 + c + e < len) ? u[e] : 0.f;
+        }
+        av[mi] = Mfma<bf16>::pack(v);
       }
       __syncthreads();                     // previous slice consumed
       *reinterpret_cast<bf16x8*>(&bt[kr * kKtPitch + c]) = rv;
