@@ -24,7 +24,8 @@
 //      ddelta_k += A sum_{l>=k} da_l and dA += sum_k delta_k sum_{l>=k} da_l,
 //      and ddt = ddelta softplus'(dt + dt_bias) where the clamp passes it.
 //   4. per group g (B and C are shared by its heads, so the intra-chunk
-//      parts contract dCB summed over the heads, once per group):
+//      parts contract dCB summed over the heads, once per group, and the
+//      state terms are one contraction over (head, p)):
 //      dC[l] = sum_{s<=l} (sum_h dCB_h[l,s]) B_s + sum_h exp(a_l) dy_l H,
 //      dB[s] = sum_{l>=s} (sum_h dCB_h[l,s]) C_l
 //              + sum_h delta_s exp(a_last - a_s) x_s dS_j;
@@ -32,12 +33,22 @@
 // Everything accumulates in fp32; dx, dB and dC are rounded once to x's
 // dtype.  Deterministic: fixed loop orders, no atomics.
 //
+// Launches: Q tiles (1, and each chunk's log-decay) -> reverse chain (2,
+// and <dS_j, H_j> in pieces) -> V tiles (3's intra sums, dCB summed over
+// head blocks) -> head-block sum of dCB -> dB/dC per group (4, and the inter
+// and state row dots of da per head) -> dx tiles -> per-token pass (3's
+// da, ddelta, ddt) -> per-head sums (5).
+//
 // The contractions are 64 x 64 output tiles.  With bf16 inputs they run on
-// the bf16 MFMA: rows read with 16-byte loads, or k-major slices staged in
-// LDS as bf16 and read with the gfx950 transpose read; an operand that is
+// the bf16 MFMA: a head's rows staged in LDS from whole-line loads, or
+// k-major slices read with the gfx950 transpose read; an operand that is
 // scaled or fp32 is rounded to bf16 once, and row factors are applied to
-// the product where they can be.  The fp32 path uses fp32 tiles on the
-// vector ALUs, staged through LDS with 16-byte loads.
+// the product where they can be.  Loops over heads or token slices load the
+// next step's operands while the current one is multiplied, with buffer
+// loads issued without branches (a branch around a load or store makes the
+// compiler wait for every outstanding load at the loop's head).  The fp32
+// path uses fp32 tiles on the vector ALUs, staged through LDS with 16-byte
+// loads.
 #include "ssd_kernels.h"
 
 namespace ssd {
