@@ -56,6 +56,9 @@ namespace ssd {
 namespace {
 
 constexpr int kBwdThreads = 256;
+// Largest |a_last| log2(e) of a chunk for which dx factors its decay
+// exp(a_l - a_s) into exp(a_l) exp(-a_s): both stay far inside fp32.
+constexpr float kBwdFastMaxLog2 = 64.f;
 // Most blocks a group's heads are split into for the summed dCB and the
 // dB/dC state terms.  More blocks: more workgroups in 3a and 4a, but more
 // partial sums written there and read in 3b' and 4b; the launcher takes the
@@ -1093,11 +1096,19 @@ __global__ __launch_bounds__(kBwdThreads, 8) void bwd_dx_tiled_kernel(
     mfma_rows<N>(q, B + ((t0 + s0) * G + g) * N, (int64_t)G * N, len - s0, dS16 + (jh * P + p0) * N, N,
                  P - p0, d);
     __syncthreads();                       // es, av staged
+    // Factored decay when the chunk's total decay is within 2^64 (uniform
+    // over the workgroup): exp(a_l - a_s) = exp(a_l) exp(-a_s), so the dy rows
+    // enter scaled by exp(a_l), the CB rows as stored (0 above the diagonal:
+    // no mask), and the product's rows are scaled by exp(-a_s) at the end --
+    // the state term by exp(a_last) now, to leave exp(a_last - a_s).
+    // Otherwise each CB element is masked with its decay.
+    const bool fast = fabsf(alast) * kLog2e <= kBwdFastMaxLog2;
+    const float ealast = exp2_fast(alast * kLog2e);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float f = es[s0 + q.row(mi, r)];
+        const float f = fast ? ealast : es[s0 + q.row(mi, r)];
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) d[mi][ni][r] *= f;
       }
@@ -1119,22 +1130,44 @@ __global__ __launch_bounds__(kBwdThreads, 8) void bwd_dx_tiled_kernel(
       const int l = kb + kr;
       const bool lok = l < len;
       const float avl = av[l];
-      float mv[8];
+      bf16x8 mcur, ycur;
+      if (fast) {
+        mcur = cv;
+        // rows past the chunk: factor 0 (their a is not defined)
+        const float el = lok ? exp2_fast(avl * kLog2e) : 0.f;
+        float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // the mask selects the exponent (exp2 of -inf is 0), so no branch
-        // and nothing undefined enters the product
-        const int sx = s0 + c + e;
-        const float arg = (lok && l >= sx) ? (avl - av[sx]) * kLog2e : -INFINITY;
-        mv[e] = static_cast<float>(cv[e]) * exp2_fast(arg);
+        for (int e = 0; e < 8; ++e) v[e] = el * static_cast<float>(yv[e]);
+        ycur = Mfma<bf16>::pack(v);
+      } else {
+        float mv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // the mask selects the exponent (exp2 of -inf is 0), so no branch
+          // and nothing undefined enters the product
+          const int sx = s0 + c + e;
+          const float arg = (lok && l >= sx) ? (avl - av[sx]) * kLog2e : -INFINITY;
+          mv[e] = static_cast<float>(cv[e]) * exp2_fast(arg);
+        }
+        mcur = Mfma<bf16>::pack(mv);
+        ycur = yv;
       }
-      const bf16x8 ycur = yv;
       fetch(kb + 32);                      // past the chunk: zeros
       __syncthreads();                     // previous slice consumed
-      *reinterpret_cast<bf16x8*>(&mt[kr * kKtPitch + c]) = Mfma<bf16>::pack(mv);
+      *reinterpret_cast<bf16x8*>(&mt[kr * kKtPitch + c]) = mcur;
       *reinterpret_cast<bf16x8*>(&yt[kr * kKtPitch + c]) = ycur;
       __syncthreads();
       mfma_kmajor(q, mt, yt, d);
+    }
+    if (fast) {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float f = exp2_fast(-av[s0 + q.row(mi, r)] * kLog2e);
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) d[mi][ni][r] *= f;
+        }
     }
     quarter_to_thread(q, d, acc, As, Bs);
   } else {

@@ -86,6 +86,20 @@ def test_backward_long_memory_small_steps():
     _grads_case(prob, Recipe(dt_bias="inv_softplus_uniform", init_std=0.5), seed=9)
 
 
+@pytest.mark.parametrize("shape,lens", [((1, 520, 4, 64, 128, 2, 256, "bf16"), None),
+                                        ((2, 130, 4, 32, 32, 2, 64, "bf16"), None),
+                                        ((1, 230, 2, 32, 32, 1, 64, "bf16"), (100, 1, 64, 65))],
+                         ids=["L256", "L64", "packed"])
+def test_backward_small_steps_bf16(shape, lens):
+    # small steps (dt near dt_bias in [1e-3, 1e-1]): every chunk's total
+    # decay stays within 2^64, so dx takes its factored-decay path (dy rows
+    # scaled by exp(a_l), CB unmasked, rows rescaled by exp(-a_s)); the
+    # default recipe's larger steps exercise the masked path
+    b, T, H, P, N, G, L, dt = shape
+    prob = Problem(b, T, H, P, N, G, L, dt, seq_lens=lens)
+    _grads_case(prob, Recipe(dt_bias="inv_softplus_uniform", dt_shift=-4.0, init_std=0.3), seed=T + L)
+
+
 @pytest.mark.parametrize("lens,L,dt", [((100, 1, 64, 65), 64, "bf16"), ((70, 200, 3), 64, "f32")],
                          ids=lambda v: str(v))
 def test_backward_packed(lens, L, dt):
