@@ -546,6 +546,91 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_tiled_kernel(
   }
 }
 
+// 1, bf16 inputs: one workgroup per (chunk, head, 64 rows p) computes all
+// N columns, so the chunk's dy rows are loaded and scaled once: wave w holds
+// rows 32 (w / 2) .. of columns 64 (w % 2) .. (2 x 4 MFMA tiles).  Slices
+// of 32 tokens l: exp(a_l) dy_l (rounded once) and C_l staged k-major in LDS,
+// the next slice's rows loaded while the current one is multiplied.
+template <int P, int N, int L>
+__global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(
+    ChunkMap cm, int nslots, const bf16* __restrict__ dy, const bf16* __restrict__ C,
+    const float* __restrict__ dAcs, int H, int G, float* __restrict__ Q, float* __restrict__ dla) {
+  constexpr int PT = (P + 63) / 64;
+  constexpr int NT = (N + 63) / 64;
+  static_assert(NT <= 2, "one or two 64-column halves");
+  __shared__ float sc[L];
+  __shared__ __align__(16) bf16 yt[32 * kKtPitch], ct[NT][32 * kKtPitch];
+  const int2 ci = xcd_chunk_head(blockIdx.x, PT * H);
+  if (ci.x >= nslots) return;
+  const int pt = ci.y % PT, m0 = pt * 64;
+  const int h = ci.y / PT, j = ci.x, g = h / (H / G);
+  const ChunkDesc cd = cm.desc(j);
+  const int64_t jh = (int64_t)j * H + h;
+  for (int l = threadIdx.x; l < L; l += kBwdThreads) sc[l] = exp2_fast(dAcs[jh * L + l] * kLog2e);
+  if (pt == 0 && threadIdx.x == 0) dla[jh] = cd.len > 0 ? dAcs[jh * L + cd.len - 1] : 0.f;
+  __syncthreads();
+  static_assert(32 * 8 == kBwdThreads, "one 8-wide piece of each slice tile per thread");
+  const int lane = threadIdx.x & (kWave - 1), w = wave_id();
+  const int wr = (w >> 1) * 32, half = w & 1;
+  const int len = max(cd.len, 0), kr = threadIdx.x >> 3, c = (threadIdx.x & 7) * 8;
+  const __amdgpu_buffer_rsrc_t rdy =
+      buf_rsrc_u(dy + (int64_t)cd.start * H * P, (uint32_t)((int64_t)len * H * P * sizeof(bf16)));
+  const __amdgpu_buffer_rsrc_t rc =
+      buf_rsrc_u(C + (int64_t)cd.start * G * N, (uint32_t)((int64_t)len * G * N * sizeof(bf16)));
+  f32x4 d[2][4];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) d[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 yv, cv[NT];
+  auto fetch = [&](int kb) {
+    const int l = kb + kr;
+    yv = frag_buf(rdy, (uint32_t)(((l * H + h) * P + m0 + c) * sizeof(bf16)), m0 + c < P);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      cv[t] = frag_buf(rc, (uint32_t)(((l * G + g) * N + 64 * t + c) * sizeof(bf16)), 64 * t + c < N);
+  };
+  if (len > 0) fetch(0);
+  for (int kb = 0; kb < len; kb += 32) {
+    const int l = kb + kr;
+    const float f = l < len ? sc[l] : 0.f;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = f * static_cast<float>(yv[e]);
+    bf16x8 ccur[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ccur[t] = cv[t];
+    fetch(kb + 32);                        // past the chunk: zeros
+    __syncthreads();                       // previous slice consumed
+    *reinterpret_cast<bf16x8*>(&yt[kr * kKtPitch + c]) = Mfma<bf16>::pack(v);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<bf16x8*>(&ct[t][kr * kKtPitch + c]) = ccur[t];
+    __syncthreads();
+    if (half < NT) {                       // wave-uniform: N = 64 leaves the second half idle
+      bf16x8 a[2], b[4];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) a[mi] = lds_operand_kmajor(yt, kKtPitch, 0, wr + mi * 16, lane);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) b[ni] = lds_operand_kmajor(ct[half], kKtPitch, 0, ni * 16, lane);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) d[mi][ni] = Mfma<bf16>::mma(a[mi], b[ni], d[mi][ni]);
+    }
+  }
+  if (half >= NT) return;
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = m0 + wr + mi * 16 + 4 * lg + r, n = 64 * half + ni * 16 + lr;
+        if (p < P && n < N) Q[(jh * P + p) * N + n] = d[mi][ni][r];
+      }
+}
+
 // Four consecutive values rounded once to T (8- or 16-byte store).
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
@@ -1714,8 +1799,13 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   const T* cb = (const T*)a.cb;
   const T* hin = (const T*)a.states_in;
   constexpr int NT = (N + 63) / 64;
-  hipLaunchKernelGGL((bwd_q_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, ((P + 63) / 64) * NT * H)),
-                     dim3(kBwdThreads), 0, s, cm, mc, dy, C, a.dAcs, H, G, b.Q, b.dla);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((bwd_q_mfma_kernel<P, N, L>), dim3(xcd_grid(mc, ((P + 63) / 64) * H)),
+                       dim3(kBwdThreads), 0, s, cm, mc, (const bf16*)dy, (const bf16*)C, a.dAcs, H, G, b.Q,
+                       b.dla);
+  else
+    hipLaunchKernelGGL((bwd_q_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, ((P + 63) / 64) * NT * H)),
+                       dim3(kBwdThreads), 0, s, cm, mc, dy, C, a.dAcs, H, G, b.Q, b.dla);
   static_assert((P * N) % 4 == 0, "four state elements per thread");
   static_assert(PN % (4 * kWave) == 0, "whole waves of the chain");
   hipLaunchKernelGGL((bwd_chain_kernel<T>), dim3((PN / 4 + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
