@@ -298,14 +298,6 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
     for (int k = 0; k < NK; ++k)
       fc[i][k] = __builtin_bit_cast(bf16x8, buf_load16(rc, ((uint32_t)lrow[i] * GN + 32 * k + kq) * 2u));
   const auto rcb = buf_rsrc(cb + ((int64_t)T.j * G + g) * L * L, L * L * 2);
-  // CB ring loads are issued whether or not the row group still has the
-  // step (a load it does not need aims past the records and reads zeros):
-  // a load under a branch would make the compiler wait for every load in
-  // flight where the branches join, which would undo the ring.
-  constexpr uint32_t kNoCb = 0x80000000u;
-  auto cb_piece = [&](int i, int q, bool ok) {
-    return __builtin_bit_cast(bf16x8, buf_load16<CBAUX>(rcb, ok ? ((uint32_t)lrow[i] * L + kq + 32 * q) * 2u : kNoCb));
-  };
 
   // ---- stage x as loaded (swizzled; rows past the end arrived as zeros),
   // the state, the running sums and the per-token factors
@@ -317,9 +309,7 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
 #pragma unroll
   for (int u = 0; u < HU; ++u) {
     const int i = tid + NT * u, r = i / HPR, c = i % HPR;
-    // (when the pieces divide evenly, no guard: a store under a branch would
-    // pull its load under the branch too)
-    if ((P * HPR) % NT == 0 || i < P * HPR) *reinterpret_cast<uint4*>(&hsm[r * HP + c * 8]) = hv[u];
+    if (i < P * HPR) *reinterpret_cast<uint4*>(&hsm[r * HP + c * 8]) = hv[u];
   }
   {
     const float a2 = dA_t * kLog2e;
@@ -359,7 +349,9 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
 #pragma unroll
     for (int i = 0; i < RGW; ++i)
 #pragma unroll
-      for (int q = 0; q < RM - 1; ++q) mring[i][q] = cb_piece(i, q, q < nq[i]);
+      for (int q = 0; q < RM - 1; ++q)
+        if (q < nq[i])                     // wave-uniform
+          mring[i][q] = __builtin_bit_cast(bf16x8, buf_load16<CBAUX>(rcb, ((uint32_t)lrow[i] * L + kq + 32 * q) * 2u));
   }
 
   if constexpr (FAST) {
@@ -398,7 +390,9 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
 #pragma unroll
     for (int i = 0; i < RGW; ++i)
 #pragma unroll
-      for (int q = 0; q < RD - 1; ++q) ring[i][q] = cb_piece(i, q, q < nq[i]);
+      for (int q = 0; q < RD - 1; ++q)
+        if (q < nq[i])                     // wave-uniform
+          ring[i][q] = __builtin_bit_cast(bf16x8, buf_load16<CBAUX>(rcb, ((uint32_t)lrow[i] * L + kq + 32 * q) * 2u));
     __syncthreads();                       // x as loaded is no longer read
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
@@ -423,7 +417,10 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
       if (a == 0) {
         if (q >= nq_wave) break;           // wave-uniform
 #pragma unroll
-        for (int i = 0; i < RGW; ++i) ring[i][(q + RD - 1) % RD] = cb_piece(i, q + RD - 1, q + RD - 1 < nq[i]);
+        for (int i = 0; i < RGW; ++i)
+          if (q + RD - 1 < nq[i])          // wave-uniform
+            ring[i][(q + RD - 1) % RD] = __builtin_bit_cast(
+                bf16x8, buf_load16<CBAUX>(rcb, ((uint32_t)lrow[i] * L + kq + 32 * (q + RD - 1)) * 2u));
 #pragma unroll
         for (int i = 0; i < RGW; ++i)
           if (q < nq[i]) fb[i] = ring[i][q % RD];
@@ -457,7 +454,10 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
       for (int q = 0; q < NQ; ++q) {
         if (q >= nq_wave) break;           // wave-uniform
 #pragma unroll
-        for (int i = 0; i < RGW; ++i) mring[i][(q + RM - 1) % RM] = cb_piece(i, q + RM - 1, q + RM - 1 < nq[i]);
+        for (int i = 0; i < RGW; ++i)
+          if (q + RM - 1 < nq[i])          // wave-uniform
+            mring[i][(q + RM - 1) % RM] = __builtin_bit_cast(
+                bf16x8, buf_load16<CBAUX>(rcb, ((uint32_t)lrow[i] * L + kq + 32 * (q + RM - 1)) * 2u));
         bf16x8 fm[RGW];
 #pragma unroll
         for (int i = 0; i < RGW; ++i)
