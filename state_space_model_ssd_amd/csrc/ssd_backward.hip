@@ -69,76 +69,9 @@ constexpr int kBwdMinWgPerCu = 2;
 template <typename T>
 __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
 
-// A 64 x 64 fp32 output tile of sum_k A(m, k) B(k, n) for k in [k0, k1),
-// accumulated into acc (4 x 4 per thread of 256).  Operand slices of 32
-// k-values pass through registers into LDS: As[k][m] and Bs[k][n] (row pitch
-// 68 floats).  PF: the next slice is loaded while the current one is
-// multiplied (more registers; pays off where occupancy has room).
-// A_KFAST: A(m, k) is contiguous in k (else in m); B(k, n) is read with n
-// fastest.  The loaders return 0 outside the operands.
+// 64 x 64 fp32 tiles on the vector ALUs (the fp32 path): operand slices
+// staged in LDS as S[k * kGemmPitch + i], 4 x 4 outputs per thread of 256.
 constexpr int kGemmPitch = 68;
-
-template <bool A_KFAST, bool B_KFAST = false, bool PF = false, typename LA, typename LB>
-__device__ __forceinline__ void gemm_tile(int k0, int k1, LA loadA, LB loadB, float (&acc)[4][4],
-                                          float* As, float* Bs) {
-  const int tid = threadIdx.x;
-  const int tm = (tid >> 4) * 4, tn = (tid & 15) * 4;
-  constexpr int E = 64 * 32 / kBwdThreads;   // operand elements per thread and slice
-  float ra[E], rb[E];
-  auto fetch = [&](int kb) {
-#pragma unroll
-    for (int u = 0; u < E; ++u) {
-      const int i = tid + kBwdThreads * u;
-      int m, k;
-      if constexpr (A_KFAST) { m = i >> 5; k = i & 31; } else { k = i >> 6; m = i & 63; }
-      ra[u] = kb + k < k1 ? loadA(m, kb + k) : 0.f;
-      int kk, n;
-      if constexpr (B_KFAST) { n = i >> 5; kk = i & 31; } else { kk = i >> 6; n = i & 63; }
-      rb[u] = kb + kk < k1 ? loadB(kb + kk, n) : 0.f;
-    }
-  };
-  if constexpr (PF) {
-    __syncthreads();                       // what the caller staged for the loaders
-    if (k0 < k1) fetch(k0);
-  }
-  for (int kb = k0; kb < k1; kb += 32) {
-    __syncthreads();                       // previous slice consumed
-    if constexpr (PF) {
-#pragma unroll
-      for (int u = 0; u < E; ++u) {
-        const int i = tid + kBwdThreads * u;
-        int m, k;
-        if constexpr (A_KFAST) { m = i >> 5; k = i & 31; } else { k = i >> 6; m = i & 63; }
-        As[k * kGemmPitch + m] = ra[u];
-        int kk, n;
-        if constexpr (B_KFAST) { n = i >> 5; kk = i & 31; } else { kk = i >> 6; n = i & 63; }
-        Bs[kk * kGemmPitch + n] = rb[u];
-      }
-    } else {
-      for (int i = tid; i < 64 * 32; i += kBwdThreads) {
-        int m, k;
-        if constexpr (A_KFAST) { m = i >> 5; k = i & 31; } else { k = i >> 6; m = i & 63; }
-        As[k * kGemmPitch + m] = kb + k < k1 ? loadA(m, kb + k) : 0.f;
-        int kk, n;
-        if constexpr (B_KFAST) { n = i >> 5; kk = i & 31; } else { kk = i >> 6; n = i & 63; }
-        Bs[kk * kGemmPitch + n] = kb + kk < k1 ? loadB(kb + kk, n) : 0.f;
-      }
-    }
-    __syncthreads();
-    if constexpr (PF)
-      if (kb + 32 < k1) fetch(kb + 32);
-#pragma unroll 8
-    for (int k = 0; k < 32; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(&As[k * kGemmPitch + tm]);
-      const float4 b = *reinterpret_cast<const float4*>(&Bs[k * kGemmPitch + tn]);
-      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jn = 0; jn < 4; ++jn) acc[i][jn] += av[i] * bv[jn];
-    }
-  }
-}
 
 template <typename T>
 __device__ __forceinline__ void load16_f32(const T* p, bool ok, float* v);
@@ -146,13 +79,6 @@ template <>
 __device__ __forceinline__ void load16_f32<float>(const float* p, bool ok, float* v) {
   const float4 t = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
   v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-}
-template <>
-__device__ __forceinline__ void load16_f32<bf16>(const bf16* p, bool ok, float* v) {
-  const uint4 t = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
-  const bf16x8 b = __builtin_bit_cast(bf16x8, t);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(b[e]);
 }
 
 // One KS-long slice (k in [kb, kb + KS)) of a 64-wide GEMM operand staged in
@@ -199,7 +125,6 @@ __device__ __forceinline__ void stage_slice(const T* p, int64_t stride, int ni, 
 
 // acc += A B over k in [k0, k1) for a 64 x 64 tile, both operands staged
 // per slice by stage_slice (A's i = m, B's i = n; TRI and ioff mask A).
-// Products and their order are those of gemm_tile.
 template <typename TA, bool AK, typename TB, bool BK, int KS = 32, int TRI = 0>
 __device__ __forceinline__ void gemm_staged(const TA* pa, int64_t sa, int na, const float* scale_a,
                                             const TB* pb, int64_t sb, int nb, int k0, int k1,
@@ -250,18 +175,9 @@ __device__ __forceinline__ void zero_quarter(f32x4 (&d)[2][2]) {
     for (int ni = 0; ni < 2; ++ni) d[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// 8 consecutive values of an fp32 row as a bf16 operand (rounded once).
-__device__ __forceinline__ bf16x8 frag_f32(const float* p, bool ok) {
-  float v[8];
-  const float4 a = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-  const float4 b = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  return Mfma<bf16>::pack(v);
-}
 __device__ __forceinline__ bf16x8 frag_row(const bf16* p, bool ok) {
   return __builtin_bit_cast(bf16x8, load16(p, ok));
 }
-__device__ __forceinline__ bf16x8 frag_row(const float* p, bool ok) { return frag_f32(p, ok); }
 
 // 16 bytes at byte offset off of a buffer resource, or zeros when !ok.  The
 // load is issued whatever ok is (the offset of a lane without data lies
@@ -279,9 +195,6 @@ constexpr uint32_t kPastRecords = 0x80000000u;
 // the other prefetches.
 __device__ __forceinline__ float ld_vmem(const float* p) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(p, 4), 0u, 0, 0));
-}
-__device__ __forceinline__ int4 ld_vmem(const int4* p) {
-  return __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(p, 16), 0u, 0, 0));
 }
 // A buffer resource whose base and size are the workgroup's (read from the
 // first lane): the compiler cannot always prove a workgroup-wide address
@@ -329,12 +242,12 @@ __device__ __forceinline__ void quarter_to_thread(const MfmaQuarter& q, const f3
   }
 }
 
-// d += A B^T over k < K, A(m, k) = arow[m * astride + k] (bf16 rows) and
-// B^T(n, k) = brow[n * bstride + k] (bf16 or fp32 rows, fp32 rounded once to
-// bf16), both from 16-byte loads; rows at or past na (nb) read as 0.
-template <int K, typename TB>
+// d += A B^T over k < K, A(m, k) = arow[m * astride + k] and B^T(n, k) =
+// brow[n * bstride + k] (bf16 rows), both from 16-byte loads; rows at or
+// past na (nb) read as 0.
+template <int K>
 __device__ __forceinline__ void mfma_rows(const MfmaQuarter& q, const bf16* arow, int64_t astride,
-                                          int na, const TB* brow, int64_t bstride, int nb,
+                                          int na, const bf16* brow, int64_t bstride, int nb,
                                           f32x4 (&d)[2][2]) {
   using M = Mfma<bf16>;
   static_assert(K % M::K == 0, "row length");
@@ -373,30 +286,6 @@ __device__ __forceinline__ void mfma_kmajor(const MfmaQuarter& q, const bf16* at
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) d[mi][ni] = M::mma(a[mi], b[ni], d[mi][ni]);
-}
-
-// d += A B with A^T(m, k) = arow rows as in mfma_rows and B(k, n) from the
-// k-major bf16 LDS tile bt[k * kKtPitch + n], k < K.
-template <int K>
-__device__ __forceinline__ void mfma_rows_kmajor(const MfmaQuarter& q, const bf16* arow,
-                                                 int64_t astride, int na, const bf16* bt,
-                                                 f32x4 (&d)[2][2]) {
-  using M = Mfma<bf16>;
-#pragma unroll
-  for (int k0 = 0; k0 < K; k0 += M::K) {
-    bf16x8 a[2], b[2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int r = q.wr + mi * 16 + q.lr;
-      a[mi] = frag_row(arow + r * astride + k0 + q.kq, r < na);
-    }
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) b[ni] = lds_operand_kmajor(bt, kKtPitch, k0, q.wc + ni * 16, q.lane);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) d[mi][ni] = M::mma(a[mi], b[ni], d[mi][ni]);
-  }
 }
 
 // Lower-triangular tile index t -> (row tile, column tile <= row tile).
@@ -768,12 +657,6 @@ template <>
 __device__ __forceinline__ void unpack16<float>(const uint4& u, float* v) {
   v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
   v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
-}
-template <>
-__device__ __forceinline__ void unpack16<bf16>(const uint4& u, float* v) {
-  const bf16x8 b = __builtin_bit_cast(bf16x8, u);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(b[e]);
 }
 
 // 3a. For each head, V[l,s] = exp(a_l - a_s) (dy_l . x_s) for s <= l as
