@@ -69,6 +69,39 @@ template <> struct NormVec<float> {
   }
 };
 
+// v plus the value of the lane that DPP control CTRL selects.
+template <int CTRL>
+__device__ __forceinline__ float dpp_xadd(float v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false);
+  return v + __builtin_bit_cast(float, o);
+}
+
+// run_sum's butterfly (lane i adds lane i ^ off, off = 1, 2, 4, ... below n),
+// the same additions in the same order and so the same result bit for bit,
+// with the exchanges in registers instead of LDS permutes.  Lanes ^1 and ^2
+// come by quad permutes; ^4 and ^8 by mirroring within 8 and 16 lanes, which
+// reaches a lane holding the same value once the smaller runs agree.  Then
+// every row of 16 lanes holds one value r0..r3, so the ^16 step gives
+// r0 + r1 in the lower half and r2 + r3 in the upper one (a lane's own row
+// plus its partner's, in either order the same sum) and the ^32 step their
+// sum.  n: a power of two <= 64, the same in every lane.
+__device__ __forceinline__ float run_sum_dpp(float v, int n) {
+  if (n > 1) v = dpp_xadd<0xb1>(v);    // quad_perm [1,0,3,2]
+  if (n > 2) v = dpp_xadd<0x4e>(v);    // quad_perm [2,3,0,1]
+  if (n > 4) v = dpp_xadd<0x141>(v);   // row_half_mirror
+  if (n > 8) v = dpp_xadd<0x140>(v);   // row_mirror
+  if (n > 16) {
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    const float lo = r0 + r1, hi = r2 + r3;
+    v = n > 32 ? lo + hi : ((threadIdx.x & 32) ? hi : lo);
+  }
+  return v;
+}
+
 // Group sums of s[k] (this thread's vector t + TH k), in place.  `chunk`
 // is LDS scratch of KT * TH / 64 floats, nchunks (<= KT * TH / 64) the row's
 // 64-vector chunks; every thread of the workgroup must call it (it holds a
@@ -79,13 +112,13 @@ __device__ __forceinline__ void group_sums(float (&s)[KT], int NV, int nchunks, 
   constexpr int NW = TH / 64;
   if (NV <= 64) {
 #pragma unroll
-    for (int k = 0; k < KT; ++k) s[k] = run_sum(s[k], NV);
+    for (int k = 0; k < KT; ++k) s[k] = run_sum_dpp(s[k], NV);
     return;
   }
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
-    const float c = run_sum(s[k], 64);      // chunk q = NW k + w
+    const float c = run_sum_dpp(s[k], 64);  // chunk q = NW k + w
     if (lane == 0) chunk[NW * k + w] = c;
   }
   __syncthreads();
@@ -108,25 +141,58 @@ __device__ __forceinline__ void launder(uint4& q) {
   asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
 }
 
-// Row r's vectors of y, z (and d, if given) owned by thread t; zeros for a
-// row past the end or a vector past the row's last.
-template <int KT, int TH, int V, typename T>
+// Offset for a lane with nothing to load or store: past every resource's
+// records, so the load reads zeros and the store is dropped.
+constexpr uint32_t kNormPast = 0x80000000u;
+
+// Byte offset of thread t's vector k in a row, or kNormPast past the row's last.
+template <int TH>
+__device__ __forceinline__ uint32_t vec_off(int t, int k, int nvec) {
+  const int v = t + TH * k;
+  return v < nvec ? (uint32_t)v * 16u : kNormPast;
+}
+
+// Row r's vectors of y, z (and dout, with D) owned by thread t, through
+// resources over the row: a row past the end has no records and a vector past
+// the row's last is aimed past them, so both read as zeros without a branch
+// around the loads (a branch would make the first use of any load in flight,
+// the next row's included, wait for all of them).
+template <int KT, int TH, bool D, typename T>
 __device__ __forceinline__ void load_row(const T* y, const T* z, const T* d, int64_t r,
                                          int64_t rows, int C, int nvec, int t, uint4 (&yv)[KT],
-                                         uint4 (&zv)[KT], uint4* dv) {
+                                         uint4 (&zv)[KT], uint4 (&dv)[KT]) {
+  const bool in = r < rows;
+  const int64_t o = in ? r * C : 0;
+  const uint32_t bytes = in ? (uint32_t)C * (uint32_t)sizeof(T) : 0u;
+  const auto ry = buf_rsrc(y + o, bytes), rz = buf_rsrc(z + o, bytes);
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
-    const int v = t + TH * k;
-    const bool ok = r < rows && v < nvec;
-    const int64_t o = r * C + (int64_t)v * V;
-    yv[k] = ok ? *reinterpret_cast<const uint4*>(y + o) : make_uint4(0, 0, 0, 0);
-    zv[k] = ok ? *reinterpret_cast<const uint4*>(z + o) : make_uint4(0, 0, 0, 0);
-    if (d) dv[k] = ok ? *reinterpret_cast<const uint4*>(d + o) : make_uint4(0, 0, 0, 0);
+    const uint32_t off = vec_off<TH>(t, k, nvec);
+    yv[k] = buf_load16(ry, off);
+    zv[k] = buf_load16(rz, off);
+    if constexpr (D) dv[k] = buf_load16(buf_rsrc(d + o, bytes), off);
   }
 }
 
-__device__ __forceinline__ void load_w(const float* w, int v, int nvec, float* wv, int V) {
-  for (int e = 0; e < V; ++e) wv[e] = v < nvec ? w[v * V + e] : 0.f;
+// The weights of thread t's vectors (zeros past the row's last).
+template <int KT, int TH, int V>
+__device__ __forceinline__ void load_w(const float* w, int C, int nvec, int t,
+                                       float (&wv)[KT][V]) {
+  const auto rw = buf_rsrc(w, (uint32_t)C * 4u);
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    const uint32_t off = vec_off<TH>(t, k, nvec);
+    // V floats per vector: V / 4 loads of 16 bytes (a vector's channels lie at
+    // V * sizeof(T) = 16 bytes of T, V * 4 bytes of w)
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      const uint4 u = buf_load16(rw, off == kNormPast ? kNormPast : off * (V / 4) + 16u * q);
+      wv[k][4 * q + 0] = __builtin_bit_cast(float, u.x);
+      wv[k][4 * q + 1] = __builtin_bit_cast(float, u.y);
+      wv[k][4 * q + 2] = __builtin_bit_cast(float, u.z);
+      wv[k][4 * q + 3] = __builtin_bit_cast(float, u.w);
+    }
+  }
 }
 
 template <typename T, int KT, int TH>
@@ -139,11 +205,20 @@ __global__ __launch_bounds__(TH) void gated_norm_fwd_kernel(
   const int t = threadIdx.x;
   const int nvec = C / V, NV = GS / V, ng = C / GS;
   const float inv_gs = 1.f / (float)GS;
+  float wr[KT][V];                          // the weights of this thread's channels
+  load_w<KT, TH, V>(w, C, nvec, t, wr);
+  // r per group, stored by the group's first vector (no records without rstd)
+  uint32_t roff[KT];
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    const int v = t + TH * k;
+    roff[k] = (v < nvec && v % NV == 0) ? (uint32_t)(v / NV) * 4u : kNormPast;
+  }
   int par = 0;                              // LDS buffer of this row's group sums
 #pragma unroll 1
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x, par ^= 1) {
-    uint4 yv[KT], zv[KT];
-    load_row<KT, TH, V>(y, z, static_cast<const T*>(nullptr), r, rows, C, nvec, t, yv, zv, nullptr);
+    uint4 yv[KT], zv[KT], unused[KT];
+    load_row<KT, TH, false>(y, z, y, r, rows, C, nvec, t, yv, zv, unused);
     float g[KT][V], s[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
@@ -153,17 +228,16 @@ __global__ __launch_bounds__(TH) void gated_norm_fwd_kernel(
       s[k] = gate_values<V>(yf, zf, g[k]);
     }
     group_sums<KT, TH>(s, NV, (nvec + 63) / 64, chunk + par * NCH);
+    const auto ro = buf_rsrc(out + r * C, (uint32_t)C * (uint32_t)sizeof(T));
+    const auto rr = rstd ? buf_rsrc(rstd + r * ng, (uint32_t)ng * 4u) : buf_rsrc(out, 0u);
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-      const int v = t + TH * k;
-      if (v >= nvec) continue;
       const float rs = gate_rstd(s[k], inv_gs, eps);
-      float wv[V], o[V];
-      load_w(w, v, nvec, wv, V);
+      float o[V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) o[e] = (g[k][e] * rs) * wv[e];
-      *reinterpret_cast<uint4*>(out + r * C + v * V) = NVc::pack(o);
-      if (rstd && (v % NV) == 0) rstd[r * ng + v / NV] = rs;
+      for (int e = 0; e < V; ++e) o[e] = (g[k][e] * rs) * wr[k][e];
+      buf_store16(ro, vec_off<TH>(t, k, nvec), NVc::pack(o));
+      buf_store4(rr, roff[k], rs);
     }
   }
 }
@@ -183,20 +257,20 @@ __global__ __launch_bounds__(TH) void gated_norm_bwd_kernel(
   const int t = threadIdx.x;
   const int nvec = C / V, NV = GS / V;
   const float inv_gs = 1.f / (float)GS;
+  const uint32_t row_bytes = (uint32_t)C * (uint32_t)sizeof(T);
   float dwa[KT][V], wr[KT][V];             // dw sums and the weights of this thread's channels
+  load_w<KT, TH, V>(w, C, nvec, t, wr);
 #pragma unroll
-  for (int k = 0; k < KT; ++k) {
-    load_w(w, t + TH * k, nvec, wr[k], V);
+  for (int k = 0; k < KT; ++k)
 #pragma unroll
     for (int e = 0; e < V; ++e) dwa[k][e] = 0.f;
-  }
   // the next row's inputs are loaded while this row is processed
   uint4 yv[KT], zv[KT], dv[KT];
-  load_row<KT, TH, V>(y, z, dout, (int64_t)blockIdx.x, rows, C, nvec, t, yv, zv, dv);
+  load_row<KT, TH, true>(y, z, dout, (int64_t)blockIdx.x, rows, C, nvec, t, yv, zv, dv);
 #pragma unroll 1
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
     uint4 ny[KT], nz[KT], nd[KT];
-    load_row<KT, TH, V>(y, z, dout, r + gridDim.x, rows, C, nvec, t, ny, nz, nd);
+    load_row<KT, TH, true>(y, z, dout, r + gridDim.x, rows, C, nvec, t, ny, nz, nd);
     // g = y silu(z) and the group sums of g^2
     float u[KT][V], s[KT], sg[KEEP ? KT : 1][V];
 #pragma unroll
@@ -224,18 +298,22 @@ __global__ __launch_bounds__(TH) void gated_norm_bwd_kernel(
       }
     }
     group_sums<KT, TH>(p, NV, (nvec + 63) / 64, chunk + NCH);
-    // unpacking again from the packed registers (the laundering keeps the
-    // compiler from holding the unpacked values across the sums)
+    // with several vectors per thread, unpacking again from the packed
+    // registers (the laundering keeps the compiler from holding the unpacked
+    // values across the sums); with one, the unpacked values fit
+    if constexpr (KT > 1) {
 #pragma unroll
-    for (int k = 0; k < KT; ++k) {
-      launder(yv[k]);
-      launder(zv[k]);
-      launder(dv[k]);
+      for (int k = 0; k < KT; ++k) {
+        launder(yv[k]);
+        launder(zv[k]);
+        launder(dv[k]);
+      }
     }
+    const auto rdy = buf_rsrc(dy + r * C, row_bytes), rdz = buf_rsrc(dz + r * C, row_bytes);
+    // vectors past the row's last hold zeros, compute finite values and
+    // store past the records
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-      const int v = t + TH * k;
-      if (v >= nvec) continue;
       float yf[V], zf[V], df[V];
       NVc::unpack(yv[k], yf);
       NVc::unpack(zv[k], zf);
@@ -256,8 +334,9 @@ __global__ __launch_bounds__(TH) void gated_norm_bwd_kernel(
         ody[e] = dg * gate;
         odz[e] = dg * yf[e] * sig * (1.f + zf[e] * (1.f - sig));
       }
-      *reinterpret_cast<uint4*>(dy + r * C + v * V) = NVc::pack(ody);
-      *reinterpret_cast<uint4*>(dz + r * C + v * V) = NVc::pack(odz);
+      const uint32_t off = vec_off<TH>(t, k, nvec);
+      buf_store16(rdy, off, NVc::pack(ody));
+      buf_store16(rdz, off, NVc::pack(odz));
     }
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
@@ -276,32 +355,53 @@ __global__ __launch_bounds__(TH) void gated_norm_bwd_kernel(
   }
 }
 
-// Sums of the partial rows [y R, min((y + 1) R, nparts)) of `part`
-// ([nparts][C]), in row order, four channels per thread: row y of `out`.
+// Column sums of the partial rows [y R, min((y + 1) R, nparts)) of `part`
+// ([nparts][C]) into row y of `out`, for the 256 channels of column block x
+// (four per lane).  Wave w sums rows [y R + w R / 4, y R + (w + 1) R / 4) in
+// row order, kDwBatch loads in flight at a time, then the four wave sums are
+// added in wave order.  R is a multiple of 4; rows and channels past the
+// ends read as zeros through the resource and leave every sum as it is.
+constexpr int kDwBatch = 8;
 __global__ __launch_bounds__(kNormThreads) void gated_norm_dw_kernel(
     const float* __restrict__ part, int nparts, int R, int C, float* __restrict__ out) {
-  const int c = (blockIdx.x * kNormThreads + threadIdx.x) * 4;
-  if (c >= C) return;
-  const int p0 = blockIdx.y * R, p1 = min(p0 + R, nparts);
+  __shared__ float4 wsum[3][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = (blockIdx.x * 64 + lane) * 4;
+  const auto rp = buf_rsrc(part, (uint32_t)nparts * (uint32_t)C * 4u);
+  const int rw = R / 4, a = blockIdx.y * R + w * rw;
+  const int b = min(a + rw, nparts);
   float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-  constexpr int kB = 8;                     // rows loaded together, then added in order
-  for (int pb = p0; pb < p1; pb += kB) {
-    float4 v[kB];
+  for (int pb = a; pb < b; pb += kDwBatch) {
+    uint4 v[kDwBatch];
 #pragma unroll
-    for (int i = 0; i < kB; ++i)
-      v[i] = pb + i < p1 ? *reinterpret_cast<const float4*>(part + (int64_t)(pb + i) * C + c)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < kDwBatch; ++i) {
+      const int row = pb + i;
+      v[i] = buf_load16(rp, (row < b && c < C) ? ((uint32_t)row * (uint32_t)C + c) * 4u
+                                                : kNormPast);
+    }
 #pragma unroll
-    for (int i = 0; i < kB; ++i) {
-      if (pb + i < p1) {
-        t.x += v[i].x;
-        t.y += v[i].y;
-        t.z += v[i].z;
-        t.w += v[i].w;
-      }
+    for (int i = 0; i < kDwBatch; ++i) {
+      t.x += __builtin_bit_cast(float, v[i].x);
+      t.y += __builtin_bit_cast(float, v[i].y);
+      t.z += __builtin_bit_cast(float, v[i].z);
+      t.w += __builtin_bit_cast(float, v[i].w);
     }
   }
-  *reinterpret_cast<float4*>(out + (int64_t)blockIdx.y * C + c) = t;
+  if (w > 0) wsum[w - 1][lane] = t;
+  __syncthreads();
+  if (w > 0) return;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const float4 u = wsum[q][lane];
+    t.x += u.x;
+    t.y += u.y;
+    t.z += u.z;
+    t.w += u.w;
+  }
+  const auto ro = buf_rsrc(out + (int64_t)blockIdx.y * C, (uint32_t)C * 4u);
+  buf_store16(ro, c < C ? (uint32_t)c * 4u : kNormPast,
+              make_uint4(__builtin_bit_cast(uint32_t, t.x), __builtin_bit_cast(uint32_t, t.y),
+                         __builtin_bit_cast(uint32_t, t.z), __builtin_bit_cast(uint32_t, t.w)));
 }
 
 // Workgroups of the norm kernels: `per_cu` per CU (several rows of loads in
@@ -317,19 +417,20 @@ int norm_grid(int64_t rows, int per_cu) {
 }
 
 // dw from the backward's nparts partial rows: sums of kNormDwRows rows at a
-// time into the scratch after them, then the sum of those (both in row order).
+// time into the scratch after them, then the sum of those (both in a fixed
+// order).
 hipError_t norm_dw(const NormArgs& a, int nparts, hipStream_t s) {
-  const int gx = (a.C / 4 + kNormThreads - 1) / kNormThreads;
+  const int gx = (a.C + 255) / 256;
   const int n1 = (nparts + kNormDwRows - 1) / kNormDwRows;
   float* mid = a.dw_part + (int64_t)kNormMaxParts * a.C;
   if (n1 > 1) {
     hipLaunchKernelGGL(gated_norm_dw_kernel, dim3(gx, n1), dim3(kNormThreads), 0, s,
                        (const float*)a.dw_part, nparts, kNormDwRows, a.C, mid);
     hipLaunchKernelGGL(gated_norm_dw_kernel, dim3(gx, 1), dim3(kNormThreads), 0, s,
-                       (const float*)mid, n1, n1, a.C, a.dw);
+                       (const float*)mid, n1, (n1 + 3) / 4 * 4, a.C, a.dw);
   } else {
     hipLaunchKernelGGL(gated_norm_dw_kernel, dim3(gx, 1), dim3(kNormThreads), 0, s,
-                       (const float*)a.dw_part, nparts, nparts, a.C, a.dw);
+                       (const float*)a.dw_part, nparts, (nparts + 3) / 4 * 4, a.C, a.dw);
   }
   return hipGetLastError();
 }
