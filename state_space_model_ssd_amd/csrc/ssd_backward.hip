@@ -50,6 +50,7 @@
 // path uses fp32 tiles on the vector ALUs, staged through LDS with 16-byte
 // loads.
 #include "ssd_kernels.h"
+#include "ssd_scan_tile.h"
 
 namespace ssd {
 
@@ -175,10 +176,6 @@ __device__ __forceinline__ void zero_quarter(f32x4 (&d)[2][2]) {
     for (int ni = 0; ni < 2; ++ni) d[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-__device__ __forceinline__ bf16x8 frag_row(const bf16* p, bool ok) {
-  return __builtin_bit_cast(bf16x8, load16(p, ok));
-}
-
 // 16 bytes at byte offset off of a buffer resource, or zeros when !ok.  The
 // load is issued whatever ok is (the offset of a lane without data lies
 // past the resource's records, which reads zeros), so no branch surrounds
@@ -239,35 +236,6 @@ __device__ __forceinline__ void quarter_to_thread(const MfmaQuarter& q, const f3
   for (int i = 0; i < 4; ++i) {
     const float4 v = *reinterpret_cast<const float4*>(&src[((tm + i) & 31) * kGemmPitch + tn]);
     acc[i][0] = v.x; acc[i][1] = v.y; acc[i][2] = v.z; acc[i][3] = v.w;
-  }
-}
-
-// d += A B^T over k < K, A(m, k) = arow[m * astride + k] and B^T(n, k) =
-// brow[n * bstride + k] (bf16 rows), both from 16-byte loads; rows at or
-// past na (nb) read as 0.
-template <int K>
-__device__ __forceinline__ void mfma_rows(const MfmaQuarter& q, const bf16* arow, int64_t astride,
-                                          int na, const bf16* brow, int64_t bstride, int nb,
-                                          f32x4 (&d)[2][2]) {
-  using M = Mfma<bf16>;
-  static_assert(K % M::K == 0, "row length");
-#pragma unroll
-  for (int k0 = 0; k0 < K; k0 += M::K) {
-    bf16x8 a[2], b[2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int r = q.wr + mi * 16 + q.lr;
-      a[mi] = frag_row(arow + r * astride + k0 + q.kq, r < na);
-    }
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int c = q.wc + ni * 16 + q.lr;
-      b[ni] = frag_row(brow + c * bstride + k0 + q.kq, c < nb);
-    }
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) d[mi][ni] = M::mma(a[mi], b[ni], d[mi][ni]);
   }
 }
 
@@ -847,7 +815,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_mfma_kernel(
     ChunkMap cm, int nslots, const bf16* __restrict__ x, const bf16* __restrict__ dy,
     const bf16* __restrict__ cb, const float* __restrict__ delta, const float* __restrict__ dAcs, int H,
     int G, int HB, float* __restrict__ dcbp, float* __restrict__ rowpart, float* __restrict__ colpart,
-    float* __restrict__ ddot) {
+    float* __restrict__ ddot, bf16* __restrict__ cbt) {
   // per head: a at the tile's rows, a at its columns, delta at its columns
   __shared__ __align__(16) float fac[2][3][64];
   // per head: the tile's dy rows and x rows (P bf16 each, padded rows)
@@ -884,6 +852,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_mfma_kernel(
         const int l = l0 + q.row(mi, r), sx = s0 + q.col(ni);
         cbq[mi][ni][r] = (l < len && sx <= l) ? static_cast<float>(cbj[(int64_t)l * L + sx]) : 0.f;
       }
+  // the first head block also writes these values transposed for dx: a
+  // lane's four rows l of column s are four consecutive entries of row s
+  {
+    const __amdgpu_buffer_rsrc_t rt = buf_rsrc_u(cbt + ((int64_t)j * G + g) * L * L, L * L * sizeof(bf16));
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = static_cast<bf16>(cbq[mi][ni][r]);
+        const uint32_t off = ((uint32_t)(s0 + q.col(ni)) * L + l0 + q.row(mi, 0)) * sizeof(bf16);
+        buf_store8(rt, hb == 0 ? off : kPastRecords, __builtin_bit_cast(uint2, v));
+      }
+  }
   f32x4 w[2][2];                           // this block's sum of delta_s V[l,s]
   zero_quarter(w);
   const __amdgpu_buffer_rsrc_t rdy =
@@ -1019,7 +1002,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_mfma_kernel(
     }
 }
 
-// 3b. dx as 64 x 64 tiles of (token s, p):
+// 3b, fp32 inputs: dx as 64 x 64 tiles of (token s, p):
 //   dx_s = delta_s [ sum_{l>=s} CB[l,s] exp(a_l - a_s) dy_l + exp(a_last - a_s) dS_j B_s ]
 //          + D dy_s;
 // grid: xcd_grid(chunk slots, L/64 * ceil(P/64) * H), a chunk's tiles on its XCD.
@@ -1027,7 +1010,6 @@ template <typename T, int P, int N, int L>
 __global__ __launch_bounds__(kBwdThreads, 8) void bwd_dx_tiled_kernel(
     ChunkMap cm, int nslots, const T* __restrict__ B, const T* __restrict__ dy, const T* __restrict__ cb,
     const float* __restrict__ delta, const float* __restrict__ dAcs, const float* __restrict__ dS,
-    const bf16* __restrict__ dS16,
     const float* __restrict__ D, int H, int G, T* __restrict__ dx) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   __shared__ float es[L], av[L];
@@ -1050,95 +1032,6 @@ __global__ __launch_bounds__(kBwdThreads, 8) void bwd_dx_tiled_kernel(
   }
   const T* cbj = cb + ((int64_t)j * G + g) * L * L;
   float acc[4][4] = {};
-  if constexpr (sizeof(T) == 2) {
-    // bf16 MFMA.  exp(a_last - a_s) B_s . dS_j[p, :] first (B rows exact,
-    // dS rounded once to bf16), times its row factor; then the slices of 32
-    // tokens l of sum_{l >= s} CB[l,s] exp(a_l - a_s) dy_l, the decay-masked
-    // CB (rounded once) and dy staged k-major in LDS (in As and Bs).
-    static_assert(32 * kKtPitch * sizeof(bf16) <= 32 * kGemmPitch * sizeof(float), "slice tiles");
-    bf16* mt = reinterpret_cast<bf16*>(As);
-    bf16* yt = reinterpret_cast<bf16*>(Bs);
-    const MfmaQuarter q;
-    f32x4 d[2][2];
-    zero_quarter(d);
-    mfma_rows<N>(q, B + ((t0 + s0) * G + g) * N, (int64_t)G * N, len - s0, dS16 + (jh * P + p0) * N, N,
-                 P - p0, d);
-    __syncthreads();                       // es, av staged
-    // Factored decay when the chunk's total decay is within 2^64 (uniform
-    // over the workgroup): exp(a_l - a_s) = exp(a_l) exp(-a_s), so the dy rows
-    // enter scaled by exp(a_l), the CB rows as stored (0 above the diagonal:
-    // no mask), and the product's rows are scaled by exp(-a_s) at the end --
-    // the state term by exp(a_last) now, to leave exp(a_last - a_s).
-    // Otherwise each CB element is masked with its decay.
-    const bool fast = fabsf(alast) * kLog2e <= kBwdFastMaxLog2;
-    const float ealast = exp2_fast(alast * kLog2e);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float f = fast ? ealast : es[s0 + q.row(mi, r)];
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) d[mi][ni][r] *= f;
-      }
-    static_assert(32 * 8 == kBwdThreads, "one 8-wide piece of each slice tile per thread");
-    const int kr = threadIdx.x >> 3, c = (threadIdx.x & 7) * 8;
-    // The next slice's CB and dy pieces are loaded while the current slice
-    // is multiplied: buffer loads issued without a branch (rows past the
-    // chunk read zeros), so the wait before their use leaves them in flight.
-    const __amdgpu_buffer_rsrc_t rcb = buf_rsrc_u(cbj, (uint32_t)(len * L * sizeof(T)));
-    const __amdgpu_buffer_rsrc_t rdy = buf_rsrc_u(dy + t0 * H * P, (uint32_t)((int64_t)len * H * P * sizeof(T)));
-    bf16x8 cv, yv;
-    auto fetch = [&](int kb) {
-      const int l = kb + kr;
-      cv = frag_buf(rcb, (uint32_t)((l * L + s0 + c) * sizeof(T)));
-      yv = frag_buf(rdy, (uint32_t)(((l * H + h) * P + p0 + c) * sizeof(T)), p0 + c < P);
-    };
-    fetch(s0);
-    for (int kb = s0; kb < len; kb += 32) {
-      const int l = kb + kr;
-      const bool lok = l < len;
-      const float avl = av[l];
-      bf16x8 mcur, ycur;
-      if (fast) {
-        mcur = cv;
-        // rows past the chunk: factor 0 (their a is not defined)
-        const float el = lok ? exp2_fast(avl * kLog2e) : 0.f;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = el * static_cast<float>(yv[e]);
-        ycur = Mfma<bf16>::pack(v);
-      } else {
-        float mv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // the mask selects the exponent (exp2 of -inf is 0), so no branch
-          // and nothing undefined enters the product
-          const int sx = s0 + c + e;
-          const float arg = (lok && l >= sx) ? (avl - av[sx]) * kLog2e : -INFINITY;
-          mv[e] = static_cast<float>(cv[e]) * exp2_fast(arg);
-        }
-        mcur = Mfma<bf16>::pack(mv);
-        ycur = yv;
-      }
-      fetch(kb + 32);                      // past the chunk: zeros
-      __syncthreads();                     // previous slice consumed
-      *reinterpret_cast<bf16x8*>(&mt[kr * kKtPitch + c]) = mcur;
-      *reinterpret_cast<bf16x8*>(&yt[kr * kKtPitch + c]) = ycur;
-      __syncthreads();
-      mfma_kmajor(q, mt, yt, d);
-    }
-    if (fast) {
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float f = exp2_fast(-av[s0 + q.row(mi, r)] * kLog2e);
-#pragma unroll
-          for (int ni = 0; ni < 2; ++ni) d[mi][ni][r] *= f;
-        }
-    }
-    quarter_to_thread(q, d, acc, As, Bs);
-  } else {
   // sum_{l >= s} CB[l,s] exp(a_l - a_s) dy_l: slices of 32 tokens l, each a
   // CB row (columns s) and a dy row (columns p) in 16-byte pieces
   {
@@ -1177,7 +1070,6 @@ __global__ __launch_bounds__(kBwdThreads, 8) void bwd_dx_tiled_kernel(
   gemm_staged<T, true, float, true, (N < 32 ? N : 32)>(B + ((t0 + s0) * G + g) * N, (int64_t)G * N,
                                                        len - s0, es + s0, dS + (jh * P + p0) * N, N,
                                                        P - p0, 0, N, acc, As, Bs);
-  }
   const float Dh = D ? D[h] : 0.f;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
   static_assert(P % 4 == 0, "4-wide pieces of a row");
@@ -1200,6 +1092,277 @@ __global__ __launch_bounds__(kBwdThreads, 8) void bwd_dx_tiled_kernel(
     store4(dx + o, dsv[i] * acc[i][0] + Dh * y.x, dsv[i] * acc[i][1] + Dh * y.y,
            dsv[i] * acc[i][2] + Dh * y.z, dsv[i] * acc[i][3] + Dh * y.w);
   }
+}
+
+// 3b, bf16 inputs: dx as one tile per (chunk, head), the adjoint of the
+// forward's chunk_scan tile,
+//   dx^T[p][s] = delta_s [ sum_{l >= s} dy^T[p][l] CBt[s][l] exp(a_l - a_s)
+//                          + exp(a_last - a_s) sum_n dS[p][n] B[s][n] ] + D dy_s[p],
+// with that tile's operand flow: dy rows staged XOR-swizzled in LDS give the
+// dy^T operands by transpose read (x^T there); rows of CB's transposed copy,
+// written by 3a, stream from memory through a register ring as the B
+// operands (CB rows there); the dS term is its inter-chunk term with dS as
+// the state and B rows as the C rows.  A lane holds four consecutive p of
+// one token s.  Waves own mirror pairs of 16-row groups of s: row group m
+// meets the k-steps from m / 2 on, so a pair carries the same work as any
+// other.
+// FAST (the chunk's whole decay within 2^kBwdFastMaxLog2): dy rows are
+// staged times exp(a_l) (0 past the chunk), CBt enters the MFMAs as loaded
+// (0 where l < s), the dS term is scaled by exp(a_last), and row s by
+// delta_s exp(-a_s) at the end.  Otherwise dy is staged as loaded, each CBt
+// piece is scaled by its decay -- below the diagonal split around the
+// block's first token r as exp(a_l - a_r) exp(a_r - a_s), both <= 1, one
+// exponential per piece; on it masked exponentials -- the dS term by
+// exp(a_last - a_s), and row s by delta_s.  D dy_s joins in fp32 from dy as
+// loaded.
+template <int L> constexpr int kDxWaves = kTileWaves<L>;
+
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+
+// CBt piece of row s (row group m) at k-step q times its decay (exact path).
+__device__ __forceinline__ bf16x8 dx_masked_cbt(const bf16x8& v, int m, int q, int s, int kq,
+                                                const float* dal2, const float* cfr) {
+  const int l0 = 32 * q;
+  const float das = dal2[s];
+  float mv[8];
+  if (l0 >= 16 * m + 16) {               // the block lies after every row of the group
+    const float rf = exp2_fast(dal2[l0] - das);
+    const float4 f0 = *reinterpret_cast<const float4*>(&cfr[l0 + kq]);
+    const float4 f1 = *reinterpret_cast<const float4*>(&cfr[l0 + kq + 4]);
+    const float cf[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mv[e] = static_cast<float>(v[e]) * (cf[e] * rf);
+  } else {                               // on the diagonal
+    const float4 a0 = *reinterpret_cast<const float4*>(&dal2[l0 + kq]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&dal2[l0 + kq + 4]);
+    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // before the row the exponent is -inf, and exp2 gives exactly 0
+      const float arg = l0 + kq + e >= s ? av[e] - das : -__builtin_inff();
+      mv[e] = static_cast<float>(v[e]) * exp2_fast(arg);
+    }
+  }
+  return Mfma<bf16>::pack(mv);
+}
+
+template <int P, int N, int L, bool FAST>
+__device__ __forceinline__ void bwd_dx_tile(const ScanTile& T, float last2, const bf16* __restrict__ B,
+                                            const bf16* __restrict__ dy, const bf16* __restrict__ cbt,
+                                            const float* __restrict__ delta, const float* __restrict__ dAcs,
+                                            const bf16* __restrict__ dS16, const float* __restrict__ D,
+                                            int H, int G, bf16* __restrict__ dx, bf16* ys, bf16* hsm,
+                                            float* dal2, float* dls, float* cfr) {
+  using M = Mfma<bf16>;
+  constexpr int NW = kDxWaves<L>, NT = 64 * NW;
+  constexpr int HP = N + 8;              // dS tile pitch, as the forward's state tile
+  constexpr int RG = L / 16, RGW = RG / NW, PT = P / 16, NK = N / 32, NQ = L / 32;
+  constexpr int CPR = P / 8, XU = L * CPR / NT, HPR = N / 8, HU = (P * HPR + NT - 1) / NT;
+  static_assert(RGW * NW == RG && (RGW == 1 || RGW == 2), "row-group split");
+  static_assert((L * CPR) % NT == 0 && L <= NT, "dy staging");
+  const int h = T.h, g = h / (H / G);
+  const uint32_t HPx = (uint32_t)H * P, GN = (uint32_t)G * N;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
+  const int lr = lane & 15, kg = lane >> 4, kq = kg * 8;
+  const int64_t jh = (int64_t)T.j * H + h;
+  int mg[RGW], srow[RGW], qs[RGW];
+  mg[0] = w;
+  if constexpr (RGW == 2) mg[1] = RG - 1 - w;
+#pragma unroll
+  for (int i = 0; i < RGW; ++i) {
+    srow[i] = 16 * mg[i] + lr;
+    qs[i] = mg[i] / 2;                     // first k-step that reaches the row group
+  }
+  const int nqv = (T.len + 31) / 32;       // k-steps inside the chunk
+
+  // ---- global loads, in the order of use
+  const auto rdy = rows_rsrc(dy, T, H, P, HPx);
+  const auto rda = buf_rsrc(dAcs + jh * L, L * 4);
+  uint4 yv[XU];
+  float ya[XU];                            // a at the row of each piece (FAST)
+#pragma unroll
+  for (int u = 0; u < XU; ++u) {
+    const int i = tid + NT * u, r = i / CPR, c = i % CPR;
+    yv[u] = buf_load16(rdy, ((uint32_t)r * HPx + c * 8) * 2u);
+    if constexpr (FAST) ya[u] = buf_load4(rda, (uint32_t)r * 4u);
+  }
+  const auto rh = buf_rsrc(dS16 + jh * P * N, P * N * 2);
+  uint4 hv[HU];
+#pragma unroll
+  for (int u = 0; u < HU; ++u) hv[u] = buf_load16(rh, (uint32_t)(tid + NT * u) * 16);
+  const float dA_t = buf_load4(rda, tid * 4);
+  const float dl_t = buf_load4(buf_rsrc(delta + jh * L, L * 4), tid * 4);
+  const auto rb = buf_rsrc(B + ((int64_t)T.start * G + g) * N, ((uint32_t)(T.len - 1) * GN + N) * 2u);
+  bf16x8 fb[RGW][NK];                      // B rows of this lane, all n-steps
+#pragma unroll
+  for (int i = 0; i < RGW; ++i)
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+      fb[i][k] = __builtin_bit_cast(bf16x8, buf_load16(rb, ((uint32_t)srow[i] * GN + 32 * k + kq) * 2u));
+  const auto rct = buf_rsrc(cbt + ((int64_t)T.j * G + g) * L * L, L * L * 2);
+
+  // ---- stage dy (FAST: times exp(a_l), 0 past the chunk), the dS tile and
+  // the per-token values
+#pragma unroll
+  for (int u = 0; u < XU; ++u) {
+    const int i = tid + NT * u, r = i / CPR, c = i % CPR;
+    uint4 v = yv[u];
+    if constexpr (FAST)                    // exp2(-inf) = 0 past the chunk
+      v = __builtin_bit_cast(uint4, scale_bf16x8(v, exp2_fast(r < T.len ? ya[u] * kLog2e : -__builtin_inff())));
+    *reinterpret_cast<uint4*>(&ys[r * P + ((c ^ tile_sw<CPR>(r)) << 3)]) = v;
+  }
+#pragma unroll
+  for (int u = 0; u < HU; ++u) {
+    const int i = tid + NT * u, r = i / HPR, c = i % HPR;
+    if (i < P * HPR) *reinterpret_cast<uint4*>(&hsm[r * HP + c * 8]) = hv[u];
+  }
+  {
+    const float a2 = dA_t * kLog2e;
+    if (tid < L) {                         // whole waves
+      dal2[tid] = a2;
+      dls[tid] = dl_t;
+    }
+    if constexpr (!FAST) {
+      const float a2r = __shfl(a2, lane & ~31);   // the first token of the 32-token block
+      if (tid < L) cfr[tid] = exp2_fast(a2 - a2r);
+    }
+  }
+  f32x4 acc[RGW][PT];
+#pragma unroll
+  for (int i = 0; i < RGW; ++i)
+#pragma unroll
+    for (int a = 0; a < PT; ++a) acc[i][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  scan_tile_inter<P, N, RGW, HP>(acc, fb, hsm, lr, kq);
+#pragma unroll
+  for (int i = 0; i < RGW; ++i) {
+    const float f = FAST ? exp2_fast(last2) : exp2_fast(last2 - dal2[srow[i]]);
+#pragma unroll
+    for (int a = 0; a < PT; ++a) acc[i][a] *= f;
+  }
+
+  // ---- intra-chunk term: CBt pieces through a ring of RD per row group,
+  // RD - 1 k-steps ahead; dy^T operands through a ring of XR over the
+  // sequence (step, p-tile).  Every ring load is issued, without a branch:
+  // one a row group does not need (before its first k-step, past the
+  // chunk's last) aims past the records and reads zeros.  Steps before a
+  // row group's first multiply nothing; the loop ends at the chunk's last
+  // k-step.
+  // (two operand slots with 256-token chunks keep the tile within 128 VGPRs)
+  constexpr int RD = 3, XR = L >= 256 ? 2 : 3, NOP = NQ * PT;
+  const int xrow = 8 * kg + (lr >> 2);
+  const int xsl = tile_sw<CPR>(xrow) >> 1;
+  const int xcol = ((lr & 3) >> 1) * 8 + (lr & 1) * 4;
+  const auto cbt_off = [&](int i, int q) {
+    return (q >= qs[i] && q < nqv) ? ((uint32_t)srow[i] * L + 32 * q + kq) * 2u : kPastRecords;
+  };
+  bf16x8 ring[RGW][RD];
+#pragma unroll
+  for (int i = 0; i < RGW; ++i)
+#pragma unroll
+    for (int q = 0; q < RD - 1; ++q) ring[i][q] = __builtin_bit_cast(bf16x8, buf_load16(rct, cbt_off(i, q)));
+  bf16x8 fxr[XR];
+#pragma unroll
+  for (int n = 0; n < XR; ++n) fxr[n] = scan_x_operand<P>(ys, n / PT, n % PT, xrow, xsl, xcol);
+  bf16x8 fm[RGW];
+#pragma unroll
+  for (int n = 0; n < NOP; ++n) {
+    const int q = n / PT, a = n % PT;
+    if (a == 0) {
+      if (q >= nqv) break;                 // wave-uniform
+      if (q + RD - 1 < NQ) {
+#pragma unroll
+        for (int i = 0; i < RGW; ++i)
+          ring[i][(q + RD - 1) % RD] = __builtin_bit_cast(bf16x8, buf_load16(rct, cbt_off(i, q + RD - 1)));
+      }
+#pragma unroll
+      for (int i = 0; i < RGW; ++i) {
+        if (q >= qs[i]) {                  // wave-uniform
+          if constexpr (FAST) fm[i] = ring[i][q % RD];
+          else fm[i] = dx_masked_cbt(ring[i][q % RD], mg[i], q, srow[i], kq, dal2, cfr);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RGW; ++i)
+      if (q >= qs[i]) acc[i][a] = M::mma(fxr[n % XR], fm[i], acc[i][a]);   // wave-uniform
+    if (n + XR < NOP) fxr[n % XR] = scan_x_operand<P>(ys, (n + XR) / PT, (n + XR) % PT, xrow, xsl, xcol);
+  }
+
+  // ---- epilogue: row factor and D dy in fp32 (dy as loaded at this lane's
+  // outputs), rounded once; the tile goes to LDS over dy (every wave is done
+  // with it) in the out_sw layout, a lane's four p of one token as one
+  // 8-byte piece, and leaves as whole rows
+  uint2 dyr[RGW][PT];
+#pragma unroll
+  for (int i = 0; i < RGW; ++i)
+#pragma unroll
+    for (int a = 0; a < PT; ++a)
+      dyr[i][a] = buf_load8(rdy, ((uint32_t)srow[i] * HPx + 16 * a + 4 * kg) * 2u);
+  const float Dh = D ? D[h] : 0.f;
+  float rsc[RGW];
+#pragma unroll
+  for (int i = 0; i < RGW; ++i)
+    rsc[i] = FAST ? dls[srow[i]] * exp2_fast(-dal2[srow[i]]) : dls[srow[i]];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < RGW; ++i)
+#pragma unroll
+    for (int a = 0; a < PT; ++a) {
+      const int s = srow[i];
+      const bf16x4 raw = __builtin_bit_cast(bf16x4, dyr[i][a]);
+      bf16x4 yo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yo[r] = static_cast<bf16>(acc[i][a][r] * rsc[i] + Dh * static_cast<float>(raw[r]));
+      *reinterpret_cast<bf16x4*>(&ys[s * P + ((4 * a + kg) ^ out_sw<P>(s)) * 4]) = yo;
+    }
+  __syncthreads();
+  const auto rdx = rows_rsrc(dx, T, H, P, HPx);
+#pragma unroll
+  for (int u = 0; u < XU; ++u) {
+    const int i = tid + NT * u, r = i / CPR, c = i % CPR;
+    const int sw = out_sw<P>(r);
+    const uint2 v0 = *reinterpret_cast<const uint2*>(&ys[r * P + ((2 * c) ^ sw) * 4]);
+    const uint2 v1 = *reinterpret_cast<const uint2*>(&ys[r * P + ((2 * c + 1) ^ sw) * 4]);
+    buf_store16(rdx, ((uint32_t)r * HPx + c * 8) * 2u, make_uint4(v0.x, v0.y, v1.x, v1.y));
+  }
+}
+
+// grid: xcd_grid(chunk slots, H), a chunk's heads on its XCD.
+template <int P, int N, int L>
+__global__ __launch_bounds__(64 * kDxWaves<L>) __attribute__((amdgpu_waves_per_eu(
+    kTileWavesPerEU<L, kDxWaves<L>>))) void bwd_dx_scan_kernel(ChunkMap cm, int nslots,
+                                                              const bf16* __restrict__ B,
+                                                              const bf16* __restrict__ dy,
+                                                              const bf16* __restrict__ cbt,
+                                                              const float* __restrict__ delta,
+                                                              const float* __restrict__ dAcs,
+                                                              const bf16* __restrict__ dS16,
+                                                              const float* __restrict__ D, int H, int G,
+                                                              bf16* __restrict__ dx) {
+  __shared__ __align__(16) bf16 ys[L * P];
+  __shared__ __align__(16) bf16 hsm[P * (N + 8)];
+  __shared__ __align__(16) float dal2[L];  // running sum of delta*A, times log2(e)
+  __shared__ __align__(16) float dls[L];   // delta
+  __shared__ __align__(16) float cfr[L];   // exp(a_l - a_r), r = first token of l's 32-block
+  const int2 ci = xcd_chunk_head(blockIdx.x, H);
+  if (ci.x >= nslots) return;
+  // the running sum is monotone inside a chunk and flat past its end: its
+  // value at the last position bounds every |a_s|
+  const float last = dAcs[((int64_t)ci.x * H + ci.y) * L + L - 1];
+  const ChunkDesc cd = cm.desc(ci.x);
+  if (cd.len <= 0) return;
+  const ScanTile T{ci.x, ci.y, cd.start, cd.len};
+  if (fabsf(last) * kLog2e <= kBwdFastMaxLog2)   // uniform over the workgroup
+    bwd_dx_tile<P, N, L, true>(T, last * kLog2e, B, dy, cbt, delta, dAcs, dS16, D, H, G, dx, ys, hsm, dal2,
+                               dls, cfr);
+  else
+    bwd_dx_tile<P, N, L, false>(T, last * kLog2e, B, dy, cbt, delta, dAcs, dS16, D, H, G, dx, ys, hsm, dal2,
+                                dls, cfr);
 }
 
 // 3b'. The group's dCB: the HB partial sums of 3a added into the first,
@@ -1703,7 +1866,7 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((bwd_v_mfma_kernel<P, L>), dim3(xcd_grid(mc, LT * (LT + 1) / 2 * G * HB)),
                        dim3(kBwdThreads), 0, s, cm, mc, (const bf16*)x, (const bf16*)dy, (const bf16*)cb,
-                       a.delta, a.dAcs, H, G, HB, b.dcb, b.rowpart, b.colpart, b.ddot);
+                       a.delta, a.dAcs, H, G, HB, b.dcb, b.rowpart, b.colpart, b.ddot, static_cast<bf16*>(b.cbt));
   else
     hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * (LT + 1) / 2 * G * HB)),
                        dim3(kBwdThreads), 0, s, cm, mc, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb,
@@ -1715,9 +1878,14 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
                      dim3(kBwdThreads), 0, s, cm, mc, x, B, C, dy, a.delta, a.dAcs, hin, b.dS,
                      static_cast<const bf16*>(b.dS16), b.dcb, H, G, HB, (T*)b.dB, (T*)b.dC, b.interpart,
                      b.vxpart);
-  hipLaunchKernelGGL((bwd_dx_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * ((P + 63) / 64) * H)),
-                     dim3(kBwdThreads), 0, s, cm, mc, B, dy, cb, a.delta, a.dAcs, b.dS,
-                     static_cast<const bf16*>(b.dS16), a.D, H, G, (T*)b.dx);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((bwd_dx_scan_kernel<P, N, L>), dim3(xcd_grid(mc, H)), dim3(64 * kDxWaves<L>), 0, s,
+                       cm, mc, (const bf16*)B, (const bf16*)dy, static_cast<const bf16*>(b.cbt), a.delta,
+                       a.dAcs, static_cast<const bf16*>(b.dS16), a.D, H, G, (bf16*)b.dx);
+  else
+    hipLaunchKernelGGL((bwd_dx_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * ((P + 63) / 64) * H)),
+                       dim3(kBwdThreads), 0, s, cm, mc, B, dy, cb, a.delta, a.dAcs, b.dS, a.D, H, G,
+                       (T*)b.dx);
   hipLaunchKernelGGL((bwd_token_kernel<T, P, N, L>), dim3(H, mc), dim3(L), 0, s, cm, a.dt, a.dt_bias,
                      a.A, a.delta, a.dAcs, b.ghpart, b.rowpart, b.colpart, b.vxpart, b.interpart,
                      b.ddot, H, a.dt_min, a.dt_max, b.ddt, b.dA_part, b.dD_part, b.dbias_part);

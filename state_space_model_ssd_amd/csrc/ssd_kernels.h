@@ -89,6 +89,9 @@ struct BwdArgs {
   float* dD_part;           // [max_chunks][H]
   float* dbias_part;        // [max_chunks][H]
   float* ddot;              // [max_chunks][H][L]: dy_t . x_t per token
+  void* cbt;                // [max_chunks][G][L][L] bf16 (bf16 inputs): CB transposed,
+                            // cbt[s][l] = CB[l][s] for s <= l < len, else 0, in the 64 x 64
+                            // tiles with l-tile >= s-tile and l-tile inside the chunk
 };
 
 // Devices whose per-device launch parameters the library caches.
