@@ -1106,21 +1106,27 @@ __global__ __launch_bounds__(kBwdThreads, 8) void bwd_dx_tiled_kernel(
 // one token s.  Waves own mirror pairs of 16-row groups of s: row group m
 // meets the k-steps from m / 2 on, so a pair carries the same work as any
 // other.
-// FAST (the chunk's whole decay within 2^kBwdFastMaxLog2): dy rows are
-// staged times exp(a_l) (0 past the chunk), CBt enters the MFMAs as loaded
-// (0 where l < s), the dS term is scaled by exp(a_last), and row s by
-// delta_s exp(-a_s) at the end.  Otherwise dy is staged as loaded, each CBt
-// piece is scaled by its decay -- below the diagonal split around the
-// block's first token r as exp(a_l - a_r) exp(a_r - a_s), both <= 1, one
-// exponential per piece; on it masked exponentials -- the dS term by
-// exp(a_last - a_s), and row s by delta_s.  D dy_s joins in fp32 from dy as
-// loaded.
-template <int L> constexpr int kDxWaves = kTileWaves<L>;
+// dy is staged as loaded, and each CBt piece is scaled before its MFMA.
+// FAST (the chunk's whole decay within 2^kBwdFastMaxLog2): by exp(a_l) (0
+// where l < s as CBt itself), the dS term by exp(a_last), and row s by
+// delta_s exp(-a_s) at the end.  Otherwise by the decay exp(a_l - a_s) --
+// below the diagonal split around the block's first token r as
+// exp(a_l - a_r) exp(a_r - a_s), both <= 1, one exponential per piece; on
+// it masked exponentials -- the dS term by exp(a_last - a_s), and row s by
+// delta_s.  D dy_s joins in fp32, from the staged dy.
+// Waves of a dx tile: eight from 128-token chunks on (one or two row groups
+// each), four for 64-token chunks.
+template <int L> constexpr int kDxWaves = L >= 128 ? 8 : 4;
 
-__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-  return make_uint2(v[0], v[1]);
+// CBt piece at k-step q times exp(a_l) (el: exp(a) per token; factored path).
+__device__ __forceinline__ bf16x8 dx_scaled_cbt(const bf16x8& v, int q, int kq, const float* el) {
+  const float4 f0 = *reinterpret_cast<const float4*>(&el[32 * q + kq]);
+  const float4 f1 = *reinterpret_cast<const float4*>(&el[32 * q + kq + 4]);
+  const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+  float mv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mv[e] = static_cast<float>(v[e]) * f[e];
+  return Mfma<bf16>::pack(mv);
 }
 
 // CBt piece of row s (row group m) at k-step q times its decay (exact path).
@@ -1183,12 +1189,10 @@ __device__ __forceinline__ void bwd_dx_tile(const ScanTile& T, float last2, cons
   const auto rdy = rows_rsrc(dy, T, H, P, HPx);
   const auto rda = buf_rsrc(dAcs + jh * L, L * 4);
   uint4 yv[XU];
-  float ya[XU];                            // a at the row of each piece (FAST)
 #pragma unroll
   for (int u = 0; u < XU; ++u) {
     const int i = tid + NT * u, r = i / CPR, c = i % CPR;
     yv[u] = buf_load16(rdy, ((uint32_t)r * HPx + c * 8) * 2u);
-    if constexpr (FAST) ya[u] = buf_load4(rda, (uint32_t)r * 4u);
   }
   const auto rh = buf_rsrc(dS16 + jh * P * N, P * N * 2);
   uint4 hv[HU];
@@ -1205,15 +1209,12 @@ __device__ __forceinline__ void bwd_dx_tile(const ScanTile& T, float last2, cons
       fb[i][k] = __builtin_bit_cast(bf16x8, buf_load16(rb, ((uint32_t)srow[i] * GN + 32 * k + kq) * 2u));
   const auto rct = buf_rsrc(cbt + ((int64_t)T.j * G + g) * L * L, L * L * 2);
 
-  // ---- stage dy (FAST: times exp(a_l), 0 past the chunk), the dS tile and
-  // the per-token values
+  // ---- stage dy as loaded (rows past the chunk arrived as zeros), the dS
+  // tile and the per-token values
 #pragma unroll
   for (int u = 0; u < XU; ++u) {
     const int i = tid + NT * u, r = i / CPR, c = i % CPR;
-    uint4 v = yv[u];
-    if constexpr (FAST)                    // exp2(-inf) = 0 past the chunk
-      v = __builtin_bit_cast(uint4, scale_bf16x8(v, exp2_fast(r < T.len ? ya[u] * kLog2e : -__builtin_inff())));
-    *reinterpret_cast<uint4*>(&ys[r * P + ((c ^ tile_sw<CPR>(r)) << 3)]) = v;
+    *reinterpret_cast<uint4*>(&ys[r * P + ((c ^ tile_sw<CPR>(r)) << 3)]) = yv[u];
   }
 #pragma unroll
   for (int u = 0; u < HU; ++u) {
@@ -1226,7 +1227,9 @@ __device__ __forceinline__ void bwd_dx_tile(const ScanTile& T, float last2, cons
       dal2[tid] = a2;
       dls[tid] = dl_t;
     }
-    if constexpr (!FAST) {
+    if constexpr (FAST) {
+      if (tid < L) cfr[tid] = exp2_fast(a2);   // exp(a_l); past the chunk a is flat: finite
+    } else {
       const float a2r = __shfl(a2, lane & ~31);   // the first token of the 32-token block
       if (tid < L) cfr[tid] = exp2_fast(a2 - a2r);
     }
@@ -1252,8 +1255,8 @@ __device__ __forceinline__ void bwd_dx_tile(const ScanTile& T, float last2, cons
   // chunk's last) aims past the records and reads zeros.  Steps before a
   // row group's first multiply nothing; the loop ends at the chunk's last
   // k-step.
-  // (two operand slots with 256-token chunks keep the tile within 128 VGPRs)
-  constexpr int RD = 3, XR = L >= 256 ? 2 : 3, NOP = NQ * PT;
+  // (two operand slots from 128-token chunks on keep the tile within 128 VGPRs)
+  constexpr int RD = 3, XR = L >= 128 ? 2 : 3, NOP = NQ * PT;
   const int xrow = 8 * kg + (lr >> 2);
   const int xsl = tile_sw<CPR>(xrow) >> 1;
   const int xcol = ((lr & 3) >> 1) * 8 + (lr & 1) * 4;
@@ -1282,7 +1285,7 @@ __device__ __forceinline__ void bwd_dx_tile(const ScanTile& T, float last2, cons
 #pragma unroll
       for (int i = 0; i < RGW; ++i) {
         if (q >= qs[i]) {                  // wave-uniform
-          if constexpr (FAST) fm[i] = ring[i][q % RD];
+          if constexpr (FAST) fm[i] = dx_scaled_cbt(ring[i][q % RD], q, kq, cfr);
           else fm[i] = dx_masked_cbt(ring[i][q % RD], mg[i], q, srow[i], kq, dal2, cfr);
         }
       }
@@ -1293,16 +1296,18 @@ __device__ __forceinline__ void bwd_dx_tile(const ScanTile& T, float last2, cons
     if (n + XR < NOP) fxr[n % XR] = scan_x_operand<P>(ys, (n + XR) / PT, (n + XR) % PT, xrow, xsl, xcol);
   }
 
-  // ---- epilogue: row factor and D dy in fp32 (dy as loaded at this lane's
-  // outputs), rounded once; the tile goes to LDS over dy (every wave is done
-  // with it) in the out_sw layout, a lane's four p of one token as one
-  // 8-byte piece, and leaves as whole rows
+  // ---- epilogue: row factor and D dy in fp32 (dy from the staged tile, at
+  // this lane's outputs), rounded once; the tile goes to LDS over dy (every
+  // wave is done with it) in the out_sw layout, a lane's four p of one token
+  // as one 8-byte piece, and leaves as whole rows
   uint2 dyr[RGW][PT];
 #pragma unroll
   for (int i = 0; i < RGW; ++i)
 #pragma unroll
-    for (int a = 0; a < PT; ++a)
-      dyr[i][a] = buf_load8(rdy, ((uint32_t)srow[i] * HPx + 16 * a + 4 * kg) * 2u);
+    for (int a = 0; a < PT; ++a) {
+      const int s = srow[i], c = 2 * a + (kg >> 1);   // p = 16 a + 4 kg: piece c, half kg & 1
+      dyr[i][a] = *reinterpret_cast<const uint2*>(&ys[s * P + ((c ^ tile_sw<CPR>(s)) << 3) + 4 * (kg & 1)]);
+    }
   const float Dh = D ? D[h] : 0.f;
   float rsc[RGW];
 #pragma unroll
@@ -1348,7 +1353,7 @@ __global__ __launch_bounds__(64 * kDxWaves<L>) __attribute__((amdgpu_waves_per_e
   __shared__ __align__(16) bf16 hsm[P * (N + 8)];
   __shared__ __align__(16) float dal2[L];  // running sum of delta*A, times log2(e)
   __shared__ __align__(16) float dls[L];   // delta
-  __shared__ __align__(16) float cfr[L];   // exp(a_l - a_r), r = first token of l's 32-block
+  __shared__ __align__(16) float cfr[L];   // exp(a_l) (factored) or exp(a_l - a_r), r = first of l's 32-block
   const int2 ci = xcd_chunk_head(blockIdx.x, H);
   if (ci.x >= nslots) return;
   // the running sum is monotone inside a chunk and flat past its end: its
