@@ -165,6 +165,27 @@ def test_backward_after_forward_reuses_its_intermediates(packed):
         assert torch.equal(got[k], ref[k]), k
 
 
+def test_backward_repeated_calls_on_one_workspace():
+    # every call on one workspace (first filled with stale bytes) gives the
+    # fresh-workspace gradients bit for bit: nothing a call reads from the
+    # workspace is left over from an earlier call
+    prob = Problem(1, 700, 6, 64, 128, 2, 256, "bf16")
+    inp = make_inputs(prob, Recipe(init_std=0.3), seed=31)
+    gen = torch.Generator().manual_seed(1031)
+    dy = torch.randn(inp["x"].shape, generator=gen, dtype=torch.float32).to(inp["x"].dtype).cuda()
+    dfin = torch.randn((prob.nseq, prob.nheads, prob.headdim, prob.dstate), generator=gen).cuda()
+    d = to_dev(inp)
+    kw = dict(D=d["D"], dt_bias=d["dt_bias"], initial_states=d["init"], cu_seqlens=d["cu_seqlens"])
+    ref = binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, dy, dfin, **kw)
+    ws = torch.full_like(ref["workspace"], 0x5a)
+    for _ in range(3):
+        got = binding.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], prob.chunk_size, dy, dfin,
+                              workspace=ws, **kw)
+        torch.cuda.synchronize()
+        for k in ("A", "D", "dt_bias", "dt", "x"):
+            assert torch.equal(got[k], ref[k]), k
+
+
 def test_backward_after_forward_needs_a_workspace():
     prob = Problem(1, 100, 2, 32, 32, 1, 64, "bf16")
     d = to_dev(make_inputs(prob, Recipe(), seed=1))
