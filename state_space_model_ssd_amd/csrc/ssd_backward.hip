@@ -36,8 +36,9 @@
 // Launches: Q tiles (1, and each chunk's log-decay) -> reverse chain (2,
 // and <dS_j, H_j> in pieces) -> V tiles (3's intra sums, dCB summed over
 // head blocks) -> head-block sum of dCB -> dB/dC per group (4, and the inter
-// and state row dots of da per head) -> dx tiles -> per-token pass (3's
-// da, ddelta, ddt) -> per-head sums (5).
+// and state row dots of da per head) -> per-token pass (3's da, ddelta,
+// ddt) -> dx (with bf16 inputs it also does 5; with fp32 inputs a per-head
+// sum launch follows).
 //
 // The contractions are 64 x 64 output tiles.  With bf16 inputs they run on
 // the bf16 MFMA: a head's rows staged in LDS from whole-line loads, or
@@ -63,9 +64,11 @@ constexpr float kBwdFastMaxLog2 = 64.f;
 // Most blocks a group's heads are split into for the summed dCB and the
 // dB/dC state terms.  More blocks: more workgroups in 3a and 4a, but more
 // partial sums written there and read in 3b' and 4b; the launcher takes the
-// fewest that give kBwdMinWgPerCu workgroups per CU.
+// fewest that give kBwdMinWgPerCu workgroups per CU (three: V 30.7 -> 28.7
+// us on the Mamba-2 layer shape against 0.9 us more in the dCB sum and dB/dC;
+// four gain nothing in V).
 constexpr int kBwdHeadBlocks = 8;
-constexpr int kBwdMinWgPerCu = 2;
+constexpr int kBwdMinWgPerCu = 3;
 
 template <typename T>
 __device__ __forceinline__ float ld(const T* p) { return to_f32(*p); }
@@ -1327,9 +1330,12 @@ __device__ __forceinline__ void bwd_dx_tile(const ScanTile& T, float last2, cons
     }
   __syncthreads();
   const auto rdx = rows_rsrc(dx, T, H, P, HPx);
+  // the store rows from a fresh copy of the thread index: indices shared with
+  // the staging loop would stay live across the tile
+  const int tids = opaque_tid();
 #pragma unroll
   for (int u = 0; u < XU; ++u) {
-    const int i = tid + NT * u, r = i / CPR, c = i % CPR;
+    const int i = tids + NT * u, r = i / CPR, c = i % CPR;
     const int sw = out_sw<P>(r);
     const uint2 v0 = *reinterpret_cast<const uint2*>(&ys[r * P + ((2 * c) ^ sw) * 4]);
     const uint2 v1 = *reinterpret_cast<const uint2*>(&ys[r * P + ((2 * c + 1) ^ sw) * 4]);
@@ -1338,6 +1344,36 @@ __device__ __forceinline__ void bwd_dx_tile(const ScanTile& T, float last2, cons
 }
 
 // grid: xcd_grid(chunk slots, H), a chunk's heads on its XCD.
+// dA, dD and dt_bias of head h: the per-token pass's parts summed over the
+// chunk slots (lanes stride the slots, then a shuffle sum; one wave).
+__device__ __forceinline__ void head_sums(const float* __restrict__ dA_part,
+                                          const float* __restrict__ dD_part,
+                                          const float* __restrict__ dbias_part, int h, int H,
+                                          int nslots, int lane, float* __restrict__ dA,
+                                          float* __restrict__ dD, float* __restrict__ dbias) {
+  float sa = 0.f, sd = 0.f, sb = 0.f;
+  for (int j = lane; j < nslots; j += kWave) {
+    sa += dA_part[(int64_t)j * H + h];
+    sd += dD_part[(int64_t)j * H + h];
+    sb += dbias_part[(int64_t)j * H + h];
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    sa += __shfl_xor(sa, off);
+    sd += __shfl_xor(sd, off);
+    sb += __shfl_xor(sb, off);
+  }
+  if (lane == 0) {
+    dA[h] = sa;
+    if (dD) dD[h] = sd;
+    if (dbias) dbias[h] = sb;
+  }
+}
+
+// grid: xcd_grid(chunk slots, H), a chunk's heads on its XCD.  The first
+// wave of chunk slot 0's workgroup for head h, once its tile is stored, also
+// writes that head's dA, dD and dt_bias (the per-token pass runs before this
+// launch).
 template <int P, int N, int L>
 __global__ __launch_bounds__(64 * kDxWaves<L>) __attribute__((amdgpu_waves_per_eu(
     kTileWavesPerEU<L, kDxWaves<L>>))) void bwd_dx_scan_kernel(ChunkMap cm, int nslots,
@@ -1348,7 +1384,12 @@ __global__ __launch_bounds__(64 * kDxWaves<L>) __attribute__((amdgpu_waves_per_e
                                                               const float* __restrict__ dAcs,
                                                               const bf16* __restrict__ dS16,
                                                               const float* __restrict__ D, int H, int G,
-                                                              bf16* __restrict__ dx) {
+                                                              bf16* __restrict__ dx,
+                                                              const float* __restrict__ dA_part,
+                                                              const float* __restrict__ dD_part,
+                                                              const float* __restrict__ dbias_part,
+                                                              float* __restrict__ dA, float* __restrict__ dD,
+                                                              float* __restrict__ dbias) {
   __shared__ __align__(16) bf16 ys[L * P];
   __shared__ __align__(16) bf16 hsm[P * (N + 8)];
   __shared__ __align__(16) float dal2[L];  // running sum of delta*A, times log2(e)
@@ -1360,14 +1401,17 @@ __global__ __launch_bounds__(64 * kDxWaves<L>) __attribute__((amdgpu_waves_per_e
   // value at the last position bounds every |a_s|
   const float last = dAcs[((int64_t)ci.x * H + ci.y) * L + L - 1];
   const ChunkDesc cd = cm.desc(ci.x);
-  if (cd.len <= 0) return;
-  const ScanTile T{ci.x, ci.y, cd.start, cd.len};
-  if (fabsf(last) * kLog2e <= kBwdFastMaxLog2)   // uniform over the workgroup
-    bwd_dx_tile<P, N, L, true>(T, last * kLog2e, B, dy, cbt, delta, dAcs, dS16, D, H, G, dx, ys, hsm, dal2,
-                               dls, cfr);
-  else
-    bwd_dx_tile<P, N, L, false>(T, last * kLog2e, B, dy, cbt, delta, dAcs, dS16, D, H, G, dx, ys, hsm, dal2,
-                                dls, cfr);
+  if (cd.len > 0) {
+    const ScanTile T{ci.x, ci.y, cd.start, cd.len};
+    if (fabsf(last) * kLog2e <= kBwdFastMaxLog2)   // uniform over the workgroup
+      bwd_dx_tile<P, N, L, true>(T, last * kLog2e, B, dy, cbt, delta, dAcs, dS16, D, H, G, dx, ys, hsm,
+                                 dal2, dls, cfr);
+    else
+      bwd_dx_tile<P, N, L, false>(T, last * kLog2e, B, dy, cbt, delta, dAcs, dS16, D, H, G, dx, ys, hsm,
+                                  dal2, dls, cfr);
+  }
+  if (ci.x == 0 && threadIdx.x < kWave)
+    head_sums(dA_part, dD_part, dbias_part, ci.y, H, nslots, threadIdx.x, dA, dD, dbias);
 }
 
 // 3b'. The group's dCB: the HB partial sums of 3a added into the first,
@@ -1790,8 +1834,10 @@ __global__ __launch_bounds__(L) void bwd_token_kernel(
   }
 }
 
-// 5. dA, dD, dt_bias: sums over the chunk slots; one wave per head (lanes
-// stride the slots, then a shuffle sum).  grid (H), kWave threads.
+// 5, with fp32 inputs and for a problem without chunks (with bf16 inputs
+// dx's launch does it): dA, dD, dt_bias as sums over the chunk slots; one
+// wave per head (lanes stride the slots, then a shuffle sum).  grid (H),
+// kWave threads.
 __global__ __launch_bounds__(kWave) void bwd_head_reduce_kernel(
     const float* __restrict__ dA_part, const float* __restrict__ dD_part,
     const float* __restrict__ dbias_part, int H, int nslots, float* __restrict__ dA,
@@ -1883,19 +1929,23 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
                      dim3(kBwdThreads), 0, s, cm, mc, x, B, C, dy, a.delta, a.dAcs, hin, b.dS,
                      static_cast<const bf16*>(b.dS16), b.dcb, H, G, HB, (T*)b.dB, (T*)b.dC, b.interpart,
                      b.vxpart);
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((bwd_dx_scan_kernel<P, N, L>), dim3(xcd_grid(mc, H)), dim3(64 * kDxWaves<L>), 0, s,
-                       cm, mc, (const bf16*)B, (const bf16*)dy, static_cast<const bf16*>(b.cbt), a.delta,
-                       a.dAcs, static_cast<const bf16*>(b.dS16), a.D, H, G, (bf16*)b.dx);
-  else
-    hipLaunchKernelGGL((bwd_dx_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * ((P + 63) / 64) * H)),
-                       dim3(kBwdThreads), 0, s, cm, mc, B, dy, cb, a.delta, a.dAcs, b.dS, a.D, H, G,
-                       (T*)b.dx);
+  // the per-token pass, then dx; with bf16 inputs dx's launch also sums the
+  // per-token pass's parts of dA, dD and dt_bias per head
   hipLaunchKernelGGL((bwd_token_kernel<T, P, N, L>), dim3(H, mc), dim3(L), 0, s, cm, a.dt, a.dt_bias,
                      a.A, a.delta, a.dAcs, b.ghpart, b.rowpart, b.colpart, b.vxpart, b.interpart,
                      b.ddot, H, a.dt_min, a.dt_max, b.ddt, b.dA_part, b.dD_part, b.dbias_part);
-  hipLaunchKernelGGL(bwd_head_reduce_kernel, dim3(H), dim3(kWave), 0, s, b.dA_part, b.dD_part,
-                     b.dbias_part, H, mc, b.dA, b.dD, b.ddt_bias);
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((bwd_dx_scan_kernel<P, N, L>), dim3(xcd_grid(mc, H)), dim3(64 * kDxWaves<L>), 0, s,
+                       cm, mc, (const bf16*)B, (const bf16*)dy, static_cast<const bf16*>(b.cbt), a.delta,
+                       a.dAcs, static_cast<const bf16*>(b.dS16), a.D, H, G, (bf16*)b.dx, b.dA_part,
+                       b.dD_part, b.dbias_part, b.dA, b.dD, b.ddt_bias);
+  } else {
+    hipLaunchKernelGGL((bwd_dx_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * ((P + 63) / 64) * H)),
+                       dim3(kBwdThreads), 0, s, cm, mc, B, dy, cb, a.delta, a.dAcs, b.dS, a.D, H, G,
+                       (T*)b.dx);
+    hipLaunchKernelGGL(bwd_head_reduce_kernel, dim3(H), dim3(kWave), 0, s, b.dA_part, b.dD_part,
+                       b.dbias_part, H, mc, b.dA, b.dD, b.ddt_bias);
+  }
   return hipGetLastError();
 }
 
