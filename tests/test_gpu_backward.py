@@ -87,13 +87,15 @@ def test_backward_long_memory_small_steps():
 
 
 @pytest.mark.parametrize("shape,lens", [((1, 520, 4, 64, 128, 2, 256, "bf16"), None),
+                                        ((1, 300, 2, 64, 128, 1, 128, "bf16"), None),
+                                        ((2, 100, 2, 64, 128, 1, 64, "bf16"), None),
                                         ((2, 130, 4, 32, 32, 2, 64, "bf16"), None),
                                         ((1, 230, 2, 32, 32, 1, 64, "bf16"), (100, 1, 64, 65))],
-                         ids=["L256", "L64", "packed"])
+                         ids=["L256", "L128", "P64N128L64", "L64", "packed"])
 def test_backward_small_steps_bf16(shape, lens):
     # small steps (dt near dt_bias in [1e-3, 1e-1]): every chunk's total
-    # decay stays within 2^64, so dx takes its factored-decay path (dy rows
-    # scaled by exp(a_l), CB unmasked, rows rescaled by exp(-a_s)); the
+    # decay stays within 2^64, so dx takes its factored-decay path (CB^T
+    # pieces scaled by exp(a_l), rows rescaled by delta_s exp(-a_s)); the
     # default recipe's larger steps exercise the masked path
     b, T, H, P, N, G, L, dt = shape
     prob = Problem(b, T, H, P, N, G, L, dt, seq_lens=lens)
