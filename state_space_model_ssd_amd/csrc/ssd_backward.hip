@@ -1106,9 +1106,9 @@ __global__ __launch_bounds__(kBwdThreads, 8) void bwd_dx_tiled_kernel(
 // written by 3a, stream from memory through a register ring as the B
 // operands (CB rows there); the dS term is its inter-chunk term with dS as
 // the state and B rows as the C rows.  A lane holds four consecutive p of
-// one token s.  Waves own mirror pairs of 16-row groups of s: row group m
-// meets the k-steps from m / 2 on, so a pair carries the same work as any
-// other.
+// one token s.  Row group m (16 tokens s) meets the k-steps from m / 2 on;
+// with 256-token chunks each wave owns a mirror pair of row groups, so every
+// wave carries the same work, otherwise one row group.
 // dy is staged as loaded, and each CBt piece is scaled before its MFMA.
 // FAST (the chunk's whole decay within 2^kBwdFastMaxLog2): by exp(a_l) (0
 // where l < s as CBt itself), the dS term by exp(a_last), and row s by
@@ -1117,6 +1117,7 @@ __global__ __launch_bounds__(kBwdThreads, 8) void bwd_dx_tiled_kernel(
 // exp(a_l - a_r) exp(a_r - a_s), both <= 1, one exponential per piece; on
 // it masked exponentials -- the dS term by exp(a_last - a_s), and row s by
 // delta_s.  D dy_s joins in fp32, from the staged dy.
+
 // Waves of a dx tile: eight from 128-token chunks on (one or two row groups
 // each), four for 64-token chunks.
 template <int L> constexpr int kDxWaves = L >= 128 ? 8 : 4;
