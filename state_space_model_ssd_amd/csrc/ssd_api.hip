@@ -342,7 +342,7 @@ ssd_status_t run(const ssd_problem_t* p, const void* x, const float* dt, const f
 // The backward's regions follow the forward's in its workspace.
 struct BwdLayout {
   size_t Q, dS, dS16, dcb, rowpart, colpart, vxpart, interpart, ghpart, dla, dA_part, dD_part, dbias_part,
-      ddot, cbt, total;
+      ddot, cbt, dcb16, total;
 };
 
 void bwd_layout_of(const ssd_problem_t* p, const ssd_workspace_layout_t& w, BwdLayout* b) {
@@ -365,6 +365,7 @@ void bwd_layout_of(const ssd_problem_t* p, const ssd_workspace_layout_t& w, BwdL
   b->dbias_part = off; off = align_up(off + sizeof(float) * mc * H);
   b->ddot = off;       off = align_up(off + sizeof(float) * mc * H * L);
   b->cbt = off;        off = align_up(off + sizeof(uint16_t) * mc * p->ngroups * L * L);
+  b->dcb16 = off;      off = align_up(off + sizeof(uint16_t) * mc * p->ngroups * L * L);
   b->total = off;
 }
 
@@ -415,6 +416,7 @@ ssd_status_t run_bwd(const ssd_problem_t* p, const void* x, const float* dt, con
   b.dbias_part = reinterpret_cast<float*>(base + bl.dbias_part);
   b.ddot = reinterpret_cast<float*>(base + bl.ddot);
   b.cbt = base + bl.cbt;
+  b.dcb16 = base + bl.dcb16;
   const Kernels* k = find_kernels(p->dtype, p->headdim, p->dstate, p->chunk_size);
   if (k->backward(a, b, static_cast<hipStream_t>(stream)) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;

@@ -818,7 +818,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_mfma_kernel(
     ChunkMap cm, int nslots, const bf16* __restrict__ x, const bf16* __restrict__ dy,
     const bf16* __restrict__ cb, const float* __restrict__ delta, const float* __restrict__ dAcs, int H,
     int G, int HB, float* __restrict__ dcbp, float* __restrict__ rowpart, float* __restrict__ colpart,
-    float* __restrict__ ddot, bf16* __restrict__ cbt) {
+    float* __restrict__ ddot, bf16* __restrict__ cbt, bf16* __restrict__ dcb16) {
   // per head: a at the tile's rows, a at its columns, delta at its columns
   __shared__ __align__(16) float fac[2][3][64];
   // per head: the tile's dy rows and x rows (P bf16 each, padded rows)
@@ -991,18 +991,33 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_mfma_kernel(
     take(set ^ 1);                         // the next head's rows and factors
   }
   // the block's sum, rows in the chunk (w is 0 above the diagonal; entries
-  // there and past the chunk are never read)
-  float* W = dcbp + (((int64_t)j * G + g) * HB + hb) * L * L;
+  // there and past the chunk are never read): a partial sum in fp32, or,
+  // with one block per group, the group's dCB rounded once to bf16
+  if (HB > 1) {                            // uniform
+    float* W = dcbp + (((int64_t)j * G + g) * HB + hb) * L * L;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int l = l0 + q.row(mi, r);
-      if (l < len) {
+      for (int r = 0; r < 4; ++r) {
+        const int l = l0 + q.row(mi, r);
+        if (l < len) {
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) W[(int64_t)l * L + s0 + q.col(ni)] = w[mi][ni][r];
+          for (int ni = 0; ni < 2; ++ni) W[(int64_t)l * L + s0 + q.col(ni)] = w[mi][ni][r];
+        }
       }
-    }
+  } else {
+    bf16* W = dcb16 + ((int64_t)j * G + g) * L * L;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int l = l0 + q.row(mi, r);
+        if (l < len) {
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) W[(int64_t)l * L + s0 + q.col(ni)] = static_cast<bf16>(w[mi][ni][r]);
+        }
+      }
+  }
 }
 
 // 3b, fp32 inputs: dx as 64 x 64 tiles of (token s, p):
@@ -1415,16 +1430,17 @@ __global__ __launch_bounds__(64 * kDxWaves<L>) __attribute__((amdgpu_waves_per_e
     head_sums(dA_part, dD_part, dbias_part, ci.y, H, nslots, threadIdx.x, dA, dD, dbias);
 }
 
-// 3b'. The group's dCB: the HB partial sums of 3a added into the first,
-// four floats per thread (entries above the diagonal or past the chunk are
-// summed too and never read).  grid (ceil(L*L / 1024), G, chunk slots).
+// 3b'. The group's dCB: the HB partial sums of 3a added, four entries per
+// thread (entries above the diagonal or past the chunk are summed too and
+// never read): into the first partial, or, given dcb16 (bf16 inputs),
+// rounded once to bf16 there.  grid (ceil(L*L / 1024), G, chunk slots).
 template <int L>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dcb_sum_kernel(int G, int HB,
-                                                                  float* __restrict__ dcbp) {
+__global__ __launch_bounds__(kBwdThreads) void bwd_dcb_sum_kernel(int G, int HB, float* __restrict__ dcbp,
+                                                                  bf16* __restrict__ dcb16) {
   const int e = blockIdx.x * kBwdThreads + threadIdx.x;
   if (e >= L * L / 4) return;
-  const int64_t LL4 = (int64_t)L * L / 4;
-  float4* W = reinterpret_cast<float4*>(dcbp) + ((int64_t)blockIdx.z * G + blockIdx.y) * HB * LL4 + e;
+  const int64_t LL4 = (int64_t)L * L / 4, jg = (int64_t)blockIdx.z * G + blockIdx.y;
+  float4* W = reinterpret_cast<float4*>(dcbp) + jg * HB * LL4 + e;
   float4 v = W[0];
   for (int k = 1; k < HB; ++k) {
     const float4 u = W[k * LL4];
@@ -1433,7 +1449,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dcb_sum_kernel(int G, int HB,
     v.z += u.z;
     v.w += u.w;
   }
-  W[0] = v;
+  if (dcb16) store4(dcb16 + (jg * LL4 + e) * 4, v.x, v.y, v.z, v.w);
+  else W[0] = v;
 }
 
 // 4. dC and dB of a group as 64 x 64 tiles of rows x n, rounded once to the
@@ -1456,7 +1473,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
     ChunkMap cm, int nslots, const T* __restrict__ x, const T* __restrict__ B, const T* __restrict__ C,
     const T* __restrict__ dy, const float* __restrict__ delta, const float* __restrict__ dAcs,
     const T* __restrict__ states_in, const float* __restrict__ dS, const bf16* __restrict__ dS16,
-    const float* __restrict__ dcbp, int H, int G, int HB, T* __restrict__ dB, T* __restrict__ dC,
+    const float* __restrict__ dcbp, const bf16* __restrict__ dcb16, int H, int G, int HB,
+    T* __restrict__ dB, T* __restrict__ dC,
     float* __restrict__ interpart, float* __restrict__ vxpart) {
   __shared__ __align__(16) float As[32 * kGemmPitch], Bs[32 * kGemmPitch];
   constexpr int NT = (N + 63) / 64;
@@ -1480,8 +1498,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
   const int nt = n0 / 64;
   float acc[4][4] = {};
   if constexpr (sizeof(T) == 2) {
-    // bf16 MFMA over 32-long k-slices, the summed dCB rounded once to bf16
-    // (masked to s <= l); B (dC) or C (dB) rows staged k-major in LDS
+    // bf16 MFMA over 32-long k-slices, the summed dCB as rounded once to
+    // bf16 by 3a or 3b' (masked to s <= l); B (dC) or C (dB) rows staged
+    // k-major in LDS
     __shared__ __align__(16) bf16 at[32 * kKtPitch], bt[32 * kKtPitch];
     static_assert(32 * 8 == kBwdThreads, "one 8-wide piece of each slice tile per thread");
     const int kr = threadIdx.x >> 3, c = (threadIdx.x & 7) * 8;
@@ -1496,50 +1515,42 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
     // dC: rows l = m0 + row of W, columns s = kb + kq ..; dB: rows l = k of
     // W, columns s = m0 + c ..
     const __amdgpu_buffer_rsrc_t rR = buf_rsrc_u(R + t0 * G * N, (uint32_t)((int64_t)len * G * N * sizeof(T)));
-    const __amdgpu_buffer_rsrc_t rW = buf_rsrc_u(W, (uint32_t)(L * L * sizeof(float)));
-    bf16x8 rvp;
-    uint4 wv[2][2];
+    const __amdgpu_buffer_rsrc_t rW =
+        buf_rsrc_u(dcb16 + ((int64_t)j * G + g) * L * L, (uint32_t)(L * L * sizeof(bf16)));
+    bf16x8 rvp, wv[2];
     auto fetch_intra = [&](int kb) {
       const int k = kb + kr;
       rvp = frag_buf(rR, (uint32_t)(((k * G + g) * N + n0 + c) * sizeof(T)), k < k1 && n0 + c < N);
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
         const int l = m0 + q.wr + mi * 16 + q.lr, s1 = kb + q.kq;
-        const uint32_t off = which == 0 ? (uint32_t)((l * L + s1) * sizeof(float))
-                                        : (uint32_t)((k * L + m0 + c) * sizeof(float));
+        const uint32_t off = which == 0 ? (uint32_t)((l * L + s1) * sizeof(bf16))
+                                        : (uint32_t)((k * L + m0 + c) * sizeof(bf16));
         const bool ok = which == 0 ? (l < len && s1 < k1) : (mi == 0 && k < k1);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) wv[mi][hf] = buf_load16(rW, ok ? off + 16 * hf : kPastRecords);
+        wv[mi] = frag_buf(rW, off, ok);
       }
     };
     fetch_intra(k0);
     for (int kb = k0; kb < k1; kb += 32) {
       const int k = kb + kr;
       const bf16x8 rv = rvp;
-      uint4 wc[2][2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) wc[mi][hf] = wv[mi][hf];
+      const bf16x8 wc[2] = {wv[0], wv[1]};
       fetch_intra(kb + 32);                // past k1: zeros
       bf16x8 av[2];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
-        float u[8];
-        unpack16<float>(wc[mi][0], u);
-        unpack16<float>(wc[mi][1], u + 4);
-        float v[8];
+        bf16x8 v;
         if (which == 0) {
           // A rows l = m0 + row: dCB[l, kb + kq ..] for s <= l
           const int l = m0 + q.wr + mi * 16 + q.lr, s1 = kb + q.kq;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (s1 + e <= l && s1 + e < k1) ? u[e] : 0.f;
+          for (int e = 0; e < 8; ++e) v[e] = (s1 + e <= l && s1 + e < k1) ? wc[mi][e] : bf16(0.f);
         } else {
           // rows l = k: dCB[l, s] for s <= l, k-major
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (m0 + c + e <= k && m0 + c + e < len) ? u[e] : 0.f;
+          for (int e = 0; e < 8; ++e) v[e] = (m0 + c + e <= k && m0 + c + e < len) ? wc[mi][e] : bf16(0.f);
         }
-        av[mi] = Mfma<bf16>::pack(v);
+        av[mi] = v;
       }
       __syncthreads();                     // previous slice consumed
       *reinterpret_cast<bf16x8*>(&bt[kr * kKtPitch + c]) = rv;
@@ -1918,18 +1929,19 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((bwd_v_mfma_kernel<P, L>), dim3(xcd_grid(mc, LT * (LT + 1) / 2 * G * HB)),
                        dim3(kBwdThreads), 0, s, cm, mc, (const bf16*)x, (const bf16*)dy, (const bf16*)cb,
-                       a.delta, a.dAcs, H, G, HB, b.dcb, b.rowpart, b.colpart, b.ddot, static_cast<bf16*>(b.cbt));
+                       a.delta, a.dAcs, H, G, HB, b.dcb, b.rowpart, b.colpart, b.ddot, static_cast<bf16*>(b.cbt),
+                       static_cast<bf16*>(b.dcb16));
   else
     hipLaunchKernelGGL((bwd_v_tiled_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * (LT + 1) / 2 * G * HB)),
                        dim3(kBwdThreads), 0, s, cm, mc, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb,
                        b.rowpart, b.colpart, b.ddot);
   if (HB > 1)
     hipLaunchKernelGGL((bwd_dcb_sum_kernel<L>), dim3((L * L / 4 + kBwdThreads - 1) / kBwdThreads, G, mc),
-                       dim3(kBwdThreads), 0, s, G, HB, b.dcb);
+                       dim3(kBwdThreads), 0, s, G, HB, b.dcb, sizeof(T) == 2 ? static_cast<bf16*>(b.dcb16) : nullptr);
   hipLaunchKernelGGL((bwd_bc_group_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * NT * 2 * G)),
                      dim3(kBwdThreads), 0, s, cm, mc, x, B, C, dy, a.delta, a.dAcs, hin, b.dS,
-                     static_cast<const bf16*>(b.dS16), b.dcb, H, G, HB, (T*)b.dB, (T*)b.dC, b.interpart,
-                     b.vxpart);
+                     static_cast<const bf16*>(b.dS16), b.dcb, static_cast<const bf16*>(b.dcb16), H, G, HB,
+                     (T*)b.dB, (T*)b.dC, b.interpart, b.vxpart);
   // the per-token pass, then dx; with bf16 inputs dx's launch also sums the
   // per-token pass's parts of dA, dD and dt_bias per head
   hipLaunchKernelGGL((bwd_token_kernel<T, P, N, L>), dim3(H, mc), dim3(L), 0, s, cm, a.dt, a.dt_bias,

@@ -92,6 +92,9 @@ struct BwdArgs {
   void* cbt;                // [max_chunks][G][L][L] bf16 (bf16 inputs): CB transposed,
                             // cbt[s][l] = CB[l][s] for s <= l < len, else 0, in the 64 x 64
                             // tiles with l-tile >= s-tile and l-tile inside the chunk
+  void* dcb16;              // [max_chunks][G][L][L] bf16 (bf16 inputs): the group's summed dCB,
+                            // rounded once (rows past the chunk and tiles above the diagonal
+                            // are not written)
 };
 
 // Devices whose per-device launch parameters the library caches.
