@@ -842,9 +842,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_mfma_kernel(
   const int64_t t0 = cd.start;
   const MfmaQuarter q;
   const int lg = q.lane >> 4;
-  const bf16* cbj = cb + ((int64_t)j * G + g) * L * L;
   // CB at this lane's 16 elements, 0 where V is not summed (s > l, rows past
-  // the chunk): the same for every head
+  // the chunk): the same for every head.  Loaded together without a branch
+  // (an element that is not summed aims past the records and reads 0).
+  const __amdgpu_buffer_rsrc_t rcbj = buf_rsrc_u(cb + ((int64_t)j * G + g) * L * L, L * L * sizeof(bf16));
   float cbq[2][2][4];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
@@ -853,7 +854,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_v_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int l = l0 + q.row(mi, r), sx = s0 + q.col(ni);
-        cbq[mi][ni][r] = (l < len && sx <= l) ? static_cast<float>(cbj[(int64_t)l * L + sx]) : 0.f;
+        const uint32_t off = (l < len && sx <= l) ? (uint32_t)(l * L + sx) * sizeof(bf16) : kPastRecords;
+        cbq[mi][ni][r] = static_cast<float>(
+            __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(rcbj, off, 0, 0)));
       }
   // the first head block also writes these values transposed for dx: a
   // lane's four rows l of column s are four consecutive entries of row s
@@ -1592,7 +1595,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
     const __amdgpu_buffer_rsrc_t rk16 =
         buf_rsrc_u(K16 + (int64_t)j * H * P * N, (uint32_t)((int64_t)H * P * N * sizeof(bf16)));
     // the row dots' M[row, n] at this lane's 8 rows and 2 columns of the
-    // product (rows past the chunk and columns past N read 0)
+    // product (rows past the chunk and columns past N read 0), loaded
+    // together without a branch
+    const __amdgpu_buffer_rsrc_t rM = buf_rsrc_u(M + t0 * G * N, (uint32_t)((int64_t)len * G * N * sizeof(T)));
     float mrow[2][2][4];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
@@ -1601,7 +1606,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = m0 + q.row(mi, r), col = n0 + q.col(ni);
-          mrow[mi][ni][r] = (row < len && col < N) ? ld(M + ((t0 + row) * G + g) * N + col) : 0.f;
+          const uint32_t off = col < N ? (uint32_t)((row * G + g) * N + col) * sizeof(T) : kPastRecords;
+          mrow[mi][ni][r] = static_cast<float>(
+              __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(rM, off, 0, 0)));
         }
     bf16x8 ra[2][NPA], rk[2][PP];
     float fl[2];
