@@ -1241,19 +1241,20 @@ __device__ __forceinline__ void bwd_dx_tile(const ScanTile& T, float last2, cons
 #pragma unroll
   for (int u = 0; u < HU; ++u) {
     const int i = tid + NT * u, r = i / HPR, c = i % HPR;
-    if (i < P * HPR) *reinterpret_cast<uint4*>(&hsm[r * HP + c * 8]) = hv[u];
+    if ((P * HPR) % NT == 0 || i < P * HPR) *reinterpret_cast<uint4*>(&hsm[r * HP + c * 8]) = hv[u];
   }
   {
+    // every thread stores its entry (one per thread; those past the chunk's
+    // L tokens are read by none), so that the loads of a and delta stay at
+    // the top
     const float a2 = dA_t * kLog2e;
-    if (tid < L) {                         // whole waves
-      dal2[tid] = a2;
-      dls[tid] = dl_t;
-    }
+    dal2[tid] = a2;
+    dls[tid] = dl_t;
     if constexpr (FAST) {
-      if (tid < L) cfr[tid] = exp2_fast(a2);   // exp(a_l); past the chunk a is flat: finite
+      cfr[tid] = exp2_fast(a2);            // exp(a_l); past the chunk a is flat: finite
     } else {
       const float a2r = __shfl(a2, lane & ~31);   // the first token of the 32-token block
-      if (tid < L) cfr[tid] = exp2_fast(a2 - a2r);
+      cfr[tid] = exp2_fast(a2 - a2r);
     }
   }
   f32x4 acc[RGW][PT];
@@ -1411,9 +1412,10 @@ __global__ __launch_bounds__(64 * kDxWaves<L>) __attribute__((amdgpu_waves_per_e
                                                               float* __restrict__ dbias) {
   __shared__ __align__(16) bf16 ys[L * P];
   __shared__ __align__(16) bf16 hsm[P * (N + 8)];
-  __shared__ __align__(16) float dal2[L];  // running sum of delta*A, times log2(e)
-  __shared__ __align__(16) float dls[L];   // delta
-  __shared__ __align__(16) float cfr[L];   // exp(a_l) (factored) or exp(a_l - a_r), r = first of l's 32-block
+  // per-token vectors, one entry per thread (64 kDxWaves >= L)
+  __shared__ __align__(16) float dal2[64 * kDxWaves<L>];  // running sum of delta*A, times log2(e)
+  __shared__ __align__(16) float dls[64 * kDxWaves<L>];   // delta
+  __shared__ __align__(16) float cfr[64 * kDxWaves<L>];   // exp(a_l) (factored) or exp(a_l - a_r), r = first of l's 32-block
   const int2 ci = xcd_chunk_head(blockIdx.x, H);
   if (ci.x >= nslots) return;
   // the running sum is monotone inside a chunk and flat past its end: its

@@ -309,7 +309,10 @@ __device__ __forceinline__ void scan_tile_body(const ScanTile& T, const bf16* __
 #pragma unroll
   for (int u = 0; u < HU; ++u) {
     const int i = tid + NT * u, r = i / HPR, c = i % HPR;
-    if (i < P * HPR) *reinterpret_cast<uint4*>(&hsm[r * HP + c * 8]) = hv[u];
+    // the guard is a constant where the threads split the tile evenly: with
+    // one that depends on the thread the compiler would move the second load
+    // of the state down to this store and wait for it there
+    if ((P * HPR) % NT == 0 || i < P * HPR) *reinterpret_cast<uint4*>(&hsm[r * HP + c * 8]) = hv[u];
   }
   {
     const float a2 = dA_t * kLog2e;
