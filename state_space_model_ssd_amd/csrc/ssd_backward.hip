@@ -1514,33 +1514,33 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
     zero_quarter(d);
     const int k0 = which == 0 ? 0 : m0, k1 = which == 0 ? min(len, m0 + 64) : len;
     const T* R = which == 0 ? B : C;       // rows k of the second operand
-    // The next slice's pieces are loaded while the current one is
-    // multiplied: buffer loads issued without a branch whichever the tile
+    // A slice's pieces are loaded two slices ahead, while the slice between
+    // is multiplied: buffer loads issued without a branch whichever the tile
     // (a load a tile does not need aims past the records and reads zeros).
     // dC: rows l = m0 + row of W, columns s = kb + kq ..; dB: rows l = k of
     // W, columns s = m0 + c ..
     const __amdgpu_buffer_rsrc_t rR = buf_rsrc_u(R + t0 * G * N, (uint32_t)((int64_t)len * G * N * sizeof(T)));
     const __amdgpu_buffer_rsrc_t rW =
         buf_rsrc_u(dcb16 + ((int64_t)j * G + g) * L * L, (uint32_t)(L * L * sizeof(bf16)));
-    bf16x8 rvp, wv[2];
-    auto fetch_intra = [&](int kb) {
+    // Two register sets (set = the slice's parity) hold them, so the loop
+    // carries no register copies and waits only for the older set.
+    bf16x8 rvp[2], wv[2][2];
+    auto fetch_intra = [&](int set, int kb) {
       const int k = kb + kr;
-      rvp = frag_buf(rR, (uint32_t)(((k * G + g) * N + n0 + c) * sizeof(T)), k < k1 && n0 + c < N);
+      rvp[set] = frag_buf(rR, (uint32_t)(((k * G + g) * N + n0 + c) * sizeof(T)), k < k1 && n0 + c < N);
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
         const int l = m0 + q.wr + mi * 16 + q.lr, s1 = kb + q.kq;
         const uint32_t off = which == 0 ? (uint32_t)((l * L + s1) * sizeof(bf16))
                                         : (uint32_t)((k * L + m0 + c) * sizeof(bf16));
         const bool ok = which == 0 ? (l < len && s1 < k1) : (mi == 0 && k < k1);
-        wv[mi] = frag_buf(rW, off, ok);
+        wv[set][mi] = frag_buf(rW, off, ok);
       }
     };
-    fetch_intra(k0);
-    for (int kb = k0; kb < k1; kb += 32) {
+    auto intra = [&](int set, int kb) {
       const int k = kb + kr;
-      const bf16x8 rv = rvp;
-      const bf16x8 wc[2] = {wv[0], wv[1]};
-      fetch_intra(kb + 32);                // past k1: zeros
+      const bf16x8 rv = rvp[set];
+      const bf16x8 wc[2] = {wv[set][0], wv[set][1]};
       bf16x8 av[2];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
@@ -1572,7 +1572,19 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
       } else {
         mfma_kmajor(q, at, bt, d);
       }
+      fetch_intra(set, kb + 64);           // past k1: zeros
+      __builtin_amdgcn_sched_barrier(0);   // keep the sets' loads in issue order
+    };
+    fetch_intra(0, k0);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_intra(1, k0 + 32);
+    __builtin_amdgcn_sched_barrier(0);
+    int kb = k0;
+    for (; kb + 32 < k1; kb += 64) {       // whole pairs of slices
+      intra(0, kb);
+      intra(1, kb + 32);
     }
+    if (kb < k1) intra(0, kb);             // an odd count's last slice
     // The state terms, head by head: the rows (dy or x, exact bf16, staged
     // in LDS from whole-line loads) times the head's P x 64 operand (the
     // entering state or dS in bf16, staged k-major); both alternate between
@@ -1813,21 +1825,43 @@ __global__ __launch_bounds__(L) void bwd_token_kernel(
   const float alast = a[len - 1];
   const float dk = delta[jh * L + k];
   const int64_t tk = cd.start + k;
-  float rowsum = 0.f, sdir = 0.f, inter = 0.f, vxe = 0.f, dd = 0.f;
-  if (valid) {
-    for (int st = 0; st <= k / 64; ++st)
+  // Every partial sum of the token is loaded at once, without a branch: a
+  // slot the token does not take (every slot, past the chunk's end) aims
+  // past the records and reads zero, and the sums run in slot order.
+  const int kt = k / 64;
+  const uint32_t ko = (uint32_t)k * 4u;
+  const __amdgpu_buffer_rsrc_t rrow = buf_rsrc_u(rowpart + jh * LT * RH * L, LT * RH * L * 4u);
+  const __amdgpu_buffer_rsrc_t rcol = buf_rsrc_u(colpart + jh * LT * RH * L, LT * RH * L * 4u);
+  const __amdgpu_buffer_rsrc_t rvx = buf_rsrc_u(vxpart + jh * VX * L, VX * L * 4u);
+  const __amdgpu_buffer_rsrc_t rin = buf_rsrc_u(interpart + jh * VX * L, VX * L * 4u);
+  float rp[LT][RH], cp[LT][RH], vp[VX], ip[VX];
 #pragma unroll
-      for (int u = 0; u < RH; ++u) rowsum += rowpart[(jh * LT * RH + st * RH + u) * L + k];
-    for (int lt = k / 64; lt < LT && lt * 64 < len; ++lt)
+  for (int st = 0; st < LT; ++st)
 #pragma unroll
-      for (int u = 0; u < RH; ++u) sdir += colpart[(jh * LT * RH + lt * RH + u) * L + k];
-#pragma unroll
-    for (int v = 0; v < VX; ++v) {
-      vxe += vxpart[(jh * VX + v) * L + k];
-      inter += interpart[(jh * VX + v) * L + k];
+    for (int u = 0; u < RH; ++u) {
+      const uint32_t o = (uint32_t)((st * RH + u) * L) * 4u + ko;
+      rp[st][u] = buf_load4(rrow, valid && st <= kt ? o : kPastRecords);
+      cp[st][u] = buf_load4(rcol, valid && st >= kt && st * 64 < len ? o : kPastRecords);
     }
+#pragma unroll
+  for (int v = 0; v < VX; ++v) {
+    vp[v] = buf_load4(rvx, valid ? (uint32_t)(v * L) * 4u + ko : kPastRecords);
+    ip[v] = buf_load4(rin, valid ? (uint32_t)(v * L) * 4u + ko : kPastRecords);
   }
-  dd = valid ? ddot[jh * L + k] : 0.f;    // dy_k . x_k, from the V tiles
+  const float dd = valid ? ddot[jh * L + k] : 0.f;    // dy_k . x_k, from the V tiles
+  float rowsum = 0.f, sdir = 0.f, inter = 0.f, vxe = 0.f;
+#pragma unroll
+  for (int st = 0; st < LT; ++st)
+#pragma unroll
+    for (int u = 0; u < RH; ++u) {
+      rowsum += rp[st][u];
+      sdir += cp[st][u];
+    }
+#pragma unroll
+  for (int v = 0; v < VX; ++v) {
+    vxe += vp[v];
+    inter += ip[v];
+  }
   const float vs = dk * vxe;
   // <dS_j, H_j>: the chain's partial sums, one per 256 state elements
   constexpr int NW = P * N / (4 * kWave);
