@@ -516,11 +516,11 @@ __device__ __forceinline__ float4 load4_f32(const bf16* p) {
 // chunk j with the state entering it (the chunk's last token's da needs
 // it), as one partial sum per wave (256 state elements): ghpart[j][h][PN /
 // 256].  dS in fp32 is written only where dS32 is given (the fp32 path's
-// operands).  Two register sets hold the Q piece, entering state and
-// log-decay of the next two chunks: every load is a vector load issued
-// without a branch, so the wait before a set's use leaves the other set's
+// operands).  A ring of D register sets holds the Q piece, entering state
+// and log-decay of the next D chunks: every load is a vector load issued
+// without a branch, so the wait before a set's use leaves the other sets'
 // loads in flight.  grid (ceil(P*N / 1024), H, nstates).
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(
     ChunkMap cm, const float* __restrict__ Q, const float* __restrict__ dla,
     const float* __restrict__ dfinal, const T* __restrict__ states_in, int H, int PN,
@@ -533,37 +533,42 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(
   float4 g = dfinal ? *reinterpret_cast<const float4*>(dfinal + ((int64_t)s * H + h) * PN + e)
                     : make_float4(0.f, 0.f, 0.f, 0.f);
   if (r.y > r.x) {
-    float4 q[2], hv[2];
-    float la[2];
+    float4 q[D], hv[D];
+    float la[D];
     auto loads = [&](int set, int j) {
       const int64_t jh = (int64_t)j * H + h;
       q[set] = *reinterpret_cast<const float4*>(Q + jh * PN + e);
       hv[set] = load4_f32(states_in + jh * PN + e);
       la[set] = ld_vmem(dla + jh);
     };
-    auto step = [&](int set, int j) {      // chunk j with set's values; then chunk j - 2's loads
+    // chunk j with set's values; then (REFILL) chunk j - D's loads into the set
+    auto step = [&](int set, int j, auto refill) {
       const int64_t jh = (int64_t)j * H + h;
       const float4 qj = q[set], hj = hv[set];
       const float dec = expf(la[set]);
-      loads(set, max(j - 2, r.x));         // before the sequence's start: its first chunk again
+      if constexpr (decltype(refill)::value) loads(set, max(j - D, r.x));   // before the start: its first chunk
       if (dS32) *reinterpret_cast<float4*>(dS32 + jh * PN + e) = g;
       if (dS16) store4(dS16 + jh * PN + e, g.x, g.y, g.z, g.w);   // rounded once, for the MFMA operands
       const float gh = wave_sum_last(g.x * hj.x + g.y * hj.y + g.z * hj.z + g.w * hj.w);
       if ((threadIdx.x & (kWave - 1)) == kWave - 1) ghpart[jh * nw + wv] = gh;
       g = make_float4(dec * g.x + qj.x, dec * g.y + qj.y, dec * g.z + qj.z, dec * g.w + qj.w);
     };
-    loads(0, r.y - 1);
-    __builtin_amdgcn_sched_barrier(0);     // set 0's loads first, as in the loop
-    loads(1, max(r.y - 2, r.x));
-    __builtin_amdgcn_sched_barrier(0);
-    int j = r.y - 1;
-    for (; j - 1 >= r.x; j -= 2) {         // whole pairs: every path issues the same loads
-      step(0, j);
-      __builtin_amdgcn_sched_barrier(0);
-      step(1, j - 1);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < D; ++u) {          // chunks r.y - 1, r.y - 2, .. in sets 0, 1, ..
+      loads(u, max(r.y - 1 - u, r.x));
+      __builtin_amdgcn_sched_barrier(0);   // the sets' loads in the order they are used
     }
-    if (j >= r.x) step(0, j);
+    int j = r.y - 1;
+    for (; j - (D - 1) >= r.x; j -= D) {   // whole rounds of the ring: every path issues the same loads
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        step(u, j - u, std::true_type{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u)        // the last chunks (fewer than D): nothing left to load
+      if (j - u >= r.x) step(u, j - u, std::false_type{});   // uniform over the workgroup
   }
   if (dinit) *reinterpret_cast<float4*>(dinit + ((int64_t)s * H + h) * PN + e) = g;
 }
@@ -1931,6 +1936,17 @@ static int bwd_head_blocks(int hpg, int64_t wg_per_block) {
   return hb;
 }
 
+// Depth of the reverse chain's ring: each chunk in flight holds about 18
+// VGPRs, so the ring gets shallower as the chain's waves fill the device
+// (4 SIMDs per CU): 8 chunks up to one wave per SIMD (long chains over few
+// heads), 4 up to four, else 2.
+static int bwd_chain_depth(int64_t waves) {
+  const int cus = device_cu_count();
+  if (cus <= 0) return 2;
+  const int64_t simds = 4LL * cus;
+  return waves <= simds ? 8 : waves <= 4 * simds ? 4 : 2;
+}
+
 template <typename T, int P, int N, int L>
 hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
   const int mc = a.max_chunks, H = a.H, G = a.G, PN = P * N;
@@ -1960,10 +1976,18 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
                        dim3(kBwdThreads), 0, s, cm, mc, dy, C, a.dAcs, H, G, b.Q, b.dla);
   static_assert((P * N) % 4 == 0, "four state elements per thread");
   static_assert(PN % (4 * kWave) == 0, "whole waves of the chain");
-  hipLaunchKernelGGL((bwd_chain_kernel<T>), dim3((PN / 4 + kBwdThreads - 1) / kBwdThreads, H, a.nstates),
-                     dim3(kBwdThreads), 0, s, cm, b.Q, b.dla, b.dfinal, hin, H, PN,
-                     sizeof(T) == 4 ? b.dS : nullptr, sizeof(T) == 2 ? static_cast<bf16*>(b.dS16) : nullptr,
-                     b.ghpart, b.dinit);
+  {
+    const dim3 cg((PN / 4 + kBwdThreads - 1) / kBwdThreads, H, a.nstates);
+    auto chain = [&](auto kern) {
+      hipLaunchKernelGGL(kern, cg, dim3(kBwdThreads), 0, s, cm, b.Q, b.dla, b.dfinal, hin, H, PN,
+                         sizeof(T) == 4 ? b.dS : nullptr,
+                         sizeof(T) == 2 ? static_cast<bf16*>(b.dS16) : nullptr, b.ghpart, b.dinit);
+    };
+    const int depth = bwd_chain_depth((int64_t)cg.x * cg.y * cg.z * (kBwdThreads / kWave));
+    if (depth == 8) chain(bwd_chain_kernel<T, 8>);
+    else if (depth == 4) chain(bwd_chain_kernel<T, 4>);
+    else chain(bwd_chain_kernel<T, 2>);
+  }
   constexpr int LT = L / 64;
   // head blocks per group for the summed dCB: the fewest that fill the GPU
   // with 3a's workgroups (their partial sums fit the workspace's H L^2
