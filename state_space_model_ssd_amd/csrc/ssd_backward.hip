@@ -1511,7 +1511,18 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
     // bf16 MFMA over 32-long k-slices, the summed dCB as rounded once to
     // bf16 by 3a or 3b' (masked to s <= l); B (dC) or C (dB) rows staged
     // k-major in LDS
-    __shared__ __align__(16) bf16 at[32 * kKtPitch], bt[32 * kKtPitch];
+    // One LDS region serves the three phases in turn -- the slices' k-major
+    // tiles (at, bt), the heads' operand and row tiles (kt, ta), the final
+    // regrouping of the quarters -- with a barrier between phases, so that
+    // three workgroups fit on a CU.
+    constexpr int kKtBytes = 2 * P * kKtPitch * 2, kTaBytes = 2 * 64 * (P + 8) * 2;
+    constexpr int kSliceBytes = 2 * 32 * kKtPitch * 2, kRegroupBytes = 2 * 32 * kGemmPitch * 4;
+    constexpr int kRegion = kKtBytes + kTaBytes > kSliceBytes
+                                ? (kKtBytes + kTaBytes > kRegroupBytes ? kKtBytes + kTaBytes : kRegroupBytes)
+                                : (kSliceBytes > kRegroupBytes ? kSliceBytes : kRegroupBytes);
+    __shared__ __align__(16) unsigned char region[kRegion];
+    bf16* at = reinterpret_cast<bf16*>(region);
+    bf16* bt = at + 32 * kKtPitch;
     static_assert(32 * 8 == kBwdThreads, "one 8-wide piece of each slice tile per thread");
     const int kr = threadIdx.x >> 3, c = (threadIdx.x & 7) * 8;
     const MfmaQuarter q;
@@ -1590,6 +1601,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
       intra(1, kb + 32);
     }
     if (kb < k1) intra(0, kb);             // an odd count's last slice
+    __syncthreads();                       // the slices' tiles read: the heads' tiles take their place
     // The state terms, head by head: the rows (dy or x, exact bf16, staged
     // in LDS from whole-line loads) times the head's P x 64 operand (the
     // entering state or dS in bf16, staged k-major); both alternate between
@@ -1600,11 +1612,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
     constexpr int KS = P / 32;             // 32-long k-steps per head
     constexpr int PP = P * 8 / kBwdThreads;   // 16-byte operand pieces per thread
     static_assert(P % 32 == 0 && PP >= 1 && P * 8 % kBwdThreads == 0, "head operand pieces");
-    __shared__ __align__(16) bf16 kt[2][P * kKtPitch];
+    bf16 (*kt)[P * kKtPitch] = reinterpret_cast<bf16 (*)[P * kKtPitch]>(region);
     // the head's rows (dy or x) of the tile, P bf16 each (padded rows)
     constexpr int RPA = P + 8, PRA = P / 8, NPA = 64 * PRA / kBwdThreads;
     static_assert(64 * PRA % kBwdThreads == 0, "pieces of the row tile");
-    __shared__ __align__(16) bf16 ta[2][64 * RPA];
+    static_assert(2 * 64 * RPA * 2 == kTaBytes, "row tiles in the region");
+    bf16 (*ta)[64 * RPA] = reinterpret_cast<bf16 (*)[64 * RPA]>(region + kKtBytes);
     const bf16* K16 = which == 0 ? reinterpret_cast<const bf16*>(states_in) : dS16;
     const int h1 = h0 + hpg;
     // the chunk's rows (tokens past its end read zeros) and its heads'
@@ -1727,7 +1740,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_bc_group_kernel(
       step(1, h + 1);
     }
     if (h < h1) step(0, h);                // an odd group's last head
-    quarter_to_thread(q, d, acc, As, Bs);
+    quarter_to_thread(q, d, acc, reinterpret_cast<float*>(region),   // its first barrier ends the heads
+                      reinterpret_cast<float*>(region) + 32 * kGemmPitch);
   } else {
     if (which == 0) {                      // dC rows m0..m0+63: s runs to the tile's last row
       // rows l of the summed dCB (columns s <= l), rows s of B
