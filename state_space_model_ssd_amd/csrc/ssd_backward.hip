@@ -1441,14 +1441,22 @@ __global__ __launch_bounds__(64 * kDxWaves<L>) __attribute__((amdgpu_waves_per_e
 }
 
 // 3b'. The group's dCB: the HB partial sums of 3a added, four entries per
-// thread (entries above the diagonal or past the chunk are summed too and
-// never read): into the first partial, or, given dcb16 (bf16 inputs),
-// rounded once to bf16 there.  grid (ceil(L*L / 1024), G, chunk slots).
+// thread: into the first partial, or, given dcb16 (bf16 inputs), rounded
+// once to bf16 there.  Only the 64 x 64 tiles on or below the diagonal,
+// the ones 3a writes and 4 reads (entries above the diagonal inside them
+// or past the chunk are summed too and never read): kDcbBlocksPerTile
+// workgroups per tile, the tiles in row order, a wave on 4 rows x 64
+// columns.  grid (L/64 (L/64 + 1) / 2 * kDcbBlocksPerTile, G, chunk slots).
+constexpr int kDcbBlocksPerTile = 64 * 64 / 4 / kBwdThreads;
 template <int L>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dcb_sum_kernel(int G, int HB, float* __restrict__ dcbp,
                                                                   bf16* __restrict__ dcb16) {
-  const int e = blockIdx.x * kBwdThreads + threadIdx.x;
-  if (e >= L * L / 4) return;
+  const int t = blockIdx.x / kDcbBlocksPerTile;   // the t-th tile on or below the diagonal
+  int ti = 0;
+  while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+  const int tj = t - ti * (ti + 1) / 2;
+  const int i = (blockIdx.x % kDcbBlocksPerTile) * kBwdThreads + threadIdx.x;   // 0 .. 1023 in the tile
+  const int e = ((ti * 64 + i / 16) * L + tj * 64 + (i % 16) * 4) / 4;
   const int64_t LL4 = (int64_t)L * L / 4, jg = (int64_t)blockIdx.z * G + blockIdx.y;
   float4* W = reinterpret_cast<float4*>(dcbp) + jg * HB * LL4 + e;
   float4 v = W[0];
@@ -2017,7 +2025,7 @@ hipError_t launch_backward(const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
                        dim3(kBwdThreads), 0, s, cm, mc, x, dy, cb, a.delta, a.dAcs, H, G, HB, b.dcb,
                        b.rowpart, b.colpart, b.ddot);
   if (HB > 1)
-    hipLaunchKernelGGL((bwd_dcb_sum_kernel<L>), dim3((L * L / 4 + kBwdThreads - 1) / kBwdThreads, G, mc),
+    hipLaunchKernelGGL((bwd_dcb_sum_kernel<L>), dim3(LT * (LT + 1) / 2 * kDcbBlocksPerTile, G, mc),
                        dim3(kBwdThreads), 0, s, G, HB, b.dcb, sizeof(T) == 2 ? static_cast<bf16*>(b.dcb16) : nullptr);
   hipLaunchKernelGGL((bwd_bc_group_kernel<T, P, N, L>), dim3(xcd_grid(mc, LT * NT * 2 * G)),
                      dim3(kBwdThreads), 0, s, cm, mc, x, B, C, dy, a.delta, a.dAcs, hin, b.dS,
